@@ -1,0 +1,235 @@
+"""Plain fp64 CPU oracle of the Range-Doppler (RD) focusing chain.
+
+TEST INFRASTRUCTURE ONLY.  This module is the parity reference for the HIP library.  Only the
+test suite, the package's smoke check and the benchmark's CPU-baseline leg may import it; the
+library itself never calls it and shares no code, table or constant generator with it.
+
+Every function is the textbook definition of its step, written for a reader to check by eye:
+no blocking, fusion or reordering beyond what the definition states.  NumPy's FFT is used as a
+library primitive.  All arithmetic is float64 / complex128; the raw echo is upcast on entry.
+
+Page references (the source pages, by site and section):
+  [SAR-GPU]  nxmr.cn/news/101525 -- "ultra-high-resolution airborne SAR imaging on GPU"
+  [M1-RD]    cf-1.com/news/2323550 -- "SAR imaging acceleration on Apple Silicon"
+  [BP-GPU]   framerc.cn/news/4459478 -- "GPU back-projection SAR imaging"
+
+Readings of points the pages leave open (sign conventions, replica placement, window, RCMC
+model, azimuth filter form) are stated at each function.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import i0 as bessel_i0
+
+C_LIGHT = 299_792_458.0
+
+
+# ----------------------------------------------------------------------------------------------
+# Parameters: the same fields as the library's parameter block.
+# ----------------------------------------------------------------------------------------------
+def _p(params, name):
+    return params[name] if isinstance(params, dict) else getattr(params, name)
+
+
+def range_spacing(params) -> float:
+    """Slant-range spacing of one range sample, dr = c / (2 Fs)."""
+    return C_LIGHT / (2.0 * _p(params, "fs_hz"))
+
+
+def replica_length(params) -> int:
+    """L = ceil(Tp * Fs) samples in the transmitted pulse (tolerant to binary rounding)."""
+    return int(math.ceil(_p(params, "pulse_s") * _p(params, "fs_hz") - 1e-6))
+
+
+def wavelength(params) -> float:
+    return C_LIGHT / _p(params, "carrier_hz")
+
+
+# ----------------------------------------------------------------------------------------------
+# Range compression.  [SAR-GPU] §2.1 states the CPU form y = ifft(fft(x) * fft(h)) per line with a
+# precomputed chirp spectrum; [M1-RD] §2.1 / §3.1: FFT per line, multiply by the precomputed
+# matched filter, IFFT.  Reading: the matched filter is the conjugate spectrum of the replica
+# (correlation with the transmitted pulse), replica at indices [0, L) of the Nr buffer, forward
+# transform e^{-j...} unnormalised, inverse with 1/N (NumPy convention).
+# ----------------------------------------------------------------------------------------------
+def replica_window(L: int, kind: int) -> np.ndarray:
+    """0 = rectangular, 1 = symmetric Hamming 0.54 - 0.46 cos(2 pi n / (L-1)).
+
+    [BP-GPU] §3.1: an unweighted matched filter has about -13 dB sidelobes; Hamming lowers them
+    at the cost of a 1.3-1.5x wider mainlobe.  The window is applied to the replica."""
+    n = np.arange(L, dtype=np.float64)
+    if kind == 0:
+        return np.ones(L)
+    if kind == 1:
+        return 0.54 - 0.46 * np.cos(2.0 * np.pi * n / (L - 1))
+    raise ValueError(f"unknown window {kind}")
+
+
+def chirp_replica(params) -> np.ndarray:
+    """h[n] = w[n] * exp(j pi Kr (n/Fs - Tp/2)^2), n < L; up-chirp Kr = B / Tp."""
+    Tp, B, Fs = _p(params, "pulse_s"), _p(params, "bandwidth_hz"), _p(params, "fs_hz")
+    L = replica_length(params)
+    t = np.arange(L, dtype=np.float64) / Fs
+    return replica_window(L, _p(params, "range_window")) * np.exp(1j * np.pi * (B / Tp) * (t - Tp / 2) ** 2)
+
+
+def matched_filter(params) -> np.ndarray:
+    """H[k] = conj(FFT_Nr(h zero-padded to Nr))."""
+    Nr = _p(params, "Nr")
+    h = np.zeros(Nr, np.complex128)
+    rep = chirp_replica(params)
+    if rep.size > Nr:
+        raise ValueError("replica longer than the range line")
+    h[:rep.size] = rep
+    return np.conj(np.fft.fft(h))
+
+
+def range_compress(echo: np.ndarray, params) -> np.ndarray:
+    """rc[m] = IFFT(FFT(echo[m]) * H) for every line m (circular correlation with the replica)."""
+    H = matched_filter(params)
+    x = np.asarray(echo, dtype=np.complex128)
+    return np.fft.ifft(np.fft.fft(x, axis=1) * H[None, :], axis=1)
+
+
+# ----------------------------------------------------------------------------------------------
+# Azimuth processing.  [M1-RD] §2.1 / §5.1: azimuth FFT, range cell migration correction (RCMC)
+# by sinc interpolation, multiply by the azimuth matched filter, azimuth IFFT.  [SAR-GPU] §2.2:
+# RCMC looks up each output at the migrated slant range of a hyperbolic history and interpolates.
+# ----------------------------------------------------------------------------------------------
+def azimuth_fft(rc: np.ndarray) -> np.ndarray:
+    """S[k][n] = sum_m rc[m][n] e^{-j 2 pi k m / Na}: forward DFT down every range bin."""
+    return np.fft.fft(rc, axis=0)
+
+
+def doppler_freqs(params) -> np.ndarray:
+    """Doppler of azimuth bin k: NumPy fftfreq order (zero squint, centroid 0)."""
+    return np.fft.fftfreq(_p(params, "Na"), 1.0 / _p(params, "prf_hz"))
+
+
+def migration_factor(params) -> np.ndarray:
+    """D_k = sqrt(1 - (lambda f_k / (2 V))^2), the cosine of the squint angle seen at Doppler f_k."""
+    u = (wavelength(params) * doppler_freqs(params) / (2.0 * _p(params, "velocity_mps"))) ** 2
+    if np.any(u >= 1.0):
+        raise ValueError("Doppler band exceeds the velocity-limited maximum")
+    return np.sqrt(1.0 - u)
+
+
+def bin_range(params, n) -> np.ndarray:
+    """R(n) = range_bin0 + n dr: slant range of range bin n (leading-edge convention)."""
+    return _p(params, "range_bin0_m") + np.asarray(n, dtype=np.float64) * range_spacing(params)
+
+
+def rcmc_shift(params, n) -> np.ndarray:
+    """Delta[k][i] = R(n_i) (1/D_k - 1) / dr  (samples), for range bins n.
+
+    A target at closest range R0 appears at range R0 / D_k in Doppler bin k, so output bin n
+    reads the input at x = n + Delta.  Evaluated as R u / (D (1 + D)) / dr, which equals
+    R (1/D - 1) / dr without the cancellation of 1/D - 1 near D = 1."""
+    D = migration_factor(params)
+    u = 1.0 - D * D
+    q = u / (D * (1.0 + D))
+    return bin_range(params, n)[None, :] * q[:, None] / range_spacing(params)
+
+
+def kaiser_sinc(t: np.ndarray, taps: int, beta: float) -> np.ndarray:
+    """Kaiser-windowed sinc kernel value at offset t (|t| <= taps/2), before normalisation:
+    sinc(t) * I0(beta sqrt(1 - (t / (taps/2))^2)) / I0(beta)."""
+    half = taps / 2.0
+    arg = np.clip(1.0 - (t / half) ** 2, 0.0, None)
+    return np.sinc(t) * bessel_i0(beta * np.sqrt(arg)) / bessel_i0(beta)
+
+
+def rcmc(S: np.ndarray, shift: np.ndarray, taps: int = 8, beta: float = 2.5,
+         out_bins=None, in_bins=None, Nr: int | None = None) -> np.ndarray:
+    """RCMC by interpolation along range in the range-Doppler domain.
+
+    out[k][i] = sum_{j=-(taps/2-1)}^{taps/2} w_j S[k][floor(x) + j],  x = n_i + shift[k][i],
+    w_j = kaiser_sinc(x - floor(x) - j) / (sum of the taps weights); samples outside [0, Nr)
+    are zero.
+
+    By default S holds every range bin and every bin is an output.  For sampled evaluation,
+    column c of S holds global range bin in_bins[c] (sorted) and out_bins lists the global
+    range bins to produce; a needed bin missing from in_bins is an error."""
+    Na, W = S.shape
+    Nr = W if Nr is None else Nr
+    out_bins = np.arange(Nr) if out_bins is None else np.asarray(out_bins)
+    column_of = np.full(Nr, -1, np.int64)          # global range bin -> column of S
+    column_of[np.arange(W) if in_bins is None else np.asarray(in_bins)] = np.arange(W)
+    x = out_bins[None, :].astype(np.float64) + shift
+    i0 = np.floor(x).astype(np.int64)
+    frac = x - i0
+    half = taps // 2
+    acc = np.zeros(x.shape, np.complex128)
+    wsum = np.zeros(x.shape, np.float64)
+    for j in range(-(half - 1), half + 1):
+        idx = i0 + j
+        w = kaiser_sinc(frac - j, taps, beta)
+        wsum += w
+        inside = (idx >= 0) & (idx < Nr)
+        col = column_of[np.clip(idx, 0, Nr - 1)]
+        if np.any(inside & (col < 0)):
+            raise ValueError("RCMC input columns do not cover a needed range bin")
+        vals = np.take_along_axis(S, np.maximum(col, 0), axis=1)
+        acc += np.where(inside, w, 0.0) * vals
+    return acc / wsum
+
+
+def azimuth_matched_filter(params, n) -> np.ndarray:
+    """Haz[k][i] = exp(+j 4 pi R(n_i) D_k / lambda).
+
+    After RCMC a target at R0 carries the range-Doppler phase exp(-j 4 pi R0 D_k / lambda)
+    (stationary phase of the hyperbolic history); the filter removes it.  Phase-only,
+    range-dependent, unwindowed."""
+    D = migration_factor(params)
+    phase = 4.0 * np.pi * bin_range(params, n)[None, :] * D[:, None] / wavelength(params)
+    return np.exp(1j * phase)
+
+
+def azimuth_ifft(Z: np.ndarray) -> np.ndarray:
+    """img[m][n] = (1/Na) sum_k Z[k][n] e^{+j 2 pi k m / Na}."""
+    return np.fft.ifft(Z, axis=0)
+
+
+# ----------------------------------------------------------------------------------------------
+# Whole chain.
+# ----------------------------------------------------------------------------------------------
+def focus_stages(echo: np.ndarray, params) -> dict:
+    """Every intermediate of the chain, [Na][Nr] layout (rows = pulses or Doppler bins)."""
+    Nr = _p(params, "Nr")
+    n = np.arange(Nr)
+    rc = range_compress(echo, params)
+    S = azimuth_fft(rc)
+    R = rcmc(S, rcmc_shift(params, n), _p(params, "rcmc_taps"), _p(params, "kaiser_beta"))
+    Z = R * azimuth_matched_filter(params, n)
+    img = azimuth_ifft(Z)
+    return {"rc": rc, "azfft": S, "rcmc": R, "img": img}
+
+
+def focus(echo: np.ndarray, params) -> np.ndarray:
+    """Focused complex image [Na][Nr]."""
+    return focus_stages(echo, params)["img"]
+
+
+def focus_columns(echo: np.ndarray, params, out_bins, block_rows: int = 1024):
+    """Image columns img[:, out_bins] from the same definitions, for scenes too large to focus
+    whole.  Range compression runs line by line and keeps only the range bins that the RCMC of
+    the requested outputs reads; azimuth FFT, RCMC, filter and IFFT then run on those columns.
+    Returns (columns [Na][len(bins)], bins) with bins = sorted unique out_bins."""
+    Na, Nr = _p(params, "Na"), _p(params, "Nr")
+    taps = _p(params, "rcmc_taps")
+    out_bins = np.asarray(sorted(set(int(b) for b in out_bins)))
+    shift = rcmc_shift(params, out_bins)
+    reach = int(np.ceil(shift.max())) + 1
+    need = set()
+    for n in out_bins:
+        need.update(range(max(0, n - taps // 2), min(Nr, n + taps // 2 + reach + 1)))
+    in_bins = np.asarray(sorted(need))
+    rc_cols = np.empty((Na, in_bins.size), np.complex128)
+    for m0 in range(0, Na, block_rows):
+        blk = range_compress(echo[m0:m0 + block_rows], params)
+        rc_cols[m0:m0 + block_rows] = blk[:, in_bins]
+    S = azimuth_fft(rc_cols)
+    R = rcmc(S, shift, taps, _p(params, "kaiser_beta"), out_bins=out_bins, in_bins=in_bins, Nr=Nr)
+    return azimuth_ifft(R * azimuth_matched_filter(params, out_bins)), out_bins

@@ -1,0 +1,289 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix (CPU only, no GPU).
+
+Each test ties an oracle function to something other than itself: hand-worked DFT pairs, a
+naive O(N^2) DFT, the time-domain correlation that range compression must equal, closed-form
+point-response figures, exact special cases of the interpolator, the range-Doppler migration
+that the scene simulator's independent forward model produces, and invariants of the chain.
+A plausible mistake (dropped conjugate, wrong sign of a shift or of a phase, transposed axis,
+off-by-one tap window, missing normalisation) fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import metrics as M
+from oracle import rd_oracle as O
+from rdscene import C1, C2, C3, C4, SceneConfig, make_scene
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+THEORY = json.load(open(os.path.join(GOLD, "point_response_theory.json")))
+
+# C3's azimuth geometry (9.6 GHz, PRF 1.5 kHz, 150 m/s, 10 km, 4096 pulses) with a shorter pulse
+# (1 us -> 360 samples) so the range axis is small enough for CPU tests; range resolution as C3.
+C3_AZ = C3.with_(name="c3_azimuth_geometry", Nr=512, pulse_s=1e-6, n_targets=1, noise_power=0.0)
+# A geometry with large migration (L band, 200 m/s, 3 km, 3.4 s aperture: ~15 samples RCM).
+BIG = SceneConfig(name="large_migration", Na=4096, Nr=1024, pulse_s=2e-6, bandwidth_hz=100e6,
+                  fs_hz=120e6, window="rect", n_targets=2, noise_power=0.0, seed=11,
+                  carrier_hz=1.0e9, prf_hz=600.0, velocity_mps=200.0, r_ref_m=3000.0,
+                  sep_range=9, sep_az=100)
+
+
+def naive_dft(x, sign=-1.0):
+    N = x.shape[0]
+    n = np.arange(N)
+    return np.exp(sign * 2j * np.pi * np.outer(n, n) / N) @ x
+
+
+def single_chirp(cfg, window, n0):
+    """One noiseless line holding the unweighted pulse at integer delay n0."""
+    p = cfg.plan_params()
+    p["range_window"] = window
+    L = cfg.replica_len
+    t = np.arange(L) / cfg.fs_hz
+    x = np.zeros((1, cfg.Nr), np.complex128)
+    x[0, n0:n0 + L] = np.exp(1j * np.pi * (cfg.bandwidth_hz / cfg.pulse_s) * (t - cfg.pulse_s / 2) ** 2)
+    return p, x
+
+
+@pytest.fixture(scope="module")
+def c3az():
+    sc = make_scene(C3_AZ, noise=False)
+    return sc, O.focus_stages(sc.echo, C3_AZ.plan_params())
+
+
+@pytest.fixture(scope="module")
+def big():
+    sc = make_scene(BIG, noise=False)
+    return sc, O.focus_stages(sc.echo, BIG.plan_params())
+
+
+# ---------------------------------------------------------------- transforms
+def test_dft_hand_worked_pairs():
+    for case in json.load(open(os.path.join(GOLD, "dft_small.json")))["cases"]:
+        x = np.array([complex(*v) for v in case["x"]])
+        X = np.array([complex(*v) for v in case["X"]])
+        np.testing.assert_allclose(O.azimuth_fft(x[:, None])[:, 0], X, atol=1e-12)
+        np.testing.assert_allclose(O.azimuth_ifft(X[:, None])[:, 0], x, atol=1e-12)
+
+
+@pytest.mark.parametrize("N", list(range(1, 65)) + [240, 256, 375, 400])
+def test_azimuth_transforms_match_naive_dft(N):
+    rng = np.random.default_rng(N)
+    x = rng.standard_normal((N, 3)) + 1j * rng.standard_normal((N, 3))
+    X = naive_dft(x)
+    np.testing.assert_allclose(O.azimuth_fft(x), X, rtol=0, atol=1e-11 * max(1, np.abs(X).max()))
+    np.testing.assert_allclose(O.azimuth_ifft(X), naive_dft(X, +1.0) / N, atol=1e-11 * max(1, np.abs(x).max()))
+
+
+def test_inverse_identity_and_parseval():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((4096, 2)) + 1j * rng.standard_normal((4096, 2))
+    X = O.azimuth_fft(x)
+    np.testing.assert_allclose(O.azimuth_ifft(X), x, atol=1e-14 * 64)
+    # cf-1.com/news/2323550 §3.2: IFFT(x) = (1/N) conj(FFT(conj(x)))
+    np.testing.assert_allclose(np.conj(O.azimuth_fft(np.conj(X))) / 4096, O.azimuth_ifft(X), atol=1e-13)
+    assert abs(np.sum(np.abs(X) ** 2) / 4096 / np.sum(np.abs(x) ** 2) - 1) < 1e-13
+
+
+# ---------------------------------------------------------------- range compression
+def test_range_compression_is_circular_correlation_with_replica():
+    p = dict(Na=3, Nr=40, pulse_s=1e-7, bandwidth_hz=80e6, fs_hz=120e6, range_window=1)
+    h = O.chirp_replica(p)
+    assert h.size == 12
+    rng = np.random.default_rng(3)
+    echo = rng.standard_normal((3, 40)) + 1j * rng.standard_normal((3, 40))
+    brute = np.zeros_like(echo)
+    for m in range(3):
+        for i in range(40):
+            brute[m, i] = sum(echo[m, (i + n) % 40] * np.conj(h[n]) for n in range(h.size))
+    np.testing.assert_allclose(O.range_compress(echo, p), brute, atol=1e-12)
+
+
+def test_replica_is_windowed_up_chirp():
+    p = C2.plan_params()
+    h = O.chirp_replica(p)
+    L = C2.replica_len
+    assert h.size == L == 1200
+    n = np.arange(L)
+    np.testing.assert_allclose(np.abs(h), 0.54 - 0.46 * np.cos(2 * np.pi * n / (L - 1)), atol=1e-14)
+    # instantaneous frequency rises linearly from -B/2 to +B/2 (up-chirp, Kr = B/Tp)
+    f_inst = np.angle(h[1:] * np.conj(h[:-1])) * C2.fs_hz / (2 * np.pi)
+    mid = (n[1:] + n[:-1]) / 2 / C2.fs_hz - C2.pulse_s / 2
+    np.testing.assert_allclose(f_inst, C2.bandwidth_hz / C2.pulse_s * mid, atol=1e-3)
+    assert C4.replica_len == 1758 and C3.replica_len == 1800 and C1.replica_len == 240
+
+
+@pytest.mark.parametrize("cfg", [C1, C2, C3, C4], ids=lambda c: c.name)
+def test_compressed_chirp_matches_closed_forms(cfg):
+    n0 = min(17, cfg.Nr - cfg.replica_len)
+    L = cfg.replica_len
+    irw = {}
+    for window in (0, 1):
+        p, x = single_chirp(cfg, window, n0)
+        rc = O.range_compress(x, p)[0]
+        k = int(np.argmax(np.abs(rc)))
+        assert k == n0
+        peak = L if window == 0 else 0.54 * L - 0.46
+        assert abs(abs(rc[k]) / peak - 1) < 1e-9
+        met = M.cut_metrics(rc[(k + np.arange(-32, 32)) % cfg.Nr])
+        irw[window] = met["irw"]
+        if window == 0:
+            assert abs(met["pslr_db"] - THEORY["sinc_pslr_db"]) < THEORY["sinc_pslr_tol_db"]
+            assert abs(met["islr_db"] - THEORY["sinc_islr_window64_db"]) < THEORY["sinc_islr_tol_db"]
+            want = THEORY["sinc_irw_factor"] * cfg.fs_hz / cfg.bandwidth_hz
+            assert abs(met["irw"] / want - 1) < THEORY["sinc_irw_rel_tol"]
+        else:
+            lo, hi = THEORY["hamming_pslr_db_range"]
+            assert lo < met["pslr_db"] < hi
+    lo, hi = THEORY["hamming_irw_ratio_range"]
+    assert lo < irw[1] / irw[0] < hi
+
+
+# ---------------------------------------------------------------- RCMC interpolator
+def _rd_field(rows=6, cols=64, seed=0):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((rows, cols)) + 1j * rng.standard_normal((rows, cols))
+
+
+def test_rcmc_zero_shift_is_identity():
+    S = _rd_field()
+    np.testing.assert_allclose(O.rcmc(S, np.zeros(S.shape)), S, rtol=0, atol=1e-14)
+
+
+def test_rcmc_integer_shift_is_exact_shift_with_zero_fill():
+    S = _rd_field()
+    for s in (1, 3, -2):
+        out = O.rcmc(S, np.full(S.shape, float(s)))
+        want = np.zeros_like(S)
+        if s > 0:
+            want[:, :-s] = S[:, s:]
+        else:
+            want[:, -s:] = S[:, :s]
+        np.testing.assert_allclose(out, want, atol=1e-15)
+
+
+def test_rcmc_keeps_a_constant_field_constant_away_from_edges():
+    S = np.full((4, 64), 2.0 - 1.0j)
+    rng = np.random.default_rng(1)
+    out = O.rcmc(S, rng.uniform(0, 3, S.shape))
+    np.testing.assert_allclose(out[:, 4:-8], 2.0 - 1.0j, atol=1e-14)
+
+
+def test_rcmc_interpolates_a_bandlimited_signal_at_the_shifted_position():
+    # Output bin n must read the input at n + shift (not n - shift), from taps floor(x)-3..+4.
+    n = np.arange(128)
+    for nu, tol in ((0.01, 2e-3), (0.03, 1e-2)):        # a reversed shift errs by >= 0.026 / 0.078
+        S = np.exp(2j * np.pi * nu * n)[None, :].repeat(3, 0)
+        for frac in (0.2, 0.5, 0.77, 2.4):
+            out = O.rcmc(S, np.full(S.shape, frac))
+            want = np.exp(2j * np.pi * nu * (n + frac))
+            assert np.max(np.abs(out[:, 8:-12] - want[8:-12])) < tol
+
+
+def test_rcmc_weights_symmetric_at_half_sample():
+    j = np.arange(-3, 5)
+    w = O.kaiser_sinc(0.5 - j, 8, 2.5)
+    np.testing.assert_allclose(w, w[::-1], atol=1e-15)
+    # beta = 0 is the plain truncated sinc
+    np.testing.assert_allclose(O.kaiser_sinc(0.3 - j, 8, 0.0), np.sinc(0.3 - j), atol=1e-15)
+
+
+def test_rcmc_shift_matches_simulated_range_doppler_migration(big):
+    """In Doppler bin k the compressed echo of a target at bin n_t peaks at n_t + Delta(n_t, k);
+    the simulator's independent hyperbolic forward model puts it there."""
+    sc, st = big
+    p = BIG.plan_params()
+    m, n = sc.targets[0]
+    S = st["azfft"]
+    shift = O.rcmc_shift(p, [n])[:, 0]
+    f = O.doppler_freqs(p)
+    half_band = BIG.velocity_mps ** 2 * 2 * (BIG.aperture_pulses / BIG.prf_hz / 2) / (BIG.wavelength * BIG.r_ref_m)
+    energy = np.abs(S[:, n - 8:n + 40]).max(1)
+    checked = 0
+    for k in range(0, BIG.Na, 7):
+        if abs(f[k]) > 0.8 * half_band or energy[k] < 0.3 * energy.max():
+            continue
+        u = M.upsample(S[k, n - 8:n + 40], 32)
+        pos = np.argmax(np.abs(u)) / 32 + n - 8
+        assert abs(pos - (n + shift[k])) < 0.1, (k, pos, n + shift[k])
+        checked += 1
+    assert checked > 100 and shift[np.abs(f) <= 0.8 * half_band].max() > 8
+
+
+# ---------------------------------------------------------------- whole chain
+def test_lone_targets_focus_at_predicted_pixels(c3az, big):
+    for sc, st in (c3az, big):
+        img = st["img"]
+        for (m, n) in sc.targets:
+            assert M.peak_near(img, m, n) == (m, n)
+    sc = make_scene(C1.with_(n_targets=1, noise_power=0.0), noise=False)
+    img = O.focus(sc.echo, C1.plan_params())
+    (m, n), = sc.targets
+    assert M.peak_near(img, m, n) == (m, n)
+
+
+def test_focused_point_response_matches_theory(c3az):
+    sc, st = c3az
+    (m, n), = sc.targets
+    pt = M.point_target(st["img"], m, n)
+    ta = C3_AZ.aperture_pulses / C3_AZ.prf_hz
+    ba = 2 * C3_AZ.velocity_mps ** 2 * ta / (C3_AZ.wavelength * (C3_AZ.range_bin0_m + n * C3_AZ.dr))
+    assert abs(pt["azimuth"]["pslr_db"] - THEORY["sinc_pslr_db"]) < 0.3
+    assert abs(pt["azimuth"]["irw"] / (0.886 * C3_AZ.prf_hz / ba) - 1) < 0.03
+    assert abs(pt["range"]["pslr_db"] - THEORY["sinc_pslr_db"]) < 0.3
+    assert abs(pt["range"]["irw"] / (0.886 * C3_AZ.fs_hz / C3_AZ.bandwidth_hz) - 1) < 0.03
+
+
+def test_missing_or_reversed_rcmc_or_mf_is_detected(big):
+    """Planted mistakes (on the CPU, in the oracle's own steps) degrade the focus visibly."""
+    sc, st = big
+    p = BIG.plan_params()
+    nn = np.arange(BIG.Nr)
+    m, n = sc.targets[0]
+    good = abs(st["img"][m, n])
+    S = st["azfft"]
+    H = O.azimuth_matched_filter(p, nn)
+    for R, Hf in ((O.rcmc(S, -O.rcmc_shift(p, nn)), H), (S, H), (st["rcmc"], np.conj(H))):
+        bad = O.azimuth_ifft(R * Hf)
+        assert np.abs(bad[m - 16:m + 17, n - 4:n + 5]).max() < 0.6 * good
+
+
+def test_chain_is_linear():
+    cfg = C1
+    a = make_scene(cfg).echo.astype(np.complex128)
+    b = make_scene(cfg.with_(seed=9)).echo.astype(np.complex128)
+    p = cfg.plan_params()
+    lhs = O.focus(0.7 * a - 1.3j * b, p)
+    rhs = 0.7 * O.focus(a, p) - 1.3j * O.focus(b, p)
+    assert M.rel_l2(lhs, rhs) < 1e-13
+
+
+def test_azimuth_processing_is_circularly_shift_equivariant():
+    cfg = C1
+    x = make_scene(cfg).echo
+    p = cfg.plan_params()
+    img = O.focus(x, p)
+    for s in (1, 37, -5):
+        np.testing.assert_allclose(O.focus(np.roll(x, s, axis=0), p), np.roll(img, s, axis=0),
+                                   atol=1e-12 * np.abs(img).max())
+
+
+def test_sampled_columns_equal_whole_image(c3az):
+    sc, st = c3az
+    bins = [0, 3, 100, 101, 250, 511]
+    cols, got_bins = O.focus_columns(sc.echo, C3_AZ.plan_params(), bins, block_rows=700)
+    assert list(got_bins) == sorted(bins)
+    np.testing.assert_allclose(cols, st["img"][:, got_bins], atol=1e-12 * np.abs(st["img"]).max())
+
+
+def test_metrics_ignore_a_linear_phase_ramp():
+    p, x = single_chirp(C3, 0, 17)
+    rc = O.range_compress(x, p)[0]
+    cut = rc[np.arange(-15, 49)]
+    ramp = cut * np.exp(1j * 2.3 * np.arange(64))
+    a, b = M.cut_metrics(cut), M.cut_metrics(ramp)
+    for key in ("pslr_db", "islr_db", "irw"):
+        assert abs(a[key] - b[key]) < 1e-6
+    assert M.rel_l2(cut * 1.001, cut) == pytest.approx(1e-3, rel=1e-9)
