@@ -1,0 +1,202 @@
+"""Benchmark of the Range-Doppler focusing path on one MI355X.
+
+One JSON line on stdout.  `value` is the headline: range-compression throughput in GB/s on the
+4096 lines x 4096 samples complex64 workload (TBP-1000 chirp, Hamming, 5 targets + unit
+clutter), counting one read and one write of every sample (2 * Na * Nr * 8 bytes per call).
+A step is one rd_range_compress call over one 4096 x 4096 batch, which for this workload is
+the whole hot path.  The line also reports the full focusing chain (rd_focus) on the
+4096 x 4096 airborne scene in Mpixel/s, with its fraction of the HBM roofline for the
+five-sweep and the compulsory byte models, and the CPU oracle timed on this host.
+
+Inputs are HBM-resident before timing starts; buffers rotate over 4 input/output pairs (1 GiB
+per workload) so successive steps do not replay from the 256 MB Infinity Cache.  Timing uses
+HIP events recorded on the stream the kernels are launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ROTATE = 4
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha1()
+    for f in ("fft_core.hpp", "rd_kernels.hip", "rd_kernels.hpp"):
+        with open(os.path.join(ROOT, "range_doppler_focusing_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def read_traffic(path: str, src_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    try:
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha1") != src_hash:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def time_steps(torch, fn, steps: int, warmup: int, stream):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+def cpu_oracle_rc(cfg, echo, runs: int = 3):
+    """The CPU oracle's range compression on the whole workload (NumPy fp64, one thread)."""
+    from oracle import rd_oracle as O
+    p = cfg.plan_params()
+    O.range_compress(echo[:64], p)
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        O.range_compress(echo, p)
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts)
+
+
+def cpu_oracle_focus(cfg, echo):
+    """The CPU oracle's whole chain (NumPy fp64, one thread) on the whole scene, one run."""
+    from oracle import rd_oracle as O
+    t0 = time.perf_counter()
+    O.focus_stages(echo, cfg.plan_params())
+    return time.perf_counter() - t0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
+    ap.add_argument("--only", choices=["rc", "focus"], default=None,
+                    help="run one workload only (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import range_doppler_focusing_amd as rdf
+    from rdscene import C2, C3, cached_scene
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    src_hash = kernel_source_hash()
+    out = {}
+
+    # ---------------------------------------------------------------- range compression (value)
+    cfg = C2
+    rc_ms = None
+    if args.only in (None, "rc"):
+        sc = cached_scene(cfg)
+        echo0 = torch.from_numpy(sc.echo).to("cuda")
+        ins = [echo0] + [echo0.clone() for _ in range(ROTATE - 1)]
+        outs = [torch.empty_like(echo0) for _ in range(ROTATE)]
+        plan = rdf.Plan(**cfg.plan_params())
+        rc_ms = time_steps(torch, lambda i: rdf.rd_range_compress(plan.handle, ins[i % ROTATE],
+                                                                  outs[i % ROTATE], stream),
+                           args.steps, args.warmup, stream)
+        plan.close()
+        del ins, outs, echo0
+        torch.cuda.empty_cache()
+    rc_bytes = 2 * cfg.Na * cfg.Nr * 8
+    rc_gbs = rc_bytes / (rc_ms * 1e-3) / 1e9 if rc_ms else None
+
+    # ---------------------------------------------------------------- full chain
+    fcfg = C3
+    focus_ms = None
+    if args.only in (None, "focus") and not args.no_focus:
+        fsc = cached_scene(fcfg)
+        e0 = torch.from_numpy(fsc.echo).to("cuda")
+        fins = [e0] + [e0.clone() for _ in range(ROTATE - 1)]
+        fouts = [torch.empty_like(e0) for _ in range(ROTATE)]
+        fplan = rdf.Plan(**fcfg.plan_params())
+        focus_ms = time_steps(torch, lambda i: rdf.rd_focus(fplan.handle, fins[i % ROTATE],
+                                                            fouts[i % ROTATE], stream),
+                              max(10, args.steps // 2), args.warmup, stream)
+        fplan.close()
+        del fins, fouts, e0
+        torch.cuda.empty_cache()
+    px = fcfg.Na * fcfg.Nr
+    mpx = px / (focus_ms * 1e-3) / 1e6 if focus_ms else None
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    cpu_focus = None
+    if not args.no_cpu and args.only is None:
+        cores = 1  # NumPy's FFT and the oracle's array code run on one thread
+        t = cpu_oracle_rc(cfg, cached_scene(cfg).echo)
+        cpu = {"value": rc_bytes / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"whole 4096x4096 range compression, median of 3 runs ({t:.2f} s each)"}
+        if focus_ms:
+            tf = cpu_oracle_focus(fcfg, cached_scene(fcfg).echo)
+            cpu_focus = {"value": px / tf / 1e6, "unit": "Mpixel/s", "cores": cores, "kind": "oracle",
+                         "sample": f"whole 4096x4096 rd focus, one run ({tf:.1f} s)"}
+
+    traffic = read_traffic(os.path.join(ROOT, "profiles", "range_compress_4096x4096_traffic.txt"), src_hash)
+    line = {
+        "metric": "range-compressed GB/s (% HBM peak) and RD-focused Mpixel/s, 4096x4096 c64",
+        "value": round(rc_gbs, 2) if rc_gbs else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(rc_ms, 5) if rc_ms else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "c64 (fp32 complex)",
+        "data": "synthetic (seeded point targets + Gaussian clutter)",
+        "config": {"workload": "range compression, 4096 lines x 4096 samples complex64, "
+                               "10 us / 100 MHz chirp at 120 MHz, Hamming",
+                   "Na": cfg.Na, "Nr": cfg.Nr, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(rc_gbs, 2) if rc_gbs else None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(rc_gbs / HBM_PEAK_GBS, 4) if rc_gbs else None,
+                     "traffic": traffic,
+                     "kernel": "k_range_compress<4096>",
+                     "algorithmic_bytes_per_launch": rc_bytes},
+        "cpu_baseline": cpu,
+        "rd_focus": None if not focus_ms else {
+            "workload": "full RD focusing, 4096 x 4096 complex64 airborne scene "
+                        "(9.6 GHz, 300 MHz, PRF 1.5 kHz, 150 m/s, 10 km, 16 targets)",
+            "ms_per_step": round(focus_ms, 4), "value": round(mpx, 1), "unit": "Mpixel/s",
+            "roofline_frac_80B_per_px": round(mpx * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4),
+            "roofline_frac_32B_per_px": round(mpx * 1e6 * 32 / (HBM_PEAK_GBS * 1e9), 4),
+            "cpu_baseline": cpu_focus},
+        "kernel_source_sha1": src_hash,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

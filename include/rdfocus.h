@@ -1,0 +1,144 @@
+/*
+ * rdfocus -- Range-Doppler SAR focusing on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The library focuses a raw SAR echo with the Range-Doppler chain:
+ *   range compression per pulse  : FFT along range, multiply by the precomputed matched filter
+ *                                  H(f), inverse FFT (one fused kernel, line resident in LDS);
+ *   azimuth processing per bin   : corner turn, azimuth FFT, range cell migration correction
+ *                                  (RCMC, 8-tap Kaiser-windowed sinc), azimuth matched filter,
+ *                                  azimuth inverse FFT, corner turn back.
+ * Sources: cf-1.com/news/2323550 ("SAR imaging acceleration on Apple Silicon") §2.1 (the RD
+ * steps), §3.1 (fused FFT -> filter -> IFFT per range line), §3.2 (inverse transform by
+ * conj-FFT-conj), §5.1 (azimuth FFT, sinc RCMC, azimuth filter + IFFT); nxmr.cn/news/101525
+ * ("ultra-high-resolution airborne SAR imaging on GPU") §2.1 (echo float2 [Na][Nr] and a chirp
+ * spectrum [Nr] precomputed on the host), §2.2 (RCMC along the hyperbolic slant range), §3.1
+ * (interleaved complex layout).
+ *
+ * Conventions (every call):
+ *  - Complex samples are interleaved float32 pairs (rd_c64), row-major [Na][Nr]: row m is the
+ *    m-th pulse (range line), column n the n-th range sample.  Outputs use the same layout.
+ *  - Data pointers are DEVICE pointers on the plan's device, 8-byte aligned, owned by the
+ *    caller; the library never frees them.  The plan owns its own filter, twiddle and
+ *    workspace buffers (about one image of workspace: Na*Nr*8 bytes).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work and return:
+ *    results are ready once the stream is synchronised.  Argument errors are reported
+ *    synchronously before anything is enqueued; launch errors are reported by the call;
+ *    faults inside a kernel surface at the caller's next synchronisation.
+ *  - A plan may be used by one stream at a time (it holds one workspace).  Calls must be made
+ *    with the plan's device current.
+ *  - No call aborts or throws; every call returns an rd_status.  rd_last_error() returns a
+ *    thread-local message describing the last failure on the calling thread.
+ *
+ * Forward transforms are unnormalised with kernel e^{-j 2 pi k n / N}; inverse transforms
+ * carry 1/N (folded into the filters).
+ */
+#ifndef RDFOCUS_H
+#define RDFOCUS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Interleaved complex float32 sample (nxmr.cn/news/101525 §3.1: real/imag adjacent). */
+typedef struct {
+  float re, im;
+} rd_c64;
+
+typedef enum {
+  RD_OK = 0,
+  RD_ERR_INVALID_ARG = -1,        /* bad pointer, size, alignment, aliasing or parameter   */
+  RD_ERR_UNSUPPORTED_LENGTH = -2, /* Na or Nr has no built transform (see rd_length_supported) */
+  RD_ERR_OUT_OF_MEMORY = -3,      /* device allocation for the plan failed                  */
+  RD_ERR_DEVICE = -4,             /* HIP runtime error, or the plan's device is not current  */
+  RD_ERR_LAUNCH = -5,             /* a kernel launch failed                                  */
+  RD_ERR_NOT_CONFIGURED = -6      /* azimuth call on a range-only plan                       */
+} rd_status;
+
+/* Weighting of the replica before its spectrum is taken (framerc.cn/news/4459478 §3.1:
+ * unweighted filters leave ~-13 dB sidelobes; Hamming lowers them and widens the mainlobe). */
+enum { RD_WINDOW_RECT = 0, RD_WINDOW_HAMMING = 1 };
+
+/* Problem statement.  Range: linear-FM up-chirp of duration pulse_s and bandwidth
+ * bandwidth_hz sampled at fs_hz; the replica holds L = ceil(pulse_s * fs_hz) samples at
+ * indices [0, L) of a range line, h[n] = w[n] exp(j pi (B/Tp) (n/Fs - Tp/2)^2), and
+ * H = conj(FFT_Nr(h)) is built in float64 on the host and rounded to float32 once.
+ * Azimuth (zero squint, Doppler centroid 0): carrier_hz, prf_hz and velocity_mps all > 0
+ * make a full-chain plan; all three == 0 make a range-only plan.  range_bin0_m is the slant
+ * range of range sample 0, so bin n lies at R(n) = range_bin0_m + n * c / (2 fs_hz).
+ * RCMC: rcmc_taps-point Kaiser(kaiser_beta)-windowed sinc, weights normalised to sum 1,
+ * samples outside the line taken as 0. */
+typedef struct {
+  int32_t Na;            /* pulses (azimuth lines); a supported transform length             */
+  int32_t Nr;            /* range samples per pulse; a supported transform length            */
+  double pulse_s;        /* Tp  > 0                                                          */
+  double bandwidth_hz;   /* B   > 0 (chirp rate +B/Tp)                                       */
+  double fs_hz;          /* Fs  > 0; requires L <= Nr                                        */
+  int32_t range_window;  /* RD_WINDOW_RECT or RD_WINDOW_HAMMING                              */
+  double carrier_hz;     /* f0 (wavelength c/f0), or 0 for a range-only plan                 */
+  double prf_hz;         /* pulse repetition frequency, or 0                                 */
+  double velocity_mps;   /* platform speed, or 0; requires (c/f0 * PRF / (4 V))^2 < 1        */
+  double range_bin0_m;   /* slant range of range sample 0 (ignored by range-only plans)      */
+  int32_t rcmc_taps;     /* 8 (the only interpolator length built)                           */
+  double kaiser_beta;    /* Kaiser window shape, 0 <= beta <= 12                             */
+  uint32_t flags;        /* reserved, must be 0                                              */
+} rd_params;
+
+typedef struct rd_plan rd_plan;
+
+/* Returns 1 if `n` is a transform length this build supports (256..16384 powers of two, and
+ * 6000 = 2^4 * 3 * 5^3), else 0. */
+int rd_length_supported(int32_t n);
+
+/* Validates `params`, builds the matched filter H (float64 -> float32), the twiddle and
+ * azimuth tables and the workspace on the current HIP device, and returns the plan in *out.
+ * On error *out is set to NULL and nothing is leaked. */
+rd_status rd_plan_create(const rd_params* params, rd_plan** out);
+
+/* Releases everything the plan owns; waits for the plan's outstanding work on the device.
+ * NULL is a no-op.  A destroyed plan must not be used again (detected where possible). */
+rd_status rd_plan_destroy(rd_plan* plan);
+
+/* Range compression of every pulse (cf-1.com/news/2323550 §3.1, §3.2; nxmr.cn/news/101525
+ * §2.1):  rc[m] = IFFT_Nr( FFT_Nr(echo[m]) * H ).  One fused kernel: each line is read from
+ * HBM once and written once.  echo == rc (in place) is allowed; other overlap is an error. */
+rd_status rd_range_compress(rd_plan* plan, const rd_c64* echo, rd_c64* rc, void* stream);
+
+/* Azimuth processing of range-compressed data rc [Na][Nr] into the focused image img
+ * [Na][Nr] (cf-1.com/news/2323550 §2.1, §5.1; nxmr.cn/news/101525 §2.2):
+ *   S[k][n]   = sum_m rc[m][n] e^{-j 2 pi k m / Na}                (azimuth FFT)
+ *   T[k][n]   = sum_{j=-3..4} w_j S[k][floor(x)+j],  x = n + R(n) (1/D_k - 1)/dr   (RCMC)
+ *   img[m][n] = (1/Na) sum_k T[k][n] exp(+j 4 pi R(n) D_k / lambda) e^{+j 2 pi k m / Na}
+ * with f_k the Doppler of bin k (FFT order), D_k = sqrt(1 - (lambda f_k / (2V))^2).
+ * rc == img is allowed.  RD_ERR_NOT_CONFIGURED on a range-only plan. */
+rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* stream);
+
+/* rd_range_compress followed by rd_azimuth_focus: raw echo to focused image.  echo == img is
+ * allowed.  RD_ERR_NOT_CONFIGURED on a range-only plan. */
+rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream);
+
+/* Test hook: the azimuth chain with its intermediates exposed.  azfft and rcmc receive the
+ * azimuth spectrum and the RCMC output in the corner-turned layout [Nr][Na] (row n = range
+ * bin, column k = Doppler bin); img receives the image [Na][Nr].  azfft, rcmc and img must be
+ * distinct from each other and from rc (img may equal rc). */
+rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft, rd_c64* rcmc,
+                                  rd_c64* img, void* stream);
+
+/* Test hook: `lines` independent transforms of length Na (axis = 0) or Nr (axis = 1), from
+ * in[lines][len] to out[lines][len] (in == out allowed): forward if inverse == 0, else the
+ * inverse including 1/len.  Uses the same LDS-resident transform as the focusing kernels. */
+rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const rd_c64* in,
+                            rd_c64* out, int64_t lines, void* stream);
+
+/* Static description of a status code. */
+const char* rd_status_string(rd_status status);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* rd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RDFOCUS_H */

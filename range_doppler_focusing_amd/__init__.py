@@ -1,0 +1,93 @@
+"""Range-Doppler SAR focusing on AMD MI355X (gfx950): Python binding of librdfocus.so.
+
+The compute path is the HIP library; this package only marshals arguments.  ``Plan`` wraps a
+plan handle and allocates outputs with torch (device memory and the current stream).  Functions
+with the C names (``rd_plan_create``, ``rd_range_compress``, ...) are re-exported from
+``_native``.
+"""
+from __future__ import annotations
+
+from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
+                      make_params, rd_azimuth_focus, rd_debug_azimuth_stages, rd_debug_line_fft,
+                      rd_focus, rd_last_error, rd_length_supported, rd_params, rd_plan_create,
+                      rd_plan_destroy, rd_range_compress, rd_status_string)
+
+
+class Plan:
+    """A focusing plan on the current HIP device (see include/rdfocus.h)."""
+
+    def __init__(self, **params):
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("a HIP device is required (torch.cuda.is_available() is False)")
+        self.params = dict(params)
+        self.Na = int(params["Na"])
+        self.Nr = int(params["Nr"])
+        self.device = torch.device("cuda", torch.cuda.current_device())
+        self.handle = rd_plan_create(make_params(**params))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            rd_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _check(self, x, shape=None):
+        import torch
+        if x.dtype != torch.complex64 or x.device != self.device or not x.is_contiguous():
+            raise ValueError(f"expected a contiguous complex64 tensor on {self.device}")
+        if shape is not None and tuple(x.shape) != tuple(shape):
+            raise ValueError(f"expected shape {shape}, got {tuple(x.shape)}")
+        return x
+
+    def _empty(self, shape):
+        import torch
+        return torch.empty(shape, dtype=torch.complex64, device=self.device)
+
+    def range_compress(self, echo, out=None):
+        self._check(echo, (self.Na, self.Nr))
+        out = self._empty((self.Na, self.Nr)) if out is None else self._check(out, (self.Na, self.Nr))
+        rd_range_compress(self.handle, echo, out)
+        return out
+
+    def azimuth_focus(self, rc, out=None):
+        self._check(rc, (self.Na, self.Nr))
+        out = self._empty((self.Na, self.Nr)) if out is None else self._check(out, (self.Na, self.Nr))
+        rd_azimuth_focus(self.handle, rc, out)
+        return out
+
+    def focus(self, echo, out=None):
+        self._check(echo, (self.Na, self.Nr))
+        out = self._empty((self.Na, self.Nr)) if out is None else self._check(out, (self.Na, self.Nr))
+        rd_focus(self.handle, echo, out)
+        return out
+
+    def azimuth_stages(self, rc):
+        """(azfft [Nr][Na], rcmc [Nr][Na], img [Na][Nr]) of the azimuth chain."""
+        self._check(rc, (self.Na, self.Nr))
+        az = self._empty((self.Nr, self.Na))
+        rcmc = self._empty((self.Nr, self.Na))
+        img = self._empty((self.Na, self.Nr))
+        rd_debug_azimuth_stages(self.handle, rc, az, rcmc, img)
+        return az, rcmc, img
+
+    def line_fft(self, x, axis: int, inverse: bool = False, out=None):
+        n = self.Na if axis == 0 else self.Nr
+        self._check(x)
+        if x.shape[-1] != n:
+            raise ValueError(f"last dimension must be {n}")
+        lines = x.numel() // n
+        out = self._empty(tuple(x.shape)) if out is None else self._check(out, tuple(x.shape))
+        rd_debug_line_fft(self.handle, axis, int(inverse), x, out, lines)
+        return out

@@ -1,0 +1,464 @@
+// LDS-resident line FFT for gfx950 (wave64, 160 KB LDS per CU).
+//
+// A line of N complex float32 points is transformed by a group of T threads.  Each pass is a
+// radix-R Stockham decimation-in-time step (the auto-sorting form, so no bit reversal):
+//   butterfly j (0 <= j < N/R) takes x[j + r N/R] (r < R), multiplies input r by
+//   W_{Ns R}^{(j mod Ns) r}, runs a length-R DFT and writes element r to
+//   (j / Ns) Ns R + (j mod Ns) + r Ns,  where Ns is the product of the earlier radices.
+// Between passes the line goes through one bank-padded LDS buffer; the first pass reads its
+// inputs straight from global memory and the last pass leaves its outputs in registers in
+// natural order (element j + r N/R_last), so a pointwise multiply and a second transform with
+// the radix list reversed can follow without another exchange.
+//
+// The inverse transform uses the same passes with the conjugate kernel e^{+j...}; in exact and
+// in round-to-nearest arithmetic this equals conj(FFT(conj(x))), the identity that
+// cf-1.com/news/2323550 §3.2 uses to share the forward code path.  1/N is folded into the
+// caller's filter.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rdf {
+
+// ---------------------------------------------------------------------------- complex helpers
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+__device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+// a * (S j) for S = +1 / -1
+template <int S>
+__device__ __forceinline__ float2 mul_j(float2 a) {
+  return S > 0 ? make_float2(-a.y, a.x) : make_float2(a.y, -a.x);
+}
+
+// The same global pointer, offset by an amount the compiler cannot see (always zero): table
+// loads behind it stay where they are written instead of being hoisted out of a line loop
+// into registers (hoisting H and every twiddle costs ~100 VGPRs and halves the occupancy).
+// Offsetting, rather than laundering the pointer itself, keeps its global address space.
+template <class T>
+__device__ __forceinline__ const T* opaque(const T* p) {
+  int zero = 0;
+  asm volatile("" : "+s"(zero));
+  return p + zero;
+}
+
+// ---------------------------------------------------------------------------- compile-time roots
+// cos / sin of 2 pi p / q in double precision, evaluated by the compiler: the angle is reduced
+// exactly (integer arithmetic) to [0, pi/4] and expanded in Taylor series there.
+constexpr double kPi = 3.141592653589793238462643383279502884;
+
+constexpr double ct_sin_small(double x) {
+  double term = x, sum = x;
+  for (int n = 1; n < 16; ++n) {
+    term *= -x * x / double((2 * n) * (2 * n + 1));
+    sum += term;
+  }
+  return sum;
+}
+constexpr double ct_cos_small(double x) {
+  double term = 1.0, sum = 1.0;
+  for (int n = 1; n < 16; ++n) {
+    term *= -x * x / double((2 * n - 1) * (2 * n));
+    sum += term;
+  }
+  return sum;
+}
+// (cos, sin) of 2 pi p / q
+struct CS {
+  double c, s;
+};
+constexpr CS ct_root(long p, long q) {
+  p %= q;
+  if (p < 0) p += q;
+  const long quad = (4 * p) / q;   // quadrant of the angle
+  const long rem = 4 * p - quad * q; // angle within the quadrant = (pi/2) rem / q
+  double c0 = 1.0, s0 = 0.0;
+  if (rem != 0) {
+    if (2 * rem <= q) {              // <= pi/4
+      const double x = (kPi / 2.0) * double(rem) / double(q);
+      c0 = ct_cos_small(x);
+      s0 = ct_sin_small(x);
+    } else {                         // use the complement angle
+      const double x = (kPi / 2.0) * double(q - rem) / double(q);
+      c0 = ct_sin_small(x);
+      s0 = ct_cos_small(x);
+    }
+  }
+  switch (quad) {
+    case 0: return {c0, s0};
+    case 1: return {-s0, c0};
+    case 2: return {-c0, -s0};
+    default: return {s0, -c0};
+  }
+}
+
+template <int N>
+struct Roots {
+  float c[N];
+  float s[N];
+  constexpr Roots() : c(), s() {
+    for (int k = 0; k < N; ++k) {
+      const CS v = ct_root(k, N);
+      c[k] = float(v.c);
+      s[k] = float(v.s);
+    }
+  }
+};
+template <int N>
+inline constexpr Roots<N> kRoots{};
+
+// x * W_N^e with W_N = e^{DIR j 2 pi / N}; e is a compile-time constant after unrolling, so
+// the branches fold and the root is an immediate.
+template <int N, int DIR>
+__device__ __forceinline__ float2 rot_const(float2 x, int e) {
+  e %= N;
+  if (e == 0) return x;
+  if (4 * e == N) return mul_j<DIR>(x);
+  if (2 * e == N) return make_float2(-x.x, -x.y);
+  if (4 * e == 3 * N) return mul_j<-DIR>(x);
+  const float c = kRoots<N>.c[e];
+  const float s = DIR > 0 ? kRoots<N>.s[e] : -kRoots<N>.s[e];
+  return cmul(x, make_float2(c, s));
+}
+
+// ---------------------------------------------------------------------------- small DFTs
+// In-place length-R DFT of v[0..R-1], natural order in and out, kernel e^{DIR j 2 pi kn/R}.
+template <int R, int DIR>
+struct Dft;
+
+template <int A, int B, int DIR>
+__device__ __forceinline__ void dft_ct(float2* v);
+
+template <int DIR>
+struct Dft<1, DIR> {
+  static __device__ __forceinline__ void run(float2*) {}
+};
+
+template <int DIR>
+struct Dft<2, DIR> {
+  static __device__ __forceinline__ void run(float2* v) {
+    const float2 a = v[0], b = v[1];
+    v[0] = cadd(a, b);
+    v[1] = csub(a, b);
+  }
+};
+
+template <int DIR>
+struct Dft<3, DIR> {
+  static __device__ __forceinline__ void run(float2* v) {
+    constexpr float h = 0.866025403784438646763723170752936183f;  // sin(2 pi / 3)
+    const float2 t = cadd(v[1], v[2]);
+    const float2 d = csub(v[1], v[2]);
+    const float2 m = make_float2(v[0].x - 0.5f * t.x, v[0].y - 0.5f * t.y);
+    const float2 jd = mul_j<DIR>(cscale(d, h));
+    v[0] = cadd(v[0], t);
+    v[1] = cadd(m, jd);
+    v[2] = csub(m, jd);
+  }
+};
+
+template <int DIR>
+struct Dft<4, DIR> {
+  static __device__ __forceinline__ void run(float2* v) {
+    const float2 t0 = cadd(v[0], v[2]), t1 = csub(v[0], v[2]);
+    const float2 t2 = cadd(v[1], v[3]), t3 = mul_j<DIR>(csub(v[1], v[3]));
+    v[0] = cadd(t0, t2);
+    v[2] = csub(t0, t2);
+    v[1] = cadd(t1, t3);
+    v[3] = csub(t1, t3);
+  }
+};
+
+template <int DIR>
+struct Dft<5, DIR> {
+  static __device__ __forceinline__ void run(float2* v) {
+    constexpr float c1 = 0.309016994374947424102293417182819059f;   // cos(2 pi / 5)
+    constexpr float c2 = -0.809016994374947424102293417182819059f;  // cos(4 pi / 5)
+    constexpr float s1 = 0.951056516295153572116439333379382143f;   // sin(2 pi / 5)
+    constexpr float s2 = 0.587785252292473129168705954639072769f;   // sin(4 pi / 5)
+    const float2 t1 = cadd(v[1], v[4]), d1 = csub(v[1], v[4]);
+    const float2 t2 = cadd(v[2], v[3]), d2 = csub(v[2], v[3]);
+    const float2 x0 = v[0];
+    const float2 a1 = make_float2(x0.x + c1 * t1.x + c2 * t2.x, x0.y + c1 * t1.y + c2 * t2.y);
+    const float2 a2 = make_float2(x0.x + c2 * t1.x + c1 * t2.x, x0.y + c2 * t1.y + c1 * t2.y);
+    const float2 b1 = mul_j<DIR>(make_float2(s1 * d1.x + s2 * d2.x, s1 * d1.y + s2 * d2.y));
+    const float2 b2 = mul_j<DIR>(make_float2(s2 * d1.x - s1 * d2.x, s2 * d1.y - s1 * d2.y));
+    v[0] = make_float2(x0.x + t1.x + t2.x, x0.y + t1.y + t2.y);
+    v[1] = cadd(a1, b1);
+    v[4] = csub(a1, b1);
+    v[2] = cadd(a2, b2);
+    v[3] = csub(a2, b2);
+  }
+};
+
+template <int DIR>
+struct Dft<8, DIR> {
+  static __device__ __forceinline__ void run(float2* v) { dft_ct<2, 4, DIR>(v); }
+};
+template <int DIR>
+struct Dft<15, DIR> {
+  static __device__ __forceinline__ void run(float2* v) { dft_ct<3, 5, DIR>(v); }
+};
+template <int DIR>
+struct Dft<16, DIR> {
+  static __device__ __forceinline__ void run(float2* v) { dft_ct<4, 4, DIR>(v); }
+};
+template <int DIR>
+struct Dft<25, DIR> {
+  static __device__ __forceinline__ void run(float2* v) { dft_ct<5, 5, DIR>(v); }
+};
+
+// Length A*B DFT in registers (one Cooley-Tukey split): input n = B n1 + n2, output
+// k = k1 + A k2; DFT_A over n1, twiddle W_{AB}^{n2 k1}, DFT_B over n2.
+template <int A, int B, int DIR>
+__device__ __forceinline__ void dft_ct(float2* v) {
+  constexpr int N = A * B;
+  float2 t[N];
+#pragma unroll
+  for (int n2 = 0; n2 < B; ++n2) {
+    float2 u[A];
+#pragma unroll
+    for (int n1 = 0; n1 < A; ++n1) u[n1] = v[B * n1 + n2];
+    Dft<A, DIR>::run(u);
+#pragma unroll
+    for (int k1 = 0; k1 < A; ++k1) t[k1 * B + n2] = rot_const<N, DIR>(u[k1], n2 * k1);
+  }
+#pragma unroll
+  for (int k1 = 0; k1 < A; ++k1) {
+    float2 u[B];
+#pragma unroll
+    for (int n2 = 0; n2 < B; ++n2) u[n2] = t[k1 * B + n2];
+    Dft<B, DIR>::run(u);
+#pragma unroll
+    for (int k2 = 0; k2 < B; ++k2) v[k1 + A * k2] = u[k2];
+  }
+}
+
+// ---------------------------------------------------------------------------- pass machinery
+template <int... Rs>
+struct IntList {};
+
+template <class L>
+struct ListInfo;
+template <int R>
+struct ListInfo<IntList<R>> {
+  static constexpr int first = R, last = R, product = R;
+};
+template <int R, int R2, int... Rs>
+struct ListInfo<IntList<R, R2, Rs...>> {
+  static constexpr int first = R;
+  static constexpr int last = ListInfo<IntList<R2, Rs...>>::last;
+  static constexpr int product = R * ListInfo<IntList<R2, Rs...>>::product;
+};
+
+// One pad element after every 16 keeps the strided Stockham writes off a single LDS bank.
+__device__ __forceinline__ int lpad(int i) { return i + (i >> 4); }
+constexpr int lds_len(int n) { return n + n / 16 + 1; }
+// lpad(base + r * STRIDE) written so that, for the strides that occur, it is one per-thread
+// base plus a compile-time offset (an LDS instruction's immediate), not a fresh shift-and-add
+// per element.  Exact when STRIDE % 16 == 0, or when base % 16 + r * STRIDE < 16.
+template <int STRIDE, bool BASE_ALIGNED16_R_FITS>
+__device__ __forceinline__ int lpad_step(int padded_base, int base, int r) {
+  if constexpr (STRIDE % 16 == 0) {
+    return padded_base + r * (STRIDE + STRIDE / 16);
+  } else if constexpr (BASE_ALIGNED16_R_FITS) {
+    return padded_base + r * STRIDE;
+  } else {
+    return lpad(base + r * STRIDE);
+  }
+}
+
+// Registers a thread needs for a radix-R pass: ceil(N/R / T) butterflies of R points.
+constexpr int pass_regs(int N, int T, int R) { return ((N / R + T - 1) / T) * R; }
+template <int N, int T, class L>
+struct MaxRegs;
+template <int N, int T, int R>
+struct MaxRegs<N, T, IntList<R>> {
+  static constexpr int value = pass_regs(N, T, R);
+};
+template <int N, int T, int R, int R2, int... Rs>
+struct MaxRegs<N, T, IntList<R, R2, Rs...>> {
+  static constexpr int a = pass_regs(N, T, R), b = MaxRegs<N, T, IntList<R2, Rs...>>::value;
+  static constexpr int value = a > b ? a : b;
+};
+
+// Register layout of a radix-R pass: v[b*R + r] holds element j + r*N/R, j = tid + b*T.
+template <int N, int T, int R>
+struct Geom {
+  static constexpr int NB = N / R;
+  static constexpr int B = (NB + T - 1) / T;
+  static constexpr bool FULL = (NB % T) == 0;
+  static __device__ __forceinline__ bool live(int j) { return FULL || j < NB; }
+};
+
+template <int N, int T, int R>
+__device__ __forceinline__ void load_global(float2* v, const float2* __restrict__ src, int tid) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[b * R + r] = src[j + r * G::NB];
+    }
+  }
+}
+
+template <int N, int T, int R>
+__device__ __forceinline__ void store_global(const float2* v, float2* dst, int tid) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) dst[j + r * G::NB] = v[b * R + r];
+    }
+  }
+}
+
+template <int N, int T, int R>
+__device__ __forceinline__ void load_lds(float2* v, const float2* lds, int tid) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+      const int pj = lpad(j);
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[b * R + r] = lds[lpad_step<G::NB, false>(pj, j, r)];
+    }
+  }
+}
+
+template <int N, int T, int R, int NS>
+__device__ __forceinline__ void store_lds(const float2* v, float2* lds, int tid) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+      const int base = (j / NS) * (NS * R) + (j % NS);
+      const int pb = lpad(base);
+      // first pass of a radix-16 (or smaller power-of-two) line: base = 16-aligned multiple of R
+      constexpr bool fits = NS == 1 && (16 % R == 0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) lds[lpad_step<NS, fits>(pb, base, r)] = v[b * R + r];
+    }
+  }
+}
+
+// Inter-pass twiddles W_{NS R}^{(j mod NS) r} = tw[(j mod NS) r N/(NS R)], tw[k] = e^{-j2pi k/N}.
+template <int N, int T, int R, int NS, int DIR>
+__device__ __forceinline__ void twiddle(float2* v, const float2* __restrict__ tw, int tid) {
+  if constexpr (NS > 1) {
+    using G = Geom<N, T, R>;
+    constexpr int STEP = N / (NS * R);
+#pragma unroll
+    for (int b = 0; b < G::B; ++b) {
+      const int j = tid + b * T;
+      if (G::live(j)) {
+        const int e = (j % NS) * STEP;
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+          float2 w = tw[e * r];
+          if (DIR > 0) w.y = -w.y;
+          v[b * R + r] = cmul(v[b * R + r], w);
+        }
+      }
+    }
+  }
+}
+
+template <int N, int T, int R, int DIR>
+__device__ __forceinline__ void butterflies(float2* v, int tid) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    if (G::live(tid + b * T)) Dft<R, DIR>::run(v + b * R);
+  }
+}
+
+// The passes of one transform.  Every thread of the workgroup must call run() (it contains
+// workgroup barriers); threads whose butterflies fall past N/R idle through a pass.
+template <int N, int T, int DIR, int NS, class L>
+struct Passes;
+
+template <int N, int T, int DIR, int NS, int R>
+struct Passes<N, T, DIR, NS, IntList<R>> {
+  static __device__ __forceinline__ void run(float2* v, float2* lds, const float2* __restrict__ tw,
+                                             int tid) {
+    twiddle<N, T, R, NS, DIR>(v, opaque(tw), tid);
+    butterflies<N, T, R, DIR>(v, tid);
+  }
+};
+
+template <int N, int T, int DIR, int NS, int R, int R2, int... Rs>
+struct Passes<N, T, DIR, NS, IntList<R, R2, Rs...>> {
+  static __device__ __forceinline__ void run(float2* v, float2* lds, const float2* __restrict__ tw,
+                                             int tid) {
+    twiddle<N, T, R, NS, DIR>(v, opaque(tw), tid);
+    butterflies<N, T, R, DIR>(v, tid);
+    __syncthreads();  // the line buffer may still be read by the previous exchange
+    store_lds<N, T, R, NS>(v, lds, tid);
+    __syncthreads();
+    load_lds<N, T, R2>(v, lds, tid);
+    Passes<N, T, DIR, NS * R, IntList<R2, Rs...>>::run(v, lds, tw, tid);
+  }
+};
+
+// ---------------------------------------------------------------------------- line configurations
+// T threads per line (16 points per thread in radix-16 passes), LPW lines per workgroup.
+template <int N>
+struct LineCfg;
+
+#define RDF_LINE_CFG(N_, T_, FWD, INV)                                            \
+  template <>                                                                     \
+  struct LineCfg<N_> {                                                            \
+    static constexpr int N = N_;                                                  \
+    static constexpr int T = T_;                                                  \
+    using Fwd = FWD;                                                              \
+    using Inv = INV;                                                              \
+    static constexpr int LPW = T_ >= 256 ? 1 : 256 / T_;                          \
+    static constexpr int WG = T_ * LPW;                                           \
+    static constexpr int LDS = lds_len(N_);                                       \
+    static constexpr int P = MaxRegs<N_, T_, FWD>::value > MaxRegs<N_, T_, INV>::value \
+                                 ? MaxRegs<N_, T_, FWD>::value                    \
+                                 : MaxRegs<N_, T_, INV>::value;                   \
+    static_assert(ListInfo<FWD>::product == N_ && ListInfo<INV>::product == N_,   \
+                  "radix list must multiply to N");                               \
+    static_assert(ListInfo<FWD>::first == ListInfo<INV>::last &&                  \
+                      ListInfo<FWD>::last == ListInfo<INV>::first,                \
+                  "inverse list must be the forward list reversed at its ends");  \
+  };
+
+using L_16_16 = IntList<16, 16>;
+using L_16_16_2 = IntList<16, 16, 2>;
+using L_2_16_16 = IntList<2, 16, 16>;
+using L_16_16_4 = IntList<16, 16, 4>;
+using L_4_16_16 = IntList<4, 16, 16>;
+using L_16_16_8 = IntList<16, 16, 8>;
+using L_8_16_16 = IntList<8, 16, 16>;
+using L_16_16_16 = IntList<16, 16, 16>;
+using L_16_16_16_2 = IntList<16, 16, 16, 2>;
+using L_2_16_16_16 = IntList<2, 16, 16, 16>;
+using L_16_16_16_4 = IntList<16, 16, 16, 4>;
+using L_4_16_16_16 = IntList<4, 16, 16, 16>;
+using L_16_15_25 = IntList<16, 15, 25>;
+using L_25_15_16 = IntList<25, 15, 16>;
+
+RDF_LINE_CFG(256, 16, L_16_16, L_16_16)
+RDF_LINE_CFG(512, 32, L_16_16_2, L_2_16_16)
+RDF_LINE_CFG(1024, 64, L_16_16_4, L_4_16_16)
+RDF_LINE_CFG(2048, 128, L_16_16_8, L_8_16_16)
+RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16)
+RDF_LINE_CFG(8192, 512, L_16_16_16_2, L_2_16_16_16)
+RDF_LINE_CFG(16384, 1024, L_16_16_16_4, L_4_16_16_16)
+RDF_LINE_CFG(6000, 400, L_16_15_25, L_25_15_16)
+
+#undef RDF_LINE_CFG
+
+}  // namespace rdf

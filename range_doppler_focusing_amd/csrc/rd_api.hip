@@ -1,0 +1,455 @@
+// Host side of the C ABI declared in include/rdfocus.h: parameter validation, plan construction
+// (float64 matched filter and tables, rounded to float32 once), launch sequences.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "../../include/rdfocus.h"
+#include "rd_kernels.hpp"
+
+namespace {
+
+constexpr double kC = 299792458.0;
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+thread_local std::string g_last_error;
+
+rd_status fail(rd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+std::mutex g_plans_mu;
+std::set<const rd_plan*> g_plans;  // live plans, so a destroyed plan is recognised
+
+}  // namespace
+
+struct rd_plan {
+  rd_params p{};
+  int device = 0;
+  int cus = 0;
+  int L = 0;           // replica length
+  double dr = 0.0;     // range-bin spacing
+  bool azimuth = false;
+  const rdf::LineOps* rops = nullptr;  // range-length kernels
+  const rdf::LineOps* aops = nullptr;  // azimuth-length kernels
+  int rc_grid = 0;      // persistent grid of the range kernels
+  int afft_grid = 0;    // persistent grid of the azimuth FFT
+  int azc_grid = 0;     // persistent grid of the azimuth filter + IFFT
+  int rfft_grid = 0;    // persistent grid of a range-length FFT
+  float2* H = nullptr;       // [Nr] conj(FFT(h)) / Nr
+  float2* tw_r = nullptr;    // [Nr] e^{-j 2 pi k / Nr}
+  float2* tw_a = nullptr;    // [Na] e^{-j 2 pi k / Na}
+  double* Dk = nullptr;      // [Na] sqrt(1 - (lambda f_k / 2V)^2)
+  double* Qk = nullptr;      // [Na] u_k / (D_k (1 + D_k)) / dr
+  float2* work = nullptr;    // [Na * Nr] workspace
+  rdf::AzFilterConst azc{};
+  rdf::RcmcConst rcmc{};
+};
+
+namespace {
+
+bool live_plan(const rd_plan* p) {
+  std::lock_guard<std::mutex> g(g_plans_mu);
+  return g_plans.count(p) != 0;
+}
+
+void free_plan(rd_plan* p) {
+  (void)hipFree(p->H);
+  (void)hipFree(p->tw_r);
+  (void)hipFree(p->tw_a);
+  (void)hipFree(p->Dk);
+  (void)hipFree(p->Qk);
+  (void)hipFree(p->work);
+  delete p;
+}
+
+template <class T>
+rd_status upload(T** dst, const std::vector<T>& src, const char* what) {
+  if (hipMalloc(dst, src.size() * sizeof(T)) != hipSuccess) {
+    *dst = nullptr;
+    return fail(RD_ERR_OUT_OF_MEMORY, "hipMalloc of %s (%zu bytes) failed", what,
+                src.size() * sizeof(T));
+  }
+  if (hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice) != hipSuccess)
+    return fail(RD_ERR_DEVICE, "upload of %s failed", what);
+  return RD_OK;
+}
+
+// e^{-j 2 pi k / N}, k < N, evaluated in float64 and rounded once
+std::vector<float2> roots_table(int N) {
+  std::vector<float2> t(N);
+  for (int k = 0; k < N; ++k) {
+    const double a = kTwoPi * double(k) / double(N);
+    t[k] = make_float2(float(std::cos(a)), float(-std::sin(a)));
+  }
+  return t;
+}
+
+// Matched filter of nxmr.cn/news/101525 §2.1 (chirp spectrum precomputed on the host):
+// h[n] = w[n] exp(j pi Kr (n/Fs - Tp/2)^2) on [0, L), H[k] = conj(sum_n h[n] e^{-j2pi kn/Nr}),
+// by direct summation in float64 (exact twiddle index k n mod Nr), scaled by 1/Nr for the
+// inverse transform, rounded to float32 once.
+std::vector<float2> matched_filter(const rd_params& p, int L) {
+  const int Nr = p.Nr;
+  const double Kr = p.bandwidth_hz / p.pulse_s;
+  std::vector<double> hr(L), hi(L);
+  for (int n = 0; n < L; ++n) {
+    const double t = double(n) / p.fs_hz - p.pulse_s / 2.0;
+    double w = 1.0;
+    if (p.range_window == RD_WINDOW_HAMMING && L > 1) w = 0.54 - 0.46 * std::cos(kTwoPi * n / (L - 1));
+    const double ph = M_PI * Kr * t * t;
+    hr[n] = w * std::cos(ph);
+    hi[n] = w * std::sin(ph);
+  }
+  std::vector<double> c(Nr), s(Nr);
+  for (int m = 0; m < Nr; ++m) {
+    c[m] = std::cos(kTwoPi * m / Nr);
+    s[m] = std::sin(kTwoPi * m / Nr);
+  }
+  std::vector<float2> H(Nr);
+  for (int k = 0; k < Nr; ++k) {
+    double re = 0.0, im = 0.0;
+    int64_t idx = 0;  // (k * n) mod Nr
+    for (int n = 0; n < L; ++n) {
+      // h[n] e^{-j 2 pi idx / Nr}
+      re += hr[n] * c[idx] + hi[n] * s[idx];
+      im += hi[n] * c[idx] - hr[n] * s[idx];
+      idx += k;
+      if (idx >= Nr) idx -= Nr;
+    }
+    H[k] = make_float2(float(re / Nr), float(-im / Nr));  // conjugate, 1/Nr
+  }
+  return H;
+}
+
+rd_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RD_OK;
+  return fail(RD_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+rd_status check_call(rd_plan* plan) {
+  if (!plan || !live_plan(plan)) return fail(RD_ERR_INVALID_ARG, "null or destroyed plan");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+    return fail(RD_ERR_DEVICE, "the plan was created on device %d but device %d is current",
+                plan->device, dev);
+  return RD_OK;
+}
+
+bool aligned8(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+// [a, a + n) and [b, b + n) overlap but are not the same buffer
+bool partial_overlap(const void* a, const void* b, size_t n) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x != y && x < y + n && y < x + n;
+}
+
+int persistent_grid(int occ, int cus, int64_t lines, int lpw) {
+  const int64_t need = (lines + lpw - 1) / lpw;
+  const int64_t resident = int64_t(occ > 0 ? occ : 1) * int64_t(cus > 0 ? cus : 1);
+  const int64_t g = need < resident ? need : resident;
+  return int(g > 0 ? g : 1);
+}
+
+// -------------------------------------------------------------------------- launch sequences
+rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, hipStream_t s) {
+  return check_hip(P->rops->range_compress(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid, s),
+                   "range compression launch");
+}
+
+// rc [Na][Nr] -> azT [Nr][Na] (corner turn + azimuth FFT along each row)
+rd_status run_az_fft(rd_plan* P, const float2* rc, float2* azT, hipStream_t s) {
+  rd_status st = check_hip(rdf::launch_corner_turn(rc, azT, P->p.Na, P->p.Nr, s), "corner turn");
+  if (st != RD_OK) return st;
+  return check_hip(P->aops->fft(azT, azT, P->tw_a, P->p.Nr, 0, 1.0f, P->afft_grid, s),
+                   "azimuth FFT launch");
+}
+
+rd_status run_rcmc(rd_plan* P, const float2* azT, float2* rcmcT, hipStream_t s) {
+  return check_hip(rdf::launch_rcmc8(azT, rcmcT, P->Qk, P->rcmc, P->p.Nr, P->p.Na, s),
+                   "RCMC launch");
+}
+
+// rcmcT [Nr][Na] -> (filter, inverse azimuth FFT) tmpT [Nr][Na] -> corner turn -> img [Na][Nr]
+rd_status run_az_compress(rd_plan* P, const float2* rcmcT, float2* tmpT, float2* img,
+                          hipStream_t s) {
+  rd_status st = check_hip(
+      P->aops->az_compress(rcmcT, tmpT, P->tw_a, P->Dk, P->azc, P->p.Nr, P->azc_grid, s),
+      "azimuth compression launch");
+  if (st != RD_OK) return st;
+  return check_hip(rdf::launch_corner_turn(tmpT, img, P->p.Nr, P->p.Na, s), "corner turn");
+}
+
+rd_status run_azimuth(rd_plan* P, const float2* rc, float2* img, hipStream_t s) {
+  // rc is consumed by the first corner turn, so img may alias it
+  rd_status st = run_az_fft(P, rc, P->work, s);
+  if (st != RD_OK) return st;
+  st = run_rcmc(P, P->work, img, s);
+  if (st != RD_OK) return st;
+  return run_az_compress(P, img, P->work, img, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rd_length_supported(int32_t n) { return rdf::line_ops(n) != nullptr ? 1 : 0; }
+
+const char* rd_status_string(rd_status st) {
+  switch (st) {
+    case RD_OK: return "ok";
+    case RD_ERR_INVALID_ARG: return "invalid argument";
+    case RD_ERR_UNSUPPORTED_LENGTH: return "unsupported transform length";
+    case RD_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case RD_ERR_DEVICE: return "device error";
+    case RD_ERR_LAUNCH: return "kernel launch failed";
+    case RD_ERR_NOT_CONFIGURED: return "azimuth processing not configured (range-only plan)";
+  }
+  return "unknown status";
+}
+
+const char* rd_last_error(void) { return g_last_error.c_str(); }
+
+rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
+  if (!out) return fail(RD_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!params) return fail(RD_ERR_INVALID_ARG, "params is NULL");
+  const rd_params p = *params;
+  if (p.Na <= 0 || p.Nr <= 0) return fail(RD_ERR_INVALID_ARG, "Na=%d and Nr=%d must be > 0", p.Na, p.Nr);
+  if (int64_t(p.Na) * p.Nr > (int64_t(1) << 32))
+    return fail(RD_ERR_INVALID_ARG, "Na*Nr = %lld exceeds 2^32 samples", (long long)p.Na * p.Nr);
+  if (!(p.pulse_s > 0) || !(p.bandwidth_hz > 0) || !(p.fs_hz > 0) || !std::isfinite(p.pulse_s) ||
+      !std::isfinite(p.bandwidth_hz) || !std::isfinite(p.fs_hz))
+    return fail(RD_ERR_INVALID_ARG, "pulse_s, bandwidth_hz and fs_hz must be finite and > 0");
+  if (p.range_window != RD_WINDOW_RECT && p.range_window != RD_WINDOW_HAMMING)
+    return fail(RD_ERR_INVALID_ARG, "range_window %d is not RD_WINDOW_RECT or RD_WINDOW_HAMMING",
+                p.range_window);
+  if (p.flags != 0) return fail(RD_ERR_INVALID_ARG, "flags must be 0");
+  const double Lf = std::ceil(p.pulse_s * p.fs_hz - 1e-6);
+  if (Lf < 1 || Lf > p.Nr)
+    return fail(RD_ERR_INVALID_ARG, "replica length ceil(Tp*Fs) = %.0f must be in [1, Nr=%d]", Lf, p.Nr);
+  const bool any_az = p.carrier_hz != 0 || p.prf_hz != 0 || p.velocity_mps != 0;
+  const bool all_az = p.carrier_hz > 0 && p.prf_hz > 0 && p.velocity_mps > 0 &&
+                      std::isfinite(p.carrier_hz) && std::isfinite(p.prf_hz) &&
+                      std::isfinite(p.velocity_mps);
+  if (any_az && !all_az)
+    return fail(RD_ERR_INVALID_ARG,
+                "carrier_hz, prf_hz, velocity_mps must all be > 0 (full chain) or all 0 (range only)");
+  const rdf::LineOps* rops = rdf::line_ops(p.Nr);
+  if (!rops) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length Nr=%d is built", p.Nr);
+  const rdf::LineOps* aops = nullptr;
+  if (all_az) {
+    aops = rdf::line_ops(p.Na);
+    if (!aops) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length Na=%d is built", p.Na);
+    if (p.rcmc_taps != 8)
+      return fail(RD_ERR_INVALID_ARG, "rcmc_taps=%d: only the 8-tap interpolator is built", p.rcmc_taps);
+    if (!(p.kaiser_beta >= 0.0 && p.kaiser_beta <= 12.0))
+      return fail(RD_ERR_INVALID_ARG, "kaiser_beta=%g must be in [0, 12]", p.kaiser_beta);
+    const double lam = kC / p.carrier_hz;
+    const double umax = std::pow(lam * (p.prf_hz / 2.0) / (2.0 * p.velocity_mps), 2);
+    if (!(umax < 1.0))
+      return fail(RD_ERR_INVALID_ARG, "Doppler band exceeds 2V/lambda ((lambda PRF / 4V)^2 = %g)", umax);
+    if (!std::isfinite(p.range_bin0_m) || p.range_bin0_m <= 0)
+      return fail(RD_ERR_INVALID_ARG, "range_bin0_m must be finite and > 0");
+  }
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(RD_ERR_DEVICE, "no current HIP device");
+  rd_plan* P = new (std::nothrow) rd_plan();
+  if (!P) return fail(RD_ERR_OUT_OF_MEMORY, "host allocation failed");
+  P->p = p;
+  P->device = dev;
+  P->L = int(Lf);
+  P->dr = kC / (2.0 * p.fs_hz);
+  P->azimuth = all_az;
+  P->rops = rops;
+  P->aops = aops;
+  if (hipDeviceGetAttribute(&P->cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    P->cus = 256;
+
+  rd_status st = RD_OK;
+  auto bail = [&](rd_status s) {
+    free_plan(P);
+    return s;
+  };
+  if ((st = upload(&P->H, matched_filter(p, P->L), "matched filter")) != RD_OK) return bail(st);
+  if ((st = upload(&P->tw_r, roots_table(p.Nr), "range twiddles")) != RD_OK) return bail(st);
+  int occ_rc = 0, occ_fft = 0, occ_azc = 0;
+  if (rops->occupancy(&occ_rc, &occ_fft, &occ_azc) != hipSuccess)
+    return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
+  P->rc_grid = persistent_grid(occ_rc, P->cus, p.Na, rops->lpw);
+  P->rfft_grid = occ_fft;  // scaled by lines at launch time
+
+  if (all_az) {
+    const int Na = p.Na;
+    const double lam = kC / p.carrier_hz;
+    std::vector<double> D(Na), Q(Na);
+    for (int k = 0; k < Na; ++k) {
+      const int kk = (k <= (Na - 1) / 2) ? k : k - Na;  // FFT bin order
+      const double f = double(kk) * p.prf_hz / double(Na);
+      const double u = std::pow(lam * f / (2.0 * p.velocity_mps), 2);
+      D[k] = std::sqrt(1.0 - u);
+      Q[k] = u / (D[k] * (1.0 + D[k])) / P->dr;
+    }
+    if ((st = upload(&P->tw_a, roots_table(Na), "azimuth twiddles")) != RD_OK) return bail(st);
+    if ((st = upload(&P->Dk, D, "azimuth migration factors")) != RD_OK) return bail(st);
+    if ((st = upload(&P->Qk, Q, "RCMC shift factors")) != RD_OK) return bail(st);
+    const size_t bytes = size_t(p.Na) * size_t(p.Nr) * sizeof(float2);
+    if (hipMalloc(&P->work, bytes) != hipSuccess) {
+      P->work = nullptr;
+      return bail(fail(RD_ERR_OUT_OF_MEMORY, "hipMalloc of the %zu-byte workspace failed", bytes));
+    }
+    int a_rc = 0, a_fft = 0, a_azc = 0;
+    if (aops->occupancy(&a_rc, &a_fft, &a_azc) != hipSuccess)
+      return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
+    P->afft_grid = persistent_grid(a_fft, P->cus, p.Nr, aops->lpw);
+    P->azc_grid = persistent_grid(a_azc, P->cus, p.Nr, aops->lpw);
+    P->azc.rb0 = p.range_bin0_m;
+    P->azc.dr = P->dr;
+    P->azc.two_over_lambda = 2.0 / lam;
+    P->azc.inv_na = float(1.0 / double(Na));
+    // Kaiser window as a series in y = (beta/2)^2 (1 - (t/4)^2): I0 = sum y^m / (m!)^2
+    const double y0 = 0.25 * p.kaiser_beta * p.kaiser_beta;
+    int M = 1;
+    double term = y0;  // y0^m / (m!)^2 at m = M
+    while (M + 1 < rdf::kRcmcMaxTerms && term > 1e-10) {
+      ++M;
+      term *= y0 / (double(M) * double(M));
+    }
+    P->rcmc.rb0 = p.range_bin0_m;
+    P->rcmc.dr = P->dr;
+    P->rcmc.y0 = float(y0);
+    P->rcmc.y1 = float(y0 / 16.0);
+    P->rcmc.nterm = M + 1;
+    double inv_fact2 = 1.0;
+    std::vector<double> coef(M + 1);
+    for (int m = 0; m <= M; ++m) {
+      if (m > 0) inv_fact2 /= double(m) * double(m);
+      coef[m] = inv_fact2;
+    }
+    for (int m = 0; m <= M; ++m) P->rcmc.coef[m] = float(coef[M - m]);
+  } else {
+    if ((st = upload(&P->tw_a, roots_table(rdf::line_ops(p.Na) ? p.Na : 1), "azimuth twiddles")) !=
+        RD_OK)
+      return bail(st);
+  }
+  {
+    std::lock_guard<std::mutex> g(g_plans_mu);
+    g_plans.insert(P);
+  }
+  *out = P;
+  return RD_OK;
+}
+
+rd_status rd_plan_destroy(rd_plan* plan) {
+  if (!plan) return RD_OK;
+  {
+    std::lock_guard<std::mutex> g(g_plans_mu);
+    if (!g_plans.erase(plan)) return fail(RD_ERR_INVALID_ARG, "plan is not live (destroyed twice?)");
+  }
+  free_plan(plan);
+  return RD_OK;
+}
+
+rd_status rd_range_compress(rd_plan* plan, const rd_c64* echo, rd_c64* rc, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!aligned8(echo) || !aligned8(rc)) return fail(RD_ERR_INVALID_ARG, "echo and rc must be non-NULL and 8-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
+  if (partial_overlap(echo, rc, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and rc overlap without being equal");
+  return run_range_compress(plan, reinterpret_cast<const float2*>(echo),
+                            reinterpret_cast<float2*>(rc), static_cast<hipStream_t>(stream));
+}
+
+rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if (!aligned8(rc) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "rc and img must be non-NULL and 8-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
+  if (partial_overlap(rc, img, bytes)) return fail(RD_ERR_INVALID_ARG, "rc and img overlap without being equal");
+  return run_azimuth(plan, reinterpret_cast<const float2*>(rc), reinterpret_cast<float2*>(img),
+                     static_cast<hipStream_t>(stream));
+}
+
+rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if (!aligned8(echo) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "echo and img must be non-NULL and 8-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
+  if (partial_overlap(echo, img, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and img overlap without being equal");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* I = reinterpret_cast<float2*>(img);
+  st = run_range_compress(plan, reinterpret_cast<const float2*>(echo), I, s);
+  if (st != RD_OK) return st;
+  return run_azimuth(plan, I, I, s);
+}
+
+rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft, rd_c64* rcmc,
+                                  rd_c64* img, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if (!aligned8(rc) || !aligned8(azfft) || !aligned8(rcmc) || !aligned8(img))
+    return fail(RD_ERR_INVALID_ARG, "all buffers must be non-NULL and 8-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
+  const void* bufs[4] = {rc, azfft, rcmc, img};
+  for (int a = 0; a < 4; ++a)
+    for (int b = a + 1; b < 4; ++b) {
+      const bool same_ok = (a == 0 && b == 3);  // img may equal rc
+      const char* x = static_cast<const char*>(bufs[a]);
+      const char* y = static_cast<const char*>(bufs[b]);
+      const bool overlap = x < y + bytes && y < x + bytes;
+      if (overlap && !(same_ok && x == y))
+        return fail(RD_ERR_INVALID_ARG, "debug buffers %d and %d overlap", a, b);
+    }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* A = reinterpret_cast<float2*>(azfft);
+  float2* R = reinterpret_cast<float2*>(rcmc);
+  if ((st = run_az_fft(plan, reinterpret_cast<const float2*>(rc), A, s)) != RD_OK) return st;
+  if ((st = run_rcmc(plan, A, R, s)) != RD_OK) return st;
+  return run_az_compress(plan, R, plan->work, reinterpret_cast<float2*>(img), s);
+}
+
+rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const rd_c64* in,
+                            rd_c64* out, int64_t lines, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (axis != 0 && axis != 1) return fail(RD_ERR_INVALID_ARG, "axis must be 0 (Na) or 1 (Nr)");
+  const int n = axis == 0 ? plan->p.Na : plan->p.Nr;
+  const rdf::LineOps* ops = rdf::line_ops(n);
+  if (!ops) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length %d is built", n);
+  if (lines < 0) return fail(RD_ERR_INVALID_ARG, "lines must be >= 0");
+  if (lines == 0) return RD_OK;
+  if (!aligned8(in) || !aligned8(out)) return fail(RD_ERR_INVALID_ARG, "in and out must be non-NULL and 8-byte aligned");
+  if (partial_overlap(in, out, size_t(lines) * n * sizeof(rd_c64)))
+    return fail(RD_ERR_INVALID_ARG, "in and out overlap without being equal");
+  int occ_rc = 0, occ_fft = 0, occ_azc = 0;
+  if (ops->occupancy(&occ_rc, &occ_fft, &occ_azc) != hipSuccess)
+    return fail(RD_ERR_DEVICE, "occupancy query failed");
+  const int grid = persistent_grid(occ_fft, plan->cus, lines, ops->lpw);
+  const float2* tw = axis == 0 ? plan->tw_a : plan->tw_r;
+  return check_hip(ops->fft(reinterpret_cast<const float2*>(in), reinterpret_cast<float2*>(out), tw,
+                            lines, inverse ? 1 : 0, inverse ? float(1.0 / n) : 1.0f, grid,
+                            static_cast<hipStream_t>(stream)),
+                   "line FFT launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+"""The C-ABI library on the CPU side: it loads, exports every symbol the header declares, its
+parameter block matches the C layout, and argument validation fails before any device work.
+No kernel is launched here (there may be no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rdfocus.h")
+LIB = os.path.join(ROOT, "range_doppler_focusing_amd", "librdfocus.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="librdfocus.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rd_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    import range_doppler_focusing_amd as rdf
+    lib = rdf.load_library()
+    declared = header_functions()
+    assert len(declared) == 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(rdf.EXPORTS) == declared
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (rd_[a-z_]+)$", out, flags=re.M))
+    assert set(declared) <= exported
+
+
+def test_param_block_layout_matches_c():
+    """Offsets of every rd_params field as gcc lays out the header, vs the ctypes mirror."""
+    from range_doppler_focusing_amd import rd_params
+    fields = [f for f, _ in rd_params._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"rdfocus.h\"\nint main(void){\n"
+    src += 'printf("%zu\\n", sizeof(rd_params));\n'
+    for f in fields:
+        src += f'printf("%zu\\n", offsetof(rd_params, {f}));\n'
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(rd_params)
+    assert got[1:] == [getattr(rd_params, f).offset for f in fields]
+
+
+def test_status_strings_and_lengths():
+    import range_doppler_focusing_amd as rdf
+    assert rdf.rd_status_string(0) == "ok"
+    assert "unsupported" in rdf.rd_status_string(-2)
+    for n in (256, 512, 1024, 2048, 4096, 8192, 16384, 6000):
+        assert rdf.rd_length_supported(n)
+    for n in (0, -1, 100, 1000, 4095, 6001, 32768):
+        assert not rdf.rd_length_supported(n)
+
+
+def good_params(**kw):
+    from rdscene import C3
+    p = C3.plan_params()
+    p.update(kw)
+    return p
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(Na=0), -1), (dict(Nr=-4), -1), (dict(pulse_s=0.0), -1), (dict(fs_hz=float("nan")), -1),
+    (dict(range_window=7), -1), (dict(flags=1), -1),
+    (dict(pulse_s=1e-3), -1),                       # replica longer than the line
+    (dict(prf_hz=0.0), -1),                         # half-configured azimuth
+    (dict(Nr=4000), -2), (dict(Na=3000), -2),       # no transform of that length
+    (dict(rcmc_taps=6), -1), (dict(kaiser_beta=-1.0), -1),
+    (dict(velocity_mps=1.0), -1),                   # Doppler band beyond 2V/lambda
+    (dict(range_bin0_m=0.0), -1),
+])
+def test_invalid_parameters_rejected_before_device_work(bad, status):
+    import range_doppler_focusing_amd as rdf
+    with pytest.raises(rdf.RdError) as ei:
+        rdf.rd_plan_create(good_params(**bad))
+    assert ei.value.status == status
+    assert rdf.rd_last_error() != ""
+
+
+def test_null_arguments():
+    import range_doppler_focusing_amd as rdf
+    lib = rdf.load_library()
+    assert lib.rd_plan_create(None, None) == -1
+    h = ctypes.c_void_p()
+    assert lib.rd_plan_create(None, ctypes.byref(h)) == -1 and h.value is None
+    assert lib.rd_plan_destroy(None) == 0
+    assert lib.rd_range_compress(None, None, None, None) == -1
+    assert lib.rd_focus(None, None, None, None) == -1
+    assert "plan" in rdf.rd_last_error()

@@ -1,0 +1,233 @@
+"""Parity of the HIP path (through the C ABI) with the CPU fp64 oracle, on the GPU.
+
+Bars: relative L2 <= 1e-5 per stage and <= 1e-4 for the focused image; target peak indices
+identical to the oracle's; PSLR / ISLR of every target within 0.1 dB of the oracle's.
+Sizes: the five workloads at their full sizes (the 16384 x 16384 scene on sampled lines and
+range bins, which the oracle computes one by one), plus ragged line counts and every built
+transform length for the line FFT.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import metrics as M
+from oracle import rd_oracle as O
+from rdscene import C1, C2, C3, C4, C5, cached_scene, make_scene
+
+pytestmark = pytest.mark.gpu
+
+STAGE_TOL = 1e-5
+IMAGE_TOL = 1e-4
+LENGTHS = (256, 512, 1024, 2048, 4096, 8192, 16384, 6000)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    torch.cuda.set_device(0)
+    return torch
+
+
+@pytest.fixture(scope="module")
+def rdf(torch_dev):
+    import range_doppler_focusing_amd as rdf
+    rdf.load_library()
+    return rdf
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.complex64)).to("cuda")
+
+
+_oracle_cache = {}
+
+
+def scene_and_stages(cfg):
+    if cfg.name not in _oracle_cache:
+        sc = make_scene(cfg)
+        log(f"[oracle] {cfg.name}: focusing on the CPU")
+        _oracle_cache[cfg.name] = (sc, O.focus_stages(sc.echo, cfg.plan_params()))
+    return _oracle_cache[cfg.name]
+
+
+# ------------------------------------------------------------------------------ line transform
+@pytest.mark.parametrize("n", LENGTHS)
+def test_line_fft_matches_dft(torch_dev, rdf, n):
+    torch = torch_dev
+    lines = 37                       # not a multiple of any lines-per-workgroup count
+    rng = np.random.default_rng(n)
+    x = (rng.standard_normal((lines, n)) + 1j * rng.standard_normal((lines, n))).astype(np.complex64)
+    log(f"[line fft] n={n} lines={lines}")
+    with rdf.Plan(Na=64, Nr=n, pulse_s=1e-6, bandwidth_hz=100e6, fs_hz=120e6) as plan:
+        xd = dev(torch, x)
+        X = plan.line_fft(xd, axis=1).cpu().numpy()
+        xi = plan.line_fft(dev(torch, X), axis=1, inverse=True).cpu().numpy()
+        # in place gives the same bits
+        y = xd.clone()
+        rdf.rd_debug_line_fft(plan.handle, 1, 0, y, y, lines)
+        torch.cuda.synchronize()
+        assert torch.equal(y.cpu(), torch.from_numpy(X))
+    ref = np.fft.fft(x.astype(np.complex128), axis=1)
+    assert M.rel_l2(X, ref) < 2e-7 * np.log2(n)
+    assert M.rel_l2(xi, x) < 4e-7 * np.log2(n)
+
+
+def test_line_fft_zero_lines_is_a_no_op(torch_dev, rdf):
+    with rdf.Plan(Na=64, Nr=256, pulse_s=1e-6, bandwidth_hz=100e6, fs_hz=120e6) as plan:
+        x = torch_dev.zeros((1, 256), dtype=torch_dev.complex64, device="cuda")
+        rdf.rd_debug_line_fft(plan.handle, 1, 0, x, x, 0)
+
+
+# ------------------------------------------------------------------------------ range compression
+@pytest.mark.parametrize("cfg", [C1, C2, C3, C4], ids=lambda c: c.name)
+def test_range_compression_full(torch_dev, rdf, cfg):
+    torch = torch_dev
+    sc = make_scene(cfg)
+    log(f"[range] {cfg.name} {cfg.Na}x{cfg.Nr}")
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        echo = dev(torch, sc.echo)
+        rc = plan.range_compress(echo).cpu().numpy()
+        # in place gives the same bits
+        plan.range_compress(echo, out=echo)
+        torch.cuda.synchronize()
+        assert np.array_equal(echo.cpu().numpy(), rc)
+    ref = O.range_compress(sc.echo, cfg.plan_params())
+    err = M.rel_l2(rc, ref)
+    log(f"[range] {cfg.name} rel-L2 {err:.2e}")
+    assert err <= STAGE_TOL
+    if not cfg.full_chain:
+        # every target's compressed peak sits at its delay in every sampled line
+        for m in (0, cfg.Na // 2, cfg.Na - 1):
+            for (_, n) in sc.targets:
+                win = np.abs(rc[m, n - 4:n + 5])
+                assert int(np.argmax(win)) == 4 == int(np.argmax(np.abs(ref[m, n - 4:n + 5])))
+
+
+def test_range_compression_large_sampled_lines(torch_dev, rdf):
+    torch = torch_dev
+    cfg = C5
+    log("[range] 16384 x 16384 scene: generating echo")
+    sc = cached_scene(cfg)
+    rows = np.array([0, 1, 777, 8191, 8192, 12345, 16382, 16383])
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        echo = dev(torch, sc.echo)
+        rc = plan.range_compress(echo)
+        got = rc[torch.from_numpy(rows).to("cuda")].cpu().numpy()
+        del rc, echo
+    ref = O.range_compress(sc.echo[rows], cfg.plan_params())
+    err = M.rel_l2(got, ref)
+    log(f"[range] 16384 sampled rel-L2 {err:.2e}")
+    assert err <= STAGE_TOL
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------ full chain
+def check_targets(img, ref_img, targets):
+    for (m, n) in targets:
+        pk = M.peak_near(img, m, n)
+        assert pk == M.peak_near(ref_img, m, n), (m, n)
+        got, want = M.point_target(img, *pk), M.point_target(ref_img, *pk)
+        for axis in ("range", "azimuth"):
+            for key in ("pslr_db", "islr_db"):
+                assert abs(got[axis][key] - want[axis][key]) <= 0.1, (m, n, axis, key)
+
+
+@pytest.mark.parametrize("cfg", [C1, C3], ids=lambda c: c.name)
+def test_focus_every_stage(torch_dev, rdf, cfg):
+    torch = torch_dev
+    sc, ref = scene_and_stages(cfg)
+    log(f"[focus] {cfg.name}")
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        echo = dev(torch, sc.echo)
+        rc = plan.range_compress(echo)
+        az, rcmc, img_dbg = plan.azimuth_stages(rc)
+        img = plan.focus(echo)
+        img_az = plan.azimuth_focus(rc)
+        torch.cuda.synchronize()
+        stages = {"rc": rc.cpu().numpy(), "azfft": az.cpu().numpy().T, "rcmc": rcmc.cpu().numpy().T,
+                  "img": img.cpu().numpy()}
+        assert torch.equal(img, img_dbg) and torch.equal(img, img_az)
+    for name in ("rc", "azfft", "rcmc"):
+        err = M.rel_l2(stages[name], ref[name])
+        log(f"[focus] {cfg.name} {name} rel-L2 {err:.2e}")
+        assert err <= STAGE_TOL, name
+    err = M.rel_l2(stages["img"], ref["img"])
+    log(f"[focus] {cfg.name} img rel-L2 {err:.2e}")
+    assert err <= IMAGE_TOL
+    check_targets(stages["img"], ref["img"], sc.targets)
+
+
+def test_focus_in_place_and_noiseless_targets(torch_dev, rdf):
+    torch = torch_dev
+    cfg = C3
+    sc = make_scene(cfg, noise=False)
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        echo = dev(torch, sc.echo)
+        img = plan.focus(echo)
+        plan.focus(echo, out=echo)            # echo == img
+        torch.cuda.synchronize()
+        assert torch.equal(echo, img)
+        gi = img.cpu().numpy()
+    for (m, n) in sc.targets:
+        assert M.peak_near(gi, m, n) == (m, n)
+
+
+def test_focus_large_sampled_range_bins(torch_dev, rdf):
+    torch = torch_dev
+    cfg = C5
+    log("[focus] 16384 x 16384: echo")
+    sc = cached_scene(cfg)
+    tg = sorted(sc.targets, key=lambda t: t[1])
+    bins = set()
+    for (m, n) in (tg[0], tg[len(tg) // 2]):
+        bins.update(range(n - 16, n + 17))
+    bins.update([0, 1, cfg.Nr // 2, cfg.Nr - 2, cfg.Nr - 1])
+    bins = sorted(bins)
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        echo = dev(torch, sc.echo)
+        img = plan.focus(echo)
+        torch.cuda.synchronize()
+        got = img[:, torch.tensor(bins, device="cuda")].cpu().numpy()
+        del img, echo
+    torch.cuda.empty_cache()
+    log("[focus] 16384 x 16384: oracle on sampled range bins")
+    ref, ref_bins = O.focus_columns(sc.echo, cfg.plan_params(), bins)
+    assert list(ref_bins) == bins
+    err = M.rel_l2(got, ref)
+    log(f"[focus] 16384 sampled rel-L2 {err:.2e}")
+    assert err <= IMAGE_TOL
+    col = {b: i for i, b in enumerate(bins)}
+    for (m, n) in (tg[0], tg[len(tg) // 2]):
+        sub_g = got[:, [col[b] for b in range(n - 16, n + 17)]]
+        sub_r = ref[:, [col[b] for b in range(n - 16, n + 17)]]
+        assert M.peak_near(sub_g, m, 16) == M.peak_near(sub_r, m, 16) == (m, 16)
+        a = M.point_target(sub_g, m, 16, axes=("azimuth",))["azimuth"]
+        b = M.point_target(sub_r, m, 16, axes=("azimuth",))["azimuth"]
+        assert abs(a["pslr_db"] - b["pslr_db"]) <= 0.1 and abs(a["islr_db"] - b["islr_db"]) <= 0.1
+
+
+# ------------------------------------------------------------------------------ error paths
+def test_error_paths_on_device(torch_dev, rdf):
+    torch = torch_dev
+    with rdf.Plan(**C2.with_(Na=256, Nr=4096).plan_params()) as plan:
+        x = torch.zeros((256, 4096), dtype=torch.complex64, device="cuda")
+        with pytest.raises(rdf.RdError) as ei:
+            plan.focus(x)
+        assert ei.value.status == -6
+        with pytest.raises(rdf.RdError) as ei:
+            rdf.rd_range_compress(plan.handle, x.data_ptr() + 4, x)
+        assert ei.value.status == -1
+        with pytest.raises(rdf.RdError) as ei:   # partial overlap
+            rdf.rd_range_compress(plan.handle, x, x.data_ptr() + 8)
+        assert ei.value.status == -1
+        h = plan.handle
+    with pytest.raises(rdf.RdError) as ei:        # destroyed plan
+        rdf.rd_range_compress(h, x, x)
+    assert ei.value.status == -1
