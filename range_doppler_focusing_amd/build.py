@@ -4,6 +4,7 @@ Usage: python -m range_doppler_focusing_amd.build [--jobs N]
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -39,29 +40,32 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False, jobs: int = 2) -> str:
-    """Compile every HIP source for gfx950 and link librdfocus.so; returns its path."""
+def build(verbose: bool = False, jobs: int = 2, extra_flags=(), out: str | None = None) -> str:
+    """Compile every HIP source for gfx950 and link librdfocus.so (or `out`); returns its path.
+    `extra_flags` go to every compile (used to build measured kernel variants side by side)."""
     t0 = time.time()
     hipcc = _hipcc()
-    objdir = os.path.join(HERE, "_build")
+    lib = out or LIB
+    tag = "" if out is None else "_" + hashlib.sha1(repr(tuple(extra_flags)).encode()).hexdigest()[:8]
+    objdir = os.path.join(HERE, "_build" + tag)
     os.makedirs(objdir, exist_ok=True)
     objs = []
 
     def one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        out = _run([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-        if verbose and out.strip():
-            print(out, file=sys.stderr)
+        msg = _run([hipcc, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose and msg.strip():
+            print(msg, file=sys.stderr)
         return obj
 
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         objs = list(ex.map(one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f}s", file=sys.stderr)
-    return LIB
+        print(f"built {lib} in {time.time() - t0:.1f}s", file=sys.stderr)
+    return lib
 
 
 if __name__ == "__main__":

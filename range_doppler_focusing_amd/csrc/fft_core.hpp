@@ -45,6 +45,16 @@ __device__ __forceinline__ const T* opaque(const T* p) {
   return p + zero;
 }
 
+// Marks registers as read here.  Placed after a line's stores, it makes the compiler wait for
+// prefetched registers at that point, where the outstanding stores are younger than the
+// prefetch and need not complete; otherwise the wait lands at the loop head, whose merged
+// state (loop entry: the prefetch is the youngest access) forces every store to complete first.
+template <int K>
+__device__ __forceinline__ void touch(const float2* v) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) asm volatile("" ::"v"(v[i].x), "v"(v[i].y));
+}
+
 // ---------------------------------------------------------------------------- compile-time roots
 // cos / sin of 2 pi p / q in double precision, evaluated by the compiler: the angle is reduced
 // exactly (integer arithmetic) to [0, pi/4] and expanded in Taylor series there.
@@ -294,28 +304,57 @@ struct Geom {
   static __device__ __forceinline__ bool live(int j) { return FULL || j < NB; }
 };
 
+// Line data streams through once (HBM in, HBM out).  Its loads and stores are buffer
+// instructions on a resource covering the workgroup's lines: the line base lives in scalar
+// registers, each lane's offset j*8 is one loop-invariant VGPR and the pass stride r*N/R*8 is a
+// scalar offset, so no per-line 64-bit address arithmetic (and no address registers that a
+// pending store would pin) exists.  The resource's size bounds every access: lanes past the end
+// read zeros and their stores are dropped, which makes ragged tails branch-free.  Accesses carry
+// the non-temporal hint so they do not displace the filter and twiddle tables from the caches.
+typedef unsigned int rdf_v2u __attribute__((ext_vector_type(2)));
+constexpr int kBufNonTemporal = 2;
+constexpr int kBufDword3 = 0x00020000;  // raw (untyped) 32-bit data format
+
+struct LineIO {
+  __amdgpu_buffer_rsrc_t rsrc;
+  // lines [first, first + count) of a row-major [*][N] complex array, clipped to `total` lines
+  __device__ __forceinline__ LineIO(const float2* base, int N, int64_t first, int count,
+                                    int64_t total) {
+    int64_t n = total - first;
+    n = n < 0 ? 0 : (n > count ? count : n);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(base + first * N), 0,
+                                             int(n * N * 8), kBufDword3);
+  }
+};
+
 template <int N, int T, int R>
-__device__ __forceinline__ void load_global(float2* v, const float2* __restrict__ src, int tid) {
+__device__ __forceinline__ void load_line(float2* v, const LineIO& io, int elem0, int tid) {
   using G = Geom<N, T, R>;
 #pragma unroll
   for (int b = 0; b < G::B; ++b) {
     const int j = tid + b * T;
     if (G::live(j)) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) v[b * R + r] = src[j + r * G::NB];
+      for (int r = 0; r < R; ++r) {
+        const rdf_v2u x = __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, (elem0 + j) * 8,
+                                                               r * G::NB * 8, kBufNonTemporal);
+        v[b * R + r] = __builtin_bit_cast(float2, x);
+      }
     }
   }
 }
 
 template <int N, int T, int R>
-__device__ __forceinline__ void store_global(const float2* v, float2* dst, int tid) {
+__device__ __forceinline__ void store_line(const float2* v, const LineIO& io, int elem0, int tid) {
   using G = Geom<N, T, R>;
 #pragma unroll
   for (int b = 0; b < G::B; ++b) {
     const int j = tid + b * T;
     if (G::live(j)) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) dst[j + r * G::NB] = v[b * R + r];
+      for (int r = 0; r < R; ++r)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, v[b * R + r]), io.rsrc,
+                                              (elem0 + j) * 8, r * G::NB * 8, kBufNonTemporal);
     }
   }
 }
@@ -410,6 +449,119 @@ struct Passes<N, T, DIR, NS, IntList<R, R2, Rs...>> {
   }
 };
 
+// ---------------------------------------------------------------------------- register-cached twiddles
+// The inter-pass twiddles of a whole transform, loaded once into registers.  A persistent
+// workgroup that transforms many lines then issues no table loads inside its line loop, so the
+// only global loads in flight are line data (which can be prefetched a line ahead: vector
+// memory counters complete in order, so any table load waited on mid-line would also wait for
+// the prefetch).
+template <int N, int T, int NS, class L>
+struct TwCache;
+
+// A pass whose twiddle set is small (NS (R-1) entries, at most 4 KB) keeps it in LDS, stored
+// r-major so the lanes of a wave read consecutive entries; larger sets (one per thread) stay in
+// registers.  tw_lds points at this pass's slice of the workgroup's twiddle LDS.
+template <int NS, int R>
+constexpr bool tw_in_lds() { return NS > 1 && NS * (R - 1) * 8 <= 4096; }
+template <int NS, int R>
+constexpr int tw_lds_len() { return tw_in_lds<NS, R>() ? NS * (R - 1) : 0; }
+
+template <int N, int T, int NS, int R>
+struct TwCacheBase {
+  using G = Geom<N, T, R>;
+  static constexpr bool IN_LDS = tw_in_lds<NS, R>();
+  static constexpr int K = (NS > 1 && !IN_LDS) ? G::B * (R - 1) : 1;
+  float2 w[K];
+  const float2* lw = nullptr;
+  // every thread of the workgroup calls this; the caller synchronises before first use
+  __device__ __forceinline__ void load(const float2* __restrict__ tw, float2* tw_lds, int tid,
+                                       int wg_tid, int wg_size) {
+    constexpr int STEP = N / (NS * R);
+    if constexpr (IN_LDS) {
+      for (int i = wg_tid; i < NS * (R - 1); i += wg_size) {
+        const int r = i / NS + 1, m = i % NS;     // entry (r, m) = W_N^{m STEP r}
+        tw_lds[i] = tw[m * STEP * r];
+      }
+      lw = tw_lds;
+    } else if constexpr (NS > 1) {
+#pragma unroll
+      for (int b = 0; b < G::B; ++b) {
+        const int j = tid + b * T;
+        const int e = (j % NS) * STEP;
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+          w[b * (R - 1) + r - 1] = G::live(j) ? tw[e * r] : make_float2(1.f, 0.f);
+      }
+    }
+  }
+  template <int DIR>
+  __device__ __forceinline__ void apply(float2* v, int tid) const {
+    if constexpr (NS > 1) {
+#pragma unroll
+      for (int b = 0; b < G::B; ++b) {
+        const int j = tid + b * T;
+        if (G::live(j)) {
+#pragma unroll
+          for (int r = 1; r < R; ++r) {
+            float2 x = IN_LDS ? lw[(r - 1) * NS + (j % NS)] : w[b * (R - 1) + r - 1];
+            if (DIR > 0) x.y = -x.y;
+            v[b * R + r] = cmul(v[b * R + r], x);
+          }
+        }
+      }
+    }
+  }
+};
+
+template <int N, int T, int NS, int R>
+struct TwCache<N, T, NS, IntList<R>> : TwCacheBase<N, T, NS, R> {
+  static constexpr int LDS = tw_lds_len<NS, R>();
+  __device__ __forceinline__ void load_all(const float2* __restrict__ tw, float2* tw_lds, int tid,
+                                           int wg_tid, int wg_size) {
+    this->load(tw, tw_lds, tid, wg_tid, wg_size);
+  }
+};
+
+template <int N, int T, int NS, int R, int R2, int... Rs>
+struct TwCache<N, T, NS, IntList<R, R2, Rs...>> : TwCacheBase<N, T, NS, R> {
+  using Next = TwCache<N, T, NS * R, IntList<R2, Rs...>>;
+  static constexpr int LDS = tw_lds_len<NS, R>() + Next::LDS;  // twiddle LDS entries, all passes
+  Next next;
+  __device__ __forceinline__ void load_all(const float2* __restrict__ tw, float2* tw_lds, int tid,
+                                           int wg_tid, int wg_size) {
+    this->load(tw, tw_lds, tid, wg_tid, wg_size);
+    next.load_all(tw, tw_lds + tw_lds_len<NS, R>(), tid, wg_tid, wg_size);
+  }
+};
+
+// The passes of one transform with twiddles from a TwCache (same contract as Passes).
+template <int N, int T, int DIR, int NS, class L>
+struct PassesCached;
+
+template <int N, int T, int DIR, int NS, int R>
+struct PassesCached<N, T, DIR, NS, IntList<R>> {
+  static __device__ __forceinline__ void run(float2* v, float2* lds,
+                                             const TwCache<N, T, NS, IntList<R>>& c, int tid) {
+    c.template apply<DIR>(v, tid);
+    butterflies<N, T, R, DIR>(v, tid);
+  }
+};
+
+template <int N, int T, int DIR, int NS, int R, int R2, int... Rs>
+struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>> {
+  static __device__ __forceinline__ void run(float2* v, float2* lds,
+                                             const TwCache<N, T, NS, IntList<R, R2, Rs...>>& c,
+                                             int tid) {
+    c.template apply<DIR>(v, tid);
+    butterflies<N, T, R, DIR>(v, tid);
+    __syncthreads();
+    store_lds<N, T, R, NS>(v, lds, tid);
+    __syncthreads();
+    load_lds<N, T, R2>(v, lds, tid);
+    PassesCached<N, T, DIR, NS * R, IntList<R2, Rs...>>::run(v, lds, c.next, tid);
+  }
+};
+
 // ---------------------------------------------------------------------------- line configurations
 // T threads per line (16 points per thread in radix-16 passes), LPW lines per workgroup.
 template <int N>
@@ -454,7 +606,12 @@ RDF_LINE_CFG(256, 16, L_16_16, L_16_16)
 RDF_LINE_CFG(512, 32, L_16_16_2, L_2_16_16)
 RDF_LINE_CFG(1024, 64, L_16_16_4, L_4_16_16)
 RDF_LINE_CFG(2048, 128, L_16_16_8, L_8_16_16)
+#if defined(RD_CFG4096_RADIX8)
+using L_8_8_8_8 = IntList<8, 8, 8, 8>;
+RDF_LINE_CFG(4096, 512, L_8_8_8_8, L_8_8_8_8)
+#else
 RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16)
+#endif
 RDF_LINE_CFG(8192, 512, L_16_16_16_2, L_2_16_16_16)
 RDF_LINE_CFG(16384, 1024, L_16_16_16_4, L_4_16_16_16)
 RDF_LINE_CFG(6000, 400, L_16_15_25, L_25_15_16)

@@ -11,10 +11,14 @@
 #include "fft_core.hpp"
 #include "rd_kernels.hpp"
 
+#ifndef RD_PF_WAVES
+#define RD_PF_WAVES 1
+#endif
 namespace rdf {
 
 // ------------------------------------------------------------------------------------------
-// fused range compression: load -> FFT -> x H (H already carries 1/N) -> IFFT -> store
+// fused range compression: load -> FFT -> x H (H already carries 1/N) -> IFFT -> store.
+// Table variant: twiddles and H are read from global tables inside the line loop.
 template <int N>
 __global__ void __launch_bounds__(LineCfg<N>::WG)
     k_range_compress(const float2* in, float2* out, const float2* __restrict__ H,
@@ -28,12 +32,9 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * C::LDS;
   for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < lines; l0 += int64_t(gridDim.x) * C::LPW) {
-    const int64_t line = l0 + grp;
-    const bool live = line < lines;
+    const LineIO src(in, N, l0, C::LPW, lines), dst(out, N, l0, C::LPW, lines);
     float2 v[C::P];
-#pragma unroll
-    for (int i = 0; i < C::P; ++i) v[i] = make_float2(0.f, 0.f);
-    if (live) load_global<N, T, R0>(v, in + line * N, tid);
+    load_line<N, T, R0>(v, src, grp * N, tid);
     Passes<N, T, -1, 1, typename C::Fwd>::run(v, my, tw, tid);
     {
       using G = Geom<N, T, RL>;
@@ -48,7 +49,140 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
       }
     }
     Passes<N, T, +1, 1, typename C::Inv>::run(v, my, tw, tid);
-    if (live) store_global<N, T, R0>(v, out + line * N, tid);
+    store_line<N, T, R0>(v, dst, grp * N, tid);
+  }
+}
+
+// Register-cached variant: the twiddles (small sets in LDS) and H are loaded once for the
+// workgroup's lifetime, so the line loop issues no table loads; with PREFETCH the next line's
+// samples are loaded into a second register set while the current line is transformed.  Needs
+// Fwd == Inv (one twiddle cache serves both directions).
+template <int N>
+__device__ __forceinline__ void rc_line(float2* v, float2* lds,
+                                        const TwCache<N, LineCfg<N>::T, 1, typename LineCfg<N>::Fwd>& twc,
+                                        const float2* h, int tid) {
+  using C = LineCfg<N>;
+  using L = typename C::Fwd;
+  constexpr int T = C::T;
+  constexpr int RL = ListInfo<L>::last;
+  using GL = Geom<N, T, RL>;
+  PassesCached<N, T, -1, 1, L>::run(v, lds, twc, tid);
+#pragma unroll
+  for (int b = 0; b < GL::B; ++b) {
+    if (GL::live(tid + b * T)) {
+#pragma unroll
+      for (int r = 0; r < RL; ++r) v[b * RL + r] = cmul(v[b * RL + r], h[b * RL + r]);
+    }
+  }
+  PassesCached<N, T, +1, 1, L>::run(v, lds, twc, tid);
+}
+
+template <int N>
+__device__ __forceinline__ void load_filter(float2* h, const float2* __restrict__ H, int tid) {
+  using C = LineCfg<N>;
+  constexpr int RL = ListInfo<typename C::Fwd>::last;
+  using GL = Geom<N, C::T, RL>;
+#pragma unroll
+  for (int b = 0; b < GL::B; ++b) {
+    const int j = tid + b * C::T;
+#pragma unroll
+    for (int r = 0; r < RL; ++r) h[b * RL + r] = GL::live(j) ? H[j + r * GL::NB] : make_float2(0.f, 0.f);
+  }
+}
+
+template <int N, bool PREFETCH>
+__global__ void __launch_bounds__(LineCfg<N>::WG)
+    k_range_compress_pf(const float2* in, float2* out, const float2* __restrict__ H,
+                        const float2* __restrict__ tw, int64_t lines) {
+  using C = LineCfg<N>;
+  using L = typename C::Fwd;
+  static_assert(std::is_same<typename C::Fwd, typename C::Inv>::value, "needs Fwd == Inv");
+  constexpr int T = C::T;
+  constexpr int R0 = ListInfo<L>::first;
+  constexpr int RL = ListInfo<L>::last;
+  using TC = TwCache<N, T, 1, L>;
+  __shared__ float2 lds[C::LPW * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
+  const int grp = threadIdx.x / T;
+  const int tid = threadIdx.x - grp * T;
+  float2* my = lds + grp * C::LDS;
+  TC twc;
+  twc.load_all(tw, lds + C::LPW * C::LDS, tid, threadIdx.x, C::WG);
+  // (the first pass's barrier orders the LDS twiddle table before its first use)
+  float2 h[Geom<N, T, RL>::B * RL];
+  load_filter<N>(h, H, tid);
+  const int64_t stride = int64_t(gridDim.x) * C::LPW;
+  float2 nxt[C::P];
+  if (PREFETCH) {
+    load_line<N, T, R0>(nxt, LineIO(in, N, int64_t(blockIdx.x) * C::LPW, C::LPW, lines), grp * N, tid);
+    touch<C::P>(nxt);
+  }
+  for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < lines; l0 += stride) {
+    float2 v[C::P];
+    if (PREFETCH) {
+#pragma unroll
+      for (int i = 0; i < C::P; ++i) v[i] = nxt[i];
+      load_line<N, T, R0>(nxt, LineIO(in, N, l0 + stride, C::LPW, lines), grp * N, tid);
+    } else {
+      load_line<N, T, R0>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
+    }
+    rc_line<N>(v, my, twc, h, tid);
+    store_line<N, T, R0>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
+    // Wait for the prefetch here, where the stores just issued are younger than it and need not
+    // complete; a wait at the loop head would merge with the loop entry and drain the stores.
+    if (PREFETCH) touch<C::P>(nxt);
+  }
+}
+
+// Two lines per loop trip with alternating register sets: line A's output registers stay
+// untouched while line B is transformed (a pending store pins its data registers until it
+// completes), and the next line is prefetched into a third set.  One line per workgroup.
+template <int N>
+__global__ void __launch_bounds__(LineCfg<N>::WG)
+    k_range_compress_pf2(const float2* in, float2* out, const float2* __restrict__ H,
+                         const float2* __restrict__ tw, int64_t lines) {
+  using C = LineCfg<N>;
+  using L = typename C::Fwd;
+  static_assert(std::is_same<typename C::Fwd, typename C::Inv>::value, "needs Fwd == Inv");
+  static_assert(C::LPW == 1, "one line per workgroup");
+  constexpr int T = C::T;
+  constexpr int P = C::P;
+  constexpr int R0 = ListInfo<L>::first;
+  constexpr int RL = ListInfo<L>::last;
+  using TC = TwCache<N, T, 1, L>;
+  __shared__ float2 lds[C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
+  const int tid = threadIdx.x;
+  TC twc;
+  twc.load_all(tw, lds + C::LDS, tid, tid, C::WG);
+  float2 h[Geom<N, T, RL>::B * RL];
+  load_filter<N>(h, H, tid);
+  const int64_t stride = gridDim.x;
+  int64_t line = blockIdx.x;
+  float2 pf[P], a[P], b[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) b[i] = make_float2(0.f, 0.f);
+  load_line<N, T, R0>(pf, LineIO(in, N, line, 1, lines), 0, tid);
+  touch<P>(pf);
+  for (; line + stride < lines; line += 2 * stride) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) a[i] = pf[i];
+    load_line<N, T, R0>(pf, LineIO(in, N, line + stride, 1, lines), 0, tid);
+    rc_line<N>(a, lds, twc, h, tid);
+    store_line<N, T, R0>(a, LineIO(out, N, line, 1, lines), 0, tid);
+    touch<P>(pf);
+    touch<P>(b);
+#pragma unroll
+    for (int i = 0; i < P; ++i) b[i] = pf[i];
+    load_line<N, T, R0>(pf, LineIO(in, N, line + 2 * stride, 1, lines), 0, tid);
+    rc_line<N>(b, lds, twc, h, tid);
+    store_line<N, T, R0>(b, LineIO(out, N, line + stride, 1, lines), 0, tid);
+    touch<P>(pf);
+    touch<P>(a);
+  }
+  if (line < lines) {  // odd tail
+#pragma unroll
+    for (int i = 0; i < P; ++i) a[i] = pf[i];
+    rc_line<N>(a, lds, twc, h, tid);
+    store_line<N, T, R0>(a, LineIO(out, N, line, 1, lines), 0, tid);
   }
 }
 
@@ -68,18 +202,14 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * C::LDS;
   for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < lines; l0 += int64_t(gridDim.x) * C::LPW) {
-    const int64_t line = l0 + grp;
-    const bool live = line < lines;
     float2 v[C::P];
-#pragma unroll
-    for (int i = 0; i < C::P; ++i) v[i] = make_float2(0.f, 0.f);
-    if (live) load_global<N, T, RI>(v, in + line * N, tid);
+    load_line<N, T, RI>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
     Passes<N, T, DIR, 1, L>::run(v, my, tw, tid);
     if (scale != 1.0f) {
 #pragma unroll
       for (int i = 0; i < C::P; ++i) v[i] = cscale(v[i], scale);
     }
-    if (live) store_global<N, T, RO>(v, out + line * N, tid);
+    store_line<N, T, RO>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
   }
 }
 
@@ -103,32 +233,27 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   float2* my = lds + grp * C::LDS;
   for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < lines; l0 += int64_t(gridDim.x) * C::LPW) {
     const int64_t line = l0 + grp;
-    const bool live = line < lines;
     float2 v[C::P];
-#pragma unroll
-    for (int i = 0; i < C::P; ++i) v[i] = make_float2(0.f, 0.f);
+    load_line<N, T, RI>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
     const double* Dl = opaque(Dk);
-    if (live) {
-      load_global<N, T, RI>(v, in + line * N, tid);
-      const double a = c.two_over_lambda * (c.rb0 + double(line) * c.dr);
-      using G = Geom<N, T, RI>;
+    const double a = c.two_over_lambda * (c.rb0 + double(line) * c.dr);
+    using G = Geom<N, T, RI>;
 #pragma unroll
-      for (int b = 0; b < G::B; ++b) {
-        const int j = tid + b * T;
-        if (G::live(j)) {
+    for (int b = 0; b < G::B; ++b) {
+      const int j = tid + b * T;
+      if (G::live(j)) {
 #pragma unroll
-          for (int r = 0; r < RI; ++r) {
-            const double cyc = a * Dl[j + r * G::NB];
-            const float f = float(cyc - rint(cyc));
-            float s, co;
-            sincospif(2.0f * f, &s, &co);
-            v[b * RI + r] = cmul(v[b * RI + r], make_float2(co * c.inv_na, s * c.inv_na));
-          }
+        for (int r = 0; r < RI; ++r) {
+          const double cyc = a * Dl[j + r * G::NB];
+          const float f = float(cyc - rint(cyc));
+          float s, co;
+          sincospif(2.0f * f, &s, &co);
+          v[b * RI + r] = cmul(v[b * RI + r], make_float2(co * c.inv_na, s * c.inv_na));
         }
       }
     }
     Passes<N, T, +1, 1, L>::run(v, my, tw, tid);
-    if (live) store_global<N, T, RO>(v, out + line * N, tid);
+    store_line<N, T, RO>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
   }
 }
 
@@ -243,10 +368,52 @@ hipError_t occupancy(int* rc, int* fft, int* azc) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(azc, k_az_compress<N>, LineCfg<N>::WG, 0);
 }
 
+#ifndef RD_RC_PREFETCH
+#define RD_RC_PREFETCH true
+#endif
+template <int N>
+hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const float2* tw,
+                        int64_t lines, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_range_compress_pf<N, RD_RC_PREFETCH>), dim3(grid), dim3(LineCfg<N>::WG), 0,
+                     s, in, out, H, tw, lines);
+  return hipGetLastError();
+}
+
+template <int N>
+hipError_t launch_rc_pf2(const float2* in, float2* out, const float2* H, const float2* tw,
+                         int64_t lines, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_range_compress_pf2<N>, dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, H,
+                     tw, lines);
+  return hipGetLastError();
+}
+
+template <int N>
+hipError_t occupancy_pf(int* rc) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf<N, RD_RC_PREFETCH>,
+                                                      LineCfg<N>::WG, 0);
+}
+
+template <int N>
+hipError_t occupancy_pf2(int* rc) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf2<N>, LineCfg<N>::WG,
+                                                      0);
+}
+
 template <int N>
 constexpr LineOps make_ops() {
-  return LineOps{N,           LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>,
-                 &launch_fft<N>, &launch_azc<N>, &occupancy<N>};
+  constexpr bool sym = std::is_same<typename LineCfg<N>::Fwd, typename LineCfg<N>::Inv>::value;
+  if constexpr (sym && LineCfg<N>::LPW == 1) {
+    return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
+                   &launch_azc<N>, &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>,
+                   &launch_rc_pf2<N>, &occupancy_pf2<N>};
+  } else if constexpr (sym) {
+    return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
+                   &launch_azc<N>, &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>,
+                   nullptr, nullptr};
+  } else {
+    return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
+                   &launch_azc<N>, &occupancy<N>, nullptr, nullptr, nullptr, nullptr};
+  }
 }
 
 static const LineOps kOps[] = {make_ops<256>(),  make_ops<512>(),  make_ops<1024>(),

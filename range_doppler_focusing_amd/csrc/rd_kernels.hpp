@@ -39,6 +39,15 @@ struct LineOps {
                             AzFilterConst c, int64_t lines, int grid, hipStream_t s);
   // workgroups of each persistent kernel that fit on one CU
   hipError_t (*occupancy)(int* rc, int* fft, int* azc);
+  // register-cached, prefetching range compression (nullptr where the forward and inverse
+  // radix lists differ) and its occupancy
+  hipError_t (*range_compress_pf)(const float2* in, float2* out, const float2* H,
+                                  const float2* tw, int64_t lines, int grid, hipStream_t s);
+  hipError_t (*occupancy_pf)(int* rc);
+  // two lines per trip with alternating register sets (one line per workgroup only)
+  hipError_t (*range_compress_pf2)(const float2* in, float2* out, const float2* H,
+                                   const float2* tw, int64_t lines, int grid, hipStream_t s);
+  hipError_t (*occupancy_pf2)(int* rc);
 };
 
 // nullptr if the length has no built transform
