@@ -4,9 +4,12 @@
  * The library focuses a raw SAR echo with the Range-Doppler chain:
  *   range compression per pulse  : FFT along range, multiply by the precomputed matched filter
  *                                  H(f), inverse FFT (one fused kernel, line resident in LDS);
- *   azimuth processing per bin   : corner turn, azimuth FFT, range cell migration correction
- *                                  (RCMC, 8-tap Kaiser-windowed sinc), azimuth matched filter,
- *                                  azimuth inverse FFT, corner turn back.
+ *   azimuth processing           : azimuth FFT down every range bin, range cell migration
+ *                                  correction (RCMC, 8-tap Kaiser-windowed sinc) along range in
+ *                                  every Doppler row, azimuth matched filter, azimuth inverse
+ *                                  FFT -- all on the [Na][Nr] array in place, without corner
+ *                                  turns (the azimuth transforms run as two passes of short
+ *                                  transforms over strided / contiguous row sets).
  * Sources: cf-1.com/news/2323550 ("SAR imaging acceleration on Apple Silicon") §2.1 (the RD
  * steps), §3.1 (fused FFT -> filter -> IFFT per range line), §3.2 (inverse transform by
  * conj-FFT-conj), §5.1 (azimuth FFT, sinc RCMC, azimuth filter + IFFT); nxmr.cn/news/101525
@@ -18,8 +21,8 @@
  *  - Complex samples are interleaved float32 pairs (rd_c64), row-major [Na][Nr]: row m is the
  *    m-th pulse (range line), column n the n-th range sample.  Outputs use the same layout.
  *  - Data pointers are DEVICE pointers on the plan's device, 8-byte aligned, owned by the
- *    caller; the library never frees them.  The plan owns its own filter, twiddle and
- *    workspace buffers (about one image of workspace: Na*Nr*8 bytes).
+ *    caller; the library never frees them.  The plan owns its filter, twiddle and coefficient
+ *    tables (a few hundred KB); focusing needs no further workspace.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue work and return:
  *    results are ready once the stream is synchronised.  Argument errors are reported
  *    synchronously before anything is enqueued; launch errors are reported by the call;
@@ -87,8 +90,10 @@ typedef struct {
 
 typedef struct rd_plan rd_plan;
 
-/* Returns 1 if `n` is a transform length this build supports (256..16384 powers of two, and
- * 6000 = 2^4 * 3 * 5^3), else 0. */
+/* Returns 1 if `n` is a range-line length this build supports (256..16384 powers of two, and
+ * 6000 = 2^4 * 3 * 5^3), else 0.  Full-chain plans also need Na a power of two in
+ * [256, 16384], Na*Nr*8 < 4 GiB, and a range migration R(n)(1/D_k - 1)/dr below Nr/8 - 4
+ * samples over the whole Doppler band (checked by rd_plan_create). */
 int rd_length_supported(int32_t n);
 
 /* Validates `params`, builds the matched filter H (float64 -> float32), the twiddle and
@@ -119,9 +124,10 @@ rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* s
 rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream);
 
 /* Test hook: the azimuth chain with its intermediates exposed.  azfft and rcmc receive the
- * azimuth spectrum and the RCMC output in the corner-turned layout [Nr][Na] (row n = range
- * bin, column k = Doppler bin); img receives the image [Na][Nr].  azfft, rcmc and img must be
- * distinct from each other and from rc (img may equal rc). */
+ * azimuth spectrum S[k][n] and the RCMC output T[k][n], [Na][Nr] with row k = Doppler bin in
+ * FFT order; img receives the image [Na][Nr].  azfft, rcmc and img must be distinct from each
+ * other and from rc (img may equal rc).  The first call allocates a stage workspace of one
+ * image (Na*Nr*8 bytes) owned by the plan. */
 rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft, rd_c64* rcmc,
                                   rd_c64* img, void* stream);
 

@@ -74,10 +74,11 @@ class Plan:
         return out
 
     def azimuth_stages(self, rc):
-        """(azfft [Nr][Na], rcmc [Nr][Na], img [Na][Nr]) of the azimuth chain."""
+        """(azfft, rcmc, img), each [Na][Nr]: azimuth spectrum and RCMC output with row k the
+        Doppler bin in FFT order, and the focused image."""
         self._check(rc, (self.Na, self.Nr))
-        az = self._empty((self.Nr, self.Na))
-        rcmc = self._empty((self.Nr, self.Na))
+        az = self._empty((self.Na, self.Nr))
+        rcmc = self._empty((self.Na, self.Nr))
         img = self._empty((self.Na, self.Nr))
         rd_debug_azimuth_stages(self.handle, rc, az, rcmc, img)
         return az, rcmc, img

@@ -618,4 +618,43 @@ RDF_LINE_CFG(6000, 400, L_16_15_25, L_25_15_16)
 
 #undef RDF_LINE_CFG
 
+// ---------------------------------------------------------------------------- column configurations
+// Length-L transforms along the rows of a row-major array (one column per lane, 64 columns per
+// workgroup).  T = L/16 threads per column hold 16 points each in radix-16 passes.
+template <int L>
+struct ColCfg;
+
+#define RDF_COL_CFG(L_, FWD, INV)                                                 \
+  template <>                                                                     \
+  struct ColCfg<L_> {                                                             \
+    static constexpr int L = L_;                                                  \
+    static constexpr int T = L_ / 16;                                             \
+    static constexpr int COLS = 64;                                               \
+    static constexpr int WG = T * COLS;                                           \
+    using Fwd = FWD;                                                              \
+    using Inv = INV;                                                              \
+    static constexpr int LDS = lds_len(L_) | 1;                                   \
+    static constexpr int P = MaxRegs<L_, T, FWD>::value > MaxRegs<L_, T, INV>::value \
+                                 ? MaxRegs<L_, T, FWD>::value                     \
+                                 : MaxRegs<L_, T, INV>::value;                    \
+    static_assert(ListInfo<FWD>::product == L_ && ListInfo<INV>::product == L_,   \
+                  "radix list must multiply to L");                               \
+  };
+
+using L_16 = IntList<16>;
+using L_16_2 = IntList<16, 2>;
+using L_2_16 = IntList<2, 16>;
+using L_16_4 = IntList<16, 4>;
+using L_4_16 = IntList<4, 16>;
+using L_16_8 = IntList<16, 8>;
+using L_8_16 = IntList<8, 16>;
+
+RDF_COL_CFG(16, L_16, L_16)
+RDF_COL_CFG(32, L_16_2, L_2_16)
+RDF_COL_CFG(64, L_16_4, L_4_16)
+RDF_COL_CFG(128, L_16_8, L_8_16)
+RDF_COL_CFG(256, L_16_16, L_16_16)
+
+#undef RDF_COL_CFG
+
 }  // namespace rdf

@@ -50,17 +50,15 @@ struct rd_plan {
   const rdf::LineOps* aops = nullptr;  // azimuth-length kernels
   int rc_variant = 0;   // 0 table loads, 1 register-cached (pf), 2 two-line alternating (pf2)
   int rc_grid = 0;      // persistent grid of the range kernels
-  int afft_grid = 0;    // persistent grid of the azimuth FFT
-  int azc_grid = 0;     // persistent grid of the azimuth filter + IFFT
-  int rfft_grid = 0;    // persistent grid of a range-length FFT
+  int A = 0, B = 0;     // Na = A B: strided and block steps of the azimuth transform
   float2* H = nullptr;       // [Nr] conj(FFT(h)) / Nr
   float2* tw_r = nullptr;    // [Nr] e^{-j 2 pi k / Nr}
-  float2* tw_a = nullptr;    // [Na] e^{-j 2 pi k / Na}
-  double* Dk = nullptr;      // [Na] sqrt(1 - (lambda f_k / 2V)^2)
-  double* Qk = nullptr;      // [Na] u_k / (D_k (1 + D_k)) / dr
-  float2* work = nullptr;    // [Na * Nr] workspace
-  rdf::AzFilterConst azc{};
-  rdf::RcmcConst rcmc{};
+  float2* tw_a = nullptr;    // [Na] e^{-j 2 pi k / Na} (line-transform test hook)
+  float2* tw_A = nullptr;    // [A] e^{-j 2 pi k / A}
+  float2* tw_B = nullptr;    // [B] e^{-j 2 pi k / B}
+  double* rowc = nullptr;    // [Na][4] RCMC shift and filter phase coefficients per Doppler bin
+  float2* work = nullptr;    // [Na * Nr] workspace (stage test hook only, allocated on first use)
+  rdf::AzRowConst az{};
 };
 
 namespace {
@@ -74,8 +72,9 @@ void free_plan(rd_plan* p) {
   (void)hipFree(p->H);
   (void)hipFree(p->tw_r);
   (void)hipFree(p->tw_a);
-  (void)hipFree(p->Dk);
-  (void)hipFree(p->Qk);
+  (void)hipFree(p->tw_A);
+  (void)hipFree(p->tw_B);
+  (void)hipFree(p->rowc);
   (void)hipFree(p->work);
   delete p;
 }
@@ -139,6 +138,75 @@ std::vector<float2> matched_filter(const rd_params& p, int L) {
   return H;
 }
 
+// RCMC tap weights (nxmr.cn/news/101525 §2.2 interpolates the migrated range; the 8-tap
+// Kaiser-windowed sinc is the interpolator).  For fraction f in [0, 1) the output reads samples
+// floor(x) - 3 .. floor(x) + 4 with weights w_j = sinc(f - j) K(f - j) / sum, K the Kaiser
+// window over the 8-tap span.  sinc(f - j) = (-1)^j sin(pi f) / (pi (f - j)); multiplying every
+// tap by the common factor pi prod_i (f - i) / sin(pi f) gives
+//   b_j(f) = (-1)^j K(f - j) prod_{i != j} (f - i),
+// smooth in f (no division, no f = 0 special case), with the same normalised weights.  Each b_j
+// is interpolated at 9 Chebyshev points of [0, 1] (degree 8; max error ~5e-9 of max|b|) and
+// stored as monomial coefficients in x = f - 1/2 for Horner evaluation in float32.
+double bessel_i0(double z) {
+  const double y = 0.25 * z * z;
+  double term = 1.0, sum = 1.0;
+  for (int m = 1; m < 200 && term > 1e-18 * sum; ++m) {
+    term *= y / (double(m) * double(m));
+    sum += term;
+  }
+  return sum;
+}
+
+void rcmc_weight_polys(double beta, rdf::RcmcPoly* out) {
+  constexpr int D = rdf::kRcmcDeg, M = D + 1;
+  const double half = rdf::kRcmcTaps / 2.0;
+  const double i0b = bessel_i0(beta);
+  for (int t = 0; t < rdf::kRcmcTaps; ++t) {
+    const int j = t - (rdf::kRcmcTaps / 2 - 1);
+    auto b = [&](double f) {
+      const double tt = f - j;
+      const double a = 1.0 - (tt / half) * (tt / half);
+      double v = bessel_i0(beta * std::sqrt(a > 0 ? a : 0.0)) / i0b;
+      for (int i = -(rdf::kRcmcTaps / 2 - 1); i <= rdf::kRcmcTaps / 2; ++i)
+        if (i != j) v *= (f - i);
+      return (j & 1) ? -v : v;
+    };
+    double cheb[M] = {};
+    for (int k = 0; k < M; ++k) {
+      double acc = 0.0;
+      for (int i = 0; i < M; ++i) {
+        const double th = M_PI * (i + 0.5) / M;
+        acc += b(0.5 + 0.5 * std::cos(th)) * std::cos(k * th);
+      }
+      cheb[k] = acc * 2.0 / M;
+    }
+    cheb[0] *= 0.5;
+    // sum_k cheb[k] T_k(u) -> monomials in u, then u = 2x
+    double mono[M] = {}, tkm1[M] = {}, tk[M] = {};
+    tkm1[0] = 1.0;                 // T_0
+    tk[1] = 1.0;                   // T_1
+    mono[0] += cheb[0];
+    for (int m = 0; m < M; ++m) mono[m] += cheb[1] * tk[m];
+    for (int k = 2; k < M; ++k) {
+      double tn[M] = {};
+      for (int m = 0; m < M; ++m) {
+        if (m > 0) tn[m] += 2.0 * tk[m - 1];
+        tn[m] -= tkm1[m];
+      }
+      for (int m = 0; m < M; ++m) {
+        mono[m] += cheb[k] * tn[m];
+        tkm1[m] = tk[m];
+        tk[m] = tn[m];
+      }
+    }
+    double p2 = 1.0;
+    for (int m = 0; m < M; ++m) {
+      out->c[t][m] = float(mono[m] * p2);
+      p2 *= 2.0;
+    }
+  }
+}
+
 rd_status check_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return RD_OK;
   return fail(RD_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -181,36 +249,50 @@ rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, hipStrea
                    "range compression launch");
 }
 
-// rc [Na][Nr] -> azT [Nr][Na] (corner turn + azimuth FFT along each row)
-rd_status run_az_fft(rd_plan* P, const float2* rc, float2* azT, hipStream_t s) {
-  rd_status st = check_hip(rdf::launch_corner_turn(rc, azT, P->p.Na, P->p.Nr, s), "corner turn");
-  if (st != RD_OK) return st;
-  return check_hip(P->aops->fft(azT, azT, P->tw_a, P->p.Nr, 0, 1.0f, P->afft_grid, s),
-                   "azimuth FFT launch");
+// Azimuth processing in place on [Na][Nr] (no corner turns):
+//   forward transform, strided step (reads `src`, writes `dst`) then block step;
+//   RCMC + filter per Doppler row; inverse transform, block step then strided step.
+rdf::ColStep col_step(const rd_plan* P, bool forward, bool strided) {
+  rdf::ColStep st{};
+  st.dir = forward ? -1 : +1;
+  if (strided) {
+    st.L = P->A;
+    st.base_mul = 1;
+    st.stride = P->B;
+    st.sets = P->B;
+    st.twiddle = forward ? 1 : 0;
+  } else {
+    st.L = P->B;
+    st.base_mul = P->B;
+    st.stride = 1;
+    st.sets = P->A;
+    st.twiddle = forward ? 0 : 1;
+  }
+  return st;
 }
 
-rd_status run_rcmc(rd_plan* P, const float2* azT, float2* rcmcT, hipStream_t s) {
-  return check_hip(rdf::launch_rcmc8(azT, rcmcT, P->Qk, P->rcmc, P->p.Nr, P->p.Na, s),
-                   "RCMC launch");
+rd_status run_col(rd_plan* P, const float2* src, float2* dst, bool forward, bool strided,
+                  hipStream_t s) {
+  const rdf::ColStep st = col_step(P, forward, strided);
+  return check_hip(rdf::launch_col_fft(src, dst, strided ? P->tw_A : P->tw_B, st, P->p.Nr, P->p.Na, s),
+                   "azimuth transform launch");
 }
 
-// rcmcT [Nr][Na] -> (filter, inverse azimuth FFT) tmpT [Nr][Na] -> corner turn -> img [Na][Nr]
-rd_status run_az_compress(rd_plan* P, const float2* rcmcT, float2* tmpT, float2* img,
-                          hipStream_t s) {
-  rd_status st = check_hip(
-      P->aops->az_compress(rcmcT, tmpT, P->tw_a, P->Dk, P->azc, P->p.Nr, P->azc_grid, s),
-      "azimuth compression launch");
-  if (st != RD_OK) return st;
-  return check_hip(rdf::launch_corner_turn(tmpT, img, P->p.Nr, P->p.Na, s), "corner turn");
+rd_status run_rows(rd_plan* P, const float2* src, float2* dst, bool filter, hipStream_t s) {
+  rdf::AzRowConst c = P->az;
+  c.filter = filter ? 1 : 0;
+  const int grid = int((P->p.Na + P->rops->lpw - 1) / P->rops->lpw);
+  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, grid, s), "RCMC launch");
 }
 
 rd_status run_azimuth(rd_plan* P, const float2* rc, float2* img, hipStream_t s) {
-  // rc is consumed by the first corner turn, so img may alias it
-  rd_status st = run_az_fft(P, rc, P->work, s);
-  if (st != RD_OK) return st;
-  st = run_rcmc(P, P->work, img, s);
-  if (st != RD_OK) return st;
-  return run_az_compress(P, img, P->work, img, s);
+  // rc is read only by the first step, so img may alias it
+  rd_status st;
+  if ((st = run_col(P, rc, img, true, true, s)) != RD_OK) return st;
+  if ((st = run_col(P, img, img, true, false, s)) != RD_OK) return st;
+  if ((st = run_rows(P, img, img, true, s)) != RD_OK) return st;
+  if ((st = run_col(P, img, img, false, false, s)) != RD_OK) return st;
+  return run_col(P, img, img, false, true, s);
 }
 
 }  // namespace
@@ -265,6 +347,11 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   if (all_az) {
     aops = rdf::line_ops(p.Na);
     if (!aops) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length Na=%d is built", p.Na);
+    if (p.Na < 256 || p.Na > 16384 || (p.Na & (p.Na - 1)) != 0)
+      return fail(RD_ERR_UNSUPPORTED_LENGTH,
+                  "full-chain plans need Na a power of two in [256, 16384] (Na=%d)", p.Na);
+    if (int64_t(p.Na) * p.Nr * 8 > int64_t(0xFFFFFFF0))
+      return fail(RD_ERR_INVALID_ARG, "full-chain plans need Na*Nr*8 < 4 GiB");
     if (p.rcmc_taps != 8)
       return fail(RD_ERR_INVALID_ARG, "rcmc_taps=%d: only the 8-tap interpolator is built", p.rcmc_taps);
     if (!(p.kaiser_beta >= 0.0 && p.kaiser_beta <= 12.0))
@@ -324,60 +411,43 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     const char* g = std::getenv("RD_RC_GRID");  // workgroups of the range kernel (tuning)
     if (g && std::atoi(g) > 0) P->rc_grid = std::atoi(g);
   }
-  P->rfft_grid = occ_fft;  // scaled by lines at launch time
 
+  if ((st = upload(&P->tw_a, roots_table(rdf::line_ops(p.Na) ? p.Na : 1), "azimuth twiddles")) != RD_OK)
+    return bail(st);
   if (all_az) {
     const int Na = p.Na;
     const double lam = kC / p.carrier_hz;
-    std::vector<double> D(Na), Q(Na);
+    // Na = A B with A the largest power of two <= sqrt(Na)
+    P->A = 1;
+    while (P->A * P->A * 4 <= Na) P->A *= 2;
+    P->B = Na / P->A;
+    std::vector<double> rowc(size_t(Na) * 4);
+    double max_shift = 0.0;
     for (int k = 0; k < Na; ++k) {
       const int kk = (k <= (Na - 1) / 2) ? k : k - Na;  // FFT bin order
       const double f = double(kk) * p.prf_hz / double(Na);
       const double u = std::pow(lam * f / (2.0 * p.velocity_mps), 2);
-      D[k] = std::sqrt(1.0 - u);
-      Q[k] = u / (D[k] * (1.0 + D[k])) / P->dr;
+      const double D = std::sqrt(1.0 - u);
+      const double Q = u / (D * (1.0 + D)) / P->dr;  // shift per metre of slant range, samples
+      rowc[4 * k + 0] = p.range_bin0_m * Q;          // Delta(n) = alpha + n beta
+      rowc[4 * k + 1] = P->dr * Q;
+      rowc[4 * k + 2] = 2.0 * D * p.range_bin0_m / lam;  // phase cycles = gamma + n delta
+      rowc[4 * k + 3] = 2.0 * D * P->dr / lam;
+      max_shift = std::max(max_shift, rowc[4 * k] + double(p.Nr - 1) * rowc[4 * k + 1]);
     }
-    if ((st = upload(&P->tw_a, roots_table(Na), "azimuth twiddles")) != RD_OK) return bail(st);
-    if ((st = upload(&P->Dk, D, "azimuth migration factors")) != RD_OK) return bail(st);
-    if ((st = upload(&P->Qk, Q, "RCMC shift factors")) != RD_OK) return bail(st);
-    const size_t bytes = size_t(p.Na) * size_t(p.Nr) * sizeof(float2);
-    if (hipMalloc(&P->work, bytes) != hipSuccess) {
-      P->work = nullptr;
-      return bail(fail(RD_ERR_OUT_OF_MEMORY, "hipMalloc of the %zu-byte workspace failed", bytes));
-    }
-    int a_rc = 0, a_fft = 0, a_azc = 0;
-    if (aops->occupancy(&a_rc, &a_fft, &a_azc) != hipSuccess)
-      return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
-    P->afft_grid = persistent_grid(a_fft, P->cus, p.Nr, aops->lpw);
-    P->azc_grid = persistent_grid(a_azc, P->cus, p.Nr, aops->lpw);
-    P->azc.rb0 = p.range_bin0_m;
-    P->azc.dr = P->dr;
-    P->azc.two_over_lambda = 2.0 / lam;
-    P->azc.inv_na = float(1.0 / double(Na));
-    // Kaiser window as a series in y = (beta/2)^2 (1 - (t/4)^2): I0 = sum y^m / (m!)^2
-    const double y0 = 0.25 * p.kaiser_beta * p.kaiser_beta;
-    int M = 1;
-    double term = y0;  // y0^m / (m!)^2 at m = M
-    while (M + 1 < rdf::kRcmcMaxTerms && term > 1e-10) {
-      ++M;
-      term *= y0 / (double(M) * double(M));
-    }
-    P->rcmc.rb0 = p.range_bin0_m;
-    P->rcmc.dr = P->dr;
-    P->rcmc.y0 = float(y0);
-    P->rcmc.y1 = float(y0 / 16.0);
-    P->rcmc.nterm = M + 1;
-    double inv_fact2 = 1.0;
-    std::vector<double> coef(M + 1);
-    for (int m = 0; m <= M; ++m) {
-      if (m > 0) inv_fact2 /= double(m) * double(m);
-      coef[m] = inv_fact2;
-    }
-    for (int m = 0; m <= M; ++m) P->rcmc.coef[m] = float(coef[M - m]);
-  } else {
-    if ((st = upload(&P->tw_a, roots_table(rdf::line_ops(p.Na) ? p.Na : 1), "azimuth twiddles")) !=
-        RD_OK)
-      return bail(st);
+    if (std::floor(max_shift) + 4 > double(rops->margin))
+      return bail(fail(RD_ERR_UNSUPPORTED_LENGTH,
+                       "range migration of %.1f samples exceeds the %d-sample margin built for Nr=%d",
+                       max_shift, rops->margin - 4, p.Nr));
+    if ((st = upload(&P->tw_A, roots_table(P->A), "azimuth step twiddles")) != RD_OK) return bail(st);
+    if ((st = upload(&P->tw_B, roots_table(P->B), "azimuth step twiddles")) != RD_OK) return bail(st);
+    if ((st = upload(&P->rowc, rowc, "azimuth row coefficients")) != RD_OK) return bail(st);
+    P->az.row = P->rowc;
+    P->az.A = P->A;
+    P->az.B = P->B;
+    P->az.inv_na = float(1.0 / double(Na));
+    P->az.filter = 1;
+    rcmc_weight_polys(p.kaiser_beta, &P->az.w);
   }
   {
     std::lock_guard<std::mutex> g(g_plans_mu);
@@ -450,12 +520,26 @@ rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft
       if (overlap && !(same_ok && x == y))
         return fail(RD_ERR_INVALID_ARG, "debug buffers %d and %d overlap", a, b);
     }
+  if (!plan->work && hipMalloc(&plan->work, bytes) != hipSuccess) {
+    plan->work = nullptr;
+    return fail(RD_ERR_OUT_OF_MEMORY, "hipMalloc of the %zu-byte stage workspace failed", bytes);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float2* A = reinterpret_cast<float2*>(azfft);
-  float2* R = reinterpret_cast<float2*>(rcmc);
-  if ((st = run_az_fft(plan, reinterpret_cast<const float2*>(rc), A, s)) != RD_OK) return st;
-  if ((st = run_rcmc(plan, A, R, s)) != RD_OK) return st;
-  return run_az_compress(plan, R, plan->work, reinterpret_cast<float2*>(img), s);
+  float2* I = reinterpret_cast<float2*>(img);
+  float2* W = plan->work;
+  const int64_t Nr = plan->p.Nr;
+  if ((st = run_col(plan, reinterpret_cast<const float2*>(rc), I, true, true, s)) != RD_OK) return st;
+  if ((st = run_col(plan, I, I, true, false, s)) != RD_OK) return st;
+  if ((st = run_rows(plan, I, W, false, s)) != RD_OK) return st;  // RCMC alone
+  if ((st = check_hip(rdf::launch_row_unpermute(I, reinterpret_cast<float2*>(azfft), plan->A, plan->B,
+                                                Nr, s), "row order launch")) != RD_OK)
+    return st;
+  if ((st = check_hip(rdf::launch_row_unpermute(W, reinterpret_cast<float2*>(rcmc), plan->A, plan->B,
+                                                Nr, s), "row order launch")) != RD_OK)
+    return st;
+  if ((st = run_rows(plan, I, I, true, s)) != RD_OK) return st;
+  if ((st = run_col(plan, I, I, false, false, s)) != RD_OK) return st;
+  return run_col(plan, I, I, false, true, s);
 }
 
 rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const rd_c64* in,

@@ -214,118 +214,178 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
 }
 
 // ------------------------------------------------------------------------------------------
-// azimuth filter + inverse azimuth FFT, one row (range bin n) of the [Nr][Na] layout per line:
-//   out[n][m] = (1/Na) sum_k in[n][k] exp(+j 4 pi R(n) D_k / lambda) e^{+j 2 pi k m / Na}
-// The filter phase is formed in float64 (4 pi R D / lambda reaches ~1e7 rad), reduced to the
-// nearest whole cycle, and only the residual (|frac| <= 1/2 cycle) is taken to float32.
+// Azimuth transforms without corner turns (four-step over the rows of the [Na][Nr] array).
+// With Na = A B, row m = B m1 + m2 and Doppler k = k1 + A k2:
+//   forward step 1 (strided): for each m2, DFT_A over rows B m1 + m2, then x W_Na^{m2 k1};
+//                              row B k1 + m2 then holds Y[k1][m2]
+//   forward step 2 (block):    for each k1, DFT_B over the contiguous rows B k1 + m2;
+//                              row B k1 + k2 then holds X[k1 + A k2]  (Doppler-digit order)
+//   inverse step 1 (block):    for each k1, DFT_B^-1 over rows B k1 + k2, then x W_Na^{-m2 k1}
+//   inverse step 2 (strided):  for each m2, DFT_A^-1 over rows B k1 + m2 -> row B m1 + m2.
+// A workgroup takes one row set (L rows) x 64 columns; each lane owns one column, so every
+// global access of a wave is one contiguous 512-byte row segment.  In place (out may equal in).
+struct ColGeom {
+  int64_t cols;      // row length (elements)
+  int base_mul;      // first row of row set g = g * base_mul
+  int stride;        // row stride inside a set
+  int chunks;        // column chunks of 64
+  int na;            // total transform length (for the inter-step twiddle), power of two
+  int twiddle;       // multiply output t by W_Na^{DIR g t} after the transform
+};
+
+template <int L, int DIR>
+__global__ void __launch_bounds__(ColCfg<L>::WG)
+    k_col_fft(const float2* in, float2* out, const float2* __restrict__ tw, ColGeom cg,
+              uint32_t bytes) {
+  using C = ColCfg<L>;
+  using LST = typename std::conditional<(DIR < 0), typename C::Fwd, typename C::Inv>::type;
+  constexpr int T = C::T;
+  constexpr int RI = ListInfo<LST>::first;
+  constexpr int RO = ListInfo<LST>::last;
+  using TC = TwCache<L, T, 1, LST>;
+  __shared__ float2 lds[C::COLS * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
+  const int col = threadIdx.x & 63;
+  const int tid = threadIdx.x >> 6;
+  float2* my = lds + col * C::LDS;
+  TC twc;
+  twc.load_all(tw, lds + C::COLS * C::LDS, tid, threadIdx.x, C::WG);
+  const int g = blockIdx.x / cg.chunks;
+  const int64_t c = int64_t(blockIdx.x - g * cg.chunks) * 64 + col;
+  const bool live = c < cg.cols;
+  const int64_t row0 = int64_t(g) * cg.base_mul;
+  // byte offset of element t of this lane's column (out of range -> zero / dropped)
+  auto off = [&](int t) -> uint32_t {
+    return live ? uint32_t(((row0 + int64_t(t) * cg.stride) * cg.cols + c) * 8) : 0xFFFFFFF0u;
+  };
+  const __amdgpu_buffer_rsrc_t rin =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(in), 0, int(bytes), kBufDword3);
+  const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(out, 0, int(bytes), kBufDword3);
+  float2 v[C::P];
+  {
+    using G = Geom<L, T, RI>;
+#pragma unroll
+    for (int b = 0; b < G::B; ++b) {
+      const int j = tid + b * T;
+#pragma unroll
+      for (int r = 0; r < RI; ++r)
+        v[b * RI + r] = __builtin_bit_cast(
+            float2, __builtin_amdgcn_raw_buffer_load_b64(rin, off(j + r * G::NB), 0, kBufNonTemporal));
+    }
+  }
+  PassesCached<L, T, DIR, 1, LST>::run(v, my, twc, tid);
+  {
+    using G = Geom<L, T, RO>;
+#pragma unroll
+    for (int b = 0; b < G::B; ++b) {
+      const int j = tid + b * T;
+#pragma unroll
+      for (int r = 0; r < RO; ++r) {
+        const int t = j + r * G::NB;
+        float2 x = v[b * RO + r];
+        if (cg.twiddle) {
+          // exact argument: (g t mod Na) / Na, Na a power of two
+          const int e = (g * t) & (cg.na - 1);
+          float sn, cs;
+          sincospif(float(e) * (2.0f / float(cg.na)), &sn, &cs);
+          x = cmul(x, make_float2(cs, DIR > 0 ? sn : -sn));
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout, off(t), 0,
+                                              kBufNonTemporal);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// RCMC + azimuth filter per Doppler row (constants in rd_kernels.hpp).  The row is staged in LDS
+// between 3 leading and MARGIN trailing zeros, so every tap is a plain LDS read and samples
+// outside the line read as zero.  Shift and filter phase are formed in float64 (the phase
+// reaches ~1e7 rad) and reduced before they are taken to float32.
+template <int N>
+struct RowStage {
+  static constexpr int MARGIN = N / 8;
+  static constexpr int LEN = 3 + N + MARGIN;
+};
+
 template <int N>
 __global__ void __launch_bounds__(LineCfg<N>::WG)
-    k_az_compress(const float2* in, float2* out, const float2* __restrict__ tw,
-                  const double* __restrict__ Dk, AzFilterConst c, int64_t lines) {
+    k_rcmc_mf(const float2* in, float2* out, AzRowConst c, int64_t rows) {
   using C = LineCfg<N>;
-  using L = typename C::Inv;
+  using RS = RowStage<N>;
   constexpr int T = C::T;
-  constexpr int RI = ListInfo<L>::first;
-  constexpr int RO = ListInfo<L>::last;
-  __shared__ float2 lds[C::LPW * C::LDS];
+  constexpr int R0 = ListInfo<typename C::Fwd>::first;
+  using G = Geom<N, T, R0>;
+  __shared__ float2 lds[C::LPW * RS::LEN];
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
-  float2* my = lds + grp * C::LDS;
-  for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < lines; l0 += int64_t(gridDim.x) * C::LPW) {
-    const int64_t line = l0 + grp;
+  float2* my = lds + grp * RS::LEN;
+  for (int i = threadIdx.x; i < C::LPW * RS::LEN; i += C::WG) lds[i] = make_float2(0.f, 0.f);
+  for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < rows; l0 += int64_t(gridDim.x) * C::LPW) {
+    const int64_t row = l0 + grp;
+    const int64_t rr = row < rows ? row : rows - 1;
+    const int k = int(rr / c.B) + c.A * int(rr % c.B);
+    const double alpha = c.row[4 * k], beta = c.row[4 * k + 1];
+    const double gamma = c.row[4 * k + 2], delta = c.row[4 * k + 3];
     float2 v[C::P];
-    load_line<N, T, RI>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
-    const double* Dl = opaque(Dk);
-    const double a = c.two_over_lambda * (c.rb0 + double(line) * c.dr);
-    using G = Geom<N, T, RI>;
+    load_line<N, T, R0>(v, LineIO(in, N, l0, C::LPW, rows), grp * N, tid);
+    __syncthreads();  // the previous row's taps have been read
 #pragma unroll
     for (int b = 0; b < G::B; ++b) {
       const int j = tid + b * T;
       if (G::live(j)) {
 #pragma unroll
-        for (int r = 0; r < RI; ++r) {
-          const double cyc = a * Dl[j + r * G::NB];
-          const float f = float(cyc - rint(cyc));
-          float s, co;
-          sincospif(2.0f * f, &s, &co);
-          v[b * RI + r] = cmul(v[b * RI + r], make_float2(co * c.inv_na, s * c.inv_na));
+        for (int r = 0; r < R0; ++r) my[3 + j + r * G::NB] = v[b * R0 + r];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < G::B; ++b) {
+      const int j = tid + b * T;
+      if (G::live(j)) {
+#pragma unroll
+        for (int r = 0; r < R0; ++r) {
+          const int n = j + r * G::NB;
+          const double x = alpha + double(n) * beta;
+          const double fl = floor(x);
+          const float f = float(x - fl) - 0.5f;
+          const float2* tap = my + (n + int(fl));  // tap t reads sample n + fl + t - 3
+          float2 acc = make_float2(0.f, 0.f);
+          float ws = 0.f;
+#pragma unroll
+          for (int t = 0; t < kRcmcTaps; ++t) {
+            float w = c.w.c[t][kRcmcDeg];
+#pragma unroll
+            for (int m = kRcmcDeg - 1; m >= 0; --m) w = fmaf(w, f, c.w.c[t][m]);
+            const float2 sv = tap[t];
+            acc.x = fmaf(w, sv.x, acc.x);
+            acc.y = fmaf(w, sv.y, acc.y);
+            ws += w;
+          }
+          const float sc = (c.filter ? c.inv_na : 1.0f) / ws;
+          float2 o = make_float2(acc.x * sc, acc.y * sc);
+          if (c.filter) {
+            const double cyc = gamma + double(n) * delta;
+            const float ph = float(cyc - rint(cyc));
+            float sn, cs;
+            sincospif(2.0f * ph, &sn, &cs);
+            o = cmul(o, make_float2(cs, sn));
+          }
+          v[b * R0 + r] = o;
         }
       }
     }
-    Passes<N, T, +1, 1, L>::run(v, my, tw, tid);
-    store_line<N, T, RO>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
+    store_line<N, T, R0>(v, LineIO(out, N, l0, C::LPW, rows), grp * N, tid);
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// RCMC, 8 taps, on [Nr][Na]: out[n][k] = sum_{j=-3..4} w_j in[i0 + j][k], x = n + R(n) Q_k,
-// i0 = floor(x), f = x - i0, w_j = kaiser-sinc(f - j) / sum.  The shift is formed in float64
-// and only its fraction goes to float32, so large range indices cost no precision.
-// Workgroups of consecutive rows run on the same XCD (blocks are dealt to the 8 XCDs
-// round-robin), so the 8-row neighbourhood of a row is mostly served from that XCD's L2.
-__device__ __forceinline__ int xcd_contiguous(int b, int G) {
-  const int q = G / 8, r = G % 8;
-  const int x = b % 8, i = b / 8;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
-}
-
+// Doppler-digit row order -> natural order (stage test hook only)
 __global__ void __launch_bounds__(256)
-    k_rcmc8(const float2* __restrict__ in, float2* __restrict__ out,
-            const double* __restrict__ Qk, RcmcConst c, int Nr, int Na, int kblocks) {
-  const int logical = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int n = logical / kblocks;
-  const int k = (logical - n * kblocks) * 256 + threadIdx.x;
-  if (k >= Na) return;
-  const double x = (c.rb0 + double(n) * c.dr) * Qk[k];
-  const double fl = floor(x);
-  const int i0 = n + int(fl);
-  const float f = float(x - fl);
-  float2 acc = make_float2(0.f, 0.f);
-  if (f == 0.0f) {
-    if (i0 >= 0 && i0 < Nr) acc = in[int64_t(i0) * Na + k];
-  } else {
-    float wsum = 0.f;
-#pragma unroll
-    for (int j = -3; j <= 4; ++j) {
-      const float t = f - float(j);
-      const float y = c.y0 - c.y1 * t * t;
-      float p = c.coef[0];
-      for (int m = 1; m < c.nterm; ++m) p = fmaf(p, y, c.coef[m]);
-      const float a = ((j & 1) ? -p : p) / t;
-      wsum += a;
-      const int i = i0 + j;
-      if (i >= 0 && i < Nr) {
-        const float2 s = in[int64_t(i) * Na + k];
-        acc.x = fmaf(a, s.x, acc.x);
-        acc.y = fmaf(a, s.y, acc.y);
-      }
-    }
-    const float inv = 1.0f / wsum;
-    acc = cscale(acc, inv);
-  }
-  out[int64_t(n) * Na + k] = acc;
-}
-
-// ------------------------------------------------------------------------------------------
-// corner turn: out[c][r] = in[r][c] through a 64 x 64 LDS tile padded by one element per row
-// (nxmr.cn/news/101525 §2.2.1: the pad moves consecutive rows onto different banks).
-__global__ void __launch_bounds__(256)
-    k_corner_turn(const float2* __restrict__ in, float2* __restrict__ out, int64_t rows,
-                  int64_t cols) {
-  __shared__ float2 tile[64][65];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int64_t r0 = int64_t(blockIdx.y) * 64, c0 = int64_t(blockIdx.x) * 64;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
-    if (r < rows && c < cols) tile[ty + 4 * i][tx] = in[r * cols + c];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int64_t c = c0 + ty + 4 * i, r = r0 + tx;
-    if (r < rows && c < cols) out[c * rows + r] = tile[tx][ty + 4 * i];
-  }
+    k_row_unpermute(const float2* __restrict__ in, float2* __restrict__ out, int A, int B,
+                    int64_t cols) {
+  const int k = blockIdx.x;
+  const int64_t src = int64_t(k % A) * B + k / A;
+  for (int64_t i = threadIdx.x; i < cols; i += 256) out[int64_t(k) * cols + i] = in[src * cols + i];
 }
 
 // ------------------------------------------------------------------------------------------
@@ -351,21 +411,13 @@ hipError_t launch_fft(const float2* in, float2* out, const float2* tw, int64_t l
 }
 
 template <int N>
-hipError_t launch_azc(const float2* in, float2* out, const float2* tw, const double* Dk,
-                      AzFilterConst c, int64_t lines, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_az_compress<N>, dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, tw, Dk, c,
-                     lines);
-  return hipGetLastError();
-}
-
-template <int N>
 hipError_t occupancy(int* rc, int* fft, int* azc) {
   hipError_t e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress<N>, LineCfg<N>::WG, 0);
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(fft, k_line_fft<N, -1>, LineCfg<N>::WG, 0);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(azc, k_az_compress<N>, LineCfg<N>::WG, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(azc, k_rcmc_mf<N>, LineCfg<N>::WG, 0);
 }
 
 #ifndef RD_RC_PREFETCH
@@ -394,6 +446,13 @@ hipError_t occupancy_pf(int* rc) {
 }
 
 template <int N>
+hipError_t launch_rcmc_mf(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
+                          int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_rcmc_mf<N>, dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, c, rows);
+  return hipGetLastError();
+}
+
+template <int N>
 hipError_t occupancy_pf2(int* rc) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf2<N>, LineCfg<N>::WG,
                                                       0);
@@ -404,15 +463,17 @@ constexpr LineOps make_ops() {
   constexpr bool sym = std::is_same<typename LineCfg<N>::Fwd, typename LineCfg<N>::Inv>::value;
   if constexpr (sym && LineCfg<N>::LPW == 1) {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
-                   &launch_azc<N>, &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>,
-                   &launch_rc_pf2<N>, &occupancy_pf2<N>};
+                   &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>,
+                   &launch_rc_pf2<N>, &occupancy_pf2<N>, &launch_rcmc_mf<N>,
+                   RowStage<N>::MARGIN};
   } else if constexpr (sym) {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
-                   &launch_azc<N>, &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>,
-                   nullptr, nullptr};
+                   &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>,
+                   nullptr, nullptr, &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
   } else {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
-                   &launch_azc<N>, &occupancy<N>, nullptr, nullptr, nullptr, nullptr};
+                   &occupancy<N>, nullptr, nullptr, nullptr, nullptr,
+                   &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
   }
 }
 
@@ -426,19 +487,42 @@ const LineOps* line_ops(int n) {
   return nullptr;
 }
 
-hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64_t cols,
-                              hipStream_t s) {
-  const dim3 grid(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64));
-  hipLaunchKernelGGL(k_corner_turn, grid, dim3(256), 0, s, in, out, rows, cols);
+template <int L>
+hipError_t launch_col(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
+                      int64_t cols, int na, hipStream_t s) {
+  ColGeom cg;
+  cg.cols = cols;
+  cg.base_mul = st.base_mul;
+  cg.stride = st.stride;
+  cg.chunks = int((cols + 63) / 64);
+  cg.na = na;
+  cg.twiddle = st.twiddle;
+  const uint64_t bytes = uint64_t(na) * uint64_t(cols) * 8u;
+  if (bytes > 0xFFFFFFF0ull) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(int64_t(st.sets) * cg.chunks));
+  if (st.dir < 0)
+    hipLaunchKernelGGL((k_col_fft<L, -1>), grid, dim3(ColCfg<L>::WG), 0, s, in, out, tw_L, cg,
+                       uint32_t(bytes));
+  else
+    hipLaunchKernelGGL((k_col_fft<L, +1>), grid, dim3(ColCfg<L>::WG), 0, s, in, out, tw_L, cg,
+                       uint32_t(bytes));
   return hipGetLastError();
 }
 
-hipError_t launch_rcmc8(const float2* in, float2* out, const double* Qk, const RcmcConst& c,
-                        int Nr, int Na, hipStream_t s) {
-  const int kblocks = (Na + 255) / 256;
-  const int64_t blocks = int64_t(kblocks) * Nr;
-  hipLaunchKernelGGL(k_rcmc8, dim3(unsigned(blocks)), dim3(256), 0, s, in, out, Qk, c, Nr, Na,
-                     kblocks);
+hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
+                          int64_t cols, int na, hipStream_t s) {
+  switch (st.L) {
+    case 16: return launch_col<16>(in, out, tw_L, st, cols, na, s);
+    case 32: return launch_col<32>(in, out, tw_L, st, cols, na, s);
+    case 64: return launch_col<64>(in, out, tw_L, st, cols, na, s);
+    case 128: return launch_col<128>(in, out, tw_L, st, cols, na, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_row_unpermute(const float2* in, float2* out, int A, int B, int64_t cols,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(k_row_unpermute, dim3(unsigned(A * B)), dim3(256), 0, s, in, out, A, B, cols);
   return hipGetLastError();
 }
 

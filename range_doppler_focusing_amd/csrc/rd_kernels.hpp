@@ -6,25 +6,24 @@
 
 namespace rdf {
 
-// Azimuth matched filter exp(+j 4 pi R(n) D_k / lambda) / Na, R(n) = rb0 + n dr.
-struct AzFilterConst {
-  double rb0;             // slant range of range bin 0
-  double dr;              // range-bin spacing
-  double two_over_lambda; // 2 / lambda: cycles of the two-way path per metre
-  float inv_na;           // 1 / Na (inverse-transform scale)
+// RCMC + azimuth filter on one Doppler row k of the [Na][Nr] array (range along the row):
+//   Delta(n) = alpha_k + n beta_k   (= R(n) (1/D_k - 1) / dr, samples)
+//   T[n]     = sum_{j=-3..4} w_j(f) S[floor(n + Delta) + j],  f = frac(n + Delta)
+//   out[n]   = T[n] exp(+j 2 pi (gamma_k + n delta_k)) / Na   (= 4 pi R(n) D_k / lambda)
+// w_j(f) = b_j(f) / sum_i b_i(f), b_j(f) = (-1)^j K(f - j) prod_{i != j} (f - i): the Kaiser-
+// windowed sinc times a factor common to all taps (it cancels in the normalisation), which is
+// smooth in f and evaluated as a degree-8 polynomial in x = f - 1/2 fitted on the host.
+constexpr int kRcmcTaps = 8;
+constexpr int kRcmcDeg = 8;
+struct RcmcPoly {
+  float c[kRcmcTaps][kRcmcDeg + 1];  // ascending powers of x, tap j = t - 3
 };
-
-// RCMC: output bin n of Doppler bin k reads x = n + R(n) Q_k with Q_k = u/(D(1+D))/dr;
-// weights are the Kaiser-windowed sinc, evaluated as (-1)^j I0-series(y_j) / (f - j) and
-// normalised by their sum (the common factor sin(pi f)/(pi I0(beta)) cancels).
-constexpr int kRcmcMaxTerms = 32;
-struct RcmcConst {
-  double rb0;
-  double dr;
-  float y0;          // (beta/2)^2
-  float y1;          // (beta/2)^2 / (taps/2)^2:  y_j = y0 - y1 t_j^2
-  int nterm;         // series terms kept
-  float coef[kRcmcMaxTerms];  // 1/(m!)^2, highest order first
+struct AzRowConst {
+  const double* row;   // [Na][4]: alpha, beta, gamma, delta per Doppler bin (FFT order)
+  int A, B;            // Na = A B; row r holds Doppler bin (r / B) + A (r % B)
+  float inv_na;
+  int filter;          // 0: RCMC only (no filter, no 1/Na), for the stage test hook
+  RcmcPoly w;
 };
 
 struct LineOps {
@@ -35,8 +34,6 @@ struct LineOps {
                                int64_t lines, int grid, hipStream_t s);
   hipError_t (*fft)(const float2* in, float2* out, const float2* tw, int64_t lines, int inverse,
                     float scale, int grid, hipStream_t s);
-  hipError_t (*az_compress)(const float2* in, float2* out, const float2* tw, const double* Dk,
-                            AzFilterConst c, int64_t lines, int grid, hipStream_t s);
   // workgroups of each persistent kernel that fit on one CU
   hipError_t (*occupancy)(int* rc, int* fft, int* azc);
   // register-cached, prefetching range compression (nullptr where the forward and inverse
@@ -48,17 +45,30 @@ struct LineOps {
   hipError_t (*range_compress_pf2)(const float2* in, float2* out, const float2* H,
                                    const float2* tw, int64_t lines, int grid, hipStream_t s);
   hipError_t (*occupancy_pf2)(int* rc);
+  // RCMC + azimuth filter over rows of this length (in == out allowed); margin = zero samples
+  // kept after each staged row (the largest shift the kernel accepts is margin - 4)
+  hipError_t (*rcmc_mf)(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
+                        int grid, hipStream_t s);
+  int margin;
 };
 
 // nullptr if the length has no built transform
 const LineOps* line_ops(int n);
 
-// out[c][r] = in[r][c] for an R x C row-major complex array
-hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64_t cols,
-                              hipStream_t s);
+// In-place four-step azimuth transforms on [rows][cols]; see rd_kernels.hip.
+struct ColStep {
+  int L;          // transform length of this step
+  int dir;        // -1 forward, +1 inverse
+  int base_mul;   // first row of set g is g * base_mul
+  int stride;     // row stride within a set
+  int sets;       // number of row sets
+  int twiddle;    // apply the inter-step twiddle W_Na^{dir g t}
+};
+hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
+                          int64_t cols, int na, hipStream_t s);
 
-// 8-tap RCMC on the corner-turned layout: in/out [Nr][Na] (row = range bin, column = Doppler)
-hipError_t launch_rcmc8(const float2* in, float2* out, const double* Qk, const RcmcConst& c,
-                        int Nr, int Na, hipStream_t s);
+// out[k] = in[(k % A) B + k / A] for rows of `cols` samples: Doppler-digit row order to natural
+hipError_t launch_row_unpermute(const float2* in, float2* out, int A, int B, int64_t cols,
+                                hipStream_t s);
 
 }  // namespace rdf

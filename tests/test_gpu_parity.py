@@ -151,7 +151,7 @@ def test_focus_every_stage(torch_dev, rdf, cfg):
         img = plan.focus(echo)
         img_az = plan.azimuth_focus(rc)
         torch.cuda.synchronize()
-        stages = {"rc": rc.cpu().numpy(), "azfft": az.cpu().numpy().T, "rcmc": rcmc.cpu().numpy().T,
+        stages = {"rc": rc.cpu().numpy(), "azfft": az.cpu().numpy(), "rcmc": rcmc.cpu().numpy(),
                   "img": img.cpu().numpy()}
         assert torch.equal(img, img_dbg) and torch.equal(img, img_az)
     for name in ("rc", "azfft", "rcmc"):
