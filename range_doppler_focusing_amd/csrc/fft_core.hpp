@@ -327,7 +327,7 @@ struct LineIO {
   }
 };
 
-template <int N, int T, int R>
+template <int N, int T, int R, int AUX = kBufNonTemporal>
 __device__ __forceinline__ void load_line(float2* v, const LineIO& io, int elem0, int tid) {
   using G = Geom<N, T, R>;
 #pragma unroll
@@ -337,14 +337,14 @@ __device__ __forceinline__ void load_line(float2* v, const LineIO& io, int elem0
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const rdf_v2u x = __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, (elem0 + j) * 8,
-                                                               r * G::NB * 8, kBufNonTemporal);
+                                                               r * G::NB * 8, AUX);
         v[b * R + r] = __builtin_bit_cast(float2, x);
       }
     }
   }
 }
 
-template <int N, int T, int R>
+template <int N, int T, int R, int AUX = kBufNonTemporal>
 __device__ __forceinline__ void store_line(const float2* v, const LineIO& io, int elem0, int tid) {
   using G = Geom<N, T, R>;
 #pragma unroll
@@ -354,7 +354,7 @@ __device__ __forceinline__ void store_line(const float2* v, const LineIO& io, in
 #pragma unroll
       for (int r = 0; r < R; ++r)
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, v[b * R + r]), io.rsrc,
-                                              (elem0 + j) * 8, r * G::NB * 8, kBufNonTemporal);
+                                              (elem0 + j) * 8, r * G::NB * 8, AUX);
     }
   }
 }

@@ -146,7 +146,8 @@ std::vector<float2> matched_filter(const rd_params& p, int L) {
 //   b_j(f) = (-1)^j K(f - j) prod_{i != j} (f - i),
 // smooth in f (no division, no f = 0 special case), with the same normalised weights.  Each b_j
 // is interpolated at 9 Chebyshev points of [0, 1] (degree 8; max error ~5e-9 of max|b|) and
-// stored as monomial coefficients in x = f - 1/2 for Horner evaluation in float32.
+// expanded in monomials of x = f - 1/2.  By the symmetry b_{1-j}(x) = b_j(-x) only taps
+// j = 0, -1, -2, -3 are fitted; their even and odd parts serve the mirrored taps too.
 double bessel_i0(double z) {
   const double y = 0.25 * z * z;
   double term = 1.0, sum = 1.0;
@@ -161,8 +162,8 @@ void rcmc_weight_polys(double beta, rdf::RcmcPoly* out) {
   constexpr int D = rdf::kRcmcDeg, M = D + 1;
   const double half = rdf::kRcmcTaps / 2.0;
   const double i0b = bessel_i0(beta);
-  for (int t = 0; t < rdf::kRcmcTaps; ++t) {
-    const int j = t - (rdf::kRcmcTaps / 2 - 1);
+  for (int q = 0; q < rdf::kRcmcTaps / 2; ++q) {
+    const int j = -q;
     auto b = [&](double f) {
       const double tt = f - j;
       const double a = 1.0 - (tt / half) * (tt / half);
@@ -201,7 +202,11 @@ void rcmc_weight_polys(double beta, rdf::RcmcPoly* out) {
     }
     double p2 = 1.0;
     for (int m = 0; m < M; ++m) {
-      out->c[t][m] = float(mono[m] * p2);
+      const double cm = mono[m] * p2;  // coefficient of x^m
+      if (m % 2 == 0)
+        out->even[q][m / 2] = float(cm);
+      else
+        out->odd[q][m / 2] = float(cm);
       p2 *= 2.0;
     }
   }

@@ -14,7 +14,14 @@
 #ifndef RD_PF_WAVES
 #define RD_PF_WAVES 1
 #endif
+#ifndef RD_AZ_AUX
+#define RD_AZ_AUX 0
+#endif
 namespace rdf {
+// cache policy of the azimuth passes: ordinary (cacheable) accesses; the in-place passes re-read
+// an image that the 256 MB Infinity Cache partly holds (measured 6% faster on the 4096^2 chain
+// than non-temporal hints)
+constexpr int kAzAux = RD_AZ_AUX;
 
 // ------------------------------------------------------------------------------------------
 // fused range compression: load -> FFT -> x H (H already carries 1/N) -> IFFT -> store.
@@ -269,7 +276,7 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
 #pragma unroll
       for (int r = 0; r < RI; ++r)
         v[b * RI + r] = __builtin_bit_cast(
-            float2, __builtin_amdgcn_raw_buffer_load_b64(rin, off(j + r * G::NB), 0, kBufNonTemporal));
+            float2, __builtin_amdgcn_raw_buffer_load_b64(rin, off(j + r * G::NB), 0, kAzAux));
     }
   }
   PassesCached<L, T, DIR, 1, LST>::run(v, my, twc, tid);
@@ -289,8 +296,7 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
           sincospif(float(e) * (2.0f / float(cg.na)), &sn, &cs);
           x = cmul(x, make_float2(cs, DIR > 0 ? sn : -sn));
         }
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout, off(t), 0,
-                                              kBufNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout, off(t), 0, kAzAux);
       }
     }
   }
@@ -327,7 +333,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     const double alpha = c.row[4 * k], beta = c.row[4 * k + 1];
     const double gamma = c.row[4 * k + 2], delta = c.row[4 * k + 3];
     float2 v[C::P];
-    load_line<N, T, R0>(v, LineIO(in, N, l0, C::LPW, rows), grp * N, tid);
+    load_line<N, T, R0, kAzAux>(v, LineIO(in, N, l0, C::LPW, rows), grp * N, tid);
     __syncthreads();  // the previous row's taps have been read
 #pragma unroll
     for (int b = 0; b < G::B; ++b) {
@@ -342,39 +348,54 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     for (int b = 0; b < G::B; ++b) {
       const int j = tid + b * T;
       if (G::live(j)) {
+        // filter phasor exp(j 2 pi (gamma + n delta)) for n = j + r NB: exact at r = 0 (phase
+        // reduced in float64), then advanced by the exact step rotation exp(j 2 pi NB delta)
+        float2 z = make_float2(1.f, 0.f), rot = make_float2(1.f, 0.f);
+        if (c.filter) {
+          const double c0 = gamma + double(j) * delta;
+          const double c1 = double(G::NB) * delta;
+          float sn, cs;
+          sincospif(2.0f * float(c0 - rint(c0)), &sn, &cs);
+          z = make_float2(cs * c.inv_na, sn * c.inv_na);
+          sincospif(2.0f * float(c1 - rint(c1)), &sn, &cs);
+          rot = make_float2(cs, sn);
+        }
 #pragma unroll
         for (int r = 0; r < R0; ++r) {
           const int n = j + r * G::NB;
           const double x = alpha + double(n) * beta;
           const double fl = floor(x);
-          const float f = float(x - fl) - 0.5f;
+          const float xf = float(x - fl) - 0.5f;
+          const float y = xf * xf;
           const float2* tap = my + (n + int(fl));  // tap t reads sample n + fl + t - 3
           float2 acc = make_float2(0.f, 0.f);
           float ws = 0.f;
 #pragma unroll
-          for (int t = 0; t < kRcmcTaps; ++t) {
-            float w = c.w.c[t][kRcmcDeg];
+          for (int q = 0; q < kRcmcTaps / 2; ++q) {
+            float e = c.w.even[q][kRcmcDeg / 2];
 #pragma unroll
-            for (int m = kRcmcDeg - 1; m >= 0; --m) w = fmaf(w, f, c.w.c[t][m]);
-            const float2 sv = tap[t];
-            acc.x = fmaf(w, sv.x, acc.x);
-            acc.y = fmaf(w, sv.y, acc.y);
-            ws += w;
+            for (int m = kRcmcDeg / 2 - 1; m >= 0; --m) e = fmaf(e, y, c.w.even[q][m]);
+            float o = c.w.odd[q][kRcmcDeg / 2 - 1];
+#pragma unroll
+            for (int m = kRcmcDeg / 2 - 2; m >= 0; --m) o = fmaf(o, y, c.w.odd[q][m]);
+            const float wa = fmaf(xf, o, e);    // tap j = -q   (t = 3 - q)
+            const float wb = fmaf(-xf, o, e);   // tap j = 1 + q (t = 4 + q)
+            const float2 sa = tap[3 - q], sb = tap[4 + q];
+            acc.x = fmaf(wa, sa.x, fmaf(wb, sb.x, acc.x));
+            acc.y = fmaf(wa, sa.y, fmaf(wb, sb.y, acc.y));
+            ws += wa + wb;
           }
-          const float sc = (c.filter ? c.inv_na : 1.0f) / ws;
+          const float sc = __builtin_amdgcn_rcpf(ws);
           float2 o = make_float2(acc.x * sc, acc.y * sc);
           if (c.filter) {
-            const double cyc = gamma + double(n) * delta;
-            const float ph = float(cyc - rint(cyc));
-            float sn, cs;
-            sincospif(2.0f * ph, &sn, &cs);
-            o = cmul(o, make_float2(cs, sn));
+            o = cmul(o, z);
+            z = cmul(z, rot);
           }
           v[b * R0 + r] = o;
         }
       }
     }
-    store_line<N, T, R0>(v, LineIO(out, N, l0, C::LPW, rows), grp * N, tid);
+    store_line<N, T, R0, kAzAux>(v, LineIO(out, N, l0, C::LPW, rows), grp * N, tid);
   }
 }
 

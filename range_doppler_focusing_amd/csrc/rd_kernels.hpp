@@ -12,11 +12,14 @@ namespace rdf {
 //   out[n]   = T[n] exp(+j 2 pi (gamma_k + n delta_k)) / Na   (= 4 pi R(n) D_k / lambda)
 // w_j(f) = b_j(f) / sum_i b_i(f), b_j(f) = (-1)^j K(f - j) prod_{i != j} (f - i): the Kaiser-
 // windowed sinc times a factor common to all taps (it cancels in the normalisation), which is
-// smooth in f and evaluated as a degree-8 polynomial in x = f - 1/2 fitted on the host.
+// smooth in f.  The interpolator is symmetric, b_{1-j}(x) = b_j(-x) with x = f - 1/2, so taps
+// j = -q and 1 + q (q = 0..3) come from one degree-8 polynomial p_q(x) = E_q(x^2) + x O_q(x^2),
+// fitted on the host: b_{-q}(x) = E + x O and b_{1+q}(x) = E - x O.
 constexpr int kRcmcTaps = 8;
 constexpr int kRcmcDeg = 8;
 struct RcmcPoly {
-  float c[kRcmcTaps][kRcmcDeg + 1];  // ascending powers of x, tap j = t - 3
+  float even[kRcmcTaps / 2][kRcmcDeg / 2 + 1];  // E_q, ascending powers of x^2
+  float odd[kRcmcTaps / 2][kRcmcDeg / 2];       // O_q, ascending powers of x^2
 };
 struct AzRowConst {
   const double* row;   // [Na][4]: alpha, beta, gamma, delta per Doppler bin (FFT order)
