@@ -8,9 +8,15 @@ the whole hot path.  The line also reports the full focusing chain (rd_focus) on
 4096 x 4096 airborne scene in Mpixel/s, with its fraction of the HBM roofline for the
 five-sweep and the compulsory byte models, and the CPU oracle timed on this host.
 
+Also reported (not the headline): range compression of the 8192 x 6000 (mixed-radix) and
+16384 x 16384 workloads, focusing of the 16384 x 16384 scene, per-stage times of the 4096 x 4096
+chain, and the vendor FFT library (torch.fft on rocFFT: forward FFT, filter multiply, inverse
+FFT as three launches) on the 4096 x 4096 range compression as a comparison.
+
 Inputs are HBM-resident before timing starts; buffers rotate over 4 input/output pairs (1 GiB
-per workload) so successive steps do not replay from the 256 MB Infinity Cache.  Timing uses
-HIP events recorded on the stream the kernels are launched on.
+per workload) so successive steps do not replay from the 256 MB Infinity Cache (the larger
+workloads exceed it on their own).  Timing uses HIP events recorded on the stream the kernels
+are launched on.
 """
 from __future__ import annotations
 
@@ -88,6 +94,49 @@ def cpu_oracle_focus(cfg, echo):
     return time.perf_counter() - t0
 
 
+def gpu_noise(torch, shape, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, dtype=torch.complex64, device="cuda", generator=g)
+
+
+def vendor_fft_comparison(torch, rdf, cfg, stream, steps, warmup):
+    """Range compression with the vendor FFT library through torch.fft (rocFFT): forward FFT,
+    multiply by the matched filter, inverse FFT -- three launches and three HBM round trips.
+    A reported comparison only; its result is checked against rd_range_compress."""
+    import math
+    p = cfg.plan_params()
+    fs, tp, bw = p["fs_hz"], p["pulse_s"], p["bandwidth_hz"]
+    L = math.ceil(tp * fs - 1e-6)
+    n = torch.arange(L, dtype=torch.float64)
+    t = n / fs - tp / 2
+    w = (0.54 - 0.46 * torch.cos(2 * math.pi * n / (L - 1))) if p["range_window"] == 1 else 1.0
+    h = torch.zeros(cfg.Nr, dtype=torch.complex128)
+    h[:L] = w * torch.exp(1j * math.pi * (bw / tp) * t * t)
+    H = torch.fft.fft(h).conj().to(torch.complex64).to("cuda")
+    xs = [gpu_noise(torch, (cfg.Na, cfg.Nr), cfg.seed + i) for i in range(ROTATE)]
+    ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
+
+    def step(i):
+        X = torch.fft.fft(xs[i % ROTATE], dim=1)
+        X.mul_(H)
+        torch.fft.ifft(X, dim=1, out=ys[i % ROTATE])
+
+    ms = time_steps(torch, step, steps, warmup, stream)
+    plan = rdf.Plan(**p)
+    ref = plan.range_compress(xs[0])
+    plan.close()
+    step(0)
+    torch.cuda.synchronize()
+    err = float(torch.linalg.vector_norm(ys[0] - ref) / torch.linalg.vector_norm(ref))
+    del xs, ys
+    torch.cuda.empty_cache()
+    gbs = 2 * cfg.Na * cfg.Nr * 8 / (ms * 1e-3) / 1e9
+    return {"workload": "range compression 4096 x 4096 complex64 via torch.fft (rocFFT), 3 launches",
+            "ms_per_step": round(ms, 5), "value": round(gbs, 1), "unit": "GB/s",
+            "rel_l2_vs_rd_range_compress": err}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,18 +144,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
-    ap.add_argument("--only", choices=["rc", "focus"], default=None,
+    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor"], default=None,
                     help="run one workload only (for profiling)")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the 8192 x 6000 and 16384 x 16384 workloads")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is a design note only)", file=sys.stderr)
+        print(f"bench.py: the focusing path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is a design note, not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
 
     import range_doppler_focusing_amd as rdf
-    from rdscene import C2, C3, cached_scene
+    from rdscene import C2, C3, C4, C5, cached_scene
 
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
@@ -134,6 +185,7 @@ def main():
     # ---------------------------------------------------------------- full chain
     fcfg = C3
     focus_ms = None
+    stage_ms = None
     if args.only in (None, "focus") and not args.no_focus:
         fsc = cached_scene(fcfg)
         e0 = torch.from_numpy(fsc.echo).to("cuda")
@@ -143,6 +195,12 @@ def main():
         focus_ms = time_steps(torch, lambda i: rdf.rd_focus(fplan.handle, fins[i % ROTATE],
                                                             fouts[i % ROTATE], stream),
                               max(10, args.steps // 2), args.warmup, stream)
+        # the chain's two halves on their own (the range half is the same kernel as the headline)
+        az_ms = time_steps(torch, lambda i: rdf.rd_azimuth_focus(fplan.handle, fins[i % ROTATE],
+                                                                 fouts[i % ROTATE], stream),
+                           max(10, args.steps // 2), args.warmup, stream)
+        stage_ms = {"rd_azimuth_focus_ms": round(az_ms, 4),
+                    "rd_range_compress_ms": round(focus_ms - az_ms, 4)}
         fplan.close()
         del fins, fouts, e0
         torch.cuda.empty_cache()
@@ -161,6 +219,40 @@ def main():
             tf = cpu_oracle_focus(fcfg, cached_scene(fcfg).echo)
             cpu_focus = {"value": px / tf / 1e6, "unit": "Mpixel/s", "cores": cores, "kind": "oracle",
                          "sample": f"whole 4096x4096 rd focus, one run ({tf:.1f} s)"}
+
+    # ---------------------------------------------------------------- larger workloads
+    large = None
+    if (args.only in (None, "large")) and not args.no_large:
+        large = []
+        for wcfg, kind, steps in ((C4, "rc", 20), (C5, "rc", 10), (C5, "focus", 5)):
+            x = gpu_noise(torch, (wcfg.Na, wcfg.Nr), wcfg.seed)
+            y = torch.empty_like(x)
+            plan = rdf.Plan(**wcfg.plan_params())
+            call = rdf.rd_range_compress if kind == "rc" else rdf.rd_focus
+            ms = time_steps(torch, lambda i: call(plan.handle, x, y, stream), steps, 2, stream)
+            plan.close()
+            del x, y
+            torch.cuda.empty_cache()
+            px = wcfg.Na * wcfg.Nr
+            rec = {"workload": f"{'range compression' if kind == 'rc' else 'full RD focusing'}, "
+                               f"{wcfg.Na} x {wcfg.Nr} complex64",
+                   "ms_per_step": round(ms, 4), "steps": steps,
+                   "data": "seeded complex Gaussian noise on the device (timing is data-independent)"}
+            if kind == "rc":
+                gbs = 2 * px * 8 / (ms * 1e-3) / 1e9
+                rec.update({"value": round(gbs, 1), "unit": "GB/s",
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "lines_per_s": round(wcfg.Na / (ms * 1e-3), 1)})
+            else:
+                m = px / (ms * 1e-3) / 1e6
+                rec.update({"value": round(m, 1), "unit": "Mpixel/s",
+                            "roofline_frac_80B_per_px": round(m * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4)})
+            large.append(rec)
+
+    # ---------------------------------------------------------------- vendor FFT comparison
+    vendor = None
+    if args.only in (None, "vendor"):
+        vendor = vendor_fft_comparison(torch, rdf, C2, stream, args.steps, args.warmup)
 
     traffic = read_traffic(os.path.join(ROOT, "profiles", "range_compress_4096x4096_traffic.txt"), src_hash)
     line = {
@@ -183,7 +275,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(rc_gbs / HBM_PEAK_GBS, 4) if rc_gbs else None,
                      "traffic": traffic,
-                     "kernel": "k_range_compress<4096>",
+                     "kernel": "k_range_compress_pf<4096>",
                      "algorithmic_bytes_per_launch": rc_bytes},
         "cpu_baseline": cpu,
         "rd_focus": None if not focus_ms else {
@@ -192,7 +284,10 @@ def main():
             "ms_per_step": round(focus_ms, 4), "value": round(mpx, 1), "unit": "Mpixel/s",
             "roofline_frac_80B_per_px": round(mpx * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4),
             "roofline_frac_32B_per_px": round(mpx * 1e6 * 32 / (HBM_PEAK_GBS * 1e9), 4),
+            "stages": stage_ms,
             "cpu_baseline": cpu_focus},
+        "other_workloads": large,
+        "vendor_fft_comparison": vendor,
         "kernel_source_sha1": src_hash,
     }
     print(json.dumps(line))

@@ -217,6 +217,10 @@ struct Dft<16, DIR> {
   static __device__ __forceinline__ void run(float2* v) { dft_ct<4, 4, DIR>(v); }
 };
 template <int DIR>
+struct Dft<20, DIR> {
+  static __device__ __forceinline__ void run(float2* v) { dft_ct<4, 5, DIR>(v); }
+};
+template <int DIR>
 struct Dft<25, DIR> {
   static __device__ __forceinline__ void run(float2* v) { dft_ct<5, 5, DIR>(v); }
 };
@@ -458,18 +462,24 @@ struct Passes<N, T, DIR, NS, IntList<R, R2, Rs...>> {
 template <int N, int T, int NS, class L>
 struct TwCache;
 
-// A pass whose twiddle set is small (NS (R-1) entries, at most 4 KB) keeps it in LDS, stored
-// r-major so the lanes of a wave read consecutive entries; larger sets (one per thread) stay in
-// registers.  tw_lds points at this pass's slice of the workgroup's twiddle LDS.
-template <int NS, int R>
-constexpr bool tw_in_lds() { return NS > 1 && NS * (R - 1) * 8 <= 4096; }
-template <int NS, int R>
-constexpr int tw_lds_len() { return tw_in_lds<NS, R>() ? NS * (R - 1) : 0; }
+// A pass whose twiddle set is small (NS (R-1) entries, at most TwLdsBudget<N>::bytes) keeps it
+// in LDS, stored r-major so the lanes of a wave read consecutive entries; larger sets (one per
+// thread) stay in registers.  tw_lds points at this pass's slice of the workgroup's twiddle LDS.
+// The budget is 4 KB unless a line configuration below raises it for its length (where the
+// line leaves LDS unused but registers are scarce).
+template <int N>
+struct TwLdsBudget {
+  static constexpr int bytes = 4096;
+};
+template <int N, int NS, int R>
+constexpr bool tw_in_lds() { return NS > 1 && NS * (R - 1) * 8 <= TwLdsBudget<N>::bytes; }
+template <int N, int NS, int R>
+constexpr int tw_lds_len() { return tw_in_lds<N, NS, R>() ? NS * (R - 1) : 0; }
 
 template <int N, int T, int NS, int R>
 struct TwCacheBase {
   using G = Geom<N, T, R>;
-  static constexpr bool IN_LDS = tw_in_lds<NS, R>();
+  static constexpr bool IN_LDS = tw_in_lds<N, NS, R>();
   static constexpr int K = (NS > 1 && !IN_LDS) ? G::B * (R - 1) : 1;
   float2 w[K];
   const float2* lw = nullptr;
@@ -515,7 +525,7 @@ struct TwCacheBase {
 
 template <int N, int T, int NS, int R>
 struct TwCache<N, T, NS, IntList<R>> : TwCacheBase<N, T, NS, R> {
-  static constexpr int LDS = tw_lds_len<NS, R>();
+  static constexpr int LDS = tw_lds_len<N, NS, R>();
   __device__ __forceinline__ void load_all(const float2* __restrict__ tw, float2* tw_lds, int tid,
                                            int wg_tid, int wg_size) {
     this->load(tw, tw_lds, tid, wg_tid, wg_size);
@@ -525,12 +535,12 @@ struct TwCache<N, T, NS, IntList<R>> : TwCacheBase<N, T, NS, R> {
 template <int N, int T, int NS, int R, int R2, int... Rs>
 struct TwCache<N, T, NS, IntList<R, R2, Rs...>> : TwCacheBase<N, T, NS, R> {
   using Next = TwCache<N, T, NS * R, IntList<R2, Rs...>>;
-  static constexpr int LDS = tw_lds_len<NS, R>() + Next::LDS;  // twiddle LDS entries, all passes
+  static constexpr int LDS = tw_lds_len<N, NS, R>() + Next::LDS;  // twiddle LDS entries, all passes
   Next next;
   __device__ __forceinline__ void load_all(const float2* __restrict__ tw, float2* tw_lds, int tid,
                                            int wg_tid, int wg_size) {
     this->load(tw, tw_lds, tid, wg_tid, wg_size);
-    next.load_all(tw, tw_lds + tw_lds_len<NS, R>(), tid, wg_tid, wg_size);
+    next.load_all(tw, tw_lds + tw_lds_len<N, NS, R>(), tid, wg_tid, wg_size);
   }
 };
 
@@ -563,17 +573,29 @@ struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>> {
 };
 
 // ---------------------------------------------------------------------------- line configurations
-// T threads per line (16 points per thread in radix-16 passes), LPW lines per workgroup.
+// T threads per line (16 points per thread in radix-16 passes), LPW lines per workgroup.  The
+// radix lists are palindromes, so the inverse transform (the list reversed) runs the same passes
+// as the forward one and one twiddle cache serves both.  PF: the range-compression kernel may
+// hold a prefetched second line in registers (not where the line needs 1024 threads, whose
+// registers are capped at 128).  HREG: the filter H is held in registers for the kernel's
+// lifetime (else read from the cached global table per line).  TWB: twiddle sets up to TWB
+// bytes live in LDS.
 template <int N>
 struct LineCfg;
 
-#define RDF_LINE_CFG(N_, T_, FWD, INV)                                            \
+#define RDF_LINE_CFG(N_, T_, FWD, INV, PF_, HREG_, TWB_)                          \
+  template <>                                                                     \
+  struct TwLdsBudget<N_> {                                                        \
+    static constexpr int bytes = TWB_;                                            \
+  };                                                                              \
   template <>                                                                     \
   struct LineCfg<N_> {                                                            \
     static constexpr int N = N_;                                                  \
     static constexpr int T = T_;                                                  \
     using Fwd = FWD;                                                              \
     using Inv = INV;                                                              \
+    static constexpr bool PF = PF_;                                               \
+    static constexpr bool HREG = HREG_;                                           \
     static constexpr int LPW = T_ >= 256 ? 1 : 256 / T_;                          \
     static constexpr int WG = T_ * LPW;                                           \
     static constexpr int LDS = lds_len(N_);                                       \
@@ -588,33 +610,22 @@ struct LineCfg;
   };
 
 using L_16_16 = IntList<16, 16>;
-using L_16_16_2 = IntList<16, 16, 2>;
-using L_2_16_16 = IntList<2, 16, 16>;
-using L_16_16_4 = IntList<16, 16, 4>;
-using L_4_16_16 = IntList<4, 16, 16>;
-using L_16_16_8 = IntList<16, 16, 8>;
-using L_8_16_16 = IntList<8, 16, 16>;
+using L_8_8_8 = IntList<8, 8, 8>;
+using L_16_4_16 = IntList<16, 4, 16>;
+using L_16_8_16 = IntList<16, 8, 16>;
 using L_16_16_16 = IntList<16, 16, 16>;
-using L_16_16_16_2 = IntList<16, 16, 16, 2>;
-using L_2_16_16_16 = IntList<2, 16, 16, 16>;
-using L_16_16_16_4 = IntList<16, 16, 16, 4>;
-using L_4_16_16_16 = IntList<4, 16, 16, 16>;
-using L_16_15_25 = IntList<16, 15, 25>;
-using L_25_15_16 = IntList<25, 15, 16>;
+using L_8_4_8_4_8 = IntList<8, 4, 8, 4, 8>;
+using L_8_16_16_8 = IntList<8, 16, 16, 8>;
+using L_20_15_20 = IntList<20, 15, 20>;
 
-RDF_LINE_CFG(256, 16, L_16_16, L_16_16)
-RDF_LINE_CFG(512, 32, L_16_16_2, L_2_16_16)
-RDF_LINE_CFG(1024, 64, L_16_16_4, L_4_16_16)
-RDF_LINE_CFG(2048, 128, L_16_16_8, L_8_16_16)
-#if defined(RD_CFG4096_RADIX8)
-using L_8_8_8_8 = IntList<8, 8, 8, 8>;
-RDF_LINE_CFG(4096, 512, L_8_8_8_8, L_8_8_8_8)
-#else
-RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16)
-#endif
-RDF_LINE_CFG(8192, 512, L_16_16_16_2, L_2_16_16_16)
-RDF_LINE_CFG(16384, 1024, L_16_16_16_4, L_4_16_16_16)
-RDF_LINE_CFG(6000, 400, L_16_15_25, L_25_15_16)
+RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096)
+RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096)
+RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 4096)
+RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096)
+RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096)
+RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, false, false, 8192)
+RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, false, false, 16384)
+RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096)
 
 #undef RDF_LINE_CFG
 

@@ -48,7 +48,7 @@ struct rd_plan {
   bool azimuth = false;
   const rdf::LineOps* rops = nullptr;  // range-length kernels
   const rdf::LineOps* aops = nullptr;  // azimuth-length kernels
-  int rc_variant = 0;   // 0 table loads, 1 register-cached (pf), 2 two-line alternating (pf2)
+  int rc_variant = 0;   // 0 table loads, 1 register-cached (pf)
   int rc_grid = 0;      // persistent grid of the range kernels
   int A = 0, B = 0;     // Na = A B: strided and block steps of the azimuth transform
   float2* H = nullptr;       // [Nr] conj(FFT(h)) / Nr
@@ -244,9 +244,6 @@ int persistent_grid(int occ, int cus, int64_t lines, int lpw) {
 
 // -------------------------------------------------------------------------- launch sequences
 rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, hipStream_t s) {
-  if (P->rc_variant == 2)
-    return check_hip(P->rops->range_compress_pf2(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid, s),
-                     "range compression launch");
   if (P->rc_variant == 1)
     return check_hip(P->rops->range_compress_pf(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid, s),
                      "range compression launch");
@@ -394,20 +391,14 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   if (rops->occupancy(&occ_rc, &occ_fft, &occ_azc) != hipSuccess)
     return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
   P->rc_grid = persistent_grid(occ_rc, P->cus, p.Na, rops->lpw);
-  // Kernel variant for range compression (measured alternatives; see the design notes):
-  // RD_RC_VARIANT=table keeps twiddle/filter loads in the line loop, =pf caches them in
-  // registers, =pf2 also alternates two register sets so stores never block the next line.
-  // Default: pf where it is built (pf2 measured slower on the 4096-point workload).
+  // Kernel variant for range compression: RD_RC_VARIANT=table keeps twiddle/filter loads in
+  // the line loop (a slower reference variant kept for measurement), otherwise the
+  // register-cached kernel (pf) runs wherever it is built.
   {
     const char* v = std::getenv("RD_RC_VARIANT");
     const std::string want = v ? v : "";
     int occ = 0;
-    if (rops->range_compress_pf2 && want == "pf2") {
-      if (rops->occupancy_pf2(&occ) != hipSuccess)
-        return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
-      P->rc_variant = 2;
-      P->rc_grid = persistent_grid(occ, P->cus, p.Na, rops->lpw);
-    } else if (rops->range_compress_pf && want != "table") {
+    if (rops->range_compress_pf && want != "table") {
       if (rops->occupancy_pf(&occ) != hipSuccess)
         return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
       P->rc_variant = 1;

@@ -63,25 +63,36 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
 // Register-cached variant: the twiddles (small sets in LDS) and H are loaded once for the
 // workgroup's lifetime, so the line loop issues no table loads; with PREFETCH the next line's
 // samples are loaded into a second register set while the current line is transformed.  Needs
-// Fwd == Inv (one twiddle cache serves both directions).
+// Fwd == Inv (one twiddle cache serves both directions).  Where registers are short (HREG
+// false), H is instead read from the (cache-resident) global table at the multiply.
 template <int N>
 __device__ __forceinline__ void rc_line(float2* v, float2* lds,
                                         const TwCache<N, LineCfg<N>::T, 1, typename LineCfg<N>::Fwd>& twc,
-                                        const float2* h, int tid) {
+                                        const float2* h, const float2* __restrict__ H, int tid) {
   using C = LineCfg<N>;
   using L = typename C::Fwd;
   constexpr int T = C::T;
   constexpr int RL = ListInfo<L>::last;
   using GL = Geom<N, T, RL>;
   PassesCached<N, T, -1, 1, L>::run(v, lds, twc, tid);
+  const float2* Hl = opaque(H);
 #pragma unroll
   for (int b = 0; b < GL::B; ++b) {
-    if (GL::live(tid + b * T)) {
+    const int j = tid + b * T;
+    if (GL::live(j)) {
 #pragma unroll
-      for (int r = 0; r < RL; ++r) v[b * RL + r] = cmul(v[b * RL + r], h[b * RL + r]);
+      for (int r = 0; r < RL; ++r)
+        v[b * RL + r] = cmul(v[b * RL + r], C::HREG ? h[b * RL + r] : Hl[j + r * GL::NB]);
     }
   }
   PassesCached<N, T, +1, 1, L>::run(v, lds, twc, tid);
+}
+
+// registers of the filter held by one thread (one dummy where H stays in global memory)
+template <int N>
+constexpr int filter_regs() {
+  using C = LineCfg<N>;
+  return C::HREG ? Geom<N, C::T, ListInfo<typename C::Fwd>::last>::B * ListInfo<typename C::Fwd>::last : 1;
 }
 
 template <int N>
@@ -89,16 +100,21 @@ __device__ __forceinline__ void load_filter(float2* h, const float2* __restrict_
   using C = LineCfg<N>;
   constexpr int RL = ListInfo<typename C::Fwd>::last;
   using GL = Geom<N, C::T, RL>;
+  if constexpr (C::HREG) {
 #pragma unroll
-  for (int b = 0; b < GL::B; ++b) {
-    const int j = tid + b * C::T;
+    for (int b = 0; b < GL::B; ++b) {
+      const int j = tid + b * C::T;
 #pragma unroll
-    for (int r = 0; r < RL; ++r) h[b * RL + r] = GL::live(j) ? H[j + r * GL::NB] : make_float2(0.f, 0.f);
+      for (int r = 0; r < RL; ++r) h[b * RL + r] = GL::live(j) ? H[j + r * GL::NB] : make_float2(0.f, 0.f);
+    }
   }
 }
 
+#ifndef RD_RC_MIN_BLOCKS
+#define RD_RC_MIN_BLOCKS 1
+#endif
 template <int N, bool PREFETCH>
-__global__ void __launch_bounds__(LineCfg<N>::WG)
+__global__ void __launch_bounds__(LineCfg<N>::WG, RD_RC_MIN_BLOCKS)
     k_range_compress_pf(const float2* in, float2* out, const float2* __restrict__ H,
                         const float2* __restrict__ tw, int64_t lines) {
   using C = LineCfg<N>;
@@ -115,7 +131,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   TC twc;
   twc.load_all(tw, lds + C::LPW * C::LDS, tid, threadIdx.x, C::WG);
   // (the first pass's barrier orders the LDS twiddle table before its first use)
-  float2 h[Geom<N, T, RL>::B * RL];
+  float2 h[filter_regs<N>()];
   load_filter<N>(h, H, tid);
   const int64_t stride = int64_t(gridDim.x) * C::LPW;
   float2 nxt[C::P];
@@ -132,64 +148,11 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     } else {
       load_line<N, T, R0>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
     }
-    rc_line<N>(v, my, twc, h, tid);
+    rc_line<N>(v, my, twc, h, H, tid);
     store_line<N, T, R0>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
     // Wait for the prefetch here, where the stores just issued are younger than it and need not
     // complete; a wait at the loop head would merge with the loop entry and drain the stores.
     if (PREFETCH) touch<C::P>(nxt);
-  }
-}
-
-// Two lines per loop trip with alternating register sets: line A's output registers stay
-// untouched while line B is transformed (a pending store pins its data registers until it
-// completes), and the next line is prefetched into a third set.  One line per workgroup.
-template <int N>
-__global__ void __launch_bounds__(LineCfg<N>::WG)
-    k_range_compress_pf2(const float2* in, float2* out, const float2* __restrict__ H,
-                         const float2* __restrict__ tw, int64_t lines) {
-  using C = LineCfg<N>;
-  using L = typename C::Fwd;
-  static_assert(std::is_same<typename C::Fwd, typename C::Inv>::value, "needs Fwd == Inv");
-  static_assert(C::LPW == 1, "one line per workgroup");
-  constexpr int T = C::T;
-  constexpr int P = C::P;
-  constexpr int R0 = ListInfo<L>::first;
-  constexpr int RL = ListInfo<L>::last;
-  using TC = TwCache<N, T, 1, L>;
-  __shared__ float2 lds[C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
-  const int tid = threadIdx.x;
-  TC twc;
-  twc.load_all(tw, lds + C::LDS, tid, tid, C::WG);
-  float2 h[Geom<N, T, RL>::B * RL];
-  load_filter<N>(h, H, tid);
-  const int64_t stride = gridDim.x;
-  int64_t line = blockIdx.x;
-  float2 pf[P], a[P], b[P];
-#pragma unroll
-  for (int i = 0; i < P; ++i) b[i] = make_float2(0.f, 0.f);
-  load_line<N, T, R0>(pf, LineIO(in, N, line, 1, lines), 0, tid);
-  touch<P>(pf);
-  for (; line + stride < lines; line += 2 * stride) {
-#pragma unroll
-    for (int i = 0; i < P; ++i) a[i] = pf[i];
-    load_line<N, T, R0>(pf, LineIO(in, N, line + stride, 1, lines), 0, tid);
-    rc_line<N>(a, lds, twc, h, tid);
-    store_line<N, T, R0>(a, LineIO(out, N, line, 1, lines), 0, tid);
-    touch<P>(pf);
-    touch<P>(b);
-#pragma unroll
-    for (int i = 0; i < P; ++i) b[i] = pf[i];
-    load_line<N, T, R0>(pf, LineIO(in, N, line + 2 * stride, 1, lines), 0, tid);
-    rc_line<N>(b, lds, twc, h, tid);
-    store_line<N, T, R0>(b, LineIO(out, N, line + stride, 1, lines), 0, tid);
-    touch<P>(pf);
-    touch<P>(a);
-  }
-  if (line < lines) {  // odd tail
-#pragma unroll
-    for (int i = 0; i < P; ++i) a[i] = pf[i];
-    rc_line<N>(a, lds, twc, h, tid);
-    store_line<N, T, R0>(a, LineIO(out, N, line, 1, lines), 0, tid);
   }
 }
 
@@ -319,7 +282,8 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   using C = LineCfg<N>;
   using RS = RowStage<N>;
   constexpr int T = C::T;
-  constexpr int R0 = ListInfo<typename C::Fwd>::first;
+  constexpr int R0 = N / T;  // each thread holds samples j + r T, r < N/T
+  static_assert(N % T == 0 && R0 <= C::P, "row layout");
   using G = Geom<N, T, R0>;
   __shared__ float2 lds[C::LPW * RS::LEN];
   const int grp = threadIdx.x / T;
@@ -447,22 +411,14 @@ hipError_t occupancy(int* rc, int* fft, int* azc) {
 template <int N>
 hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const float2* tw,
                         int64_t lines, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_range_compress_pf<N, RD_RC_PREFETCH>), dim3(grid), dim3(LineCfg<N>::WG), 0,
+  hipLaunchKernelGGL((k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF>), dim3(grid), dim3(LineCfg<N>::WG), 0,
                      s, in, out, H, tw, lines);
   return hipGetLastError();
 }
 
 template <int N>
-hipError_t launch_rc_pf2(const float2* in, float2* out, const float2* H, const float2* tw,
-                         int64_t lines, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_range_compress_pf2<N>, dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, H,
-                     tw, lines);
-  return hipGetLastError();
-}
-
-template <int N>
 hipError_t occupancy_pf(int* rc) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf<N, RD_RC_PREFETCH>,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF>,
                                                       LineCfg<N>::WG, 0);
 }
 
@@ -474,27 +430,15 @@ hipError_t launch_rcmc_mf(const float2* in, float2* out, const AzRowConst& c, in
 }
 
 template <int N>
-hipError_t occupancy_pf2(int* rc) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf2<N>, LineCfg<N>::WG,
-                                                      0);
-}
-
-template <int N>
 constexpr LineOps make_ops() {
   constexpr bool sym = std::is_same<typename LineCfg<N>::Fwd, typename LineCfg<N>::Inv>::value;
-  if constexpr (sym && LineCfg<N>::LPW == 1) {
+  if constexpr (sym) {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
-                   &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>,
-                   &launch_rc_pf2<N>, &occupancy_pf2<N>, &launch_rcmc_mf<N>,
+                   &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>, &launch_rcmc_mf<N>,
                    RowStage<N>::MARGIN};
-  } else if constexpr (sym) {
-    return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
-                   &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>,
-                   nullptr, nullptr, &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
   } else {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
-                   &occupancy<N>, nullptr, nullptr, nullptr, nullptr,
-                   &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
+                   &occupancy<N>, nullptr, nullptr, &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
   }
 }
 

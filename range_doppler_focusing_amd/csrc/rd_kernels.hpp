@@ -44,10 +44,6 @@ struct LineOps {
   hipError_t (*range_compress_pf)(const float2* in, float2* out, const float2* H,
                                   const float2* tw, int64_t lines, int grid, hipStream_t s);
   hipError_t (*occupancy_pf)(int* rc);
-  // two lines per trip with alternating register sets (one line per workgroup only)
-  hipError_t (*range_compress_pf2)(const float2* in, float2* out, const float2* H,
-                                   const float2* tw, int64_t lines, int grid, hipStream_t s);
-  hipError_t (*occupancy_pf2)(int* rc);
   // RCMC + azimuth filter over rows of this length (in == out allowed); margin = zero samples
   // kept after each staged row (the largest shift the kernel accepts is margin - 4)
   hipError_t (*rcmc_mf)(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
