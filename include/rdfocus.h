@@ -92,7 +92,7 @@ typedef struct rd_plan rd_plan;
 
 /* Returns 1 if `n` is a range-line length the library supports (256..16384 powers of two, and
  * 6000 = 2^4 * 3 * 5^3), else 0.  Full-chain plans also need Na a power of two in
- * [256, 16384], Na*Nr*8 < 4 GiB, and a range migration R(n)(1/D_k - 1)/dr below Nr/8 - 4
+ * [256, 16384], Na*Nr*8 < 4 GiB, and a range migration R(n)(1/D_k - 1)/dr below Nr/8 - 5
  * samples over the whole Doppler band (checked by rd_plan_create). */
 int rd_length_supported(int32_t n);
 

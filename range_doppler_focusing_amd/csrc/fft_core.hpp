@@ -204,25 +204,31 @@ struct Dft<5, DIR> {
   }
 };
 
-template <int DIR>
-struct Dft<8, DIR> {
-  static __device__ __forceinline__ void run(float2* v) { dft_ct<2, 4, DIR>(v); }
+// Composite lengths run as one Cooley-Tukey split R = A * B (dft_ct below); others directly.
+template <int R>
+struct DftSplit {
+  static constexpr int A = 1, B = R;
 };
-template <int DIR>
-struct Dft<15, DIR> {
-  static __device__ __forceinline__ void run(float2* v) { dft_ct<3, 5, DIR>(v); }
-};
-template <int DIR>
-struct Dft<16, DIR> {
-  static __device__ __forceinline__ void run(float2* v) { dft_ct<4, 4, DIR>(v); }
-};
-template <int DIR>
-struct Dft<20, DIR> {
-  static __device__ __forceinline__ void run(float2* v) { dft_ct<4, 5, DIR>(v); }
-};
-template <int DIR>
-struct Dft<25, DIR> {
-  static __device__ __forceinline__ void run(float2* v) { dft_ct<5, 5, DIR>(v); }
+template <> struct DftSplit<8> { static constexpr int A = 2, B = 4; };
+template <> struct DftSplit<15> { static constexpr int A = 3, B = 5; };
+template <> struct DftSplit<16> { static constexpr int A = 4, B = 4; };
+template <> struct DftSplit<20> { static constexpr int A = 4, B = 5; };
+template <> struct DftSplit<25> { static constexpr int A = 5, B = 5; };
+
+// The i-th input a length-R DFT consumes: a split DFT starts with the A inputs B n1 + 0, then
+// B n1 + 1, ...  Loading a butterfly's inputs in this order lets its first sub-DFT start as soon
+// as the first A loads have returned (memory counters complete in order).
+template <int R>
+constexpr int dft_input_order(int i) {
+  return DftSplit<R>::A == 1 ? i : DftSplit<R>::B * (i % DftSplit<R>::A) + i / DftSplit<R>::A;
+}
+
+template <int R, int DIR>
+struct Dft {
+  static_assert(DftSplit<R>::A > 1, "no DFT of this length");
+  static __device__ __forceinline__ void run(float2* v) {
+    dft_ct<DftSplit<R>::A, DftSplit<R>::B, DIR>(v);
+  }
 };
 
 // Length A*B DFT in registers (one Cooley-Tukey split): input n = B n1 + n2, output
@@ -339,7 +345,8 @@ __device__ __forceinline__ void load_line(float2* v, const LineIO& io, int elem0
     const int j = tid + b * T;
     if (G::live(j)) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
+      for (int i = 0; i < R; ++i) {
+        const int r = dft_input_order<R>(i);
         const rdf_v2u x = __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, (elem0 + j) * 8,
                                                                r * G::NB * 8, AUX);
         v[b * R + r] = __builtin_bit_cast(float2, x);
@@ -372,7 +379,10 @@ __device__ __forceinline__ void load_lds(float2* v, const float2* lds, int tid) 
     if (G::live(j)) {
       const int pj = lpad(j);
 #pragma unroll
-      for (int r = 0; r < R; ++r) v[b * R + r] = lds[lpad_step<G::NB, false>(pj, j, r)];
+      for (int i = 0; i < R; ++i) {
+        const int r = dft_input_order<R>(i);
+        v[b * R + r] = lds[lpad_step<G::NB, false>(pj, j, r)];
+      }
     }
   }
 }
@@ -466,21 +476,38 @@ struct TwCache;
 // in LDS, stored r-major so the lanes of a wave read consecutive entries; larger sets (one per
 // thread) stay in registers.  tw_lds points at this pass's slice of the workgroup's twiddle LDS.
 // The budget is 4 KB unless a line configuration below raises it for its length (where the
-// line leaves LDS unused but registers are scarce).
+// line leaves LDS unused but registers are scarce).  With `powers` set, a register-resident
+// pass keeps only its base twiddle w = W_{NS R}^{j mod NS} per butterfly and forms w^r for
+// r < R by products at each use (depth <= 4 products, so the error stays a few float32 ulps):
+// a few more VALU operations per pass for (R - 2) fewer complex registers per butterfly.
 template <int N>
-struct TwLdsBudget {
-  static constexpr int bytes = 4096;
+struct TwPolicy {
+  static constexpr int lds_bytes = 4096;
+  static constexpr bool powers = false;
 };
 template <int N, int NS, int R>
-constexpr bool tw_in_lds() { return NS > 1 && NS * (R - 1) * 8 <= TwLdsBudget<N>::bytes; }
+constexpr bool tw_in_lds() { return NS > 1 && NS * (R - 1) * 8 <= TwPolicy<N>::lds_bytes; }
 template <int N, int NS, int R>
 constexpr int tw_lds_len() { return tw_in_lds<N, NS, R>() ? NS * (R - 1) : 0; }
+
+// p[r] = w^r for 1 <= r < R from p[1] = w: p[r] = p[h] p[r - h], h the largest power of two
+// below r (or r/2 for powers of two), so w^r is at most floor(log2 r) + 1 products deep.
+template <int R>
+__device__ __forceinline__ void twiddle_powers(float2* p) {
+#pragma unroll
+  for (int r = 2; r < R; ++r) {
+    int h = 1;
+    while (2 * h < r) h *= 2;
+    p[r] = cmul(p[h], p[r - h]);
+  }
+}
 
 template <int N, int T, int NS, int R>
 struct TwCacheBase {
   using G = Geom<N, T, R>;
   static constexpr bool IN_LDS = tw_in_lds<N, NS, R>();
-  static constexpr int K = (NS > 1 && !IN_LDS) ? G::B * (R - 1) : 1;
+  static constexpr bool POW = NS > 1 && !IN_LDS && TwPolicy<N>::powers && R > 2;
+  static constexpr int K = (NS > 1 && !IN_LDS) ? G::B * (POW ? 1 : R - 1) : 1;
   float2 w[K];
   const float2* lw = nullptr;
   // every thread of the workgroup calls this; the caller synchronises before first use
@@ -493,6 +520,12 @@ struct TwCacheBase {
         tw_lds[i] = tw[m * STEP * r];
       }
       lw = tw_lds;
+    } else if constexpr (POW) {
+#pragma unroll
+      for (int b = 0; b < G::B; ++b) {
+        const int j = tid + b * T;
+        w[b] = G::live(j) ? tw[(j % NS) * STEP] : make_float2(1.f, 0.f);
+      }
     } else if constexpr (NS > 1) {
 #pragma unroll
       for (int b = 0; b < G::B; ++b) {
@@ -506,7 +539,19 @@ struct TwCacheBase {
   }
   template <int DIR>
   __device__ __forceinline__ void apply(float2* v, int tid) const {
-    if constexpr (NS > 1) {
+    if constexpr (POW) {
+#pragma unroll
+      for (int b = 0; b < G::B; ++b) {
+        if (G::live(tid + b * T)) {
+          float2 p[R];
+          p[1] = w[b];
+          if (DIR > 0) p[1].y = -p[1].y;
+          twiddle_powers<R>(p);
+#pragma unroll
+          for (int r = 1; r < R; ++r) v[b * R + r] = cmul(v[b * R + r], p[r]);
+        }
+      }
+    } else if constexpr (NS > 1) {
 #pragma unroll
       for (int b = 0; b < G::B; ++b) {
         const int j = tid + b * T;
@@ -579,14 +624,15 @@ struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>> {
 // hold a prefetched second line in registers (not where the line needs 1024 threads, whose
 // registers are capped at 128).  HREG: the filter H is held in registers for the kernel's
 // lifetime (else read from the cached global table per line).  TWB: twiddle sets up to TWB
-// bytes live in LDS.
+// bytes live in LDS.  POW: larger sets are formed from one cached base twiddle per butterfly.
 template <int N>
 struct LineCfg;
 
-#define RDF_LINE_CFG(N_, T_, FWD, INV, PF_, HREG_, TWB_)                          \
+#define RDF_LINE_CFG(N_, T_, FWD, INV, PF_, HREG_, TWB_, POW_)                    \
   template <>                                                                     \
-  struct TwLdsBudget<N_> {                                                        \
-    static constexpr int bytes = TWB_;                                            \
+  struct TwPolicy<N_> {                                                           \
+    static constexpr int lds_bytes = TWB_;                                        \
+    static constexpr bool powers = POW_;                                          \
   };                                                                              \
   template <>                                                                     \
   struct LineCfg<N_> {                                                            \
@@ -618,14 +664,18 @@ using L_8_4_8_4_8 = IntList<8, 4, 8, 4, 8>;
 using L_8_16_16_8 = IntList<8, 16, 16, 8>;
 using L_20_15_20 = IntList<20, 15, 20>;
 
-RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096)
-RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096)
-RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 4096)
-RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096)
-RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096)
-RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, false, false, 8192)
-RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, false, false, 16384)
-RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096)
+RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, false)
+RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, false)
+RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 4096, false)
+RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, false)
+#if defined(RD_CFG4096_LEAN)
+RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, false, 4096, true)
+#else
+RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, false)
+#endif
+RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, false, false, 8192, false)
+RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, false, false, 16384, false)
+RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096, false)
 
 #undef RDF_LINE_CFG
 

@@ -283,8 +283,7 @@ rd_status run_col(rd_plan* P, const float2* src, float2* dst, bool forward, bool
 rd_status run_rows(rd_plan* P, const float2* src, float2* dst, bool filter, hipStream_t s) {
   rdf::AzRowConst c = P->az;
   c.filter = filter ? 1 : 0;
-  const int grid = int((P->p.Na + P->rops->lpw - 1) / P->rops->lpw);
-  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, grid, s), "RCMC launch");
+  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, s), "RCMC launch");
 }
 
 rd_status run_azimuth(rd_plan* P, const float2* rc, float2* img, hipStream_t s) {
@@ -431,10 +430,13 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
       rowc[4 * k + 3] = 2.0 * D * P->dr / lam;
       max_shift = std::max(max_shift, rowc[4 * k] + double(p.Nr - 1) * rowc[4 * k + 1]);
     }
-    if (std::floor(max_shift) + 4 > double(rops->margin))
+    // taps reach floor(shift) + 4 samples past the output (one more for rounding differences
+    // between this bound and the kernel's float64 shift)
+    if (std::floor(max_shift) + 5 > double(rops->margin))
       return bail(fail(RD_ERR_UNSUPPORTED_LENGTH,
                        "range migration of %.1f samples exceeds the %d-sample margin built for Nr=%d",
-                       max_shift, rops->margin - 4, p.Nr));
+                       max_shift, rops->margin - 5, p.Nr));
+    P->az.halo = int(std::floor(max_shift)) + 5;
     if ((st = upload(&P->tw_A, roots_table(P->A), "azimuth step twiddles")) != RD_OK) return bail(st);
     if ((st = upload(&P->tw_B, roots_table(P->B), "azimuth step twiddles")) != RD_OK) return bail(st);
     if ((st = upload(&P->rowc, rowc, "azimuth row coefficients")) != RD_OK) return bail(st);

@@ -266,39 +266,67 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
 }
 
 // ------------------------------------------------------------------------------------------
-// RCMC + azimuth filter per Doppler row (constants in rd_kernels.hpp).  The row is staged in LDS
-// between 3 leading and MARGIN trailing zeros, so every tap is a plain LDS read and samples
-// outside the line read as zero.  Shift and filter phase are formed in float64 (the phase
-// reaches ~1e7 rad) and reduced before they are taken to float32.
+// RCMC + azimuth filter per Doppler row (constants in rd_kernels.hpp).  A row is processed in
+// chunks of CH outputs; a chunk's input window (3 samples before it, CH samples, and `halo`
+// samples after it, zero outside the row) is staged in LDS, so every tap is a plain LDS read.
+// Rows up to 4096 samples are one chunk, staged between zero margins written once; longer rows
+// split into 4096-sample chunks, which keeps the staging buffer small enough for several
+// workgroups per CU.  Shift and filter phase are formed in float64 (the phase reaches ~1e7 rad)
+// and reduced before they are taken to float32.
 template <int N>
 struct RowStage {
-  static constexpr int MARGIN = N / 8;
-  static constexpr int LEN = 3 + N + MARGIN;
+  static constexpr int CH = (N > 4096 && N % 4096 == 0) ? 4096 : N;  // outputs per chunk
+  static constexpr int CHUNKS = N / CH;
+  static constexpr int T = CHUNKS == 1 ? LineCfg<N>::T : 256;          // threads per chunk
+  static constexpr int LPW = CHUNKS == 1 ? LineCfg<N>::LPW : 1;        // chunks per workgroup
+  static constexpr int WG = T * LPW;
+  static constexpr int MARGIN = N / 8;       // staged samples after a chunk (shift + 5 <= MARGIN)
+  static constexpr int LEN = 3 + CH + MARGIN;
 };
 
 template <int N>
-__global__ void __launch_bounds__(LineCfg<N>::WG)
+__global__ void __launch_bounds__(RowStage<N>::WG)
     k_rcmc_mf(const float2* in, float2* out, AzRowConst c, int64_t rows) {
-  using C = LineCfg<N>;
   using RS = RowStage<N>;
-  constexpr int T = C::T;
-  constexpr int R0 = N / T;  // each thread holds samples j + r T, r < N/T
-  static_assert(N % T == 0 && R0 <= C::P, "row layout");
-  using G = Geom<N, T, R0>;
-  __shared__ float2 lds[C::LPW * RS::LEN];
+  constexpr int T = RS::T;
+  constexpr int CH = RS::CH;
+  constexpr int R0 = CH / T;  // each thread holds chunk samples j + r T, r < CH/T
+  static_assert(CH % T == 0 && R0 <= LineCfg<N>::P, "row layout");
+  using G = Geom<CH, T, R0>;
+  __shared__ float2 lds[RS::LPW * RS::LEN];
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * RS::LEN;
-  for (int i = threadIdx.x; i < C::LPW * RS::LEN; i += C::WG) lds[i] = make_float2(0.f, 0.f);
-  for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < rows; l0 += int64_t(gridDim.x) * C::LPW) {
-    const int64_t row = l0 + grp;
-    const int64_t rr = row < rows ? row : rows - 1;
-    const int k = int(rr / c.B) + c.A * int(rr % c.B);
+  for (int i = threadIdx.x; i < RS::LPW * RS::LEN; i += RS::WG) lds[i] = make_float2(0.f, 0.f);
+  const int64_t items = rows * RS::CHUNKS;
+  for (int64_t i0 = int64_t(blockIdx.x) * RS::LPW; i0 < items; i0 += int64_t(gridDim.x) * RS::LPW) {
+    const int64_t item = i0 + grp;
+    const int64_t it = item < items ? item : items - 1;
+    const int64_t row = it / RS::CHUNKS;
+    const int n0 = int(it % RS::CHUNKS) * CH;
+    const int k = int(row / c.B) + c.A * int(row % c.B);
     const double alpha = c.row[4 * k], beta = c.row[4 * k + 1];
     const double gamma = c.row[4 * k + 2], delta = c.row[4 * k + 3];
-    float2 v[C::P];
-    load_line<N, T, R0, kAzAux>(v, LineIO(in, N, l0, C::LPW, rows), grp * N, tid);
-    __syncthreads();  // the previous row's taps have been read
+    float2 v[LineCfg<N>::P];
+    // one chunk per group: rows [i0, i0 + LPW) when a row is one chunk, else the item's row
+    const LineIO src = RS::CHUNKS == 1 ? LineIO(in, N, i0, RS::LPW, rows)
+                                       : LineIO(in, N, item < items ? row : rows, 1, rows);
+    const int e0 = RS::CHUNKS == 1 ? grp * N : n0;
+    load_line<CH, T, R0, kAzAux>(v, src, e0, tid);
+    float2 pre = make_float2(0.f, 0.f);
+    int hs = -1;  // this thread's first halo slot, if any
+    if constexpr (RS::CHUNKS > 1) {
+      // the 3 samples before the chunk and c.halo after it (zero outside the row); the first
+      // pass of them is loaded with the chunk, before the barrier
+      const int i = tid;
+      if (i < 3 + c.halo) {
+        const int sidx = i < 3 ? n0 - 3 + i : n0 + CH + (i - 3);
+        hs = i < 3 ? i : 3 + CH + (i - 3);
+        if (sidx >= 0 && sidx < N)
+          pre = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, sidx * 8, 0, kAzAux));
+      }
+    }
+    __syncthreads();  // the previous chunk's taps have been read
 #pragma unroll
     for (int b = 0; b < G::B; ++b) {
       const int j = tid + b * T;
@@ -307,16 +335,25 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
         for (int r = 0; r < R0; ++r) my[3 + j + r * G::NB] = v[b * R0 + r];
       }
     }
+    if constexpr (RS::CHUNKS > 1) {
+      if (hs >= 0) my[hs] = pre;
+      for (int i = tid + T; i < 3 + c.halo; i += T) {  // halos longer than one pass
+        const int sidx = n0 + CH + (i - 3);
+        my[3 + CH + (i - 3)] = sidx < N ? __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 src.rsrc, sidx * 8, 0, kAzAux))
+                                        : make_float2(0.f, 0.f);
+      }
+    }
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < G::B; ++b) {
       const int j = tid + b * T;
       if (G::live(j)) {
-        // filter phasor exp(j 2 pi (gamma + n delta)) for n = j + r NB: exact at r = 0 (phase
-        // reduced in float64), then advanced by the exact step rotation exp(j 2 pi NB delta)
+        // filter phasor exp(j 2 pi (gamma + n delta)) for n = n0 + j + r NB: exact at r = 0
+        // (phase reduced in float64), then advanced by the exact step rotation
         float2 z = make_float2(1.f, 0.f), rot = make_float2(1.f, 0.f);
         if (c.filter) {
-          const double c0 = gamma + double(j) * delta;
+          const double c0 = gamma + double(n0 + j) * delta;
           const double c1 = double(G::NB) * delta;
           float sn, cs;
           sincospif(2.0f * float(c0 - rint(c0)), &sn, &cs);
@@ -326,22 +363,22 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
         }
 #pragma unroll
         for (int r = 0; r < R0; ++r) {
-          const int n = j + r * G::NB;
-          const double x = alpha + double(n) * beta;
+          const int m = j + r * G::NB;  // position in the chunk
+          const double x = alpha + double(n0 + m) * beta;
           const double fl = floor(x);
           const float xf = float(x - fl) - 0.5f;
           const float y = xf * xf;
-          const float2* tap = my + (n + int(fl));  // tap t reads sample n + fl + t - 3
+          const float2* tap = my + (m + int(fl));  // tap t reads sample n0 + m + fl + t - 3
           float2 acc = make_float2(0.f, 0.f);
           float ws = 0.f;
 #pragma unroll
           for (int q = 0; q < kRcmcTaps / 2; ++q) {
             float e = c.w.even[q][kRcmcDeg / 2];
 #pragma unroll
-            for (int m = kRcmcDeg / 2 - 1; m >= 0; --m) e = fmaf(e, y, c.w.even[q][m]);
+            for (int mm = kRcmcDeg / 2 - 1; mm >= 0; --mm) e = fmaf(e, y, c.w.even[q][mm]);
             float o = c.w.odd[q][kRcmcDeg / 2 - 1];
 #pragma unroll
-            for (int m = kRcmcDeg / 2 - 2; m >= 0; --m) o = fmaf(o, y, c.w.odd[q][m]);
+            for (int mm = kRcmcDeg / 2 - 2; mm >= 0; --mm) o = fmaf(o, y, c.w.odd[q][mm]);
             const float wa = fmaf(xf, o, e);    // tap j = -q   (t = 3 - q)
             const float wb = fmaf(-xf, o, e);   // tap j = 1 + q (t = 4 + q)
             const float2 sa = tap[3 - q], sb = tap[4 + q];
@@ -359,7 +396,9 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
         }
       }
     }
-    store_line<N, T, R0, kAzAux>(v, LineIO(out, N, l0, C::LPW, rows), grp * N, tid);
+    const LineIO dst = RS::CHUNKS == 1 ? LineIO(out, N, i0, RS::LPW, rows)
+                                       : LineIO(out, N, item < items ? row : rows, 1, rows);
+    store_line<CH, T, R0, kAzAux>(v, dst, e0, tid);
   }
 }
 
@@ -402,7 +441,7 @@ hipError_t occupancy(int* rc, int* fft, int* azc) {
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(fft, k_line_fft<N, -1>, LineCfg<N>::WG, 0);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(azc, k_rcmc_mf<N>, LineCfg<N>::WG, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(azc, k_rcmc_mf<N>, RowStage<N>::WG, 0);
 }
 
 #ifndef RD_RC_PREFETCH
@@ -425,7 +464,9 @@ hipError_t occupancy_pf(int* rc) {
 template <int N>
 hipError_t launch_rcmc_mf(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
                           int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_rcmc_mf<N>, dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, c, rows);
+  const int64_t wgs = (rows * RowStage<N>::CHUNKS + RowStage<N>::LPW - 1) / RowStage<N>::LPW;
+  if (grid <= 0 || grid > wgs) grid = int(wgs);
+  hipLaunchKernelGGL(k_rcmc_mf<N>, dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows);
   return hipGetLastError();
 }
 

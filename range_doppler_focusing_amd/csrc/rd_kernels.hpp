@@ -26,6 +26,7 @@ struct AzRowConst {
   int A, B;            // Na = A B; row r holds Doppler bin (r / B) + A (r % B)
   float inv_na;
   int filter;          // 0: RCMC only (no filter, no 1/Na), for the stage test hook
+  int halo;            // samples staged after a chunk: floor(max shift) + 5 <= margin
   RcmcPoly w;
 };
 
@@ -44,8 +45,9 @@ struct LineOps {
   hipError_t (*range_compress_pf)(const float2* in, float2* out, const float2* H,
                                   const float2* tw, int64_t lines, int grid, hipStream_t s);
   hipError_t (*occupancy_pf)(int* rc);
-  // RCMC + azimuth filter over rows of this length (in == out allowed); margin = zero samples
-  // kept after each staged row (the largest shift the kernel accepts is margin - 4)
+  // RCMC + azimuth filter over rows of this length (in == out allowed; grid 0 = one workgroup
+  // per staged chunk); margin = samples staged after a chunk, so the largest shift the kernel
+  // accepts is margin - 5
   hipError_t (*rcmc_mf)(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
                         int grid, hipStream_t s);
   int margin;

@@ -13,9 +13,16 @@ import pytest
 
 from oracle import metrics as M
 from oracle import rd_oracle as O
-from rdscene import C1, C2, C3, C4, C5, cached_scene, make_scene
+from rdscene import C1, C2, C3, C4, C5, SceneConfig, cached_scene, make_scene
 
 pytestmark = pytest.mark.gpu
+
+# L band, slow platform, long rows: ~540 samples of range migration at the Doppler band edge,
+# so the chunked RCMC kernel stages a halo longer than one pass of its threads.
+LONG_MIGRATION = SceneConfig(
+    name="long_migration_512x8192", Na=512, Nr=8192, pulse_s=2e-6, bandwidth_hz=100e6,
+    fs_hz=120e6, window="rect", n_targets=4, noise_power=0.01, seed=12, carrier_hz=1.3e9,
+    prf_hz=800.0, velocity_mps=150.0, r_ref_m=8000.0, sep_range=9, sep_az=64)
 
 STAGE_TOL = 1e-5
 IMAGE_TOL = 1e-4
@@ -110,6 +117,42 @@ def test_range_compression_full(torch_dev, rdf, cfg):
                 assert int(np.argmax(win)) == 4 == int(np.argmax(np.abs(ref[m, n - 4:n + 5])))
 
 
+@pytest.mark.parametrize("n", LENGTHS)
+@pytest.mark.parametrize("lines", [1, 37])
+def test_range_compression_every_length(torch_dev, rdf, n, lines):
+    """Every built line length, a ragged line count and a single line: the register-cached
+    kernel against the oracle, in place bit-identical to out of place."""
+    torch = torch_dev
+    rng = np.random.default_rng(1000 + n + lines)
+    fs = 120e6
+    params = dict(Na=lines, Nr=n, pulse_s=(n // 3) / fs, bandwidth_hz=90e6, fs_hz=fs,
+                  range_window=int(n % 3 == 0))
+    echo = (rng.standard_normal((lines, n)) + 1j * rng.standard_normal((lines, n))).astype(np.complex64)
+    log(f"[range] every length: n={n} lines={lines}")
+    with rdf.Plan(**params) as plan:
+        x = dev(torch, echo)
+        rc = plan.range_compress(x).cpu().numpy()
+        plan.range_compress(x, out=x)
+        torch.cuda.synchronize()
+        assert np.array_equal(x.cpu().numpy(), rc)
+    err = M.rel_l2(rc, O.range_compress(echo, params))
+    log(f"[range] n={n} lines={lines} rel-L2 {err:.2e}")
+    assert err <= STAGE_TOL
+
+
+def test_range_compression_table_variant(torch_dev, rdf, monkeypatch):
+    """The table-twiddle kernel (selected by RD_RC_VARIANT=table) meets the same bar."""
+    torch = torch_dev
+    cfg = C2.with_(Na=300)
+    sc = make_scene(cfg)
+    monkeypatch.setenv("RD_RC_VARIANT", "table")
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        rc = plan.range_compress(dev(torch, sc.echo)).cpu().numpy()
+    err = M.rel_l2(rc, O.range_compress(sc.echo, cfg.plan_params()))
+    log(f"[range] table variant rel-L2 {err:.2e}")
+    assert err <= STAGE_TOL
+
+
 def test_range_compression_large_sampled_lines(torch_dev, rdf):
     torch = torch_dev
     cfg = C5
@@ -139,7 +182,7 @@ def check_targets(img, ref_img, targets):
                 assert abs(got[axis][key] - want[axis][key]) <= 0.1, (m, n, axis, key)
 
 
-@pytest.mark.parametrize("cfg", [C1, C3], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, C3, LONG_MIGRATION], ids=lambda c: c.name)
 def test_focus_every_stage(torch_dev, rdf, cfg):
     torch = torch_dev
     sc, ref = scene_and_stages(cfg)
@@ -161,7 +204,8 @@ def test_focus_every_stage(torch_dev, rdf, cfg):
     err = M.rel_l2(stages["img"], ref["img"])
     log(f"[focus] {cfg.name} img rel-L2 {err:.2e}")
     assert err <= IMAGE_TOL
-    check_targets(stages["img"], ref["img"], sc.targets)
+    if cfg is not LONG_MIGRATION:  # its azimuth TBP is ~3: peaks are broad, compared via L2 only
+        check_targets(stages["img"], ref["img"], sc.targets)
 
 
 def test_focus_in_place_and_noiseless_targets(torch_dev, rdf):
