@@ -476,38 +476,21 @@ struct TwCache;
 // in LDS, stored r-major so the lanes of a wave read consecutive entries; larger sets (one per
 // thread) stay in registers.  tw_lds points at this pass's slice of the workgroup's twiddle LDS.
 // The budget is 4 KB unless a line configuration below raises it for its length (where the
-// line leaves LDS unused but registers are scarce).  With `powers` set, a register-resident
-// pass keeps only its base twiddle w = W_{NS R}^{j mod NS} per butterfly and forms w^r for
-// r < R by products at each use (depth <= 4 products, so the error stays a few float32 ulps):
-// a few more VALU operations per pass for (R - 2) fewer complex registers per butterfly.
+// line leaves LDS unused but registers are scarce).
 template <int N>
-struct TwPolicy {
-  static constexpr int lds_bytes = 4096;
-  static constexpr bool powers = false;
+struct TwLdsBudget {
+  static constexpr int bytes = 4096;
 };
 template <int N, int NS, int R>
-constexpr bool tw_in_lds() { return NS > 1 && NS * (R - 1) * 8 <= TwPolicy<N>::lds_bytes; }
+constexpr bool tw_in_lds() { return NS > 1 && NS * (R - 1) * 8 <= TwLdsBudget<N>::bytes; }
 template <int N, int NS, int R>
 constexpr int tw_lds_len() { return tw_in_lds<N, NS, R>() ? NS * (R - 1) : 0; }
-
-// p[r] = w^r for 1 <= r < R from p[1] = w: p[r] = p[h] p[r - h], h the largest power of two
-// below r (or r/2 for powers of two), so w^r is at most floor(log2 r) + 1 products deep.
-template <int R>
-__device__ __forceinline__ void twiddle_powers(float2* p) {
-#pragma unroll
-  for (int r = 2; r < R; ++r) {
-    int h = 1;
-    while (2 * h < r) h *= 2;
-    p[r] = cmul(p[h], p[r - h]);
-  }
-}
 
 template <int N, int T, int NS, int R>
 struct TwCacheBase {
   using G = Geom<N, T, R>;
   static constexpr bool IN_LDS = tw_in_lds<N, NS, R>();
-  static constexpr bool POW = NS > 1 && !IN_LDS && TwPolicy<N>::powers && R > 2;
-  static constexpr int K = (NS > 1 && !IN_LDS) ? G::B * (POW ? 1 : R - 1) : 1;
+  static constexpr int K = (NS > 1 && !IN_LDS) ? G::B * (R - 1) : 1;
   float2 w[K];
   const float2* lw = nullptr;
   // every thread of the workgroup calls this; the caller synchronises before first use
@@ -520,12 +503,6 @@ struct TwCacheBase {
         tw_lds[i] = tw[m * STEP * r];
       }
       lw = tw_lds;
-    } else if constexpr (POW) {
-#pragma unroll
-      for (int b = 0; b < G::B; ++b) {
-        const int j = tid + b * T;
-        w[b] = G::live(j) ? tw[(j % NS) * STEP] : make_float2(1.f, 0.f);
-      }
     } else if constexpr (NS > 1) {
 #pragma unroll
       for (int b = 0; b < G::B; ++b) {
@@ -539,19 +516,7 @@ struct TwCacheBase {
   }
   template <int DIR>
   __device__ __forceinline__ void apply(float2* v, int tid) const {
-    if constexpr (POW) {
-#pragma unroll
-      for (int b = 0; b < G::B; ++b) {
-        if (G::live(tid + b * T)) {
-          float2 p[R];
-          p[1] = w[b];
-          if (DIR > 0) p[1].y = -p[1].y;
-          twiddle_powers<R>(p);
-#pragma unroll
-          for (int r = 1; r < R; ++r) v[b * R + r] = cmul(v[b * R + r], p[r]);
-        }
-      }
-    } else if constexpr (NS > 1) {
+    if constexpr (NS > 1) {
 #pragma unroll
       for (int b = 0; b < G::B; ++b) {
         const int j = tid + b * T;
@@ -620,19 +585,19 @@ struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>> {
 // ---------------------------------------------------------------------------- line configurations
 // T threads per line (16 points per thread in radix-16 passes), LPW lines per workgroup.  The
 // radix lists are palindromes, so the inverse transform (the list reversed) runs the same passes
-// as the forward one and one twiddle cache serves both.  PF: the range-compression kernel may
-// hold a prefetched second line in registers (not where the line needs 1024 threads, whose
-// registers are capped at 128).  HREG: the filter H is held in registers for the kernel's
-// lifetime (else read from the cached global table per line).  TWB: twiddle sets up to TWB
-// bytes live in LDS.  POW: larger sets are formed from one cached base twiddle per butterfly.
+// as the forward one and one twiddle cache serves both.  PF: the range-compression kernel holds
+// a prefetched second line in registers (not where the line needs 1024 threads, whose registers
+// are capped at 128).  HREG: the filter H is held in registers for the kernel's lifetime (else read
+// from the cached global table per line).  TWB: twiddle sets up to TWB bytes live in LDS.
+// WPE: waves per SIMD the range-compression kernel's registers are sized for (the second
+// launch bound: at most 512 / WPE registers per lane).
 template <int N>
 struct LineCfg;
 
-#define RDF_LINE_CFG(N_, T_, FWD, INV, PF_, HREG_, TWB_, POW_)                    \
+#define RDF_LINE_CFG(N_, T_, FWD, INV, PF_, HREG_, TWB_, WPE_)                    \
   template <>                                                                     \
-  struct TwPolicy<N_> {                                                           \
-    static constexpr int lds_bytes = TWB_;                                        \
-    static constexpr bool powers = POW_;                                          \
+  struct TwLdsBudget<N_> {                                                        \
+    static constexpr int bytes = TWB_;                                            \
   };                                                                              \
   template <>                                                                     \
   struct LineCfg<N_> {                                                            \
@@ -642,6 +607,7 @@ struct LineCfg;
     using Inv = INV;                                                              \
     static constexpr bool PF = PF_;                                               \
     static constexpr bool HREG = HREG_;                                           \
+    static constexpr int WPE = WPE_;                                              \
     static constexpr int LPW = T_ >= 256 ? 1 : 256 / T_;                          \
     static constexpr int WG = T_ * LPW;                                           \
     static constexpr int LDS = lds_len(N_);                                       \
@@ -664,18 +630,14 @@ using L_8_4_8_4_8 = IntList<8, 4, 8, 4, 8>;
 using L_8_16_16_8 = IntList<8, 16, 16, 8>;
 using L_20_15_20 = IntList<20, 15, 20>;
 
-RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, false)
-RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, false)
-RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 4096, false)
-RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, false)
-#if defined(RD_CFG4096_LEAN)
-RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, false, 4096, true)
-#else
-RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, false)
-#endif
-RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, false, false, 8192, false)
-RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, false, false, 16384, false)
-RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096, false)
+RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, 1)
+RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, 1)
+RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 4096, 1)
+RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, 1)
+RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 1)
+RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, false, false, 8192, 4)
+RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, false, false, 16384, 1)
+RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096, 1)
 
 #undef RDF_LINE_CFG
 

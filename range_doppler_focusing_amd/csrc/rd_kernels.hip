@@ -60,39 +60,18 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   }
 }
 
-// Register-cached variant: the twiddles (small sets in LDS) and H are loaded once for the
-// workgroup's lifetime, so the line loop issues no table loads; with PREFETCH the next line's
-// samples are loaded into a second register set while the current line is transformed.  Needs
-// Fwd == Inv (one twiddle cache serves both directions).  Where registers are short (HREG
-// false), H is instead read from the (cache-resident) global table at the multiply.
-template <int N>
-__device__ __forceinline__ void rc_line(float2* v, float2* lds,
-                                        const TwCache<N, LineCfg<N>::T, 1, typename LineCfg<N>::Fwd>& twc,
-                                        const float2* h, const float2* __restrict__ H, int tid) {
-  using C = LineCfg<N>;
-  using L = typename C::Fwd;
-  constexpr int T = C::T;
-  constexpr int RL = ListInfo<L>::last;
-  using GL = Geom<N, T, RL>;
-  PassesCached<N, T, -1, 1, L>::run(v, lds, twc, tid);
-  const float2* Hl = opaque(H);
-#pragma unroll
-  for (int b = 0; b < GL::B; ++b) {
-    const int j = tid + b * T;
-    if (GL::live(j)) {
-#pragma unroll
-      for (int r = 0; r < RL; ++r)
-        v[b * RL + r] = cmul(v[b * RL + r], C::HREG ? h[b * RL + r] : Hl[j + r * GL::NB]);
-    }
-  }
-  PassesCached<N, T, +1, 1, L>::run(v, lds, twc, tid);
-}
-
-// registers of the filter held by one thread (one dummy where H stays in global memory)
+// Register-cached variant: the twiddles (small sets in LDS, larger ones in registers) are
+// loaded once for the workgroup's lifetime, so the line loop issues no twiddle loads.  Needs
+// Fwd == Inv (one twiddle cache serves both directions).  The filter H is either held in
+// registers for the kernel's lifetime (HREG) or read per line from the global table (cache
+// resident) at the multiply.  With prefetch (PF), the next line is loaded into a second register
+// set at the start of the current one.  (Measured on the 4096-point line: a prefetch issued
+// after the multiply, with H read per line so the two never hold registers together, reaches
+// occupancy 4 but is slower -- the exposed filter loads cost more than the occupancy gains.)
 template <int N>
 constexpr int filter_regs() {
   using C = LineCfg<N>;
-  return C::HREG ? Geom<N, C::T, ListInfo<typename C::Fwd>::last>::B * ListInfo<typename C::Fwd>::last : 1;
+  return Geom<N, C::T, ListInfo<typename C::Fwd>::last>::B * ListInfo<typename C::Fwd>::last;
 }
 
 template <int N>
@@ -100,21 +79,34 @@ __device__ __forceinline__ void load_filter(float2* h, const float2* __restrict_
   using C = LineCfg<N>;
   constexpr int RL = ListInfo<typename C::Fwd>::last;
   using GL = Geom<N, C::T, RL>;
-  if constexpr (C::HREG) {
 #pragma unroll
-    for (int b = 0; b < GL::B; ++b) {
-      const int j = tid + b * C::T;
+  for (int b = 0; b < GL::B; ++b) {
+    const int j = tid + b * C::T;
 #pragma unroll
-      for (int r = 0; r < RL; ++r) h[b * RL + r] = GL::live(j) ? H[j + r * GL::NB] : make_float2(0.f, 0.f);
+    for (int r = 0; r < RL; ++r) h[b * RL + r] = GL::live(j) ? H[j + r * GL::NB] : make_float2(0.f, 0.f);
+  }
+}
+
+// v *= H: from the registers h (HREG) or from the global table Hg
+template <int N>
+__device__ __forceinline__ void filter_multiply(float2* v, const float2* h,
+                                                const float2* __restrict__ Hg, int tid) {
+  using C = LineCfg<N>;
+  constexpr int RL = ListInfo<typename C::Fwd>::last;
+  using GL = Geom<N, C::T, RL>;
+#pragma unroll
+  for (int b = 0; b < GL::B; ++b) {
+    const int j = tid + b * C::T;
+    if (GL::live(j)) {
+#pragma unroll
+      for (int r = 0; r < RL; ++r)
+        v[b * RL + r] = cmul(v[b * RL + r], C::HREG ? h[b * RL + r] : Hg[j + r * GL::NB]);
     }
   }
 }
 
-#ifndef RD_RC_MIN_BLOCKS
-#define RD_RC_MIN_BLOCKS 1
-#endif
-template <int N, bool PREFETCH>
-__global__ void __launch_bounds__(LineCfg<N>::WG, RD_RC_MIN_BLOCKS)
+template <int N, bool PF>
+__global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     k_range_compress_pf(const float2* in, float2* out, const float2* __restrict__ H,
                         const float2* __restrict__ tw, int64_t lines) {
   using C = LineCfg<N>;
@@ -122,7 +114,6 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, RD_RC_MIN_BLOCKS)
   static_assert(std::is_same<typename C::Fwd, typename C::Inv>::value, "needs Fwd == Inv");
   constexpr int T = C::T;
   constexpr int R0 = ListInfo<L>::first;
-  constexpr int RL = ListInfo<L>::last;
   using TC = TwCache<N, T, 1, L>;
   __shared__ float2 lds[C::LPW * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
   const int grp = threadIdx.x / T;
@@ -131,28 +122,30 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, RD_RC_MIN_BLOCKS)
   TC twc;
   twc.load_all(tw, lds + C::LPW * C::LDS, tid, threadIdx.x, C::WG);
   // (the first pass's barrier orders the LDS twiddle table before its first use)
-  float2 h[filter_regs<N>()];
-  load_filter<N>(h, H, tid);
+  float2 h[C::HREG ? filter_regs<N>() : 1];
+  if constexpr (C::HREG) load_filter<N>(h, H, tid);
   const int64_t stride = int64_t(gridDim.x) * C::LPW;
   float2 nxt[C::P];
-  if (PREFETCH) {
+  if constexpr (PF) {
     load_line<N, T, R0>(nxt, LineIO(in, N, int64_t(blockIdx.x) * C::LPW, C::LPW, lines), grp * N, tid);
     touch<C::P>(nxt);
   }
   for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < lines; l0 += stride) {
     float2 v[C::P];
-    if (PREFETCH) {
+    if constexpr (PF) {
 #pragma unroll
       for (int i = 0; i < C::P; ++i) v[i] = nxt[i];
       load_line<N, T, R0>(nxt, LineIO(in, N, l0 + stride, C::LPW, lines), grp * N, tid);
     } else {
       load_line<N, T, R0>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
     }
-    rc_line<N>(v, my, twc, h, H, tid);
+    PassesCached<N, T, -1, 1, L>::run(v, my, twc, tid);
+    filter_multiply<N>(v, h, opaque(H), tid);
+    PassesCached<N, T, +1, 1, L>::run(v, my, twc, tid);
     store_line<N, T, R0>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
     // Wait for the prefetch here, where the stores just issued are younger than it and need not
     // complete; a wait at the loop head would merge with the loop entry and drain the stores.
-    if (PREFETCH) touch<C::P>(nxt);
+    if constexpr (PF) touch<C::P>(nxt);
   }
 }
 
