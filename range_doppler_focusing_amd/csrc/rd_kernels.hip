@@ -215,11 +215,12 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
   const int g = blockIdx.x / cg.chunks;
   const int64_t c = int64_t(blockIdx.x - g * cg.chunks) * 64 + col;
   const bool live = c < cg.cols;
-  const int64_t row0 = int64_t(g) * cg.base_mul;
-  // byte offset of element t of this lane's column (out of range -> zero / dropped)
-  auto off = [&](int t) -> uint32_t {
-    return live ? uint32_t(((row0 + int64_t(t) * cg.stride) * cg.cols + c) * 8) : 0xFFFFFFF0u;
-  };
+  // Element t of this lane's column lies at byte base + t * rowstep (32-bit: the array is
+  // below 4 GiB).  Lanes past the last column read the last column and store nothing.  (The
+  // same offsets split into a per-lane base and a wave-uniform scalar part measured ~5% slower
+  // on the 16384-row steps.)
+  const uint32_t base = uint32_t((int64_t(g) * cg.base_mul * cg.cols + (live ? c : cg.cols - 1)) * 8);
+  const uint32_t rowstep = uint32_t(int64_t(cg.stride) * cg.cols * 8);
   const __amdgpu_buffer_rsrc_t rin =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(in), 0, int(bytes), kBufDword3);
   const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(out, 0, int(bytes), kBufDword3);
@@ -232,7 +233,7 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
 #pragma unroll
       for (int r = 0; r < RI; ++r)
         v[b * RI + r] = __builtin_bit_cast(
-            float2, __builtin_amdgcn_raw_buffer_load_b64(rin, off(j + r * G::NB), 0, kAzAux));
+            float2, __builtin_amdgcn_raw_buffer_load_b64(rin, base + uint32_t(j + r * G::NB) * rowstep, 0, kAzAux));
     }
   }
   PassesCached<L, T, DIR, 1, LST>::run(v, my, twc, tid);
@@ -241,18 +242,26 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
 #pragma unroll
     for (int b = 0; b < G::B; ++b) {
       const int j = tid + b * T;
+      // inter-step twiddle W_Na^{DIR g t} for t = j + r NB: exact roots (arguments reduced as
+      // integers mod Na, a power of two) at r = 0 and for the step, then a short recurrence
+      float2 z = make_float2(1.f, 0.f), step = make_float2(1.f, 0.f);
+      if (cg.twiddle) {
+        float sn, cs;
+        sincospif(float((g * j) & (cg.na - 1)) * (2.0f / float(cg.na)), &sn, &cs);
+        z = make_float2(cs, DIR > 0 ? sn : -sn);
+        sincospif(float((g * G::NB) & (cg.na - 1)) * (2.0f / float(cg.na)), &sn, &cs);
+        step = make_float2(cs, DIR > 0 ? sn : -sn);
+      }
 #pragma unroll
       for (int r = 0; r < RO; ++r) {
-        const int t = j + r * G::NB;
         float2 x = v[b * RO + r];
         if (cg.twiddle) {
-          // exact argument: (g t mod Na) / Na, Na a power of two
-          const int e = (g * t) & (cg.na - 1);
-          float sn, cs;
-          sincospif(float(e) * (2.0f / float(cg.na)), &sn, &cs);
-          x = cmul(x, make_float2(cs, DIR > 0 ? sn : -sn));
+          x = cmul(x, z);
+          z = cmul(z, step);
         }
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout, off(t), 0, kAzAux);
+        if (live)
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout,
+                                                base + uint32_t(j + r * G::NB) * rowstep, 0, kAzAux);
       }
     }
   }
@@ -363,7 +372,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
           const float y = xf * xf;
           const float2* tap = my + (m + int(fl));  // tap t reads sample n0 + m + fl + t - 3
           float2 acc = make_float2(0.f, 0.f);
-          float ws = 0.f;
+          float es = 0.f;  // sum of the even parts: the weights sum to 2 es
 #pragma unroll
           for (int q = 0; q < kRcmcTaps / 2; ++q) {
             float e = c.w.even[q][kRcmcDeg / 2];
@@ -377,9 +386,9 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
             const float2 sa = tap[3 - q], sb = tap[4 + q];
             acc.x = fmaf(wa, sa.x, fmaf(wb, sb.x, acc.x));
             acc.y = fmaf(wa, sa.y, fmaf(wb, sb.y, acc.y));
-            ws += wa + wb;
+            es += e;
           }
-          const float sc = __builtin_amdgcn_rcpf(ws);
+          const float sc = 0.5f * __builtin_amdgcn_rcpf(es);
           float2 o = make_float2(acc.x * sc, acc.y * sc);
           if (c.filter) {
             o = cmul(o, z);
