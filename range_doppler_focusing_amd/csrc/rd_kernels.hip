@@ -207,12 +207,19 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
   constexpr int RO = ListInfo<LST>::last;
   using TC = TwCache<L, T, 1, LST>;
   __shared__ float2 lds[C::COLS * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
+  __shared__ float2 step_tw[L];  // inter-step twiddles W_Na^{DIR g t}, t < L
   const int col = threadIdx.x & 63;
   const int tid = threadIdx.x >> 6;
   float2* my = lds + col * C::LDS;
   TC twc;
   twc.load_all(tw, lds + C::COLS * C::LDS, tid, threadIdx.x, C::WG);
   const int g = blockIdx.x / cg.chunks;
+  if (cg.twiddle && threadIdx.x < L) {
+    // exact argument: (g t mod Na) / Na, Na a power of two; read after the passes' barriers
+    float sn, cs;
+    sincospif(float((g * int(threadIdx.x)) & (cg.na - 1)) * (2.0f / float(cg.na)), &sn, &cs);
+    step_tw[threadIdx.x] = make_float2(cs, DIR > 0 ? sn : -sn);
+  }
   const int64_t c = int64_t(blockIdx.x - g * cg.chunks) * 64 + col;
   const bool live = c < cg.cols;
   // Element t of this lane's column lies at byte base + t * rowstep (32-bit: the array is
@@ -242,23 +249,10 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
 #pragma unroll
     for (int b = 0; b < G::B; ++b) {
       const int j = tid + b * T;
-      // inter-step twiddle W_Na^{DIR g t} for t = j + r NB: exact roots (arguments reduced as
-      // integers mod Na, a power of two) at r = 0 and for the step, then a short recurrence
-      float2 z = make_float2(1.f, 0.f), step = make_float2(1.f, 0.f);
-      if (cg.twiddle) {
-        float sn, cs;
-        sincospif(float((g * j) & (cg.na - 1)) * (2.0f / float(cg.na)), &sn, &cs);
-        z = make_float2(cs, DIR > 0 ? sn : -sn);
-        sincospif(float((g * G::NB) & (cg.na - 1)) * (2.0f / float(cg.na)), &sn, &cs);
-        step = make_float2(cs, DIR > 0 ? sn : -sn);
-      }
 #pragma unroll
       for (int r = 0; r < RO; ++r) {
         float2 x = v[b * RO + r];
-        if (cg.twiddle) {
-          x = cmul(x, z);
-          z = cmul(z, step);
-        }
+        if (cg.twiddle) x = cmul(x, step_tw[j + r * G::NB]);
         if (live)
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout,
                                                 base + uint32_t(j + r * G::NB) * rowstep, 0, kAzAux);
