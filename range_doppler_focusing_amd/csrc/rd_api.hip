@@ -49,6 +49,7 @@ struct rd_plan {
   const rdf::LineOps* rops = nullptr;  // range-length kernels
   const rdf::LineOps* aops = nullptr;  // azimuth-length kernels
   int rc_variant = 0;   // 0 table loads, 1 register-cached (pf)
+  int cached = 0;       // image passes use ordinary (cacheable) accesses: image fits the cache
   int rc_grid = 0;      // persistent grid of the range kernels
   int A = 0, B = 0;     // Na = A B: strided and block steps of the azimuth transform
   float2* H = nullptr;       // [Nr] conj(FFT(h)) / Nr
@@ -243,9 +244,11 @@ int persistent_grid(int occ, int cus, int64_t lines, int lpw) {
 }
 
 // -------------------------------------------------------------------------- launch sequences
-rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, hipStream_t s) {
+// chained: the output feeds the azimuth chain (stored cacheable where the image fits the cache)
+rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, bool chained, hipStream_t s) {
   if (P->rc_variant == 1)
-    return check_hip(P->rops->range_compress_pf(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid, s),
+    return check_hip(P->rops->range_compress_pf(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid,
+                                                chained ? P->cached : 0, s),
                      "range compression launch");
   return check_hip(P->rops->range_compress(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid, s),
                    "range compression launch");
@@ -276,14 +279,15 @@ rdf::ColStep col_step(const rd_plan* P, bool forward, bool strided) {
 rd_status run_col(rd_plan* P, const float2* src, float2* dst, bool forward, bool strided,
                   hipStream_t s) {
   const rdf::ColStep st = col_step(P, forward, strided);
-  return check_hip(rdf::launch_col_fft(src, dst, strided ? P->tw_A : P->tw_B, st, P->p.Nr, P->p.Na, s),
+  return check_hip(rdf::launch_col_fft(src, dst, strided ? P->tw_A : P->tw_B, st, P->p.Nr, P->p.Na,
+                                       P->cached, s),
                    "azimuth transform launch");
 }
 
 rd_status run_rows(rd_plan* P, const float2* src, float2* dst, bool filter, hipStream_t s) {
   rdf::AzRowConst c = P->az;
   c.filter = filter ? 1 : 0;
-  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, s), "RCMC launch");
+  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, P->cached, s), "RCMC launch");
 }
 
 rd_status run_azimuth(rd_plan* P, const float2* rc, float2* img, hipStream_t s) {
@@ -446,6 +450,10 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     P->az.inv_na = float(1.0 / double(Na));
     P->az.filter = 1;
     rcmc_weight_polys(p.kaiser_beta, &P->az.w);
+    // The image passes run cacheable when the image fits well inside the 256 MB Infinity
+    // Cache (RD_AZ_CACHE=0/1 overrides, for measurement).
+    P->cached = int64_t(Na) * p.Nr * 8 <= (int64_t(160) << 20) ? 1 : 0;
+    if (const char* ce = std::getenv("RD_AZ_CACHE")) P->cached = std::atoi(ce) ? 1 : 0;
   }
   {
     std::lock_guard<std::mutex> g(g_plans_mu);
@@ -472,7 +480,7 @@ rd_status rd_range_compress(rd_plan* plan, const rd_c64* echo, rd_c64* rc, void*
   const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
   if (partial_overlap(echo, rc, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and rc overlap without being equal");
   return run_range_compress(plan, reinterpret_cast<const float2*>(echo),
-                            reinterpret_cast<float2*>(rc), static_cast<hipStream_t>(stream));
+                            reinterpret_cast<float2*>(rc), false, static_cast<hipStream_t>(stream));
 }
 
 rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* stream) {
@@ -495,7 +503,7 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
   if (partial_overlap(echo, img, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and img overlap without being equal");
   hipStream_t s = static_cast<hipStream_t>(stream);
   float2* I = reinterpret_cast<float2*>(img);
-  st = run_range_compress(plan, reinterpret_cast<const float2*>(echo), I, s);
+  st = run_range_compress(plan, reinterpret_cast<const float2*>(echo), I, true, s);
   if (st != RD_OK) return st;
   return run_azimuth(plan, I, I, s);
 }

@@ -14,14 +14,14 @@
 #ifndef RD_PF_WAVES
 #define RD_PF_WAVES 1
 #endif
-#ifndef RD_AZ_AUX
-#define RD_AZ_AUX 0
-#endif
 namespace rdf {
-// cache policy of the azimuth passes: ordinary (cacheable) accesses; the in-place passes re-read
-// an image that the 256 MB Infinity Cache partly holds (measured 6% faster on the 4096^2 chain
-// than non-temporal hints)
-constexpr int kAzAux = RD_AZ_AUX;
+// Cache policy of the image passes (an instruction's cache-policy bits): the azimuth chain
+// re-reads what the previous pass wrote, which the 256 MB Infinity Cache holds when the image
+// fits there -- ordinary (cacheable) accesses then (measured ~5% faster on the 4096 x 4096
+// chain); a larger image would only churn the cache, so its passes stream with the
+// non-temporal hint (measured ~5% faster on the 16384 x 16384 chain).
+constexpr int kAuxCached = 0;
+constexpr int kAuxStream = kBufNonTemporal;
 
 // ------------------------------------------------------------------------------------------
 // fused range compression: load -> FFT -> x H (H already carries 1/N) -> IFFT -> store.
@@ -105,7 +105,7 @@ __device__ __forceinline__ void filter_multiply(float2* v, const float2* h,
   }
 }
 
-template <int N, bool PF>
+template <int N, bool PF, int SAUX>
 __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     k_range_compress_pf(const float2* in, float2* out, const float2* __restrict__ H,
                         const float2* __restrict__ tw, int64_t lines) {
@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     PassesCached<N, T, -1, 1, L>::run(v, my, twc, tid);
     filter_multiply<N>(v, h, opaque(H), tid);
     PassesCached<N, T, +1, 1, L>::run(v, my, twc, tid);
-    store_line<N, T, R0>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
+    store_line<N, T, R0, SAUX>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
     // Wait for the prefetch here, where the stores just issued are younger than it and need not
     // complete; a wait at the loop head would merge with the loop entry and drain the stores.
     if constexpr (PF) touch<C::P>(nxt);
@@ -196,7 +196,7 @@ struct ColGeom {
   int twiddle;       // multiply output t by W_Na^{DIR g t} after the transform
 };
 
-template <int L, int DIR>
+template <int L, int DIR, int AUX>
 __global__ void __launch_bounds__(ColCfg<L>::WG)
     k_col_fft(const float2* in, float2* out, const float2* __restrict__ tw, ColGeom cg,
               uint32_t bytes) {
@@ -240,7 +240,7 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
 #pragma unroll
       for (int r = 0; r < RI; ++r)
         v[b * RI + r] = __builtin_bit_cast(
-            float2, __builtin_amdgcn_raw_buffer_load_b64(rin, base + uint32_t(j + r * G::NB) * rowstep, 0, kAzAux));
+            float2, __builtin_amdgcn_raw_buffer_load_b64(rin, base + uint32_t(j + r * G::NB) * rowstep, 0, AUX));
     }
   }
   PassesCached<L, T, DIR, 1, LST>::run(v, my, twc, tid);
@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
         if (cg.twiddle) x = cmul(x, step_tw[j + r * G::NB]);
         if (live)
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout,
-                                                base + uint32_t(j + r * G::NB) * rowstep, 0, kAzAux);
+                                                base + uint32_t(j + r * G::NB) * rowstep, 0, AUX);
       }
     }
   }
@@ -280,7 +280,7 @@ struct RowStage {
   static constexpr int LEN = 3 + CH + MARGIN;
 };
 
-template <int N>
+template <int N, int AUX>
 __global__ void __launch_bounds__(RowStage<N>::WG)
     k_rcmc_mf(const float2* in, float2* out, AzRowConst c, int64_t rows) {
   using RS = RowStage<N>;
@@ -308,7 +308,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
     const LineIO src = RS::CHUNKS == 1 ? LineIO(in, N, i0, RS::LPW, rows)
                                        : LineIO(in, N, item < items ? row : rows, 1, rows);
     const int e0 = RS::CHUNKS == 1 ? grp * N : n0;
-    load_line<CH, T, R0, kAzAux>(v, src, e0, tid);
+    load_line<CH, T, R0, AUX>(v, src, e0, tid);
     float2 pre = make_float2(0.f, 0.f);
     int hs = -1;  // this thread's first halo slot, if any
     if constexpr (RS::CHUNKS > 1) {
@@ -319,7 +319,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
         const int sidx = i < 3 ? n0 - 3 + i : n0 + CH + (i - 3);
         hs = i < 3 ? i : 3 + CH + (i - 3);
         if (sidx >= 0 && sidx < N)
-          pre = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, sidx * 8, 0, kAzAux));
+          pre = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, sidx * 8, 0, AUX));
       }
     }
     __syncthreads();  // the previous chunk's taps have been read
@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
       for (int i = tid + T; i < 3 + c.halo; i += T) {  // halos longer than one pass
         const int sidx = n0 + CH + (i - 3);
         my[3 + CH + (i - 3)] = sidx < N ? __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                 src.rsrc, sidx * 8, 0, kAzAux))
+                                                 src.rsrc, sidx * 8, 0, AUX))
                                         : make_float2(0.f, 0.f);
       }
     }
@@ -394,7 +394,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
     }
     const LineIO dst = RS::CHUNKS == 1 ? LineIO(out, N, i0, RS::LPW, rows)
                                        : LineIO(out, N, item < items ? row : rows, 1, rows);
-    store_line<CH, T, R0, kAzAux>(v, dst, e0, tid);
+    store_line<CH, T, R0, AUX>(v, dst, e0, tid);
   }
 }
 
@@ -437,7 +437,7 @@ hipError_t occupancy(int* rc, int* fft, int* azc) {
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(fft, k_line_fft<N, -1>, LineCfg<N>::WG, 0);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(azc, k_rcmc_mf<N>, RowStage<N>::WG, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(azc, k_rcmc_mf<N, kAuxCached>, RowStage<N>::WG, 0);
 }
 
 #ifndef RD_RC_PREFETCH
@@ -445,24 +445,32 @@ hipError_t occupancy(int* rc, int* fft, int* azc) {
 #endif
 template <int N>
 hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const float2* tw,
-                        int64_t lines, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF>), dim3(grid), dim3(LineCfg<N>::WG), 0,
-                     s, in, out, H, tw, lines);
+                        int64_t lines, int grid, int cached, hipStream_t s) {
+  constexpr bool PF = RD_RC_PREFETCH && LineCfg<N>::PF;
+  if (cached)
+    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxCached>), dim3(grid), dim3(LineCfg<N>::WG),
+                       0, s, in, out, H, tw, lines);
+  else
+    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream>), dim3(grid), dim3(LineCfg<N>::WG),
+                       0, s, in, out, H, tw, lines);
   return hipGetLastError();
 }
 
 template <int N>
 hipError_t occupancy_pf(int* rc) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF>,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream>,
                                                       LineCfg<N>::WG, 0);
 }
 
 template <int N>
 hipError_t launch_rcmc_mf(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
-                          int grid, hipStream_t s) {
+                          int grid, int cached, hipStream_t s) {
   const int64_t wgs = (rows * RowStage<N>::CHUNKS + RowStage<N>::LPW - 1) / RowStage<N>::LPW;
   if (grid <= 0 || grid > wgs) grid = int(wgs);
-  hipLaunchKernelGGL(k_rcmc_mf<N>, dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows);
+  if (cached)
+    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxCached>), dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows);
+  else
+    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxStream>), dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows);
   return hipGetLastError();
 }
 
@@ -489,9 +497,15 @@ const LineOps* line_ops(int n) {
   return nullptr;
 }
 
+template <int L, int DIR, int AUX>
+void launch_col3(const float2* in, float2* out, const float2* tw_L, const ColGeom& cg, dim3 grid,
+                 uint32_t bytes, hipStream_t s) {
+  hipLaunchKernelGGL((k_col_fft<L, DIR, AUX>), grid, dim3(ColCfg<L>::WG), 0, s, in, out, tw_L, cg, bytes);
+}
+
 template <int L>
 hipError_t launch_col(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
-                      int64_t cols, int na, hipStream_t s) {
+                      int64_t cols, int na, int cached, hipStream_t s) {
   ColGeom cg;
   cg.cols = cols;
   cg.base_mul = st.base_mul;
@@ -502,22 +516,23 @@ hipError_t launch_col(const float2* in, float2* out, const float2* tw_L, const C
   const uint64_t bytes = uint64_t(na) * uint64_t(cols) * 8u;
   if (bytes > 0xFFFFFFF0ull) return hipErrorInvalidValue;
   const dim3 grid(unsigned(int64_t(st.sets) * cg.chunks));
-  if (st.dir < 0)
-    hipLaunchKernelGGL((k_col_fft<L, -1>), grid, dim3(ColCfg<L>::WG), 0, s, in, out, tw_L, cg,
-                       uint32_t(bytes));
-  else
-    hipLaunchKernelGGL((k_col_fft<L, +1>), grid, dim3(ColCfg<L>::WG), 0, s, in, out, tw_L, cg,
-                       uint32_t(bytes));
+  if (st.dir < 0) {
+    if (cached) launch_col3<L, -1, kAuxCached>(in, out, tw_L, cg, grid, uint32_t(bytes), s);
+    else launch_col3<L, -1, kAuxStream>(in, out, tw_L, cg, grid, uint32_t(bytes), s);
+  } else {
+    if (cached) launch_col3<L, +1, kAuxCached>(in, out, tw_L, cg, grid, uint32_t(bytes), s);
+    else launch_col3<L, +1, kAuxStream>(in, out, tw_L, cg, grid, uint32_t(bytes), s);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
-                          int64_t cols, int na, hipStream_t s) {
+                          int64_t cols, int na, int cached, hipStream_t s) {
   switch (st.L) {
-    case 16: return launch_col<16>(in, out, tw_L, st, cols, na, s);
-    case 32: return launch_col<32>(in, out, tw_L, st, cols, na, s);
-    case 64: return launch_col<64>(in, out, tw_L, st, cols, na, s);
-    case 128: return launch_col<128>(in, out, tw_L, st, cols, na, s);
+    case 16: return launch_col<16>(in, out, tw_L, st, cols, na, cached, s);
+    case 32: return launch_col<32>(in, out, tw_L, st, cols, na, cached, s);
+    case 64: return launch_col<64>(in, out, tw_L, st, cols, na, cached, s);
+    case 128: return launch_col<128>(in, out, tw_L, st, cols, na, cached, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -42,14 +42,17 @@ struct LineOps {
   hipError_t (*occupancy)(int* rc, int* fft, int* azc);
   // register-cached, prefetching range compression (nullptr where the forward and inverse
   // radix lists differ) and its occupancy
+  // (cached: ordinary stores, for output that the next pass re-reads from the cache; else
+  // non-temporal stores)
   hipError_t (*range_compress_pf)(const float2* in, float2* out, const float2* H,
-                                  const float2* tw, int64_t lines, int grid, hipStream_t s);
+                                  const float2* tw, int64_t lines, int grid, int cached,
+                                  hipStream_t s);
   hipError_t (*occupancy_pf)(int* rc);
   // RCMC + azimuth filter over rows of this length (in == out allowed; grid 0 = one workgroup
   // per staged chunk); margin = samples staged after a chunk, so the largest shift the kernel
   // accepts is margin - 5
   hipError_t (*rcmc_mf)(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
-                        int grid, hipStream_t s);
+                        int grid, int cached, hipStream_t s);
   int margin;
 };
 
@@ -65,8 +68,9 @@ struct ColStep {
   int sets;       // number of row sets
   int twiddle;    // apply the inter-step twiddle W_Na^{dir g t}
 };
+// cached: ordinary loads and stores (image held by the Infinity Cache), else non-temporal
 hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
-                          int64_t cols, int na, hipStream_t s);
+                          int64_t cols, int na, int cached, hipStream_t s);
 
 // out[k] = in[(k % A) B + k / A] for rows of `cols` samples: Doppler-digit row order to natural
 hipError_t launch_row_unpermute(const float2* in, float2* out, int A, int B, int64_t cols,
