@@ -435,13 +435,27 @@ __device__ __forceinline__ void butterflies(float2* v, int tid) {
   }
 }
 
+// Ordering of an exchange through LDS.  When every thread of a transform lies in one wave
+// (WAVE), the wave's LDS accesses execute in program order, so the exchange needs only to keep
+// the compiler from moving accesses across it; otherwise it is a workgroup barrier.
+template <bool WAVE>
+__device__ __forceinline__ void exchange_sync() {
+  if constexpr (WAVE) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
+
 // The passes of one transform.  Every thread of the workgroup must call run() (it contains
-// workgroup barriers); threads whose butterflies fall past N/R idle through a pass.
-template <int N, int T, int DIR, int NS, class L>
+// workgroup barriers unless WAVE); threads whose butterflies fall past N/R idle through a pass.
+template <int N, int T, int DIR, int NS, class L, bool WAVE = false>
 struct Passes;
 
-template <int N, int T, int DIR, int NS, int R>
-struct Passes<N, T, DIR, NS, IntList<R>> {
+template <int N, int T, int DIR, int NS, int R, bool WAVE>
+struct Passes<N, T, DIR, NS, IntList<R>, WAVE> {
   static __device__ __forceinline__ void run(float2* v, float2* lds, const float2* __restrict__ tw,
                                              int tid) {
     twiddle<N, T, R, NS, DIR>(v, opaque(tw), tid);
@@ -449,17 +463,17 @@ struct Passes<N, T, DIR, NS, IntList<R>> {
   }
 };
 
-template <int N, int T, int DIR, int NS, int R, int R2, int... Rs>
-struct Passes<N, T, DIR, NS, IntList<R, R2, Rs...>> {
+template <int N, int T, int DIR, int NS, int R, int R2, int... Rs, bool WAVE>
+struct Passes<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
   static __device__ __forceinline__ void run(float2* v, float2* lds, const float2* __restrict__ tw,
                                              int tid) {
     twiddle<N, T, R, NS, DIR>(v, opaque(tw), tid);
     butterflies<N, T, R, DIR>(v, tid);
-    __syncthreads();  // the line buffer may still be read by the previous exchange
+    exchange_sync<WAVE>();  // the line buffer may still be read by the previous exchange
     store_lds<N, T, R, NS>(v, lds, tid);
-    __syncthreads();
+    exchange_sync<WAVE>();
     load_lds<N, T, R2>(v, lds, tid);
-    Passes<N, T, DIR, NS * R, IntList<R2, Rs...>>::run(v, lds, tw, tid);
+    Passes<N, T, DIR, NS * R, IntList<R2, Rs...>, WAVE>::run(v, lds, tw, tid);
   }
 };
 
@@ -483,6 +497,22 @@ struct TwLdsBudget {
 };
 template <int N, int NS, int R>
 constexpr bool tw_in_lds() { return NS > 1 && NS * (R - 1) * 8 <= TwLdsBudget<N>::bytes; }
+// A register-held twiddle set of a power-of-two radix may keep only the powers w^(2^i) of each
+// butterfly's base root w and form the others as products when applied (log2 R instead of R - 1
+// registers per butterfly, for R - 1 - log2 R extra complex multiplies per application).
+template <int N>
+struct TwDerive {
+  static constexpr bool value = false;
+};
+// Range compression of a line whose filter is not held in registers may issue the next line's
+// prefetch after the filter multiply (the prefetch then overlaps the inverse transform only, and
+// the filter loads do not wait for it).
+template <int N>
+struct PfLate {
+  static constexpr bool value = false;
+};
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+constexpr bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 template <int N, int NS, int R>
 constexpr int tw_lds_len() { return tw_in_lds<N, NS, R>() ? NS * (R - 1) : 0; }
 
@@ -490,7 +520,9 @@ template <int N, int T, int NS, int R>
 struct TwCacheBase {
   using G = Geom<N, T, R>;
   static constexpr bool IN_LDS = tw_in_lds<N, NS, R>();
-  static constexpr int K = (NS > 1 && !IN_LDS) ? G::B * (R - 1) : 1;
+  static constexpr bool DERIVE = NS > 1 && !IN_LDS && TwDerive<N>::value && R > 2;
+  static constexpr int KB = DERIVE ? ilog2(R - 1) + 1 : R - 1;  // registers per butterfly
+  static constexpr int K = (NS > 1 && !IN_LDS) ? G::B * KB : 1;
   float2 w[K];
   const float2* lw = nullptr;
   // every thread of the workgroup calls this; the caller synchronises before first use
@@ -503,6 +535,15 @@ struct TwCacheBase {
         tw_lds[i] = tw[m * STEP * r];
       }
       lw = tw_lds;
+    } else if constexpr (DERIVE) {
+#pragma unroll
+      for (int b = 0; b < G::B; ++b) {
+        const int j = tid + b * T;
+        const int e = (j % NS) * STEP;
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+          w[b * KB + i] = G::live(j) ? tw[e << i] : make_float2(1.f, 0.f);
+      }
     } else if constexpr (NS > 1) {
 #pragma unroll
       for (int b = 0; b < G::B; ++b) {
@@ -514,9 +555,39 @@ struct TwCacheBase {
       }
     }
   }
+  // Marks the register-held set as used here (see touch): placed before a line loop, it makes
+  // the wait for its loads happen there, once, instead of inside the loop, where the wait would
+  // also cover the stores of the previous line.
+  __device__ __forceinline__ void touch_regs() const {
+    if constexpr (NS > 1 && !IN_LDS) touch<K>(w);
+  }
   template <int DIR>
   __device__ __forceinline__ void apply(float2* v, int tid) const {
-    if constexpr (NS > 1) {
+    if constexpr (DERIVE) {
+#pragma unroll
+      for (int b = 0; b < G::B; ++b) {
+        if (G::live(tid + b * T)) {
+          // p[r] = w^r: powers of two from the registers, the rest as w^(2^k) * w^(r - 2^k)
+          // (the base roots pass through an empty asm statement, so the products are formed
+          // here at every application instead of being hoisted out of a line loop into R - 1
+          // live registers)
+          float2 p[R];
+#pragma unroll
+          for (int r = 1; r < R; ++r) {
+            const int hb = 1 << ilog2(r);
+            if (hb == r) {
+              p[r] = w[b * KB + ilog2(r)];
+              asm volatile("" : "+v"(p[r].x), "+v"(p[r].y));
+            } else {
+              p[r] = cmul(p[hb], p[r - hb]);
+            }
+            float2 x = p[r];
+            if (DIR > 0) x.y = -x.y;
+            v[b * R + r] = cmul(v[b * R + r], x);
+          }
+        }
+      }
+    } else if constexpr (NS > 1) {
 #pragma unroll
       for (int b = 0; b < G::B; ++b) {
         const int j = tid + b * T;
@@ -540,6 +611,7 @@ struct TwCache<N, T, NS, IntList<R>> : TwCacheBase<N, T, NS, R> {
                                            int wg_tid, int wg_size) {
     this->load(tw, tw_lds, tid, wg_tid, wg_size);
   }
+  __device__ __forceinline__ void touch_all() const { this->touch_regs(); }
 };
 
 template <int N, int T, int NS, int R, int R2, int... Rs>
@@ -552,14 +624,18 @@ struct TwCache<N, T, NS, IntList<R, R2, Rs...>> : TwCacheBase<N, T, NS, R> {
     this->load(tw, tw_lds, tid, wg_tid, wg_size);
     next.load_all(tw, tw_lds + tw_lds_len<N, NS, R>(), tid, wg_tid, wg_size);
   }
+  __device__ __forceinline__ void touch_all() const {
+    this->touch_regs();
+    next.touch_all();
+  }
 };
 
 // The passes of one transform with twiddles from a TwCache (same contract as Passes).
-template <int N, int T, int DIR, int NS, class L>
+template <int N, int T, int DIR, int NS, class L, bool WAVE = false>
 struct PassesCached;
 
-template <int N, int T, int DIR, int NS, int R>
-struct PassesCached<N, T, DIR, NS, IntList<R>> {
+template <int N, int T, int DIR, int NS, int R, bool WAVE>
+struct PassesCached<N, T, DIR, NS, IntList<R>, WAVE> {
   static __device__ __forceinline__ void run(float2* v, float2* lds,
                                              const TwCache<N, T, NS, IntList<R>>& c, int tid) {
     c.template apply<DIR>(v, tid);
@@ -567,18 +643,18 @@ struct PassesCached<N, T, DIR, NS, IntList<R>> {
   }
 };
 
-template <int N, int T, int DIR, int NS, int R, int R2, int... Rs>
-struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>> {
+template <int N, int T, int DIR, int NS, int R, int R2, int... Rs, bool WAVE>
+struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
   static __device__ __forceinline__ void run(float2* v, float2* lds,
                                              const TwCache<N, T, NS, IntList<R, R2, Rs...>>& c,
                                              int tid) {
     c.template apply<DIR>(v, tid);
     butterflies<N, T, R, DIR>(v, tid);
-    __syncthreads();
+    exchange_sync<WAVE>();
     store_lds<N, T, R, NS>(v, lds, tid);
-    __syncthreads();
+    exchange_sync<WAVE>();
     load_lds<N, T, R2>(v, lds, tid);
-    PassesCached<N, T, DIR, NS * R, IntList<R2, Rs...>>::run(v, lds, c.next, tid);
+    PassesCached<N, T, DIR, NS * R, IntList<R2, Rs...>, WAVE>::run(v, lds, c.next, tid);
   }
 };
 
@@ -586,18 +662,31 @@ struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>> {
 // T threads per line (16 points per thread in radix-16 passes), LPW lines per workgroup.  The
 // radix lists are palindromes, so the inverse transform (the list reversed) runs the same passes
 // as the forward one and one twiddle cache serves both.  PF: the range-compression kernel holds
-// a prefetched second line in registers (not where the line needs 1024 threads, whose registers
-// are capped at 128).  HREG: the filter H is held in registers for the kernel's lifetime (else read
-// from the cached global table per line).  TWB: twiddle sets up to TWB bytes live in LDS.
-// WPE: waves per SIMD the range-compression kernel's registers are sized for (the second
-// launch bound: at most 512 / WPE registers per lane).
+// a prefetched second line in registers.  HREG: the filter H is held in registers for the
+// kernel's lifetime (else read from the cached global table per line, all of a thread's filter
+// loads issued together).  TWB: twiddle sets up to TWB bytes live in LDS.  WPE: waves per SIMD
+// the range-compression kernel's registers are sized for (the second launch bound: at most
+// 512 / WPE registers per lane).  TWD: register-held twiddle sets keep only the power-of-two
+// powers of each root (PfLate/TwDerive above).  LATE: the prefetch is issued after the filter
+// multiply.  The long lines (8192, 16384: 512 / 1024 threads, at most 128 registers) need TWD
+// to fit a prefetch; measured on MI355X, prefetch + TWD + LATE is 5-7% faster there than no
+// prefetch.  At 4096, TWD would allow 4 waves per SIMD but its extra multiplies cancel the gain
+// (measured equal), so the full register sets stay.
 template <int N>
 struct LineCfg;
 
-#define RDF_LINE_CFG(N_, T_, FWD, INV, PF_, HREG_, TWB_, WPE_)                    \
+#define RDF_LINE_CFG(N_, T_, FWD, INV, PF_, HREG_, TWB_, WPE_, TWD_, LATE_)      \
+  template <>                                                                     \
+  struct PfLate<N_> {                                                             \
+    static constexpr bool value = LATE_;                                          \
+  };                                                                              \
   template <>                                                                     \
   struct TwLdsBudget<N_> {                                                        \
     static constexpr int bytes = TWB_;                                            \
+  };                                                                              \
+  template <>                                                                     \
+  struct TwDerive<N_> {                                                           \
+    static constexpr bool value = TWD_;                                           \
   };                                                                              \
   template <>                                                                     \
   struct LineCfg<N_> {                                                            \
@@ -609,6 +698,7 @@ struct LineCfg;
     static constexpr bool HREG = HREG_;                                           \
     static constexpr int WPE = WPE_;                                              \
     static constexpr int LPW = T_ >= 256 ? 1 : 256 / T_;                          \
+    static constexpr bool WAVE = 64 % T_ == 0; /* a line's threads share one wave */ \
     static constexpr int WG = T_ * LPW;                                           \
     static constexpr int LDS = lds_len(N_);                                       \
     static constexpr int P = MaxRegs<N_, T_, FWD>::value > MaxRegs<N_, T_, INV>::value \
@@ -630,14 +720,14 @@ using L_8_4_8_4_8 = IntList<8, 4, 8, 4, 8>;
 using L_8_16_16_8 = IntList<8, 16, 16, 8>;
 using L_20_15_20 = IntList<20, 15, 20>;
 
-RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, 1)
-RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, 1)
-RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 4096, 1)
-RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, 1)
-RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 1)
-RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, false, false, 8192, 4)
-RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, false, false, 16384, 1)
-RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096, 1)
+RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, 1, false, false)
+RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, 1, false, false)
+RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 4096, 1, false, false)
+RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, 1, false, false)
+RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 1, false, false)
+RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, true, false, 8192, 4, true, true)
+RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, true, false, 16384, 1, true, true)
+RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096, 1, false, false)
 
 #undef RDF_LINE_CFG
 

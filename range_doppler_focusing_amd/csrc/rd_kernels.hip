@@ -42,7 +42,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     const LineIO src(in, N, l0, C::LPW, lines), dst(out, N, l0, C::LPW, lines);
     float2 v[C::P];
     load_line<N, T, R0>(v, src, grp * N, tid);
-    Passes<N, T, -1, 1, typename C::Fwd>::run(v, my, tw, tid);
+    Passes<N, T, -1, 1, typename C::Fwd, C::WAVE>::run(v, my, tw, tid);
     {
       using G = Geom<N, T, RL>;
       const float2* Hl = opaque(H);
@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
         }
       }
     }
-    Passes<N, T, +1, 1, typename C::Inv>::run(v, my, tw, tid);
+    Passes<N, T, +1, 1, typename C::Inv, C::WAVE>::run(v, my, tw, tid);
     store_line<N, T, R0>(v, dst, grp * N, tid);
   }
 }
@@ -94,6 +94,21 @@ __device__ __forceinline__ void filter_multiply(float2* v, const float2* h,
   using C = LineCfg<N>;
   constexpr int RL = ListInfo<typename C::Fwd>::last;
   using GL = Geom<N, C::T, RL>;
+  if constexpr (!C::HREG) {
+    // Issue every filter load before the first use: left to itself the compiler serialises
+    // them (load, wait, multiply) to save registers, one cache round trip per sample.
+    float2 hv[GL::B * RL];
+    load_filter<N>(hv, Hg, tid);
+    touch<GL::B * RL>(hv);
+#pragma unroll
+    for (int b = 0; b < GL::B; ++b) {
+      if (GL::live(tid + b * C::T)) {
+#pragma unroll
+        for (int r = 0; r < RL; ++r) v[b * RL + r] = cmul(v[b * RL + r], hv[b * RL + r]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < GL::B; ++b) {
     const int j = tid + b * C::T;
@@ -115,15 +130,22 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   constexpr int T = C::T;
   constexpr int R0 = ListInfo<L>::first;
   using TC = TwCache<N, T, 1, L>;
+  constexpr bool LATE = PF && PfLate<N>::value && !C::HREG;
   __shared__ float2 lds[C::LPW * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * C::LDS;
   TC twc;
   twc.load_all(tw, lds + C::LPW * C::LDS, tid, threadIdx.x, C::WG);
-  // (the first pass's barrier orders the LDS twiddle table before its first use)
+  // (the first pass's barrier orders the LDS twiddle table before its first use, unless a line's
+  // exchanges are wave-local: then an explicit barrier does)
+  if constexpr (C::WAVE && TC::LDS > 0) __syncthreads();
   float2 h[C::HREG ? filter_regs<N>() : 1];
   if constexpr (C::HREG) load_filter<N>(h, H, tid);
+  // Wait for the filter and twiddle registers before the line loop (see touch): a wait for them
+  // inside the loop would also wait for the previous line's stores on every iteration.
+  if constexpr (C::HREG) touch<filter_regs<N>()>(h);
+  twc.touch_all();
   const int64_t stride = int64_t(gridDim.x) * C::LPW;
   float2 nxt[C::P];
   if constexpr (PF) {
@@ -135,13 +157,14 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     if constexpr (PF) {
 #pragma unroll
       for (int i = 0; i < C::P; ++i) v[i] = nxt[i];
-      load_line<N, T, R0>(nxt, LineIO(in, N, l0 + stride, C::LPW, lines), grp * N, tid);
+      if constexpr (!LATE) load_line<N, T, R0>(nxt, LineIO(in, N, l0 + stride, C::LPW, lines), grp * N, tid);
     } else {
       load_line<N, T, R0>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
     }
-    PassesCached<N, T, -1, 1, L>::run(v, my, twc, tid);
+    PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
     filter_multiply<N>(v, h, opaque(H), tid);
-    PassesCached<N, T, +1, 1, L>::run(v, my, twc, tid);
+    if constexpr (LATE) load_line<N, T, R0>(nxt, LineIO(in, N, l0 + stride, C::LPW, lines), grp * N, tid);
+    PassesCached<N, T, +1, 1, L, C::WAVE>::run(v, my, twc, tid);
     store_line<N, T, R0, SAUX>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
     // Wait for the prefetch here, where the stores just issued are younger than it and need not
     // complete; a wait at the loop head would merge with the loop entry and drain the stores.
@@ -167,7 +190,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < lines; l0 += int64_t(gridDim.x) * C::LPW) {
     float2 v[C::P];
     load_line<N, T, RI>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
-    Passes<N, T, DIR, 1, L>::run(v, my, tw, tid);
+    Passes<N, T, DIR, 1, L, C::WAVE>::run(v, my, tw, tid);
     if (scale != 1.0f) {
 #pragma unroll
       for (int i = 0; i < C::P; ++i) v[i] = cscale(v[i], scale);
