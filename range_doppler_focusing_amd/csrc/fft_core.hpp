@@ -257,6 +257,136 @@ __device__ __forceinline__ void dft_ct(float2* v) {
   }
 }
 
+// Length-8 and length-16 DFTs with the internal rotations folded into fused multiply-adds.
+// Each rotation by a constant root is written as scale * (unit-diagonal factor): the roots at
+// odd multiples of pi/4 are h (+-1 +- j) with h = sqrt(1/2), and those at odd multiples of pi/8
+// are c (1 +- j tau) times a power of j, with c = cos(pi/8), tau = tan(pi/8) (|tau| < 1, so
+// the factored form loses no accuracy).  The factor costs two additions (or two FMAs), and the
+// common scale of the two inputs that meet in the following radix-2 step multiplies their
+// combination inside that step's FMAs, so no separate multiplication remains: 144 instead of
+// 160 VALU operations for a length-16 DFT, 52 instead of 56 for length 8.  Same split as
+// dft_ct (input n = B n1 + n2, output k = k1 + A k2), so dft_input_order is unchanged.
+constexpr float kSqrtHalf = 0.707106781186547524400844362104849039f;  // cos(pi/4)
+constexpr float kCosPi8 = 0.923879532511286756128183189396788933f;    // cos(pi/8)
+constexpr float kTanPi8 = 0.414213562373095048801688724209698079f;    // tan(pi/8)
+
+// Keeps the scheduler from interleaving the output groups of one DFT: each group's
+// temporaries die before the next group starts (interleaved, the length-16 DFT needs ~10 more
+// registers, which costs a wave per SIMD or spills in the range-compression kernel).
+__device__ __forceinline__ void group_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ float2 cfma(float s, float2 q, float2 a) {
+  return make_float2(fmaf(s, q.x, a.x), fmaf(s, q.y, a.y));
+}
+// (1 + D j) u and (-1 + D j) u
+template <int D>
+__device__ __forceinline__ float2 mul_1pj(float2 u) {
+  return D > 0 ? make_float2(u.x - u.y, u.y + u.x) : make_float2(u.x + u.y, u.y - u.x);
+}
+template <int D>
+__device__ __forceinline__ float2 mul_m1pj(float2 u) {
+  return D > 0 ? make_float2(-u.x - u.y, u.x - u.y) : make_float2(u.y - u.x, -u.y - u.x);
+}
+// (1 + S j tau) u, S = +1 / -1
+template <int S>
+__device__ __forceinline__ float2 mul_1ptau(float2 u) {
+  return make_float2(fmaf(-float(S) * kTanPi8, u.y, u.x), fmaf(float(S) * kTanPi8, u.x, u.y));
+}
+
+// k1 = odd group of a split-radix step: inputs already multiplied by W^{n2 k1} except for the
+// scales; returns the four outputs k2 = 0..3 of the length-4 DFT over n2 in o[0..3].
+template <int DIR>
+__device__ __forceinline__ void dft8_odd(const float2* u, float2* o) {
+  // W8^0, W8^1 = h (1 + D j), W8^2 = D j, W8^3 = h (-1 + D j)
+  const float2 p1 = mul_1pj<DIR>(u[1]), p3 = mul_m1pj<DIR>(u[3]);
+  const float2 t2 = mul_j<DIR>(u[2]);
+  const float2 a0 = cadd(u[0], t2), a1 = csub(u[0], t2);
+  const float2 q2 = cadd(p1, p3), q3 = mul_j<DIR>(csub(p1, p3));
+  o[0] = cfma(kSqrtHalf, q2, a0);
+  o[2] = cfma(-kSqrtHalf, q2, a0);
+  o[1] = cfma(kSqrtHalf, q3, a1);
+  o[3] = cfma(-kSqrtHalf, q3, a1);
+}
+
+template <int DIR>
+struct Dft<8, DIR> {
+  static __device__ __forceinline__ void run(float2* v) {
+    // n = 4 n1 + n2, k = k1 + 2 k2
+    float2 e[4], d[4];
+#pragma unroll
+    for (int n2 = 0; n2 < 4; ++n2) {
+      e[n2] = cadd(v[n2], v[4 + n2]);
+      d[n2] = csub(v[n2], v[4 + n2]);
+    }
+    Dft<4, DIR>::run(e);
+    float2 o[4];
+    dft8_odd<DIR>(d, o);
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      v[2 * k2] = e[k2];
+      v[1 + 2 * k2] = o[k2];
+    }
+  }
+};
+
+template <int DIR>
+struct Dft<16, DIR> {
+  static __device__ __forceinline__ void run(float2* v) {
+    // n = 4 n1 + n2, k = k1 + 4 k2; U[k1][n2] = DFT4 over n1 of v[4 n1 + n2]
+    float2 U[4][4];
+#pragma unroll
+    for (int n2 = 0; n2 < 4; ++n2) {
+      float2 u[4] = {v[n2], v[4 + n2], v[8 + n2], v[12 + n2]};
+      Dft<4, DIR>::run(u);
+#pragma unroll
+      for (int k1 = 0; k1 < 4; ++k1) U[k1][n2] = u[k1];
+    }
+    // k1 = 0: no rotations
+    Dft<4, DIR>::run(U[0]);
+    group_fence();
+    // k1 = 2: W16^{0,2,4,6} = 1, h(1 + D j), D j, h(-1 + D j)
+    float2 o2[4];
+    dft8_odd<DIR>(U[2], o2);
+    group_fence();
+    // k1 = 1: W16^{0,1,2,3} = 1, c (1 + D j tau), h (1 + D j), c (D j)(1 - D j tau)
+    float2 o1[4], o3[4];
+    {
+      const float2* u = U[1];
+      const float2 p2 = mul_1pj<DIR>(u[2]);
+      const float2 y1 = mul_1ptau<DIR>(u[1]), y3 = mul_1ptau<-DIR>(u[3]);
+      const float2 a0 = cfma(kSqrtHalf, p2, u[0]), a1 = cfma(-kSqrtHalf, p2, u[0]);
+      const float2 s2 = cadd(y1, mul_j<DIR>(y3));
+      const float2 d3 = mul_j<DIR>(csub(y1, mul_j<DIR>(y3)));
+      o1[0] = cfma(kCosPi8, s2, a0);
+      o1[2] = cfma(-kCosPi8, s2, a0);
+      o1[1] = cfma(kCosPi8, d3, a1);
+      o1[3] = cfma(-kCosPi8, d3, a1);
+    }
+    group_fence();
+    // k1 = 3: W16^{0,3,6,9} = 1, c (D j)(1 - D j tau), h (-1 + D j), -c (1 + D j tau)
+    {
+      const float2* u = U[3];
+      const float2 p2 = mul_m1pj<DIR>(u[2]);
+      const float2 y1 = mul_1ptau<-DIR>(u[1]), y3 = mul_1ptau<DIR>(u[3]);
+      const float2 a0 = cfma(kSqrtHalf, p2, u[0]), a1 = cfma(-kSqrtHalf, p2, u[0]);
+      const float2 jy1 = mul_j<DIR>(y1);
+      const float2 s2 = csub(jy1, y3);
+      const float2 d3 = mul_j<DIR>(cadd(jy1, y3));
+      o3[0] = cfma(kCosPi8, s2, a0);
+      o3[2] = cfma(-kCosPi8, s2, a0);
+      o3[1] = cfma(kCosPi8, d3, a1);
+      o3[3] = cfma(-kCosPi8, d3, a1);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      v[0 + 4 * k2] = U[0][k2];
+      v[1 + 4 * k2] = o1[k2];
+      v[2 + 4 * k2] = o2[k2];
+      v[3 + 4 * k2] = o3[k2];
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------- pass machinery
 template <int... Rs>
 struct IntList {};
@@ -274,20 +404,47 @@ struct ListInfo<IntList<R, R2, Rs...>> {
   static constexpr int product = R * ListInfo<IntList<R2, Rs...>>::product;
 };
 
-// One pad element after every 16 keeps the strided Stockham writes off a single LDS bank.
-__device__ __forceinline__ int lpad(int i) { return i + (i >> 4); }
+// Exchange layout in LDS.  Measured on gfx950 (SQ_LDS_BANK_CONFLICT on single-pattern
+// kernels): 8-byte LDS reads are served 32 lanes at a time over 64 four-byte banks, 8-byte writes
+// 16 lanes at a time over 32 banks.  The exchange after a pass whose earlier radices multiply to
+// NS writes element (j/NS) NS R + j%NS + r NS and the next pass reads j + r N/R2; both are
+// stored at i + P floor(i/Q) (P pad elements after every Q), with (P, Q) chosen per line length
+// and exchange.  The default, one pad after every 16, keeps the stride-R writes of the first
+// exchange on distinct banks (its contiguous reads then meet one two-way conflict per half-wave,
+// which no block padding avoids); an exchange whose writes are already contiguous runs of 16
+// needs no padding at all (P = 0).  The choices were found by enumerating (P, Q) against that
+// bank model.
+template <int N, int NS>
+struct XPad {
+  static constexpr int P = 1, Q = 16;
+};
+template <> struct XPad<1024, 16> { static constexpr int P = 0, Q = 1024; };
+template <> struct XPad<2048, 16> { static constexpr int P = 0, Q = 2048; };
+template <> struct XPad<4096, 16> { static constexpr int P = 0, Q = 4096; };
+
+template <int N, int NS>
+__device__ __forceinline__ int xpad(int i) {
+  using X = XPad<N, NS>;
+  return i + X::P * (i / X::Q);
+}
+// LDS elements of a line buffer: the unpadded length plus at most one pad per 16 elements
+// (every XPad choice must stay within this; checked where it is used).
 constexpr int lds_len(int n) { return n + n / 16 + 1; }
-// lpad(base + r * STRIDE) written so that, for the strides that occur, it is one per-thread
+// xpad(base + r * STRIDE) written so that, for the strides that occur, it is one per-thread
 // base plus a compile-time offset (an LDS instruction's immediate), not a fresh shift-and-add
-// per element.  Exact when STRIDE % 16 == 0, or when base % 16 + r * STRIDE < 16.
-template <int STRIDE, bool BASE_ALIGNED16_R_FITS>
-__device__ __forceinline__ int lpad_step(int padded_base, int base, int r) {
-  if constexpr (STRIDE % 16 == 0) {
-    return padded_base + r * (STRIDE + STRIDE / 16);
-  } else if constexpr (BASE_ALIGNED16_R_FITS) {
+// per element.  Exact when STRIDE % Q == 0, or when base % Q + r * STRIDE < Q (FITS).
+template <int N, int NS, int STRIDE, bool FITS>
+__device__ __forceinline__ int xpad_step(int padded_base, int base, int r) {
+  using X = XPad<N, NS>;
+  static_assert(X::P * ((N - 1) / X::Q) <= N / 16, "exchange padding exceeds the line buffer");
+  if constexpr (X::P == 0) {
+    return padded_base + r * STRIDE;
+  } else if constexpr (STRIDE % X::Q == 0) {
+    return padded_base + r * (STRIDE + STRIDE / X::Q * X::P);
+  } else if constexpr (FITS) {
     return padded_base + r * STRIDE;
   } else {
-    return lpad(base + r * STRIDE);
+    return xpad<N, NS>(base + r * STRIDE);
   }
 }
 
@@ -370,18 +527,19 @@ __device__ __forceinline__ void store_line(const float2* v, const LineIO& io, in
   }
 }
 
-template <int N, int T, int R>
+// Reads of the pass after the exchange keyed NS (the product of the radices before it).
+template <int N, int T, int R, int NS>
 __device__ __forceinline__ void load_lds(float2* v, const float2* lds, int tid) {
   using G = Geom<N, T, R>;
 #pragma unroll
   for (int b = 0; b < G::B; ++b) {
     const int j = tid + b * T;
     if (G::live(j)) {
-      const int pj = lpad(j);
+      const int pj = xpad<N, NS>(j);
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int r = dft_input_order<R>(i);
-        v[b * R + r] = lds[lpad_step<G::NB, false>(pj, j, r)];
+        v[b * R + r] = lds[xpad_step<N, NS, G::NB, false>(pj, j, r)];
       }
     }
   }
@@ -395,11 +553,11 @@ __device__ __forceinline__ void store_lds(const float2* v, float2* lds, int tid)
     const int j = tid + b * T;
     if (G::live(j)) {
       const int base = (j / NS) * (NS * R) + (j % NS);
-      const int pb = lpad(base);
-      // first pass of a radix-16 (or smaller power-of-two) line: base = 16-aligned multiple of R
-      constexpr bool fits = NS == 1 && (16 % R == 0);
+      const int pb = xpad<N, NS>(base);
+      // a pad period that is a multiple of NS R keeps a thread's R outputs inside one period
+      constexpr bool fits = XPad<N, NS>::Q % (NS * R) == 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) lds[lpad_step<NS, fits>(pb, base, r)] = v[b * R + r];
+      for (int r = 0; r < R; ++r) lds[xpad_step<N, NS, NS, fits>(pb, base, r)] = v[b * R + r];
     }
   }
 }
@@ -472,7 +630,7 @@ struct Passes<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
     exchange_sync<WAVE>();  // the line buffer may still be read by the previous exchange
     store_lds<N, T, R, NS>(v, lds, tid);
     exchange_sync<WAVE>();
-    load_lds<N, T, R2>(v, lds, tid);
+    load_lds<N, T, R2, NS>(v, lds, tid);
     Passes<N, T, DIR, NS * R, IntList<R2, Rs...>, WAVE>::run(v, lds, tw, tid);
   }
 };
@@ -653,7 +811,7 @@ struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
     exchange_sync<WAVE>();
     store_lds<N, T, R, NS>(v, lds, tid);
     exchange_sync<WAVE>();
-    load_lds<N, T, R2>(v, lds, tid);
+    load_lds<N, T, R2, NS>(v, lds, tid);
     PassesCached<N, T, DIR, NS * R, IntList<R2, Rs...>, WAVE>::run(v, lds, c.next, tid);
   }
 };
@@ -724,7 +882,7 @@ RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, 1, false, false)
-RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 1, false, false)
+RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 3, false, false)
 RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, true, false, 8192, 4, true, true)
 RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, true, false, 16384, 1, true, true)
 RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096, 1, false, false)

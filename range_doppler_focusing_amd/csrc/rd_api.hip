@@ -54,6 +54,7 @@ struct rd_plan {
   int A = 0, B = 0;     // Na = A B: strided and block steps of the azimuth transform
   float2* H = nullptr;       // [Nr] conj(FFT(h)) / Nr
   float2* tw_r = nullptr;    // [Nr] e^{-j 2 pi k / Nr}
+  float2* rc_tab = nullptr;  // per-thread constants of the range kernel (null if it has none)
   float2* tw_a = nullptr;    // [Na] e^{-j 2 pi k / Na} (line-transform test hook)
   float2* tw_A = nullptr;    // [A] e^{-j 2 pi k / A}
   float2* tw_B = nullptr;    // [B] e^{-j 2 pi k / B}
@@ -72,6 +73,7 @@ bool live_plan(const rd_plan* p) {
 void free_plan(rd_plan* p) {
   (void)hipFree(p->H);
   (void)hipFree(p->tw_r);
+  (void)hipFree(p->rc_tab);
   (void)hipFree(p->tw_a);
   (void)hipFree(p->tw_A);
   (void)hipFree(p->tw_B);
@@ -247,8 +249,8 @@ int persistent_grid(int occ, int cus, int64_t lines, int lpw) {
 // chained: the output feeds the azimuth chain (stored cacheable where the image fits the cache)
 rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, bool chained, hipStream_t s) {
   if (P->rc_variant == 1)
-    return check_hip(P->rops->range_compress_pf(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid,
-                                                chained ? P->cached : 0, s),
+    return check_hip(P->rops->range_compress_pf(in, out, P->H, P->tw_r, P->rc_tab, P->p.Na,
+                                                P->rc_grid, chained ? P->cached : 0, s),
                      "range compression launch");
   return check_hip(P->rops->range_compress(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid, s),
                    "range compression launch");
@@ -388,8 +390,16 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     free_plan(P);
     return s;
   };
-  if ((st = upload(&P->H, matched_filter(p, P->L), "matched filter")) != RD_OK) return bail(st);
-  if ((st = upload(&P->tw_r, roots_table(p.Nr), "range twiddles")) != RD_OK) return bail(st);
+  {
+    const std::vector<float2> Hh = matched_filter(p, P->L), roots = roots_table(p.Nr);
+    if ((st = upload(&P->H, Hh, "matched filter")) != RD_OK) return bail(st);
+    if ((st = upload(&P->tw_r, roots, "range twiddles")) != RD_OK) return bail(st);
+    if (const int n = rops->rc_tab_len(); n > 0) {
+      std::vector<float2> tab(static_cast<size_t>(n));
+      rops->rc_tab_fill(Hh.data(), roots.data(), tab.data());
+      if ((st = upload(&P->rc_tab, tab, "range kernel table")) != RD_OK) return bail(st);
+    }
+  }
   int occ_rc = 0, occ_fft = 0, occ_azc = 0;
   if (rops->occupancy(&occ_rc, &occ_fft, &occ_azc) != hipSuccess)
     return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));

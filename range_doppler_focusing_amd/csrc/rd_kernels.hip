@@ -135,6 +135,12 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * C::LDS;
+  const int64_t stride = int64_t(gridDim.x) * C::LPW;
+  // The first line's loads go out before the table loads, so the line's HBM latency overlaps
+  // the table reads instead of following them.
+  float2 nxt[C::P];
+  if constexpr (PF)
+    load_line<N, T, R0>(nxt, LineIO(in, N, int64_t(blockIdx.x) * C::LPW, C::LPW, lines), grp * N, tid);
   TC twc;
   twc.load_all(tw, lds + C::LPW * C::LDS, tid, threadIdx.x, C::WG);
   // (the first pass's barrier orders the LDS twiddle table before its first use, unless a line's
@@ -146,12 +152,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   // inside the loop would also wait for the previous line's stores on every iteration.
   if constexpr (C::HREG) touch<filter_regs<N>()>(h);
   twc.touch_all();
-  const int64_t stride = int64_t(gridDim.x) * C::LPW;
-  float2 nxt[C::P];
-  if constexpr (PF) {
-    load_line<N, T, R0>(nxt, LineIO(in, N, int64_t(blockIdx.x) * C::LPW, C::LPW, lines), grp * N, tid);
-    touch<C::P>(nxt);
-  }
+  if constexpr (PF) touch<C::P>(nxt);
   for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < lines; l0 += stride) {
     float2 v[C::P];
     if constexpr (PF) {
@@ -169,6 +170,139 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     // Wait for the prefetch here, where the stores just issued are younger than it and need not
     // complete; a wait at the loop head would merge with the loop entry and drain the stores.
     if constexpr (PF) touch<C::P>(nxt);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Range compression of 4096-sample lines with three barriers per line.  With n = t + 256 n2
+// (t = n0 + 16 n1 < 256) and k = k0 + 16 k1 + 256 k2, the forward transform runs in the
+// decimation-in-frequency order
+//   a: DFT16 over n2 -> k0, times W_4096^{t k0}            (thread t = n0 + 16 n1)
+//   b: DFT16 over n1 -> k1, times W_256^{n0 k1}             (thread 16 k0 + n0)
+//   c: DFT16 over n0 -> k2                                   (thread 16 k0 + k1)
+// and leaves X[k0 + 16 k1 + 256 k2] in thread 16 k0 + k1, which multiplies it by the filter
+// (held in that permuted order) and runs the inverse as the mirror image in
+// decimation-in-time order (c, b, a with conjugate roots, the twiddles before the DFTs), ending
+// with y[t + 256 n2] in thread t.  Steps b -> c and their mirror exchange data only inside a
+// group of 16 lanes (one wave), so they need no workgroup barrier; a -> b and its mirror are
+// workgroup exchanges.  Both directions use the same twiddles: W_4096^{t k0} in registers and
+// W_256^{n0 k1} in an LDS table.  LDS layout: region g = 0..15 of 272 elements (rows of 256 or
+// 16 x 17, padded so that two 16-lane groups of a half-wave fall on complementary banks):
+// every exchange is free of bank conflicts under the gfx950 geometry (8-byte reads: 32 lanes
+// over 64 banks; 8-byte writes: 16 lanes over 32 banks).
+// The filter in the order the threads hold it, so that every wave reads it with contiguous
+// accesses: tab[r 256 + t] = H[g + 16 l + 256 r] (g = t / 16, l = t % 16, r = 0..15).  The
+// twiddles are evaluated in the kernel from exactly reduced arguments instead of being read
+// from a table (start-up table reads by every workgroup at once were measured to cost 2-9 us per
+// launch, most of it for strided reads).
+constexpr int kRc4096Tab = 16 * 256;
+void rc4096_tab_fill(const float2* H, const float2*, float2* out) {
+  for (int r = 0; r < 16; ++r)
+    for (int t = 0; t < 256; ++t) out[r * 256 + t] = H[(t >> 4) + 16 * (t & 15) + 256 * r];
+}
+
+// W_n^e = e^{-j 2 pi e / n} for 0 <= e < n, n a power of two (the argument e / (n/2) is exact)
+template <int n>
+__device__ __forceinline__ float2 root_pow2(int e) {
+  float sn, cs;
+  sincospif(float(e) * (2.0f / float(n)), &sn, &cs);
+  return make_float2(cs, -sn);
+}
+
+template <int SAUX>
+__global__ void __launch_bounds__(256, 3)
+    k_range_compress_4096(const float2* in, float2* out, const float2* __restrict__ tab,
+                          int64_t lines) {
+  constexpr int N = 4096, T = 256, REG = 272;
+  __shared__ float2 lds[16 * REG + 15 * 16];
+  float2* tw2 = lds + 16 * REG;  // W_256^{n0 k}: tw2[(k - 1) 16 + n0], k = 1..15
+  const int t = threadIdx.x;
+  const int g = t >> 4, l = t & 15;
+  const int64_t stride = gridDim.x;
+  // The first line's loads go out before the table loads, so the line's HBM latency overlaps
+  // the table reads instead of following them.
+  float2 nxt[16];
+  load_line<N, T, 16>(nxt, LineIO(in, N, blockIdx.x, 1, lines), 0, t);
+  // The filter is first used at the first line's multiply, so the wait for it lands there (in
+  // later lines that wait also covers the previous line's stores, which are complete by then).
+  float2 h[16];   // H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) h[r] = tab[r * 256 + t];
+  if (t < 240) tw2[t] = root_pow2<256>(((t & 15) * (t / 16 + 1)) & 255);
+  float2 w1[15];  // W_4096^{t k}, k = 1..15
+#pragma unroll
+  for (int k = 1; k < 16; ++k) w1[k - 1] = root_pow2<4096>((t * k) & 4095);
+  __syncthreads();
+  for (int64_t line = blockIdx.x; line < lines; line += stride) {
+    float2 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = nxt[i];
+    load_line<N, T, 16>(nxt, LineIO(in, N, line + stride, 1, lines), 0, t);
+    // ---- forward
+    Dft<16, -1>::run(v);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
+    __syncthreads();  // the previous line's last exchange has been read
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lds[REG * k + t] = v[k];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int n1 = dft_input_order<16>(i);
+      v[n1] = lds[REG * g + l + 16 * n1];
+    }
+    Dft<16, -1>::run(v);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], tw2[(k - 1) * 16 + l]);
+    exchange_sync<true>();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lds[REG * g + 17 * k + l] = v[k];
+    exchange_sync<true>();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int n0 = dft_input_order<16>(i);
+      v[n0] = lds[REG * g + 17 * l + n0];
+    }
+    Dft<16, -1>::run(v);
+    // ---- filter (carries 1/N)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = cmul(v[r], h[r]);
+    // ---- inverse
+    Dft<16, +1>::run(v);
+    exchange_sync<true>();
+#pragma unroll
+    for (int n0 = 0; n0 < 16; ++n0) lds[REG * g + 17 * l + n0] = v[n0];
+    exchange_sync<true>();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = dft_input_order<16>(i);
+      v[k] = lds[REG * g + 17 * k + l];
+    }
+#pragma unroll
+    for (int k = 1; k < 16; ++k) {
+      float2 w = tw2[(k - 1) * 16 + l];
+      w.y = -w.y;
+      v[k] = cmul(v[k], w);
+    }
+    Dft<16, +1>::run(v);
+    exchange_sync<true>();
+#pragma unroll
+    for (int n1 = 0; n1 < 16; ++n1) lds[REG * g + l + 16 * n1] = v[n1];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = dft_input_order<16>(i);
+      v[k] = lds[REG * k + t];
+    }
+#pragma unroll
+    for (int k = 1; k < 16; ++k) {
+      float2 w = w1[k - 1];
+      w.y = -w.y;
+      v[k] = cmul(v[k], w);
+    }
+    Dft<16, +1>::run(v);
+    store_line<N, T, 16, SAUX>(v, LineIO(out, N, line, 1, lines), 0, t);
+    touch<16>(nxt);
   }
 }
 
@@ -466,10 +600,20 @@ hipError_t occupancy(int* rc, int* fft, int* azc) {
 #ifndef RD_RC_PREFETCH
 #define RD_RC_PREFETCH true
 #endif
+#ifndef RD_RC_4096
+#define RD_RC_4096 1
+#endif
 template <int N>
 hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const float2* tw,
-                        int64_t lines, int grid, int cached, hipStream_t s) {
+                        const float2* tab, int64_t lines, int grid, int cached, hipStream_t s) {
   constexpr bool PF = RD_RC_PREFETCH && LineCfg<N>::PF;
+  if constexpr (N == 4096 && RD_RC_4096) {
+    if (cached)
+      hipLaunchKernelGGL(k_range_compress_4096<kAuxCached>, dim3(grid), dim3(256), 0, s, in, out, tab, lines);
+    else
+      hipLaunchKernelGGL(k_range_compress_4096<kAuxStream>, dim3(grid), dim3(256), 0, s, in, out, tab, lines);
+    return hipGetLastError();
+  }
   if (cached)
     hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxCached>), dim3(grid), dim3(LineCfg<N>::WG),
                        0, s, in, out, H, tw, lines);
@@ -481,6 +625,8 @@ hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const fl
 
 template <int N>
 hipError_t occupancy_pf(int* rc) {
+  if constexpr (N == 4096 && RD_RC_4096)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_4096<kAuxStream>, 256, 0);
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream>,
                                                       LineCfg<N>::WG, 0);
 }
@@ -498,15 +644,26 @@ hipError_t launch_rcmc_mf(const float2* in, float2* out, const AzRowConst& c, in
 }
 
 template <int N>
+int rc_tab_len() {
+  if constexpr (N == 4096 && RD_RC_4096) return kRc4096Tab;
+  return 0;
+}
+template <int N>
+void rc_tab_fill(const float2* H, const float2* roots, float2* out) {
+  if constexpr (N == 4096 && RD_RC_4096) rc4096_tab_fill(H, roots, out);
+}
+
+template <int N>
 constexpr LineOps make_ops() {
   constexpr bool sym = std::is_same<typename LineCfg<N>::Fwd, typename LineCfg<N>::Inv>::value;
   if constexpr (sym) {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
-                   &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>, &launch_rcmc_mf<N>,
-                   RowStage<N>::MARGIN};
+                   &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>, &rc_tab_len<N>,
+                   &rc_tab_fill<N>, &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
   } else {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
-                   &occupancy<N>, nullptr, nullptr, &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
+                   &occupancy<N>, nullptr, nullptr, &rc_tab_len<N>, &rc_tab_fill<N>,
+                   &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
   }
 }
 

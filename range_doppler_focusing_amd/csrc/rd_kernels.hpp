@@ -45,9 +45,15 @@ struct LineOps {
   // (cached: ordinary stores, for output that the next pass re-reads from the cache; else
   // non-temporal stores)
   hipError_t (*range_compress_pf)(const float2* in, float2* out, const float2* H,
-                                  const float2* tw, int64_t lines, int grid, int cached,
-                                  hipStream_t s);
+                                  const float2* tw, const float2* tab, int64_t lines, int grid,
+                                  int cached, hipStream_t s);
   hipError_t (*occupancy_pf)(int* rc);
+  // Per-thread constant table of the register-cached kernel (twiddles and filter in the order
+  // each thread holds them, so that a workgroup loads it with contiguous wave accesses):
+  // element count (0: the kernel reads H and tw directly) and host-side fill from the
+  // natural-order filter H[n] and roots e^{-j 2 pi k / n} (a permutation, no arithmetic).
+  int (*rc_tab_len)();
+  void (*rc_tab_fill)(const float2* H, const float2* roots, float2* out);
   // RCMC + azimuth filter over rows of this length (in == out allowed; grid 0 = one workgroup
   // per staged chunk); margin = samples staged after a chunk, so the largest shift the kernel
   // accepts is margin - 5
