@@ -59,7 +59,21 @@ def read_traffic(path: str, src_hash: str):
         return None
 
 
+SETTLE_S = 0.3
+
+
 def time_steps(torch, fn, steps: int, warmup: int, stream):
+    """ms per step over exactly `steps` calls, after `warmup` untimed calls.  Before those, the
+    step runs for SETTLE_S seconds (untimed, in long batches): the GPU's clocks ramp up over the
+    first few milliseconds of sustained load, and a timed region that starts from an idle GPU
+    measures the ramp rather than the kernels."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(64):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -138,10 +152,13 @@ def vendor_fft_comparison(torch, rdf, cfg, stream, steps, warmup):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed running before each warm-up (0 for counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
     ap.add_argument("--only", choices=["rc", "focus", "large", "vendor"], default=None,
@@ -149,6 +166,7 @@ def main():
     ap.add_argument("--no-large", action="store_true",
                     help="skip the 8192 x 6000 and 16384 x 16384 workloads")
     args = ap.parse_args()
+    SETTLE_S = args.settle
     if args.gpus != 1:
         print(f"bench.py: the focusing path runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is a design note, not implemented)", file=sys.stderr)
@@ -275,7 +293,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(rc_gbs / HBM_PEAK_GBS, 4) if rc_gbs else None,
                      "traffic": traffic,
-                     "kernel": "k_range_compress_pf<4096>",
+                     "kernel": "k_range_compress_4096",
                      "algorithmic_bytes_per_launch": rc_bytes},
         "cpu_baseline": cpu,
         "rd_focus": None if not focus_ms else {

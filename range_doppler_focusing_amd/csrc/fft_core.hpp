@@ -635,6 +635,28 @@ struct Passes<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
   }
 };
 
+// ---------------------------------------------------------------------------- exact roots
+// W_N^m = e^{-j 2 pi m / N} (m >= 0) evaluated on the device.  The index is reduced to its
+// quadrant in integer arithmetic, so the float32 argument 2 r / N of sincospi is below 1/2 and
+// rounded once (exact for N a power of two); the quadrant turn is a sign/swap.  Used for
+// twiddle sets that a workgroup builds once: reading them from a global table with strided
+// lane addresses (every workgroup at once) was measured to cost microseconds per launch.
+template <int N>
+__device__ __forceinline__ float2 root_of(int m) {
+  static_assert(N % 4 == 0, "quadrant reduction needs N divisible by 4");
+  m %= N;
+  const int q = (4 * m) / N;
+  const int r = m - q * (N / 4);
+  float sn, cs;
+  sincospif(float(2 * r) / float(N), &sn, &cs);
+  switch (q) {  // (cs - j sn) (-j)^q
+    case 0: return make_float2(cs, -sn);
+    case 1: return make_float2(-sn, -cs);
+    case 2: return make_float2(-cs, sn);
+    default: return make_float2(sn, cs);
+  }
+}
+
 // ---------------------------------------------------------------------------- register-cached twiddles
 // The inter-pass twiddles of a whole transform, loaded once into registers.  A persistent
 // workgroup that transforms many lines then issues no table loads inside its line loop, so the
@@ -690,7 +712,7 @@ struct TwCacheBase {
     if constexpr (IN_LDS) {
       for (int i = wg_tid; i < NS * (R - 1); i += wg_size) {
         const int r = i / NS + 1, m = i % NS;     // entry (r, m) = W_N^{m STEP r}
-        tw_lds[i] = tw[m * STEP * r];
+        tw_lds[i] = root_of<N>(m * STEP * r);
       }
       lw = tw_lds;
     } else if constexpr (DERIVE) {
@@ -700,7 +722,7 @@ struct TwCacheBase {
         const int e = (j % NS) * STEP;
 #pragma unroll
         for (int i = 0; i < KB; ++i)
-          w[b * KB + i] = G::live(j) ? tw[e << i] : make_float2(1.f, 0.f);
+          w[b * KB + i] = G::live(j) ? root_of<N>(e << i) : make_float2(1.f, 0.f);
       }
     } else if constexpr (NS > 1) {
 #pragma unroll
@@ -709,7 +731,7 @@ struct TwCacheBase {
         const int e = (j % NS) * STEP;
 #pragma unroll
         for (int r = 1; r < R; ++r)
-          w[b * (R - 1) + r - 1] = G::live(j) ? tw[e * r] : make_float2(1.f, 0.f);
+          w[b * (R - 1) + r - 1] = G::live(j) ? root_of<N>(e * r) : make_float2(1.f, 0.f);
       }
     }
   }

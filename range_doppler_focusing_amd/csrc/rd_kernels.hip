@@ -201,14 +201,6 @@ void rc4096_tab_fill(const float2* H, const float2*, float2* out) {
     for (int t = 0; t < 256; ++t) out[r * 256 + t] = H[(t >> 4) + 16 * (t & 15) + 256 * r];
 }
 
-// W_n^e = e^{-j 2 pi e / n} for 0 <= e < n, n a power of two (the argument e / (n/2) is exact)
-template <int n>
-__device__ __forceinline__ float2 root_pow2(int e) {
-  float sn, cs;
-  sincospif(float(e) * (2.0f / float(n)), &sn, &cs);
-  return make_float2(cs, -sn);
-}
-
 template <int SAUX>
 __global__ void __launch_bounds__(256, 3)
     k_range_compress_4096(const float2* in, float2* out, const float2* __restrict__ tab,
@@ -228,10 +220,10 @@ __global__ void __launch_bounds__(256, 3)
   float2 h[16];   // H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l)
 #pragma unroll
   for (int r = 0; r < 16; ++r) h[r] = tab[r * 256 + t];
-  if (t < 240) tw2[t] = root_pow2<256>(((t & 15) * (t / 16 + 1)) & 255);
+  if (t < 240) tw2[t] = root_of<256>(((t & 15) * (t / 16 + 1)) & 255);
   float2 w1[15];  // W_4096^{t k}, k = 1..15
 #pragma unroll
-  for (int k = 1; k < 16; ++k) w1[k - 1] = root_pow2<4096>((t * k) & 4095);
+  for (int k = 1; k < 16; ++k) w1[k - 1] = root_of<4096>((t * k) & 4095);
   __syncthreads();
   for (int64_t line = blockIdx.x; line < lines; line += stride) {
     float2 v[16];
