@@ -161,7 +161,7 @@ def main():
                     help="seconds of untimed running before each warm-up (0 for counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
-    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor"], default=None,
+    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn"], default=None,
                     help="run one workload only (for profiling)")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the 8192 x 6000 and 16384 x 16384 workloads")
@@ -266,6 +266,23 @@ def main():
                 rec.update({"value": round(m, 1), "unit": "Mpixel/s",
                             "roofline_frac_80B_per_px": round(m * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4)})
             large.append(rec)
+
+    # ---------------------------------------------------------------- corner turn
+    if (args.only in (None, "large", "turn")) and not args.no_large:
+        large = large or []
+        for rows, cols in ((4096, 4096), (16384, 16384)):
+            nrot = ROTATE if rows * cols <= 4096 * 4096 else 1
+            xs = [gpu_noise(torch, (rows, cols), 11 + i) for i in range(nrot)]
+            ys = [torch.empty((cols, rows), dtype=torch.complex64, device="cuda") for _ in range(nrot)]
+            ms = time_steps(torch, lambda i: rdf.rd_corner_turn(xs[i % nrot], ys[i % nrot], rows, cols, stream),
+                            50 if nrot > 1 else 10, 2, stream)
+            gbs = 2 * rows * cols * 8 / (ms * 1e-3) / 1e9
+            large.append({"workload": f"corner turn (rd_corner_turn), {rows} x {cols} complex64",
+                          "ms_per_step": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
+                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                          "data": "seeded complex Gaussian noise on the device"})
+            del xs, ys
+            torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- vendor FFT comparison
     vendor = None

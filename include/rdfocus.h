@@ -137,6 +137,16 @@ rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft
 rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const rd_c64* in,
                             rd_c64* out, int64_t lines, void* stream);
 
+/* Corner turn (cf-1.com/news/2323550 §5.1-§5.2: the transposes between range lines and azimuth
+ * lines; nxmr.cn/news/101525 §2.2.1: padded shared-memory tiles):  out[c][r] = in[r][c] for a
+ * row-major complex array in[rows][cols] (for example [Na][Nr] -> [Nr][Na]); out is [cols][rows].
+ * Device pointers, 8-byte aligned, owned by the caller; the two buffers must not overlap (out of
+ * place only).  rows = 0 or cols = 0 is a no-op.  RD_ERR_INVALID_ARG for negative sizes,
+ * rows > 65535 * 64, rows * cols > 2^40, or bad or overlapping pointers.  No plan is needed:
+ * the work runs on the current device.  rd_focus does not use it (its azimuth transforms run
+ * in place on [Na][Nr]); it serves callers that want the azimuth-major layout. */
+rd_status rd_corner_turn(const rd_c64* in, rd_c64* out, int64_t rows, int64_t cols, void* stream);
+
 /* Static description of a status code. */
 const char* rd_status_string(rd_status status);
 

@@ -98,6 +98,13 @@ def range_compress(echo: np.ndarray, params) -> np.ndarray:
 # by sinc interpolation, multiply by the azimuth matched filter, azimuth IFFT.  [SAR-GPU] §2.2:
 # RCMC looks up each output at the migrated slant range of a hyperbolic history and interpolates.
 # ----------------------------------------------------------------------------------------------
+def corner_turn(x: np.ndarray) -> np.ndarray:
+    """[M1-RD] §5.1-§5.2 and [SAR-GPU] §2.2.1: the corner turn between range lines and azimuth
+    lines, out[c][r] = x[r][c] for a [rows][cols] array (a plain transpose, returned
+    contiguous).  A data move: exact, no arithmetic."""
+    return np.ascontiguousarray(np.asarray(x).T)
+
+
 def azimuth_fft(rc: np.ndarray) -> np.ndarray:
     """S[k][n] = sum_m rc[m][n] e^{-j 2 pi k m / Na}: forward DFT down every range bin."""
     return np.fft.fft(rc, axis=0)

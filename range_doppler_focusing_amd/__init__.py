@@ -8,7 +8,7 @@ with the C names (``rd_plan_create``, ``rd_range_compress``, ...) are re-exporte
 from __future__ import annotations
 
 from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
-                      make_params, rd_azimuth_focus, rd_debug_azimuth_stages, rd_debug_line_fft,
+                      make_params, rd_azimuth_focus, rd_corner_turn, rd_debug_azimuth_stages, rd_debug_line_fft,
                       rd_focus, rd_last_error, rd_length_supported, rd_params, rd_plan_create,
                       rd_plan_destroy, rd_range_compress, rd_status_string)
 
@@ -92,3 +92,18 @@ class Plan:
         out = self._empty(tuple(x.shape)) if out is None else self._check(out, tuple(x.shape))
         rd_debug_line_fft(self.handle, axis, int(inverse), x, out, lines)
         return out
+
+
+def corner_turn(x, out=None):
+    """out[c][r] = x[r][c] for a contiguous complex64 [rows][cols] tensor on the GPU (rd_corner_turn);
+    returns the [cols][rows] result."""
+    import torch
+    if x.dtype != torch.complex64 or x.dim() != 2 or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("expected a contiguous 2-D complex64 tensor on the GPU")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=torch.complex64, device=x.device)
+    elif out.dtype != torch.complex64 or tuple(out.shape) != (cols, rows) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous complex64 tensor of shape {(cols, rows)}")
+    rd_corner_turn(x, out, rows, cols)
+    return out

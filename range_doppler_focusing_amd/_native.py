@@ -26,7 +26,7 @@ RD_WINDOW_HAMMING = 1
 # every symbol the header declares
 EXPORTS = ("rd_length_supported", "rd_plan_create", "rd_plan_destroy", "rd_range_compress",
            "rd_azimuth_focus", "rd_focus", "rd_debug_azimuth_stages", "rd_debug_line_fft",
-           "rd_status_string", "rd_last_error")
+           "rd_corner_turn", "rd_status_string", "rd_last_error")
 
 
 class rd_params(ctypes.Structure):
@@ -80,6 +80,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rd_debug_azimuth_stages.restype = ctypes.c_int
     lib.rd_debug_line_fft.argtypes = [vp, i32, i32, vp, vp, i64, vp]
     lib.rd_debug_line_fft.restype = ctypes.c_int
+    lib.rd_corner_turn.argtypes = [vp, vp, i64, i64, vp]
+    lib.rd_corner_turn.restype = ctypes.c_int
     lib.rd_status_string.argtypes = [ctypes.c_int]
     lib.rd_status_string.restype = ctypes.c_char_p
     lib.rd_last_error.argtypes = []
@@ -170,6 +172,11 @@ def rd_debug_line_fft(plan: int, axis: int, inverse: int, x, y, lines: int, stre
     _check(load_library().rd_debug_line_fft(plan, int(axis), int(inverse), _addr(x), _addr(y),
                                             int(lines), _stream(stream, x, y)),
            "rd_debug_line_fft")
+
+
+def rd_corner_turn(x, y, rows: int, cols: int, stream=None) -> None:
+    _check(load_library().rd_corner_turn(_addr(x), _addr(y), int(rows), int(cols), _stream(stream, x, y)),
+           "rd_corner_turn")
 
 
 def rd_status_string(status: int) -> str:

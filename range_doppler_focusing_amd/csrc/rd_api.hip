@@ -582,4 +582,23 @@ rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const 
                    "line FFT launch");
 }
 
+rd_status rd_corner_turn(const rd_c64* in, rd_c64* out, int64_t rows, int64_t cols,
+                         void* stream) {
+  if (rows < 0 || cols < 0) return fail(RD_ERR_INVALID_ARG, "rows and cols must be >= 0");
+  if (rows == 0 || cols == 0) return RD_OK;
+  if (rows > int64_t(65535) * 64)
+    return fail(RD_ERR_INVALID_ARG, "rows=%lld exceeds the %d-row limit", (long long)rows, 65535 * 64);
+  if (cols > (int64_t(1) << 40) / rows)
+    return fail(RD_ERR_INVALID_ARG, "rows * cols exceeds 2^40 elements");
+  if (!aligned8(in) || !aligned8(out)) return fail(RD_ERR_INVALID_ARG, "in and out must be non-NULL and 8-byte aligned");
+  const size_t bytes = size_t(rows) * size_t(cols) * sizeof(rd_c64);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(out);
+  if (a < b + bytes && b < a + bytes) return fail(RD_ERR_INVALID_ARG, "in and out overlap (the corner turn is out of place)");
+  // arrays beyond the 256 MB Infinity Cache stream with the non-temporal hint
+  const int streaming = bytes > (size_t(160) << 20) ? 1 : 0;
+  return check_hip(rdf::launch_corner_turn(reinterpret_cast<const float2*>(in), reinterpret_cast<float2*>(out),
+                                           rows, cols, streaming, static_cast<hipStream_t>(stream)),
+                   "corner turn launch");
+}
+
 }  // extern "C"

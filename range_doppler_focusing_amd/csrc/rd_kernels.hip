@@ -548,6 +548,71 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
 }
 
 // ------------------------------------------------------------------------------------------
+// Corner turn out[c][r] = in[r][c] of a row-major [rows][cols] complex array (the transpose
+// between range lines and azimuth lines in cf-1.com/news/2323550 §5.1-§5.2 and the padded
+// shared-memory tiles of nxmr.cn/news/101525 §2.2.1).  A workgroup moves one 64 x 64 tile:
+// each wave reads whole 512-byte row segments of the input, the tile passes through LDS with a
+// row pitch of 65 elements, and each wave writes whole 512-byte row segments of the output.
+// Bank geometry of gfx950 (8-byte writes: 16 lanes over 32 banks; 8-byte reads: 32 lanes over
+// 64 banks): the tile writes are runs of consecutive elements and the transposed reads step by
+// 65 elements (an odd count), so neither meets a bank conflict.  Edges of ragged shapes are
+// masked.  Every element is read once and written once (16 bytes per element).
+constexpr int kTurnTile = 64, kTurnPitch = 65;
+typedef float rdf_v2f __attribute__((ext_vector_type(2)));
+
+template <int AUX>
+__global__ void __launch_bounds__(256)
+    k_corner_turn(const float2* __restrict__ in, float2* __restrict__ out, int64_t rows,
+                  int64_t cols) {
+  __shared__ float2 tile[kTurnTile * kTurnPitch];
+  const int64_t c0 = int64_t(blockIdx.x) * kTurnTile, r0 = int64_t(blockIdx.y) * kTurnTile;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  {
+    const int64_t c = c0 + lane;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int rr = w + 4 * k;
+      const int64_t r = r0 + rr;
+      float2 v = make_float2(0.f, 0.f);
+      if (r < rows && c < cols) {
+        const rdf_v2f* src = reinterpret_cast<const rdf_v2f*>(in + r * cols + c);
+        const rdf_v2f x = AUX ? __builtin_nontemporal_load(src) : *src;
+        v = make_float2(x.x, x.y);
+      }
+      tile[rr * kTurnPitch + lane] = v;
+    }
+  }
+  __syncthreads();
+  const int64_t r = r0 + lane;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int cc = w + 4 * k;
+    const int64_t c = c0 + cc;
+    if (c < cols && r < rows) {
+      rdf_v2f* dst = reinterpret_cast<rdf_v2f*>(out + c * rows + r);
+      const float2 t = tile[lane * kTurnPitch + cc];
+      const rdf_v2f v = {t.x, t.y};
+      if (AUX)
+        __builtin_nontemporal_store(v, dst);
+      else
+        *dst = v;
+    }
+  }
+}
+
+hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64_t cols,
+                              int streaming, hipStream_t s) {
+  const int64_t gx = (cols + kTurnTile - 1) / kTurnTile, gy = (rows + kTurnTile - 1) / kTurnTile;
+  if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
+  const dim3 grid{unsigned(gx), unsigned(gy), 1u};
+  if (streaming)
+    hipLaunchKernelGGL(k_corner_turn<1>, grid, dim3(256), 0, s, in, out, rows, cols);
+  else
+    hipLaunchKernelGGL(k_corner_turn<0>, grid, dim3(256), 0, s, in, out, rows, cols);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // Doppler-digit row order -> natural order (stage test hook only)
 __global__ void __launch_bounds__(256)
     k_row_unpermute(const float2* __restrict__ in, float2* __restrict__ out, int A, int B,

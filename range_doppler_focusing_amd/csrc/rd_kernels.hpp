@@ -78,6 +78,11 @@ struct ColStep {
 hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
                           int64_t cols, int na, int cached, hipStream_t s);
 
+// out[c][r] = in[r][c] for a row-major [rows][cols] array (streaming: non-temporal accesses);
+// hipErrorInvalidValue if the tile grid does not fit (rows > 65535 * 64)
+hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64_t cols,
+                              int streaming, hipStream_t s);
+
 // out[k] = in[(k % A) B + k / A] for rows of `cols` samples: Doppler-digit row order to natural
 hipError_t launch_row_unpermute(const float2* in, float2* out, int A, int B, int64_t cols,
                                 hipStream_t s);

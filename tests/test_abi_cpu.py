@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     import range_doppler_focusing_amd as rdf
     lib = rdf.load_library()
     declared = header_functions()
-    assert len(declared) == 10
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(rdf.EXPORTS) == declared
@@ -99,3 +99,19 @@ def test_null_arguments():
     assert lib.rd_range_compress(None, None, None, None) == -1
     assert lib.rd_focus(None, None, None, None) == -1
     assert "plan" in rdf.rd_last_error()
+
+
+def test_corner_turn_argument_errors_return_before_any_launch():
+    """Invalid sizes and pointers are rejected on the host; an empty turn is a no-op."""
+    import range_doppler_focusing_amd as rdf
+    lib = rdf.load_library()
+    a, b = 1 << 20, 1 << 30          # host-side stand-in addresses (never dereferenced)
+    assert lib.rd_corner_turn(a, b, 0, 7, None) == 0
+    assert lib.rd_corner_turn(a, b, 7, 0, None) == 0
+    assert lib.rd_corner_turn(a, b, -1, 7, None) == -1
+    assert lib.rd_corner_turn(a, b, 7, -1, None) == -1
+    assert lib.rd_corner_turn(0, b, 7, 7, None) == -1
+    assert lib.rd_corner_turn(a + 4, b, 7, 7, None) == -1
+    assert lib.rd_corner_turn(a, a + 8, 7, 7, None) == -1          # overlapping buffers
+    assert lib.rd_corner_turn(a, b, 65535 * 64 + 1, 1, None) == -1  # beyond the tile grid
+    assert "overlap" in lib.rd_last_error().decode() or "rows" in lib.rd_last_error().decode()

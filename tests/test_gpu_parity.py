@@ -257,6 +257,35 @@ def test_focus_large_sampled_range_bins(torch_dev, rdf):
         assert abs(a["pslr_db"] - b["pslr_db"]) <= 0.1 and abs(a["islr_db"] - b["islr_db"]) <= 0.1
 
 
+# ------------------------------------------------------------------------------ corner turn
+@pytest.mark.parametrize("rows,cols", [(256, 256), (4096, 4096), (37, 1000), (1, 5), (5, 1),
+                                       (65, 63), (8192, 6000), (64, 16384)])
+def test_corner_turn_bit_exact(torch_dev, rdf, rows, cols):
+    """rd_corner_turn equals the oracle's transpose bit for bit (full tiles, ragged edges, a
+    single row or column, and an array above the non-temporal threshold); two turns restore."""
+    torch = torch_dev
+    rng = np.random.default_rng(rows * 7919 + cols)
+    x = (rng.standard_normal((rows, cols)) + 1j * rng.standard_normal((rows, cols))).astype(np.complex64)
+    log(f"[corner turn] {rows} x {cols}")
+    xd = dev(torch, x)
+    y = rdf.corner_turn(xd)
+    z = rdf.corner_turn(y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), O.corner_turn(x))
+    assert torch.equal(z, xd)
+
+
+def test_corner_turn_of_range_compressed_scene(torch_dev, rdf):
+    """The azimuth-major layout of the 256 x 256 scene's range-compressed data: turned on the
+    GPU equals the oracle's range compression turned on the CPU, to the stage tolerance."""
+    torch = torch_dev
+    sc, ref = scene_and_stages(C1)
+    with rdf.Plan(**C1.plan_params()) as plan:
+        rc = plan.range_compress(dev(torch, sc.echo))
+        t = rdf.corner_turn(rc).cpu().numpy()
+    assert M.rel_l2(t, O.corner_turn(ref["rc"])) <= STAGE_TOL
+
+
 # ------------------------------------------------------------------------------ error paths
 def test_error_paths_on_device(torch_dev, rdf):
     torch = torch_dev

@@ -287,3 +287,16 @@ def test_metrics_ignore_a_linear_phase_ramp():
     for key in ("pslr_db", "islr_db", "irw"):
         assert abs(a[key] - b[key]) < 1e-6
     assert M.rel_l2(cut * 1.001, cut) == pytest.approx(1e-3, rel=1e-9)
+
+
+def test_corner_turn_is_the_element_by_element_transpose():
+    """out[c][r] = x[r][c] by a brute-force double loop on ragged shapes; two turns restore x."""
+    rng = np.random.default_rng(7)
+    for rows, cols in ((1, 1), (1, 5), (3, 2), (7, 13), (64, 65)):
+        x = (rng.standard_normal((rows, cols)) + 1j * rng.standard_normal((rows, cols))).astype(np.complex64)
+        y = O.corner_turn(x)
+        assert y.shape == (cols, rows) and y.flags["C_CONTIGUOUS"]
+        for r in range(rows):
+            for c in range(cols):
+                assert y[c, r] == x[r, c]
+        assert np.array_equal(O.corner_turn(y), x)
