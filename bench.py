@@ -87,17 +87,19 @@ def time_steps(torch, fn, steps: int, warmup: int, stream):
     return start.elapsed_time(end) / steps  # ms per step
 
 
-def cpu_oracle_rc(cfg, echo, runs: int = 3):
-    """The CPU oracle's range compression on the whole workload (NumPy fp64, one thread)."""
+def cpu_oracle_rc(cfg, echo, budget_s: float = 10.0):
+    """The CPU oracle's range compression of the whole workload (NumPy fp64, one thread),
+    repeated until about `budget_s` seconds of CPU work have run; returns (median s, runs)."""
     from oracle import rd_oracle as O
     p = cfg.plan_params()
     O.range_compress(echo[:64], p)
     ts = []
-    for _ in range(runs):
+    t_start = time.perf_counter()
+    while not ts or (time.perf_counter() - t_start < budget_s and len(ts) < 200):
         t0 = time.perf_counter()
         O.range_compress(echo, p)
         ts.append(time.perf_counter() - t0)
-    return statistics.median(ts)
+    return statistics.median(ts), len(ts)
 
 
 def cpu_oracle_focus(cfg, echo):
@@ -236,9 +238,10 @@ def main():
     cpu_focus = None
     if not args.no_cpu and args.only is None:
         cores = 1  # NumPy's FFT and the oracle's array code run on one thread
-        t = cpu_oracle_rc(cfg, cached_scene(cfg).echo)
+        t, runs = cpu_oracle_rc(cfg, cached_scene(cfg).echo)
         cpu = {"value": rc_bytes / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "sample": f"whole 4096x4096 range compression, median of 3 runs ({t:.2f} s each)"}
+               "sample": f"whole 4096x4096 range compression, median of {runs} runs "
+                         f"({t:.2f} s each, ~{t * runs:.0f} s of CPU work)"}
         if focus_ms:
             tf = cpu_oracle_focus(fcfg, cached_scene(fcfg).echo)
             cpu_focus = {"value": px / tf / 1e6, "unit": "Mpixel/s", "cores": cores, "kind": "oracle",
