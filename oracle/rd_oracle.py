@@ -240,3 +240,62 @@ def focus_columns(echo: np.ndarray, params, out_bins, block_rows: int = 1024):
     S = azimuth_fft(rc_cols)
     R = rcmc(S, shift, taps, _p(params, "kaiser_beta"), out_bins=out_bins, in_bins=in_bins, Nr=Nr)
     return azimuth_ifft(R * azimuth_matched_filter(params, out_bins)), out_bins
+
+
+# ----------------------------------------------------------------------------------------------
+# Back-projection: [BP-GPU] §1.1 (principle), §1.2 (cost), §2.2 (per-pixel range history, linear
+# interpolation on the range axis, phase compensation, coherent accumulation), §4.2 (carrier
+# wavelength in the phase).
+# Readings (the page works with 3-D platform positions and leaves the grid to the user): the
+# geometry is the slant plane of the focusing scenes -- a straight track along x with the
+# platform at x_m = V m / PRF at pulse m, a pixel at along-track position x and closest-approach
+# slant range r, so its range at pulse m is d = sqrt(r^2 + (x - x_m)^2); every pulse is summed
+# (the page visits all pulses); samples outside the range line count as zero; no normalisation.
+# ----------------------------------------------------------------------------------------------
+def bp_grid_axes(grid):
+    """Pixel coordinates of a back-projection grid: along-track positions x[i] = x0 + i dx
+    (i < nx) and closest-approach slant ranges r[j] = r0 + j dr (j < ny)."""
+    nx, ny = int(_p(grid, "nx")), int(_p(grid, "ny"))
+    x = _p(grid, "x0_m") + _p(grid, "dx_m") * np.arange(nx, dtype=np.float64)
+    r = _p(grid, "r0_m") + _p(grid, "dr_m") * np.arange(ny, dtype=np.float64)
+    return x, r
+
+
+def range_line_sample(line: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Linear interpolation of one range-compressed line at fractional bins b ([BP-GPU] §2.2);
+    bins outside [0, Nr) contribute zero."""
+    Nr = line.shape[0]
+    i0 = np.floor(b).astype(np.int64)
+    w = b - i0
+    def at(i):
+        ok = (i >= 0) & (i < Nr)
+        out = np.zeros(i.shape, np.complex128)
+        out[ok] = line[i[ok]]
+        return out
+    return (1.0 - w) * at(i0) + w * at(i0 + 1)
+
+
+def backproject(rc: np.ndarray, params, grid) -> np.ndarray:
+    """Back-projection image img[i][j] = sum_m s_m(d_m) exp(+j 4 pi d_m / lambda) with
+    d_m = sqrt(r_j^2 + (x_i - V m / PRF)^2) and s_m the linear interpolation of range line m at
+    bin (d_m - range_bin0) / dr ([BP-GPU] §1.1, §2.2, §4.2).  rc is [Na][Nr]; img is [nx][ny]."""
+    rc = np.asarray(rc, dtype=np.complex128)
+    Na = rc.shape[0]
+    V, prf = _p(params, "velocity_mps"), _p(params, "prf_hz")
+    lam, rb0, dr = wavelength(params), _p(params, "range_bin0_m"), range_spacing(params)
+    x, r = bp_grid_axes(grid)
+    img = np.zeros((x.size, r.size), np.complex128)
+    for m in range(Na):
+        d = np.sqrt(r[None, :] ** 2 + (x[:, None] - V * m / prf) ** 2)
+        img += range_line_sample(rc[m], (d - rb0) / dr) * np.exp(4j * math.pi * d / lam)
+    return img
+
+
+def backproject_pixels(rc: np.ndarray, params, grid, pix) -> np.ndarray:
+    """backproject() at selected pixels only: pix is a list of (i, j); returns their values."""
+    x, r = bp_grid_axes(grid)
+    sub = {"nx": 1, "ny": 1, "dx_m": 0.0, "dr_m": 0.0}
+    out = np.empty(len(pix), np.complex128)
+    for k, (i, j) in enumerate(pix):
+        out[k] = backproject(rc, params, dict(sub, x0_m=x[i], r0_m=r[j]))[0, 0]
+    return out

@@ -7,7 +7,9 @@ that the scene simulator's independent forward model produces, and invariants of
 A plausible mistake (dropped conjugate, wrong sign of a shift or of a phase, transposed axis,
 off-by-one tap window, missing normalisation) fails at least one of them.
 """
+import cmath
 import json
+import math
 import os
 
 import numpy as np
@@ -300,3 +302,105 @@ def test_corner_turn_is_the_element_by_element_transpose():
             for c in range(cols):
                 assert y[c, r] == x[r, c]
         assert np.array_equal(O.corner_turn(y), x)
+
+
+# ------------------------------------------------------------------------------ back-projection
+def _bp_brute(rc, params, grid):
+    """Pure-Python triple loop of the back-projection definition (tiny sizes only)."""
+    Na, Nr = rc.shape
+    V, prf, lam = params["velocity_mps"], params["prf_hz"], 299_792_458.0 / params["carrier_hz"]
+    dr = 299_792_458.0 / (2 * params["fs_hz"])
+    out = np.zeros((grid["nx"], grid["ny"]), complex)
+    for i in range(grid["nx"]):
+        x = grid["x0_m"] + i * grid["dx_m"]
+        for j in range(grid["ny"]):
+            r = grid["r0_m"] + j * grid["dr_m"]
+            acc = 0j
+            for m in range(Na):
+                d = math.hypot(r, x - V * m / prf)
+                b = (d - params["range_bin0_m"]) / dr
+                i0 = math.floor(b)
+                w = b - i0
+                s0 = complex(rc[m, i0]) if 0 <= i0 < Nr else 0j
+                s1 = complex(rc[m, i0 + 1]) if 0 <= i0 + 1 < Nr else 0j
+                acc += ((1 - w) * s0 + w * s1) * cmath.exp(4j * math.pi * d / lam)
+            out[i, j] = acc
+    return out
+
+
+def test_backprojection_matches_brute_force_loops():
+    """The vectorised oracle equals a pure-Python loop over pixels and pulses, including pixels
+    whose range history leaves the line (zero samples)."""
+    rng = np.random.default_rng(11)
+    params = C1.plan_params()
+    Na, Nr = 9, 40
+    params.update(Na=Na, Nr=Nr)
+    rc = rng.standard_normal((Na, Nr)) + 1j * rng.standard_normal((Na, Nr))
+    dr = O.range_spacing(params)
+    grid = dict(nx=3, ny=5, x0_m=-0.7, dx_m=0.9, r0_m=params["range_bin0_m"] - 2.3 * dr, dr_m=9.7 * dr)
+    got = O.backproject(rc, params, grid)
+    want = _bp_brute(rc, params, grid)
+    # the phases 4 pi d / lambda reach ~2e6 rad, whose float64 rounding is ~5e-10 rad per term
+    assert np.max(np.abs(got - want)) < 1e-8 * np.max(np.abs(want))
+    assert np.allclose(O.backproject_pixels(rc, params, grid, [(0, 0), (2, 4)]), want[[0, 2], [0, 4]], rtol=1e-8)
+
+
+def test_backprojection_outside_the_swath_is_zero():
+    rc = np.ones((8, 64), complex)
+    params = C1.plan_params()
+    params.update(Na=8, Nr=64)
+    grid = dict(nx=2, ny=2, x0_m=0.0, dx_m=1.0, r0_m=params["range_bin0_m"] + 1e4, dr_m=1.0)
+    assert np.all(O.backproject(rc, params, grid) == 0)
+
+
+def test_backprojection_of_a_lone_target_is_the_coherent_sum_of_its_peaks():
+    """Closed form: with negligible range migration, a unit target's range-compressed peak is L
+    (rect window) in every illuminated pulse and the carrier phase is compensated exactly, so
+    the target pixel sums to L * (illuminated pulses), real and positive."""
+    cfg = SceneConfig(name="bp_far", Na=128, Nr=256, pulse_s=1e-6, bandwidth_hz=100e6, fs_hz=120e6,
+                      window="rect", n_targets=1, noise_power=0.0, seed=21, carrier_hz=9.6e9,
+                      prf_hz=1000.0, velocity_mps=10.0, r_ref_m=2.0e5, sep_range=4, sep_az=0)
+    sc = make_scene(cfg, noise=False)
+    p = cfg.plan_params()
+    (mt, nt), = sc.targets
+    rc = O.range_compress(sc.echo, p)
+    assert cfg.rcm_max_samples < 1e-4
+    grid = dict(nx=1, ny=1, x0_m=cfg.velocity_mps * mt / cfg.prf_hz, dx_m=0.0,
+                r0_m=p["range_bin0_m"] + nt * O.range_spacing(p), dr_m=0.0)
+    v = O.backproject(rc, p, grid)[0, 0]
+    want = cfg.replica_len * cfg.aperture_pulses
+    assert abs(v - want) < 1e-3 * want          # float32 echo; migration < 1e-4 sample
+
+
+def test_backprojection_and_range_doppler_focus_targets_at_the_same_pixels(big):
+    """Two independent focusing methods of the oracle agree on where every noiseless target of a
+    large-migration scene (~15 samples of migration) focuses: back-projection on the focusing
+    grid (one pixel per pulse and per range bin) peaks at the pixel where the range-Doppler
+    image peaks, the predicted (m_t, n_t)."""
+    cfg = BIG
+    sc, ref = big
+    p = cfg.plan_params()
+    rc = ref["rc"]
+    dr = O.range_spacing(p)
+    for (mt, nt) in sc.targets:
+        assert M.peak_near(ref["img"], mt, nt) == (mt, nt)
+        grid = dict(nx=9, ny=9, x0_m=cfg.velocity_mps * (mt - 4) / cfg.prf_hz, dx_m=cfg.velocity_mps / cfg.prf_hz,
+                    r0_m=p["range_bin0_m"] + (nt - 4) * dr, dr_m=dr)
+        img = O.backproject(rc, p, grid)
+        assert np.unravel_index(np.argmax(np.abs(img)), img.shape) == (4, 4), (mt, nt)
+
+
+def test_backprojection_misfocuses_with_a_wrong_wavelength_or_velocity(big):
+    """Planted mistakes ([BP-GPU] §3.2 and §4.2's defocus causes: wrong platform speed, wrong
+    wavelength) collapse the target's coherent sum on the large-migration geometry."""
+    sc, ref = big
+    p = BIG.plan_params()
+    (mt, nt) = sc.targets[0]
+    grid = dict(nx=1, ny=1, x0_m=BIG.velocity_mps * mt / BIG.prf_hz, dx_m=0.0,
+                r0_m=p["range_bin0_m"] + nt * O.range_spacing(p), dr_m=0.0)
+    good = abs(O.backproject(ref["rc"], p, grid)[0, 0])
+    # most of L x (illuminated pulses) survives the interpolation across ~15 samples of migration
+    assert good > 0.75 * BIG.replica_len * BIG.aperture_pulses
+    for wrong in (dict(carrier_hz=0.95e9), dict(carrier_hz=1.05e9), dict(velocity_mps=190.0),
+                  dict(velocity_mps=210.0)):
+        assert abs(O.backproject(ref["rc"], dict(p, **wrong), grid)[0, 0]) < 0.2 * good, wrong
