@@ -163,7 +163,7 @@ def main():
                     help="seconds of untimed running before each warm-up (0 for counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
-    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn"], default=None,
+    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp"], default=None,
                     help="run one workload only (for profiling)")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the 8192 x 6000 and 16384 x 16384 workloads")
@@ -292,6 +292,30 @@ def main():
                           "data": "seeded complex Gaussian noise on the device"})
             del xs, ys
             torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- back-projection
+    if (args.only in (None, "large", "bp")) and not args.no_large:
+        large = large or []
+        bcfg = C3
+        bp = bcfg.plan_params()
+        dr = 299_792_458.0 / (2.0 * bp["fs_hz"])
+        nx = ny = 1024
+        grid = dict(nx=nx, ny=ny, x0_m=bcfg.velocity_mps * (bcfg.Na // 2 - nx // 2) / bcfg.prf_hz,
+                    dx_m=bcfg.velocity_mps / bcfg.prf_hz,
+                    r0_m=bp["range_bin0_m"] + (bcfg.Nr // 2 - ny // 2) * dr, dr_m=dr)
+        rc = gpu_noise(torch, (bcfg.Na, bcfg.Nr), 21)
+        img = torch.empty((nx, ny), dtype=torch.complex64, device="cuda")
+        bplan = rdf.Plan(**bp)
+        ms = time_steps(torch, lambda i: rdf.rd_backproject(bplan.handle, rc, img, grid, stream), 5, 1, stream)
+        bplan.close()
+        pp = bcfg.Na * nx * ny
+        large.append({"workload": f"back-projection (rd_backproject), {bcfg.Na} pulses x {bcfg.Nr} samples "
+                                  f"onto {nx} x {ny} pixels (4096 x 4096 airborne geometry)",
+                      "ms_per_step": round(ms, 4), "value": round(pp / (ms * 1e-3) / 1e9, 2),
+                      "unit": "Gpixel-pulses/s",
+                      "data": "seeded complex Gaussian noise on the device (timing is data-independent)"})
+        del rc, img
+        torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- vendor FFT comparison
     vendor = None

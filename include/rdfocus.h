@@ -137,6 +137,32 @@ rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft
 rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const rd_c64* in,
                             rd_c64* out, int64_t lines, void* stream);
 
+/* Back-projection image grid (framerc.cn/news/4459478 §3.2: the imaging grid and the
+ * observation geometry).  Slant-plane geometry of the focusing scenes: the platform flies a
+ * straight track along x and is at x = V m / PRF at pulse m; pixel (i, j) lies at along-track
+ * position x0_m + i dx_m and closest-approach slant range r0_m + j dr_m (metres). */
+typedef struct {
+  int32_t nx;    /* along-track pixels: rows of the image, >= 0                     */
+  int32_t ny;    /* slant-range pixels: columns of the image, >= 0                  */
+  double x0_m;   /* along-track position of row 0                                   */
+  double dx_m;   /* row spacing                                                     */
+  double r0_m;   /* closest-approach slant range of column 0 (> 0)                   */
+  double dr_m;   /* column spacing (every column's range must stay > 0)             */
+} rd_bp_grid;
+
+/* Back-projection of range-compressed data (framerc.cn/news/4459478 §1.1, §2.2, §4.2):
+ *   img[i][j] = sum_{m < Na} s_m(d) exp(+j 4 pi d / lambda),  d = sqrt(r_j^2 + (x_i - V m/PRF)^2),
+ * where s_m(d) is range line m of rc [Na][Nr] (the output of rd_range_compress) linearly
+ * interpolated at bin (d - range_bin0_m) / dr, samples outside the line taken as zero, and
+ * lambda = c / carrier_hz.  img is [nx][ny] complex (row-major), device memory owned by the
+ * caller; it must not overlap rc.  nx = 0 or ny = 0 is a no-op.  RD_ERR_NOT_CONFIGURED on a
+ * range-only plan; RD_ERR_INVALID_ARG for a NULL grid, negative sizes, nx > 262140, non-finite
+ * or non-positive ranges, bad or overlapping pointers.  Arithmetic: float32 per pulse (range
+ * excess without cancellation, hardware sin/cos), float64 per-pixel constants and accumulation
+ * over blocks of 32 pulses. */
+rd_status rd_backproject(rd_plan* plan, const rd_c64* rc, rd_c64* img, const rd_bp_grid* grid,
+                         void* stream);
+
 /* Corner turn (cf-1.com/news/2323550 §5.1-§5.2: the transposes between range lines and azimuth
  * lines; nxmr.cn/news/101525 §2.2.1: padded shared-memory tiles):  out[c][r] = in[r][c] for a
  * row-major complex array in[rows][cols] (for example [Na][Nr] -> [Nr][Na]); out is [cols][rows].

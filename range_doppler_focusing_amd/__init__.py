@@ -8,7 +8,8 @@ with the C names (``rd_plan_create``, ``rd_range_compress``, ...) are re-exporte
 from __future__ import annotations
 
 from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
-                      make_params, rd_azimuth_focus, rd_corner_turn, rd_debug_azimuth_stages, rd_debug_line_fft,
+                      make_bp_grid, make_params, rd_azimuth_focus, rd_backproject, rd_bp_grid,
+                      rd_corner_turn, rd_debug_azimuth_stages, rd_debug_line_fft,
                       rd_focus, rd_last_error, rd_length_supported, rd_params, rd_plan_create,
                       rd_plan_destroy, rd_range_compress, rd_status_string)
 
@@ -82,6 +83,14 @@ class Plan:
         img = self._empty((self.Na, self.Nr))
         rd_debug_azimuth_stages(self.handle, rc, az, rcmc, img)
         return az, rcmc, img
+
+    def backproject(self, rc, grid: dict, out=None):
+        """Back-projection image [nx][ny] of range-compressed data rc [Na][Nr] (rd_backproject)."""
+        self._check(rc, (self.Na, self.Nr))
+        shape = (int(grid["nx"]), int(grid["ny"]))
+        out = self._empty(shape) if out is None else self._check(out, shape)
+        rd_backproject(self.handle, rc, out, grid)
+        return out
 
     def line_fft(self, x, axis: int, inverse: bool = False, out=None):
         n = self.Na if axis == 0 else self.Nr

@@ -26,7 +26,7 @@ RD_WINDOW_HAMMING = 1
 # every symbol the header declares
 EXPORTS = ("rd_length_supported", "rd_plan_create", "rd_plan_destroy", "rd_range_compress",
            "rd_azimuth_focus", "rd_focus", "rd_debug_azimuth_stages", "rd_debug_line_fft",
-           "rd_corner_turn", "rd_status_string", "rd_last_error")
+           "rd_backproject", "rd_corner_turn", "rd_status_string", "rd_last_error")
 
 
 class rd_params(ctypes.Structure):
@@ -44,6 +44,17 @@ class rd_params(ctypes.Structure):
         ("rcmc_taps", ctypes.c_int32),
         ("kaiser_beta", ctypes.c_double),
         ("flags", ctypes.c_uint32),
+    ]
+
+
+class rd_bp_grid(ctypes.Structure):
+    _fields_ = [
+        ("nx", ctypes.c_int32),
+        ("ny", ctypes.c_int32),
+        ("x0_m", ctypes.c_double),
+        ("dx_m", ctypes.c_double),
+        ("r0_m", ctypes.c_double),
+        ("dr_m", ctypes.c_double),
     ]
 
 
@@ -80,6 +91,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rd_debug_azimuth_stages.restype = ctypes.c_int
     lib.rd_debug_line_fft.argtypes = [vp, i32, i32, vp, vp, i64, vp]
     lib.rd_debug_line_fft.restype = ctypes.c_int
+    lib.rd_backproject.argtypes = [vp, vp, vp, ctypes.POINTER(rd_bp_grid), vp]
+    lib.rd_backproject.restype = ctypes.c_int
     lib.rd_corner_turn.argtypes = [vp, vp, i64, i64, vp]
     lib.rd_corner_turn.restype = ctypes.c_int
     lib.rd_status_string.argtypes = [ctypes.c_int]
@@ -172,6 +185,23 @@ def rd_debug_line_fft(plan: int, axis: int, inverse: int, x, y, lines: int, stre
     _check(load_library().rd_debug_line_fft(plan, int(axis), int(inverse), _addr(x), _addr(y),
                                             int(lines), _stream(stream, x, y)),
            "rd_debug_line_fft")
+
+
+def make_bp_grid(**kw) -> rd_bp_grid:
+    g = rd_bp_grid()
+    for k, v in kw.items():
+        if not hasattr(g, k):
+            raise TypeError(f"unknown rd_bp_grid field {k!r}")
+        setattr(g, k, v)
+    return g
+
+
+def rd_backproject(plan: int, rc, img, grid, stream=None) -> None:
+    if isinstance(grid, dict):
+        grid = make_bp_grid(**grid)
+    _check(load_library().rd_backproject(plan, _addr(rc), _addr(img), ctypes.byref(grid) if grid is not None else None,
+                                         _stream(stream, rc, img)),
+           "rd_backproject")
 
 
 def rd_corner_turn(x, y, rows: int, cols: int, stream=None) -> None:

@@ -582,6 +582,47 @@ rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const 
                    "line FFT launch");
 }
 
+rd_status rd_backproject(rd_plan* plan, const rd_c64* rc, rd_c64* img, const rd_bp_grid* grid,
+                         void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "back-projection needs a full-chain plan (carrier, PRF, velocity)");
+  if (!grid) return fail(RD_ERR_INVALID_ARG, "grid must not be NULL");
+  const rd_bp_grid g = *grid;
+  if (g.nx < 0 || g.ny < 0) return fail(RD_ERR_INVALID_ARG, "nx and ny must be >= 0");
+  if (g.nx == 0 || g.ny == 0) return RD_OK;
+  if (g.nx > 65535 * 4) return fail(RD_ERR_INVALID_ARG, "nx=%d exceeds %d", g.nx, 65535 * 4);
+  if (!std::isfinite(g.x0_m) || !std::isfinite(g.dx_m) || !std::isfinite(g.r0_m) || !std::isfinite(g.dr_m))
+    return fail(RD_ERR_INVALID_ARG, "grid origin and spacings must be finite");
+  if (!(g.r0_m > 0.0) || !(g.r0_m + double(g.ny - 1) * g.dr_m > 0.0))
+    return fail(RD_ERR_INVALID_ARG, "pixel slant ranges must be > 0");
+  if (!aligned8(rc) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "rc and img must be non-NULL and 8-byte aligned");
+  const size_t in_bytes = size_t(plan->p.Na) * size_t(plan->p.Nr) * sizeof(rd_c64);
+  const size_t out_bytes = size_t(g.nx) * size_t(g.ny) * sizeof(rd_c64);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(rc), b = reinterpret_cast<uintptr_t>(img);
+  if (a < b + out_bytes && b < a + in_bytes) return fail(RD_ERR_INVALID_ARG, "rc and img overlap");
+  rdf::BpConst c{};
+  c.nx = g.nx;
+  c.ny = g.ny;
+  c.Na = plan->p.Na;
+  c.Nr = plan->p.Nr;
+  c.x0 = g.x0_m;
+  c.dx = g.dx_m;
+  c.r0 = g.r0_m;
+  c.drp = g.dr_m;
+  c.step = plan->p.velocity_mps / plan->p.prf_hz;
+  c.rb0 = plan->p.range_bin0_m;
+  c.inv_dr = 1.0 / plan->dr;
+  c.two_over_lam = 2.0 * plan->p.carrier_hz / kC;
+  // Hardware sin/cos (turns in, ~1e-6 absolute error) unless RD_BP_SINCOS=accurate selects the
+  // library sincospi (a measurement variant).
+  const char* v = std::getenv("RD_BP_SINCOS");
+  const int native = (v && std::string(v) == "accurate") ? 0 : 1;
+  return check_hip(rdf::launch_backproject(reinterpret_cast<const float2*>(rc), reinterpret_cast<float2*>(img),
+                                           c, native, static_cast<hipStream_t>(stream)),
+                   "back-projection launch");
+}
+
 rd_status rd_corner_turn(const rd_c64* in, rd_c64* out, int64_t rows, int64_t cols,
                          void* stream) {
   if (rows < 0 || cols < 0) return fail(RD_ERR_INVALID_ARG, "rows and cols must be >= 0");

@@ -613,6 +613,115 @@ hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64
 }
 
 // ------------------------------------------------------------------------------------------
+// Back-projection (framerc.cn/news/4459478 §1.1, §2.2, §4.2): for every pixel (along-track x,
+// closest-approach slant range r) and every pulse m, the range d = sqrt(r^2 + (x - V m/PRF)^2),
+// the range-compressed line m linearly interpolated at bin (d - range_bin0)/dr (zero outside the
+// line), times exp(+j 4 pi d / lambda), summed over all pulses.  One lane per pixel; a wave holds
+// 64 consecutive range pixels of one along-track row, a workgroup 4 rows, so the pulse loop is
+// uniform and each pulse's gathers fall in one short, nearly contiguous stretch of its line
+// (read through the cache; the line is a buffer resource, so bins outside it read zero).
+// Precision: d = r + delta with delta = a^2 / (r + d) evaluated in float32 without cancellation
+// (a = x - V m/PRF formed in float64); the pixel's constant phase 2 r / lambda (turns) and its
+// bin offset (r - range_bin0)/dr are split in float64 once per pixel, so the per-pulse float32
+// quantities (delta / dr, 2 delta / lambda) stay small; partial sums of 32 pulses go to float64.
+// One pulse's contribution to a pixel, added to (sr, si).
+template <bool NATIVE_SINCOS>
+__device__ __forceinline__ void bp_pulse(const float2* __restrict__ rc, const BpConst& c, int m,
+                                         double x, float rf, float fb, int ib, float k_bin,
+                                         float k_turn, uint32_t line_bytes, float& sr, float& si) {
+  const float a = float(fma(-double(m), c.step, x));
+  const float a2 = a * a;
+  const float d = __builtin_amdgcn_sqrtf(fmaf(rf, rf, a2));   // only in the denominator below
+  const float delta = a2 * __builtin_amdgcn_rcpf(rf + d);     // d - r without cancellation
+  const float t = fmaf(delta, k_bin, fb);
+  const float fl = floorf(t);
+  const float w = t - fl;
+  // both samples outside the line read zero: clamp to -2 (both offsets wrap far past the line)
+  // or Nr (both at or past its end); idx = -1 reads zero and bin 0
+  int idx = ib + int(fl);
+  idx = idx < -2 ? -2 : (idx > c.Nr ? c.Nr : idx);
+  const __amdgpu_buffer_rsrc_t line = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float2*>(rc + int64_t(m) * c.Nr), 0, int(line_bytes), kBufDword3);
+  // Two 8-byte loads, each range-checked on its own (a negative index wraps far past the line
+  // and reads zero; bin Nr reads zero).  The second offset is hidden from the compiler, which would
+  // otherwise fuse the pair into one 16-byte load whose range check is all-or-nothing and would
+  // drop the last in-line sample.
+  const uint32_t off = uint32_t(idx) * 8u;
+  uint32_t off1 = off + 8u;
+  asm volatile("" : "+v"(off1));
+  const float2 s0 = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(line, off, 0, 0));
+  const float2 s1 = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(line, off1, 0, 0));
+  const float vr = fmaf(w, s1.x - s0.x, s0.x), vi = fmaf(w, s1.y - s0.y, s0.y);
+  const float turns = delta * k_turn;
+  float sn, cs;
+  if constexpr (NATIVE_SINCOS) {
+    const float f = __builtin_amdgcn_fractf(turns);   // hardware sin/cos take turns
+    sn = __builtin_amdgcn_sinf(f);
+    cs = __builtin_amdgcn_cosf(f);
+  } else {
+    sincospif(2.0f * (turns - rintf(turns)), &sn, &cs);
+  }
+  sr = fmaf(vr, cs, fmaf(-vi, sn, sr));
+  si = fmaf(vr, sn, fmaf(vi, cs, si));
+}
+
+template <bool NATIVE_SINCOS>
+__global__ void __launch_bounds__(256)
+    k_backproject(const float2* __restrict__ rc, float2* __restrict__ img, BpConst c) {
+  const int j = int(blockIdx.x) * 64 + int(threadIdx.x & 63);
+  const int i = int(blockIdx.y) * 4 + int(threadIdx.x >> 6);
+  const double r = c.r0 + double(j) * c.drp;
+  const double x = c.x0 + double(i) * c.dx;
+  // bin offset of the pixel's closest approach: integer part ib (clamped far outside the line,
+  // where every sample reads zero anyway) and fraction fb
+  double b0 = (r - c.rb0) * c.inv_dr;
+  b0 = b0 < -4.0 * c.Nr ? -4.0 * c.Nr : (b0 > 4.0 * c.Nr ? 4.0 * c.Nr : b0);
+  const double ibd = floor(b0);
+  const int ib = int(ibd);
+  const float fb = float(b0 - ibd);
+  const float rf = float(r);
+  const float k_bin = float(c.inv_dr), k_turn = float(c.two_over_lam);
+  const uint32_t line_bytes = uint32_t(c.Nr) * 8u;
+  double acc_r = 0.0, acc_i = 0.0;
+  constexpr int BLK = 32;  // pulses summed in float32 before each float64 accumulation
+  int m0 = 0;
+  for (; m0 + BLK <= c.Na; m0 += BLK) {
+    float sr = 0.f, si = 0.f;
+#pragma unroll
+    for (int k = 0; k < BLK; ++k)
+      bp_pulse<NATIVE_SINCOS>(rc, c, m0 + k, x, rf, fb, ib, k_bin, k_turn, line_bytes, sr, si);
+    acc_r += double(sr);
+    acc_i += double(si);
+  }
+  {
+    float sr = 0.f, si = 0.f;
+    for (int m = m0; m < c.Na; ++m)
+      bp_pulse<NATIVE_SINCOS>(rc, c, m, x, rf, fb, ib, k_bin, k_turn, line_bytes, sr, si);
+    acc_r += double(sr);
+    acc_i += double(si);
+  }
+  if (i < c.nx && j < c.ny) {
+    const double turns0 = r * c.two_over_lam;
+    float sn, cs;
+    sincospif(float(2.0 * (turns0 - rint(turns0))), &sn, &cs);
+    const float ar = float(acc_r), ai = float(acc_i);
+    img[int64_t(i) * c.ny + j] = make_float2(ar * cs - ai * sn, ar * sn + ai * cs);
+  }
+}
+
+hipError_t launch_backproject(const float2* rc, float2* img, const BpConst& c, int native_sincos,
+                              hipStream_t s) {
+  const int64_t gx = (int64_t(c.ny) + 63) / 64, gy = (int64_t(c.nx) + 3) / 4;
+  if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
+  const dim3 grid{unsigned(gx), unsigned(gy), 1u};
+  if (native_sincos)
+    hipLaunchKernelGGL(k_backproject<true>, grid, dim3(256), 0, s, rc, img, c);
+  else
+    hipLaunchKernelGGL(k_backproject<false>, grid, dim3(256), 0, s, rc, img, c);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // Doppler-digit row order -> natural order (stage test hook only)
 __global__ void __launch_bounds__(256)
     k_row_unpermute(const float2* __restrict__ in, float2* __restrict__ out, int A, int B,

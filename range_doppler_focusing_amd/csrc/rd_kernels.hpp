@@ -78,6 +78,19 @@ struct ColStep {
 hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
                           int64_t cols, int na, int cached, hipStream_t s);
 
+// Back-projection constants (see k_backproject): pixel (i, j) lies at along-track x0 + i dx and
+// closest-approach slant range r0 + j drp; pulse m at along-track m * step (= V / PRF).
+struct BpConst {
+  int nx, ny, Na, Nr;
+  double x0, dx, r0, drp;
+  double step;          // V / PRF
+  double rb0, inv_dr;   // slant range of bin 0, 1 / bin spacing
+  double two_over_lam;  // 2 / lambda: turns of the two-way carrier phase per metre
+};
+// img[i][j] for i < nx, j < ny from rc [Na][Nr]; hipErrorInvalidValue if the grid does not fit
+hipError_t launch_backproject(const float2* rc, float2* img, const BpConst& c, int native_sincos,
+                              hipStream_t s);
+
 // out[c][r] = in[r][c] for a row-major [rows][cols] array (streaming: non-temporal accesses);
 // hipErrorInvalidValue if the tile grid does not fit (rows > 65535 * 64)
 hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64_t cols,

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     import range_doppler_focusing_amd as rdf
     lib = rdf.load_library()
     declared = header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 12
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(rdf.EXPORTS) == declared
@@ -115,3 +115,28 @@ def test_corner_turn_argument_errors_return_before_any_launch():
     assert lib.rd_corner_turn(a, a + 8, 7, 7, None) == -1          # overlapping buffers
     assert lib.rd_corner_turn(a, b, 65535 * 64 + 1, 1, None) == -1  # beyond the tile grid
     assert "overlap" in lib.rd_last_error().decode() or "rows" in lib.rd_last_error().decode()
+
+
+def test_bp_grid_layout_matches_c():
+    from range_doppler_focusing_amd import rd_bp_grid
+    fields = [f for f, _ in rd_bp_grid._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"rdfocus.h\"\nint main(void){\n"
+    src += 'printf("%zu\\n", sizeof(rd_bp_grid));\n'
+    for f in fields:
+        src += f'printf("%zu\\n", offsetof(rd_bp_grid, {f}));\n'
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(rd_bp_grid)
+    assert got[1:] == [getattr(rd_bp_grid, f).offset for f in fields]
+
+
+def test_backproject_rejects_a_null_plan_before_any_launch():
+    import range_doppler_focusing_amd as rdf
+    lib = rdf.load_library()
+    g = rdf.make_bp_grid(nx=4, ny=4, x0_m=0.0, dx_m=1.0, r0_m=1000.0, dr_m=1.0)
+    assert lib.rd_backproject(None, 1 << 20, 1 << 30, ctypes.byref(g), None) == -1

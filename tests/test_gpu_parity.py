@@ -286,6 +286,97 @@ def test_corner_turn_of_range_compressed_scene(torch_dev, rdf):
     assert M.rel_l2(t, O.corner_turn(ref["rc"])) <= STAGE_TOL
 
 
+# ------------------------------------------------------------------------------ back-projection
+BP_TOL = 1e-5
+
+
+def focus_grid(cfg, m_lo, n_lo, nx, ny):
+    """The focusing image's own grid: one row per pulse position, one column per range bin."""
+    p = cfg.plan_params()
+    return dict(nx=nx, ny=ny, x0_m=cfg.velocity_mps * m_lo / cfg.prf_hz, dx_m=cfg.velocity_mps / cfg.prf_hz,
+                r0_m=p["range_bin0_m"] + n_lo * O.range_spacing(p), dr_m=O.range_spacing(p))
+
+
+@pytest.mark.parametrize("variant", ["native", "accurate"])
+def test_backproject_small_grids(torch_dev, rdf, monkeypatch, variant):
+    """Whole 256 x 256 scene on its focusing grid, and a ragged grid partly outside the swath:
+    the same complex64 range-compressed input on both sides, the kernel against the oracle."""
+    torch = torch_dev
+    if variant == "accurate":
+        monkeypatch.setenv("RD_BP_SINCOS", "accurate")
+    sc, ref = scene_and_stages(C1)
+    rc = ref["rc"].astype(np.complex64)
+    p = C1.plan_params()
+    dr = O.range_spacing(p)
+    grids = [focus_grid(C1, 0, 0, 256, 256),
+             dict(nx=37, ny=50, x0_m=-3.1, dx_m=0.37, r0_m=p["range_bin0_m"] - 20.3 * dr, dr_m=5.9 * dr)]
+    with rdf.Plan(**p) as plan:
+        rcd = dev(torch, rc)
+        for g in grids:
+            log(f"[bp] {variant} grid {g['nx']}x{g['ny']}")
+            got = plan.backproject(rcd, g).cpu().numpy()
+            want = O.backproject(rc, p, g)
+            err = M.rel_l2(got, want)
+            log(f"[bp] {variant} {g['nx']}x{g['ny']} rel-L2 {err:.2e}")
+            assert err <= BP_TOL
+    img = O.backproject(rc, p, grids[0])
+    gimg = None
+    with rdf.Plan(**p) as plan:
+        gimg = plan.backproject(dev(torch, rc), grids[0]).cpu().numpy()
+    for (m, n) in sc.targets:
+        assert M.peak_near(gimg, m, n) == M.peak_near(img, m, n)
+
+
+def test_backproject_large_grid_sampled(torch_dev, rdf):
+    """4096 pulses onto a 1024 x 1024 grid of the 4096 x 4096 airborne scene (the workload the
+    bench times): sampled pixels against the oracle computed pixel by pixel, and every target in
+    the grid peaks where the oracle's 9 x 9 neighbourhood image peaks."""
+    torch = torch_dev
+    cfg = C3
+    sc, ref = scene_and_stages(cfg)
+    rc = ref["rc"].astype(np.complex64)
+    p = cfg.plan_params()
+    m_lo, n_lo = cfg.Na // 2 - 512, cfg.Nr // 2 - 512
+    g = focus_grid(cfg, m_lo, n_lo, 1024, 1024)
+    with rdf.Plan(**p) as plan:
+        log("[bp] 4096 pulses -> 1024 x 1024")
+        img = plan.backproject(dev(torch, rc), g).cpu().numpy()
+    rng = np.random.default_rng(5)
+    pix = [(int(a), int(b)) for a, b in zip(rng.integers(0, 1024, 48), rng.integers(0, 1024, 48))]
+    inside = [(m - m_lo, n - n_lo) for (m, n) in sc.targets if 4 <= m - m_lo < 1020 and 4 <= n - n_lo < 1020]
+    pix += inside
+    want = O.backproject_pixels(rc, p, g, pix)
+    got = np.array([img[i, j] for (i, j) in pix])
+    err = M.rel_l2(got, want)
+    log(f"[bp] sampled {len(pix)} pixels rel-L2 {err:.2e} ({len(inside)} targets inside)")
+    assert err <= BP_TOL
+    for (i, j) in inside:
+        sub = dict(g, nx=9, ny=9, x0_m=g["x0_m"] + (i - 4) * g["dx_m"], r0_m=g["r0_m"] + (j - 4) * g["dr_m"])
+        w = O.backproject(rc, p, sub)
+        assert np.unravel_index(np.argmax(np.abs(w)), w.shape) == (4, 4)
+        assert M.peak_near(img, i, j) == (i, j)
+
+
+def test_backproject_error_paths(torch_dev, rdf):
+    torch = torch_dev
+    g = dict(nx=8, ny=8, x0_m=0.0, dx_m=0.1, r0_m=5000.0, dr_m=1.0)
+    with rdf.Plan(**C2.with_(Na=256, Nr=4096).plan_params()) as plan:
+        x = torch.zeros((256, 4096), dtype=torch.complex64, device="cuda")
+        with pytest.raises(rdf.RdError) as ei:
+            plan.backproject(x, g)
+        assert ei.value.status == -6
+    with rdf.Plan(**C1.plan_params()) as plan:
+        x = torch.zeros((256, 256), dtype=torch.complex64, device="cuda")
+        with pytest.raises(rdf.RdError) as ei:      # image overlapping the input
+            rdf.rd_backproject(plan.handle, x, x.data_ptr() + 8 * 64, g)
+        assert ei.value.status == -1
+        with pytest.raises(rdf.RdError) as ei:
+            rdf.rd_backproject(plan.handle, x, torch.empty((8, 8), dtype=torch.complex64, device="cuda"),
+                               dict(g, r0_m=-1.0))
+        assert ei.value.status == -1
+        rdf.rd_backproject(plan.handle, x, torch.empty((1,), dtype=torch.complex64, device="cuda"), dict(g, nx=0))
+
+
 # ------------------------------------------------------------------------------ error paths
 def test_error_paths_on_device(torch_dev, rdf):
     torch = torch_dev
