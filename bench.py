@@ -309,11 +309,23 @@ def main():
         ms = time_steps(torch, lambda i: rdf.rd_backproject(bplan.handle, rc, img, grid, stream), 5, 1, stream)
         bplan.close()
         pp = bcfg.Na * nx * ny
-        large.append({"workload": f"back-projection (rd_backproject), {bcfg.Na} pulses x {bcfg.Nr} samples "
-                                  f"onto {nx} x {ny} pixels (4096 x 4096 airborne geometry)",
-                      "ms_per_step": round(ms, 4), "value": round(pp / (ms * 1e-3) / 1e9, 2),
-                      "unit": "Gpixel-pulses/s",
-                      "data": "seeded complex Gaussian noise on the device (timing is data-independent)"})
+        rec = {"workload": f"back-projection (rd_backproject), {bcfg.Na} pulses x {bcfg.Nr} samples "
+                           f"onto {nx} x {ny} pixels (4096 x 4096 airborne geometry)",
+               "ms_per_step": round(ms, 4), "value": round(pp / (ms * 1e-3) / 1e9, 2),
+               "unit": "Gpixel-pulses/s",
+               "data": "seeded complex Gaussian noise on the device (timing is data-independent)"}
+        if not args.no_cpu:
+            # the oracle on a 32 x 32 corner of the same grid, all 4096 pulses
+            from oracle import rd_oracle as O
+            rc_h = rc.cpu().numpy()
+            sub = dict(grid, nx=32, ny=32)
+            t0 = time.perf_counter()
+            O.backproject(rc_h, bp, sub)
+            tb = time.perf_counter() - t0
+            rec["cpu_baseline"] = {"value": round(bcfg.Na * 32 * 32 / tb / 1e9, 5), "unit": "Gpixel-pulses/s",
+                                   "cores": 1, "kind": "oracle",
+                                   "sample": f"32 x 32 pixels x {bcfg.Na} pulses, one run ({tb:.1f} s)"}
+        large.append(rec)
         del rc, img
         torch.cuda.empty_cache()
 
