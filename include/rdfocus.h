@@ -52,7 +52,7 @@ typedef struct {
 typedef enum {
   RD_OK = 0,
   RD_ERR_INVALID_ARG = -1,        /* bad pointer, size, alignment, aliasing or parameter   */
-  RD_ERR_UNSUPPORTED_LENGTH = -2, /* Na or Nr has no built transform (see rd_length_supported) */
+  RD_ERR_UNSUPPORTED_LENGTH = -2, /* Na or Nr out of the supported lengths (see rd_length_supported) */
   RD_ERR_OUT_OF_MEMORY = -3,      /* device allocation for the plan failed                  */
   RD_ERR_DEVICE = -4,             /* HIP runtime error, or the plan's device is not current  */
   RD_ERR_LAUNCH = -5,             /* a kernel launch failed                                  */
@@ -73,8 +73,9 @@ enum { RD_WINDOW_RECT = 0, RD_WINDOW_HAMMING = 1 };
  * RCMC: rcmc_taps-point Kaiser(kaiser_beta)-windowed sinc, weights normalised to sum 1,
  * samples outside the line taken as 0. */
 typedef struct {
-  int32_t Na;            /* pulses (azimuth lines); a supported transform length             */
-  int32_t Nr;            /* range samples per pulse; a supported transform length            */
+  int32_t Na;            /* pulses (azimuth lines) >= 1; full-chain plans: see below         */
+  int32_t Nr;            /* range samples per pulse: a supported transform length, or on a   *
+                          * range-only plan any length 1..8192 (see rd_range_compress)       */
   double pulse_s;        /* Tp  > 0                                                          */
   double bandwidth_hz;   /* B   > 0 (chirp rate +B/Tp)                                       */
   double fs_hz;          /* Fs  > 0; requires L <= Nr                                        */
@@ -90,8 +91,9 @@ typedef struct {
 
 typedef struct rd_plan rd_plan;
 
-/* Returns 1 if `n` is a range-line length the library supports (256..16384 powers of two, and
- * 6000 = 2^4 * 3 * 5^3), else 0.  Full-chain plans also need Na a power of two in
+/* Returns 1 if `n` is a transform length the library builds (256..16384 powers of two, and
+ * 6000 = 2^4 * 3 * 5^3), else 0.  Range-only plans also accept any other Nr in 1..8192 (range
+ * compression then runs as a zero-padded convolution, see rd_range_compress).  Full-chain plans also need Na a power of two in
  * [256, 16384], Na*Nr*8 < 4 GiB, and a range migration R(n)(1/D_k - 1)/dr below Nr/8 - 5
  * samples over the whole Doppler band (checked by rd_plan_create). */
 int rd_length_supported(int32_t n);
@@ -107,7 +109,16 @@ rd_status rd_plan_destroy(rd_plan* plan);
 
 /* Range compression of every pulse (cf-1.com/news/2323550 §3.1, §3.2; nxmr.cn/news/101525
  * §2.1):  rc[m] = IFFT_Nr( FFT_Nr(echo[m]) * H ).  One fused kernel: each line is read from
- * HBM once and written once.  echo == rc (in place) is allowed; other overlap is an error. */
+ * HBM once and written once.  echo == rc (in place) is allowed; other overlap is an error.
+ * Any line length: nxmr.cn/news/101525 §4.1 names Nr = 1200 as a usual airborne length and
+ * §5.1 asks for transforms of lengths that are not powers of two.  Where Nr has no built
+ * transform (range-only plans, Nr <= 8192), the same length-Nr circular correlation
+ *   rc[m][n] = sum_i echo[m][(n + i) mod Nr] conj(h[i])
+ * is computed exactly (up to float32 rounding) as one zero-padded circular convolution of
+ * length M = the smallest power of two >= max(256, 2 Nr - 1): the kernel reads the line into
+ * a zero-padded length-M buffer in registers, multiplies its spectrum by the M-point spectrum
+ * of the periodically extended, reversed, conjugated replica, and stores outputs
+ * [Nr - 1, 2 Nr - 1) of the inverse transform.  The line is still read and written once. */
 rd_status rd_range_compress(rd_plan* plan, const rd_c64* echo, rd_c64* rc, void* stream);
 
 /* Azimuth processing of range-compressed data rc [Na][Nr] into the focused image img

@@ -527,6 +527,50 @@ __device__ __forceinline__ void store_line(const float2* v, const LineIO& io, in
   }
 }
 
+// Zero-padded line I/O: a line of n_line <= N samples (consecutive lines n_line apart) enters an
+// N-point transform with positions >= n_line read as zero, and the outputs at positions
+// [skip, skip + n_line) of the transform are stored as the line.  An access that falls outside
+// its window gets an offset past the resource's size, so the hardware range check reads zero or
+// drops the store (no branch).
+constexpr uint32_t kBufOff = 0x80000000u;  // past any line resource of this library
+
+template <int N, int T, int R, int AUX = kBufNonTemporal>
+__device__ __forceinline__ void load_line_pad(float2* v, const LineIO& io, int elem0, int tid,
+                                              int n_line) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int r = dft_input_order<R>(i);
+        const int e = j + r * G::NB;
+        const uint32_t off = e < n_line ? uint32_t(elem0 + e) * 8u : kBufOff;
+        v[b * R + r] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, off, 0, AUX));
+      }
+    }
+  }
+}
+
+template <int N, int T, int R, int AUX = kBufNonTemporal>
+__device__ __forceinline__ void store_line_pad(const float2* v, const LineIO& io, int elem0, int tid,
+                                               int n_line, int skip) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int o = j + r * G::NB - skip;
+        const uint32_t off = uint32_t(o) < uint32_t(n_line) ? uint32_t(elem0 + o) * 8u : kBufOff;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, v[b * R + r]), io.rsrc, off, 0, AUX);
+      }
+    }
+  }
+}
+
 // Reads of the pass after the exchange keyed NS (the product of the radices before it).
 template <int N, int T, int R, int NS>
 __device__ __forceinline__ void load_lds(float2* v, const float2* lds, int tid) {

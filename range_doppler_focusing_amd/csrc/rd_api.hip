@@ -49,6 +49,8 @@ struct rd_plan {
   const rdf::LineOps* rops = nullptr;  // range-length kernels
   const rdf::LineOps* aops = nullptr;  // azimuth-length kernels
   int rc_variant = 0;   // 0 table loads, 1 register-cached (pf)
+  int pad_m = 0;        // > 0: Nr has no built transform; range compression runs as a zero-padded
+                        // circular convolution of length pad_m >= 2 Nr - 1 (power of two)
   int cached = 0;       // image passes use ordinary (cacheable) accesses: image fits the cache
   int rc_grid = 0;      // persistent grid of the range kernels
   int A = 0, B = 0;     // Na = A B: strided and block steps of the azimuth transform
@@ -139,6 +141,64 @@ std::vector<float2> matched_filter(const rd_params& p, int L) {
     H[k] = make_float2(float(re / Nr), float(-im / Nr));  // conjugate, 1/Nr
   }
   return H;
+}
+
+// In-place radix-2 float64 FFT (forward, e^{-j...}) of a power-of-two length, for plan tables.
+void fft_pow2(std::vector<double>& re, std::vector<double>& im) {
+  const size_t n = re.size();
+  for (size_t i = 1, j = 0; i < n; ++i) {
+    size_t bit = n >> 1;
+    for (; j & bit; bit >>= 1) j ^= bit;
+    j ^= bit;
+    if (i < j) {
+      std::swap(re[i], re[j]);
+      std::swap(im[i], im[j]);
+    }
+  }
+  for (size_t len = 2; len <= n; len <<= 1) {
+    const size_t half = len / 2;
+    for (size_t k = 0; k < half; ++k) {
+      const double a = -kTwoPi * double(k) / double(len);
+      const double wr = std::cos(a), wi = std::sin(a);
+      for (size_t b = 0; b < n; b += len) {
+        const size_t u = b + k, v = u + half;
+        const double xr = re[v] * wr - im[v] * wi, xi = re[v] * wi + im[v] * wr;
+        re[v] = re[u] - xr;
+        im[v] = im[u] - xi;
+        re[u] += xr;
+        im[u] += xi;
+      }
+    }
+  }
+}
+
+// Range compression of a line of any length N as one zero-padded circular convolution of length
+// M >= 2N - 1.  The length-N circular correlation rc[n] = sum_k x[(n + k) mod N] conj(h[k]) is the
+// circular convolution of x with g[n] = conj(h[(-n) mod N]); with p[k] = g[(k - (N - 1)) mod N]
+// for k < 2N - 1 (zero up to M), the linear convolution x * p holds rc[n] at n + N - 1, and for
+// M >= 2N - 1 the length-M circular convolution equals it there.  Returns FFT_M(p) / M (the 1/M
+// of the inverse transform folded in), evaluated in float64 and rounded once.
+std::vector<float2> padded_filter(const rd_params& p, int L, int M) {
+  const int N = p.Nr;
+  const double Kr = p.bandwidth_hz / p.pulse_s;
+  std::vector<double> re(size_t(M), 0.0), im(size_t(M), 0.0);
+  for (int n = 0; n < L; ++n) {
+    const double t = double(n) / p.fs_hz - p.pulse_s / 2.0;
+    double w = 1.0;
+    if (p.range_window == RD_WINDOW_HAMMING && L > 1) w = 0.54 - 0.46 * std::cos(kTwoPi * n / (L - 1));
+    const double ph = M_PI * Kr * t * t;
+    // p[k] = conj(h[(N - 1 - k) mod N]) for k < 2N - 1: h[n] lands at k = N - 1 - n and, for
+    // n >= 1, again at k = 2N - 1 - n
+    for (int k : {N - 1 - n, n >= 1 ? 2 * N - 1 - n : -1}) {
+      if (k < 0) continue;
+      re[size_t(k)] = w * std::cos(ph);
+      im[size_t(k)] = -w * std::sin(ph);
+    }
+  }
+  fft_pow2(re, im);
+  std::vector<float2> out(static_cast<size_t>(M));
+  for (int k = 0; k < M; ++k) out[size_t(k)] = make_float2(float(re[size_t(k)] / M), float(im[size_t(k)] / M));
+  return out;
 }
 
 // RCMC tap weights (nxmr.cn/news/101525 §2.2 interpolates the migrated range; the 8-tap
@@ -250,7 +310,7 @@ int persistent_grid(int occ, int cus, int64_t lines, int lpw) {
 rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, bool chained, hipStream_t s) {
   if (P->rc_variant == 1)
     return check_hip(P->rops->range_compress_pf(in, out, P->H, P->tw_r, P->rc_tab, P->p.Na,
-                                                P->rc_grid, chained ? P->cached : 0, s),
+                                                P->rc_grid, chained ? P->cached : 0, P->p.Nr, s),
                      "range compression launch");
   return check_hip(P->rops->range_compress(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid, s),
                    "range compression launch");
@@ -349,7 +409,17 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     return fail(RD_ERR_INVALID_ARG,
                 "carrier_hz, prf_hz, velocity_mps must all be > 0 (full chain) or all 0 (range only)");
   const rdf::LineOps* rops = rdf::line_ops(p.Nr);
-  if (!rops) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length Nr=%d is built", p.Nr);
+  int pad_m = 0;
+  if (!rops) {
+    // any line length up to 8192 on a range-only plan: zero-padded convolution of length
+    // M = the smallest built power of two >= 2 Nr - 1
+    if (all_az) return fail(RD_ERR_UNSUPPORTED_LENGTH, "full-chain plans need a built transform of length Nr=%d", p.Nr);
+    if (p.Nr > 8192) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length Nr=%d is built, and Nr > 8192", p.Nr);
+    pad_m = 256;
+    while (pad_m < 2 * p.Nr - 1) pad_m *= 2;
+    rops = rdf::line_ops(pad_m);
+    if (!rops || !rops->range_compress_pf) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no padded transform for Nr=%d", p.Nr);
+  }
   const rdf::LineOps* aops = nullptr;
   if (all_az) {
     aops = rdf::line_ops(p.Na);
@@ -381,6 +451,7 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   P->dr = kC / (2.0 * p.fs_hz);
   P->azimuth = all_az;
   P->rops = rops;
+  P->pad_m = pad_m;
   P->aops = aops;
   if (hipDeviceGetAttribute(&P->cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     P->cus = 256;
@@ -391,10 +462,12 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     return s;
   };
   {
-    const std::vector<float2> Hh = matched_filter(p, P->L), roots = roots_table(p.Nr);
+    const int n_tf = pad_m ? pad_m : p.Nr;
+    const std::vector<float2> Hh = pad_m ? padded_filter(p, P->L, pad_m) : matched_filter(p, P->L);
+    const std::vector<float2> roots = roots_table(n_tf);
     if ((st = upload(&P->H, Hh, "matched filter")) != RD_OK) return bail(st);
     if ((st = upload(&P->tw_r, roots, "range twiddles")) != RD_OK) return bail(st);
-    if (const int n = rops->rc_tab_len(); n > 0) {
+    if (const int n = rops->rc_tab_len(); n > 0 && !pad_m) {
       std::vector<float2> tab(static_cast<size_t>(n));
       rops->rc_tab_fill(Hh.data(), roots.data(), tab.data());
       if ((st = upload(&P->rc_tab, tab, "range kernel table")) != RD_OK) return bail(st);
@@ -411,8 +484,8 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     const char* v = std::getenv("RD_RC_VARIANT");
     const std::string want = v ? v : "";
     int occ = 0;
-    if (rops->range_compress_pf && want != "table") {
-      if (rops->occupancy_pf(&occ) != hipSuccess)
+    if (rops->range_compress_pf && (want != "table" || pad_m)) {
+      if (rops->occupancy_pf(&occ, pad_m ? 1 : 0) != hipSuccess)
         return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
       P->rc_variant = 1;
       P->rc_grid = persistent_grid(occ, P->cus, p.Na, rops->lpw);

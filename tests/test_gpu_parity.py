@@ -140,6 +140,60 @@ def test_range_compression_every_length(torch_dev, rdf, n, lines):
     assert err <= STAGE_TOL
 
 
+@pytest.mark.parametrize("n", [1, 7, 127, 129, 1000, 1200, 1201, 2049, 3001, 4097, 5000, 8191])
+@pytest.mark.parametrize("lines", [1, 37])
+def test_range_compression_any_length(torch_dev, rdf, n, lines):
+    """Line lengths with no built transform (range-only plans): the zero-padded convolution of
+    the smallest power of two >= 2n - 1 against the oracle's length-n circular correlation, with
+    replicas from one sample to a third of the line, in place bit-identical to out of place."""
+    torch = torch_dev
+    rng = np.random.default_rng(2000 + n + lines)
+    fs = 120e6
+    L = max(1, n // 3) if n != 7 else 7          # n = 7: replica as long as the line
+    params = dict(Na=lines, Nr=n, pulse_s=L / fs, bandwidth_hz=90e6, fs_hz=fs,
+                  range_window=int(n % 2 == 0))
+    assert O.replica_length(params) == L
+    echo = (rng.standard_normal((lines, n)) + 1j * rng.standard_normal((lines, n))).astype(np.complex64)
+    log(f"[range] any length: n={n} lines={lines}")
+    with rdf.Plan(**params) as plan:
+        x = dev(torch, echo)
+        rc = plan.range_compress(x).cpu().numpy()
+        plan.range_compress(x, out=x)
+        torch.cuda.synchronize()
+        assert np.array_equal(x.cpu().numpy(), rc)
+    err = M.rel_l2(rc, O.range_compress(echo, params))
+    log(f"[range] n={n} lines={lines} rel-L2 {err:.2e}")
+    assert err <= STAGE_TOL
+
+
+def test_range_compression_any_length_large(torch_dev, rdf):
+    """16384 lines of 1200 samples (the padded kernel at its bench size, persistent grid over
+    many lines per workgroup) on sampled lines, and a lone chirp's peak at its delay."""
+    torch = torch_dev
+    Na, n, fs = 16384, 1200, 120e6
+    params = dict(Na=Na, Nr=n, pulse_s=400 / fs, bandwidth_hz=100e6, fs_hz=fs, range_window=1)
+    rows = np.array([0, 1, 2, 255, 4095, 8191, 12000, 16383])
+    echo = torch.empty((Na, n), dtype=torch.complex64, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    echo.view(torch.float32).normal_(generator=gen)
+    h = O.chirp_replica(params)
+    lone = np.zeros(n, np.complex128)
+    lone[333:333 + h.size] = np.exp(1j * np.pi * (100e6 / (400 / fs)) * (np.arange(h.size) / fs - 200 / fs) ** 2)
+    echo[5] = torch.from_numpy(lone.astype(np.complex64)).to("cuda")
+    rows = np.union1d(rows, [5])
+    with rdf.Plan(**params) as plan:
+        rc = plan.range_compress(echo)
+        got = rc[torch.from_numpy(rows).to("cuda")].cpu().numpy()
+        ech = echo[torch.from_numpy(rows).to("cuda")].cpu().numpy()
+        del rc, echo
+    ref = O.range_compress(ech, params)
+    err = M.rel_l2(got, ref)
+    log(f"[range] 16384x1200 sampled rel-L2 {err:.2e}")
+    assert err <= STAGE_TOL
+    k = int(np.argmax(np.abs(got[list(rows).index(5)])))
+    assert k == 333 == int(np.argmax(np.abs(ref[list(rows).index(5)])))
+
+
 def test_range_compression_table_variant(torch_dev, rdf, monkeypatch):
     """The table-twiddle kernel (selected by RD_RC_VARIANT=table) meets the same bar."""
     torch = torch_dev

@@ -90,16 +90,17 @@ def test_inverse_identity_and_parseval():
 
 
 # ---------------------------------------------------------------- range compression
-def test_range_compression_is_circular_correlation_with_replica():
-    p = dict(Na=3, Nr=40, pulse_s=1e-7, bandwidth_hz=80e6, fs_hz=120e6, range_window=1)
+@pytest.mark.parametrize("Nr", [40, 37, 12])     # composite, prime, replica as long as the line
+def test_range_compression_is_circular_correlation_with_replica(Nr):
+    p = dict(Na=3, Nr=Nr, pulse_s=1e-7, bandwidth_hz=80e6, fs_hz=120e6, range_window=1)
     h = O.chirp_replica(p)
     assert h.size == 12
     rng = np.random.default_rng(3)
-    echo = rng.standard_normal((3, 40)) + 1j * rng.standard_normal((3, 40))
+    echo = rng.standard_normal((3, Nr)) + 1j * rng.standard_normal((3, Nr))
     brute = np.zeros_like(echo)
     for m in range(3):
-        for i in range(40):
-            brute[m, i] = sum(echo[m, (i + n) % 40] * np.conj(h[n]) for n in range(h.size))
+        for i in range(Nr):
+            brute[m, i] = sum(echo[m, (i + n) % Nr] * np.conj(h[n]) for n in range(h.size))
     np.testing.assert_allclose(O.range_compress(echo, p), brute, atol=1e-12)
 
 
