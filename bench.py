@@ -163,7 +163,7 @@ def main():
                     help="seconds of untimed running before each warm-up (0 for counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
-    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp"], default=None,
+    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp", "pad"], default=None,
                     help="run one workload only (for profiling)")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the 8192 x 6000 and 16384 x 16384 workloads")
@@ -275,6 +275,39 @@ def main():
                 rec.update({"value": round(m, 1), "unit": "Mpixel/s",
                             "roofline_frac_80B_per_px": round(m * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4)})
             large.append(rec)
+
+    # ---------------------------------------------------------------- a line length with no built transform
+    if (args.only in (None, "large", "pad")) and not args.no_large:
+        large = large or []
+        na, nr, fs = 16384, 1200, 120e6
+        pp = dict(Na=na, Nr=nr, pulse_s=400 / fs, bandwidth_hz=100e6, fs_hz=fs, range_window=1)
+        x = gpu_noise(torch, (na, nr), 31)
+        y = torch.empty_like(x)
+        plan = rdf.Plan(**pp)
+        ms = time_steps(torch, lambda i: rdf.rd_range_compress(plan.handle, x, y, stream), 50, 3, stream)
+        plan.close()
+        gbs = 2 * na * nr * 8 / (ms * 1e-3) / 1e9
+        m = 256
+        while m < nr + 400 - 1:          # padded length: power of two >= Nr + L - 1
+            m *= 2
+        rec = {"workload": f"range compression of {nr}-sample lines (no built transform: exact "
+                           f"zero-padded {m}-point convolution), {na} x {nr} complex64, "
+                           "3.33 us / 100 MHz chirp at 120 MHz (400 samples), Hamming",
+               "ms_per_step": round(ms, 4), "steps": 50, "value": round(gbs, 1), "unit": "GB/s",
+               "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "lines_per_s": round(na / (ms * 1e-3), 1),
+               "data": "seeded complex Gaussian noise on the device (timing is data-independent)"}
+        if not args.no_cpu:
+            from oracle import rd_oracle as O
+            xh = x.cpu().numpy()
+            t0 = time.perf_counter()
+            O.range_compress(xh, pp)
+            tc = time.perf_counter() - t0
+            rec["cpu_baseline"] = {"value": round(2 * na * nr * 8 / tc / 1e9, 3), "unit": "GB/s",
+                                   "cores": 1, "kind": "oracle",
+                                   "sample": f"all {na} lines, one run ({tc:.2f} s)"}
+        large.append(rec)
+        del x, y
+        torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- corner turn
     if (args.only in (None, "large", "turn")) and not args.no_large:

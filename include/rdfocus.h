@@ -115,10 +115,10 @@ rd_status rd_plan_destroy(rd_plan* plan);
  * transform (range-only plans, Nr <= 8192), the same length-Nr circular correlation
  *   rc[m][n] = sum_i echo[m][(n + i) mod Nr] conj(h[i])
  * is computed exactly (up to float32 rounding) as one zero-padded circular convolution of
- * length M = the smallest power of two >= max(256, 2 Nr - 1): the kernel reads the line into
- * a zero-padded length-M buffer in registers, multiplies its spectrum by the M-point spectrum
- * of the periodically extended, reversed, conjugated replica, and stores outputs
- * [Nr - 1, 2 Nr - 1) of the inverse transform.  The line is still read and written once. */
+ * length M = the smallest power of two >= max(256, Nr + L - 1): the kernel reads the line,
+ * extended periodically by L - 1 samples and zero-padded to M, into registers, multiplies its
+ * spectrum by the M-point spectrum of the reversed, conjugated replica, and stores outputs
+ * [L - 1, L - 1 + Nr) of the inverse transform.  The line is still read and written once. */
 rd_status rd_range_compress(rd_plan* plan, const rd_c64* echo, rd_c64* rc, void* stream);
 
 /* Azimuth processing of range-compressed data rc [Na][Nr] into the focused image img

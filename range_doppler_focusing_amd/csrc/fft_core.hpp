@@ -527,16 +527,18 @@ __device__ __forceinline__ void store_line(const float2* v, const LineIO& io, in
   }
 }
 
-// Zero-padded line I/O: a line of n_line <= N samples (consecutive lines n_line apart) enters an
-// N-point transform with positions >= n_line read as zero, and the outputs at positions
-// [skip, skip + n_line) of the transform are stored as the line.  An access that falls outside
-// its window gets an offset past the resource's size, so the hardware range check reads zero or
-// drops the store (no branch).
+// Zero-padded line I/O: a line of n_line < N samples (consecutive lines n_line apart) enters an
+// N-point transform, and the outputs at positions [skip, skip + n_line) of the transform are
+// stored as the line.  An access that falls outside its window gets an offset past the
+// resource's size, so the hardware range check reads zero or drops the store (no branch).
 constexpr uint32_t kBufOff = 0x80000000u;  // past any line resource of this library
 
+// A line of n_line samples, periodically extended to n_ext (n_line <= n_ext < 2 n_line) and
+// zero-padded to N: element e reads x[e] for e < n_line, x[e - n_line] for e < n_ext, else 0
+// (an offset past the resource, which the hardware range check turns into zero).
 template <int N, int T, int R, int AUX = kBufNonTemporal>
 __device__ __forceinline__ void load_line_pad(float2* v, const LineIO& io, int elem0, int tid,
-                                              int n_line) {
+                                              int n_line, int n_ext) {
   using G = Geom<N, T, R>;
 #pragma unroll
   for (int b = 0; b < G::B; ++b) {
@@ -546,7 +548,8 @@ __device__ __forceinline__ void load_line_pad(float2* v, const LineIO& io, int e
       for (int i = 0; i < R; ++i) {
         const int r = dft_input_order<R>(i);
         const int e = j + r * G::NB;
-        const uint32_t off = e < n_line ? uint32_t(elem0 + e) * 8u : kBufOff;
+        const int w = e < n_line ? e : e - n_line;
+        const uint32_t off = e < n_ext ? uint32_t(elem0 + w) * 8u : kBufOff;
         v[b * R + r] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, off, 0, AUX));
       }
     }

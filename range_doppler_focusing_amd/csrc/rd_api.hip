@@ -50,7 +50,7 @@ struct rd_plan {
   const rdf::LineOps* aops = nullptr;  // azimuth-length kernels
   int rc_variant = 0;   // 0 table loads, 1 register-cached (pf)
   int pad_m = 0;        // > 0: Nr has no built transform; range compression runs as a zero-padded
-                        // circular convolution of length pad_m >= 2 Nr - 1 (power of two)
+                        // circular convolution of length pad_m >= Nr + L - 1 (power of two)
   int cached = 0;       // image passes use ordinary (cacheable) accesses: image fits the cache
   int rc_grid = 0;      // persistent grid of the range kernels
   int A = 0, B = 0;     // Na = A B: strided and block steps of the azimuth transform
@@ -173,13 +173,14 @@ void fft_pow2(std::vector<double>& re, std::vector<double>& im) {
 }
 
 // Range compression of a line of any length N as one zero-padded circular convolution of length
-// M >= 2N - 1.  The length-N circular correlation rc[n] = sum_k x[(n + k) mod N] conj(h[k]) is the
-// circular convolution of x with g[n] = conj(h[(-n) mod N]); with p[k] = g[(k - (N - 1)) mod N]
-// for k < 2N - 1 (zero up to M), the linear convolution x * p holds rc[n] at n + N - 1, and for
-// M >= 2N - 1 the length-M circular convolution equals it there.  Returns FFT_M(p) / M (the 1/M
-// of the inverse transform folded in), evaluated in float64 and rounded once.
+// M >= N + L - 1 (L = replica length).  The length-N circular correlation
+//   rc[n] = sum_{i < L} x[(n + i) mod N] conj(h[i])
+// reads x[0 .. N + L - 2] of the periodically extended line; with g[k] = conj(h[L - 1 - k]) for
+// k < L (zero up to M), the linear convolution of that extended line with g holds rc[n] at
+// n + L - 1, and a length-M circular convolution aliases nothing onto [L - 1, N + L - 1) when
+// M >= N + L - 1.  Returns FFT_M(g) / M (the 1/M of the inverse transform folded in),
+// evaluated in float64 and rounded once.
 std::vector<float2> padded_filter(const rd_params& p, int L, int M) {
-  const int N = p.Nr;
   const double Kr = p.bandwidth_hz / p.pulse_s;
   std::vector<double> re(size_t(M), 0.0), im(size_t(M), 0.0);
   for (int n = 0; n < L; ++n) {
@@ -187,13 +188,8 @@ std::vector<float2> padded_filter(const rd_params& p, int L, int M) {
     double w = 1.0;
     if (p.range_window == RD_WINDOW_HAMMING && L > 1) w = 0.54 - 0.46 * std::cos(kTwoPi * n / (L - 1));
     const double ph = M_PI * Kr * t * t;
-    // p[k] = conj(h[(N - 1 - k) mod N]) for k < 2N - 1: h[n] lands at k = N - 1 - n and, for
-    // n >= 1, again at k = 2N - 1 - n
-    for (int k : {N - 1 - n, n >= 1 ? 2 * N - 1 - n : -1}) {
-      if (k < 0) continue;
-      re[size_t(k)] = w * std::cos(ph);
-      im[size_t(k)] = -w * std::sin(ph);
-    }
+    re[size_t(L - 1 - n)] = w * std::cos(ph);
+    im[size_t(L - 1 - n)] = -w * std::sin(ph);
   }
   fft_pow2(re, im);
   std::vector<float2> out(static_cast<size_t>(M));
@@ -310,7 +306,8 @@ int persistent_grid(int occ, int cus, int64_t lines, int lpw) {
 rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, bool chained, hipStream_t s) {
   if (P->rc_variant == 1)
     return check_hip(P->rops->range_compress_pf(in, out, P->H, P->tw_r, P->rc_tab, P->p.Na,
-                                                P->rc_grid, chained ? P->cached : 0, P->p.Nr, s),
+                                                P->rc_grid, chained ? P->cached : 0, P->p.Nr,
+                                                P->pad_m ? P->L - 1 : 0, s),
                      "range compression launch");
   return check_hip(P->rops->range_compress(in, out, P->H, P->tw_r, P->p.Na, P->rc_grid, s),
                    "range compression launch");
@@ -412,11 +409,11 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   int pad_m = 0;
   if (!rops) {
     // any line length up to 8192 on a range-only plan: zero-padded convolution of length
-    // M = the smallest built power of two >= 2 Nr - 1
+    // M = the smallest built power of two >= Nr + L - 1
     if (all_az) return fail(RD_ERR_UNSUPPORTED_LENGTH, "full-chain plans need a built transform of length Nr=%d", p.Nr);
     if (p.Nr > 8192) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length Nr=%d is built, and Nr > 8192", p.Nr);
     pad_m = 256;
-    while (pad_m < 2 * p.Nr - 1) pad_m *= 2;
+    while (pad_m < p.Nr + int(Lf) - 1) pad_m *= 2;
     rops = rdf::line_ops(pad_m);
     if (!rops || !rops->range_compress_pf) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no padded transform for Nr=%d", p.Nr);
   }

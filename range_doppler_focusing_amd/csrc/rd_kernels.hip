@@ -123,33 +123,35 @@ __device__ __forceinline__ void filter_multiply(float2* v, const float2* h,
 // Line I/O of the range kernels: natural (n_line == N) or zero-padded (PAD, see below).
 template <int N, bool PAD>
 __device__ __forceinline__ void rc_load(float2* v, const float2* in, int64_t l0, int64_t lines, int grp,
-                                        int tid, int n_line) {
+                                        int tid, int n_line, int skip) {
   using C = LineCfg<N>;
   constexpr int R0 = ListInfo<typename C::Fwd>::first;
   if constexpr (PAD)
-    load_line_pad<N, C::T, R0>(v, LineIO(in, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line);
+    load_line_pad<N, C::T, R0>(v, LineIO(in, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
+                               n_line + skip);
   else
     load_line<N, C::T, R0>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
 }
 template <int N, bool PAD, int SAUX>
 __device__ __forceinline__ void rc_store(const float2* v, float2* out, int64_t l0, int64_t lines, int grp,
-                                         int tid, int n_line) {
+                                         int tid, int n_line, int skip) {
   using C = LineCfg<N>;
   constexpr int R0 = ListInfo<typename C::Fwd>::first;
   if constexpr (PAD)
     store_line_pad<N, C::T, R0, SAUX>(v, LineIO(out, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
-                                      n_line - 1);
+                                      skip);
   else
     store_line<N, C::T, R0, SAUX>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
 }
 
-// PAD: lines of n_line < N samples (any length): each is zero-padded to N, and the N-point
-// circular convolution with the plan's padded filter holds the length-n_line circular
-// correlation at positions [n_line - 1, 2 n_line - 1) when N >= 2 n_line - 1 (see the plan).
+// PAD: lines of n_line < N samples (any length): each is extended periodically by skip samples
+// and zero-padded to N; with the plan's filter (the N-point spectrum of the reversed, conjugated
+// replica of skip + 1 samples) the N-point circular convolution holds the length-n_line circular
+// correlation at positions [skip, skip + n_line), exactly when N >= n_line + skip.
 template <int N, bool PF, int SAUX, bool PAD = false>
 __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     k_range_compress_pf(const float2* in, float2* out, const float2* __restrict__ H,
-                        const float2* __restrict__ tw, int64_t lines, int n_line) {
+                        const float2* __restrict__ tw, int64_t lines, int n_line, int skip) {
   using C = LineCfg<N>;
   using L = typename C::Fwd;
   static_assert(std::is_same<typename C::Fwd, typename C::Inv>::value, "needs Fwd == Inv");
@@ -166,7 +168,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   // the table reads instead of following them.
   float2 nxt[C::P];
   if constexpr (PF)
-    rc_load<N, PAD>(nxt, in, int64_t(blockIdx.x) * C::LPW, lines, grp, tid, n_line);
+    rc_load<N, PAD>(nxt, in, int64_t(blockIdx.x) * C::LPW, lines, grp, tid, n_line, skip);
   TC twc;
   twc.load_all(tw, lds + C::LPW * C::LDS, tid, threadIdx.x, C::WG);
   // (the first pass's barrier orders the LDS twiddle table before its first use, unless a line's
@@ -184,15 +186,15 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     if constexpr (PF) {
 #pragma unroll
       for (int i = 0; i < C::P; ++i) v[i] = nxt[i];
-      if constexpr (!LATE) rc_load<N, PAD>(nxt, in, l0 + stride, lines, grp, tid, n_line);
+      if constexpr (!LATE) rc_load<N, PAD>(nxt, in, l0 + stride, lines, grp, tid, n_line, skip);
     } else {
-      rc_load<N, PAD>(v, in, l0, lines, grp, tid, n_line);
+      rc_load<N, PAD>(v, in, l0, lines, grp, tid, n_line, skip);
     }
     PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
     filter_multiply<N>(v, h, opaque(H), tid);
-    if constexpr (LATE) rc_load<N, PAD>(nxt, in, l0 + stride, lines, grp, tid, n_line);
+    if constexpr (LATE) rc_load<N, PAD>(nxt, in, l0 + stride, lines, grp, tid, n_line, skip);
     PassesCached<N, T, +1, 1, L, C::WAVE>::run(v, my, twc, tid);
-    rc_store<N, PAD, SAUX>(v, out, l0, lines, grp, tid, n_line);
+    rc_store<N, PAD, SAUX>(v, out, l0, lines, grp, tid, n_line, skip);
     // Wait for the prefetch here, where the stores just issued are younger than it and need not
     // complete; a wait at the loop head would merge with the loop entry and drain the stores.
     if constexpr (PF) touch<C::P>(nxt);
@@ -798,15 +800,17 @@ hipError_t occupancy(int* rc, int* fft, int* azc) {
 template <int N>
 hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const float2* tw,
                         const float2* tab, int64_t lines, int grid, int cached, int n_line,
-                        hipStream_t s) {
+                        int skip, hipStream_t s) {
   constexpr bool PF = RD_RC_PREFETCH && LineCfg<N>::PF;
   const dim3 g(grid), b(LineCfg<N>::WG);
   if (n_line != N) {
-    if (n_line <= 0 || 2 * n_line - 1 > N) return hipErrorInvalidValue;
+    if (n_line <= 0 || skip < 0 || skip >= n_line || n_line + skip > N) return hipErrorInvalidValue;
     if (cached)
-      hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxCached, true>), g, b, 0, s, in, out, H, tw, lines, n_line);
+      hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxCached, true>), g, b, 0, s, in, out, H, tw, lines,
+                         n_line, skip);
     else
-      hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream, true>), g, b, 0, s, in, out, H, tw, lines, n_line);
+      hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream, true>), g, b, 0, s, in, out, H, tw, lines,
+                         n_line, skip);
     return hipGetLastError();
   }
   if constexpr (N == 4096 && RD_RC_4096) {
@@ -817,9 +821,9 @@ hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const fl
     return hipGetLastError();
   }
   if (cached)
-    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxCached>), g, b, 0, s, in, out, H, tw, lines, N);
+    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxCached>), g, b, 0, s, in, out, H, tw, lines, N, 0);
   else
-    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream>), g, b, 0, s, in, out, H, tw, lines, N);
+    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream>), g, b, 0, s, in, out, H, tw, lines, N, 0);
   return hipGetLastError();
 }
 

@@ -45,11 +45,12 @@ struct LineOps {
   // (cached: ordinary stores, for output that the next pass re-reads from the cache; else
   // non-temporal stores)
   // n_line: samples per line in memory; n_line == n is the transform itself, a shorter
-  // n_line (2 n_line - 1 <= n) is the zero-padded fast-convolution form (H is then the plan's
-  // padded filter and the output window starts at n_line - 1)
+  // n_line (skip < n_line, n_line + skip <= n) is the fast-convolution form: lines extended
+  // periodically by skip samples and zero-padded to n, H the plan's padded filter, and the
+  // output window [skip, skip + n_line)
   hipError_t (*range_compress_pf)(const float2* in, float2* out, const float2* H,
                                   const float2* tw, const float2* tab, int64_t lines, int grid,
-                                  int cached, int n_line, hipStream_t s);
+                                  int cached, int n_line, int skip, hipStream_t s);
   hipError_t (*occupancy_pf)(int* rc, int pad);
   // Per-thread constant table of the register-cached kernel (twiddles and filter in the order
   // each thread holds them, so that a workgroup loads it with contiguous wave accesses):

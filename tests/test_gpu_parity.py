@@ -140,21 +140,26 @@ def test_range_compression_every_length(torch_dev, rdf, n, lines):
     assert err <= STAGE_TOL
 
 
-@pytest.mark.parametrize("n", [1, 7, 127, 129, 1000, 1200, 1201, 2049, 3001, 4097, 5000, 8191])
+# (line length, replica length): padded transform lengths M = nextpow2(max(256, n + L - 1))
+# 256, 512, 1024, 2048, 4096, 8192, 16384, and replicas of one sample up to the whole line
+ANY_LENGTHS = [(1, 1), (7, 7), (127, 42), (129, 43), (300, 100), (700, 233), (1000, 333),
+               (1200, 400), (1201, 1201), (2049, 683), (3001, 1000), (4097, 1365), (5000, 1666),
+               (8191, 2730), (8191, 8191)]
+
+
+@pytest.mark.parametrize("n,L", ANY_LENGTHS, ids=lambda v: str(v))
 @pytest.mark.parametrize("lines", [1, 37])
-def test_range_compression_any_length(torch_dev, rdf, n, lines):
-    """Line lengths with no built transform (range-only plans): the zero-padded convolution of
-    the smallest power of two >= 2n - 1 against the oracle's length-n circular correlation, with
-    replicas from one sample to a third of the line, in place bit-identical to out of place."""
+def test_range_compression_any_length(torch_dev, rdf, n, L, lines):
+    """Line lengths with no built transform (range-only plans): the zero-padded convolution
+    against the oracle's length-n circular correlation, in place bit-identical to out of place."""
     torch = torch_dev
-    rng = np.random.default_rng(2000 + n + lines)
+    rng = np.random.default_rng(2000 + n + L + lines)
     fs = 120e6
-    L = max(1, n // 3) if n != 7 else 7          # n = 7: replica as long as the line
     params = dict(Na=lines, Nr=n, pulse_s=L / fs, bandwidth_hz=90e6, fs_hz=fs,
                   range_window=int(n % 2 == 0))
     assert O.replica_length(params) == L
     echo = (rng.standard_normal((lines, n)) + 1j * rng.standard_normal((lines, n))).astype(np.complex64)
-    log(f"[range] any length: n={n} lines={lines}")
+    log(f"[range] any length: n={n} L={L} lines={lines}")
     with rdf.Plan(**params) as plan:
         x = dev(torch, echo)
         rc = plan.range_compress(x).cpu().numpy()
@@ -162,7 +167,7 @@ def test_range_compression_any_length(torch_dev, rdf, n, lines):
         torch.cuda.synchronize()
         assert np.array_equal(x.cpu().numpy(), rc)
     err = M.rel_l2(rc, O.range_compress(echo, params))
-    log(f"[range] n={n} lines={lines} rel-L2 {err:.2e}")
+    log(f"[range] n={n} L={L} lines={lines} rel-L2 {err:.2e}")
     assert err <= STAGE_TOL
 
 
