@@ -299,3 +299,83 @@ def backproject_pixels(rc: np.ndarray, params, grid, pix) -> np.ndarray:
     for k, (i, j) in enumerate(pix):
         out[k] = backproject(rc, params, dict(sub, x0_m=x[i], r0_m=r[j]))[0, 0]
     return out
+
+
+# ----------------------------------------------------------------------------------------------
+# omega-k (wavenumber-domain) focusing: [SAR-GPU] §3 (Stolt interpolation makes the migration
+# correction a frequency-domain operation; forward range and azimuth transforms, the inverse
+# transforms, and two large complex multiplies), §3.2 (a phase compensation built from the range
+# and Doppler frequencies), §3.3 (the Doppler band sets the extent of the mapping).
+# Readings (the page gives the steps without their formulas; these are the zero-squint
+# textbook forms in the notation of this module):
+#   * the input is the raw echo; the range matched filter H is one of the two multiplies, the
+#     reference function the other, both on the 2-D spectrum;
+#   * reference range Rref = R(ref_bin) for an integer range bin, so that the two linear phase
+#     terms below are exact roots of unity;
+#   * the Stolt interpolator is the RCMC one (8-tap Kaiser-windowed sinc, normalised weights),
+#     run along range frequency in natural (centred) order, zero outside the sampled band;
+#   * after the mapping, exp(-j 2 pi f' 2 (Rref - range_bin0) / c) puts the image on the RD grid
+#     (bin n at R(n), row m at pulse m), so the two methods can be compared pixel by pixel.
+# ----------------------------------------------------------------------------------------------
+def range_freqs(params) -> np.ndarray:
+    """Baseband range frequency of range-FFT bin j (NumPy fftfreq order), Hz."""
+    return np.fft.fftfreq(_p(params, "Nr"), 1.0 / _p(params, "fs_hz"))
+
+
+def doppler_wavenumber_sq(params) -> np.ndarray:
+    """b_k^2 = (c f_k / (2 V))^2 per Doppler bin k (Hz^2): the azimuth part of the 2-D
+    wavenumber, written as a frequency."""
+    return (C_LIGHT * doppler_freqs(params) / (2.0 * _p(params, "velocity_mps"))) ** 2
+
+
+def reference_function(params, ref_bin: int) -> np.ndarray:
+    """RFM[k][j] = exp(+j 2 pi [ (2 Rref / c) Q(f_j, f_k) - f_j tau0 ]),
+    Q = sqrt((f0 + f_j)^2 - b_k^2), tau0 = 2 range_bin0 / c (the fast time of range sample 0).
+
+    A target at closest range R0 and pulse time eta0 carries, after range compression and the
+    2-D transform, the phase -2 pi [ (2 R0 / c) Q - f tau0 + f_k eta0 ] (stationary phase of
+    the hyperbolic history); the RFM removes it exactly at R0 = Rref."""
+    f0 = _p(params, "carrier_hz")
+    f = range_freqs(params)[None, :]
+    Q = np.sqrt((f0 + f) ** 2 - doppler_wavenumber_sq(params)[:, None])
+    r_ref = float(bin_range(params, ref_bin))
+    tau0 = 2.0 * _p(params, "range_bin0_m") / C_LIGHT
+    return np.exp(2j * np.pi * ((2.0 * r_ref / C_LIGHT) * Q - f * tau0))
+
+
+def stolt_shift(params) -> np.ndarray:
+    """delta[k][u] (range-frequency bins) for output bin u in natural order
+    (f'_u = (u - Nr/2) Fs / Nr): the Stolt mapping reads the input at the frequency f with
+    Q(f, f_k) = f0 + f', i.e. f = sqrt((f0 + f')^2 + b_k^2) - f0, so the source lies
+    delta = (sqrt((f0 + f')^2 + b_k^2) - (f0 + f')) Nr / Fs bins above the output."""
+    Nr, fs, f0 = _p(params, "Nr"), _p(params, "fs_hz"), _p(params, "carrier_hz")
+    fp = (np.arange(Nr) - Nr // 2) * (fs / Nr)
+    a = f0 + fp[None, :]
+    return (np.sqrt(a * a + doppler_wavenumber_sq(params)[:, None]) - a) * (Nr / fs)
+
+
+def omega_k_stages(echo: np.ndarray, params, ref_bin: int) -> dict:
+    """Every intermediate of omega-k focusing, [Na][Nr] (rows = pulses or Doppler bins).
+
+    spec  : S[k][j] = 2-D DFT of the echo (range then azimuth), range bins in FFT order
+    rfm   : S H[j] RFM[k][j]                       (the two multiplies)
+    stolt : interpolated at f' in natural order, times exp(-j 2 pi f' 2 (Rref - range_bin0)/c),
+            returned in FFT order
+    img   : inverse 2-D DFT (1/(Na Nr))"""
+    Nr = _p(params, "Nr")
+    x = np.asarray(echo, dtype=np.complex128)
+    spec = np.fft.fft(np.fft.fft(x, axis=1), axis=0)
+    rfm = spec * matched_filter(params)[None, :] * reference_function(params, ref_bin)
+    centred = np.fft.fftshift(rfm, axes=1)
+    T = rcmc(centred, stolt_shift(params), _p(params, "rcmc_taps"), _p(params, "kaiser_beta"))
+    fp = (np.arange(Nr) - Nr // 2) * (_p(params, "fs_hz") / Nr)
+    shift_m = float(bin_range(params, ref_bin)) - _p(params, "range_bin0_m")
+    T = T * np.exp(-2j * np.pi * fp * (2.0 * shift_m / C_LIGHT))[None, :]
+    stolt = np.fft.ifftshift(T, axes=1)
+    img = np.fft.ifft(np.fft.ifft(stolt, axis=1), axis=0)
+    return {"spec": spec, "rfm": rfm, "stolt": stolt, "img": img}
+
+
+def omega_k(echo: np.ndarray, params, ref_bin: int) -> np.ndarray:
+    """Focused complex image [Na][Nr] by omega-k with Stolt interpolation."""
+    return omega_k_stages(echo, params, ref_bin)["img"]
