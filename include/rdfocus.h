@@ -93,9 +93,12 @@ typedef struct rd_plan rd_plan;
 
 /* Returns 1 if `n` is a transform length the library builds (256..16384 powers of two, and
  * 6000 = 2^4 * 3 * 5^3), else 0.  Range-only plans also accept any other Nr in 1..8192 (range
- * compression then runs as a zero-padded convolution, see rd_range_compress).  Full-chain plans also need Na a power of two in
- * [256, 16384], Na*Nr*8 < 4 GiB, and a range migration R(n)(1/D_k - 1)/dr below Nr/8 - 5
- * samples over the whole Doppler band (checked by rd_plan_create). */
+ * compression then runs as a zero-padded convolution, see rd_range_compress).  Full-chain
+ * plans also need Na a power of two in [256, 16384] and Na*Nr*8 < 4 GiB (checked by
+ * rd_plan_create).  The range-Doppler entry points (rd_azimuth_focus, rd_focus and the stage
+ * hook) further need a range migration R(n)(1/D_k - 1)/dr below Nr/8 - 5 samples over the
+ * whole Doppler band; beyond it they return RD_ERR_UNSUPPORTED_LENGTH, while the plan still
+ * serves rd_omega_k and rd_backproject. */
 int rd_length_supported(int32_t n);
 
 /* Validates `params`, builds the matched filter H (float64 -> float32), the twiddle and
@@ -133,6 +136,25 @@ rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* s
 /* rd_range_compress followed by rd_azimuth_focus: raw echo to focused image.  echo == img is
  * allowed.  RD_ERR_NOT_CONFIGURED on a range-only plan. */
 rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream);
+
+/* omega-k focusing with Stolt interpolation (nxmr.cn/news/101525 §3: the migration correction
+ * becomes a frequency-domain mapping; forward and inverse 2-D transforms and two large complex
+ * multiplies; §3.2: a phase built from the range and Doppler frequencies).  Raw echo [Na][Nr]
+ * to image [Na][Nr] on the same grid as rd_focus (row m = pulse m, bin n at R(n)):
+ *   S[k][j]  = 2-D DFT of echo (range bin j, Doppler bin k, FFT order)
+ *   S       *= H[j] exp(+j 2 pi [(2 Rref / c) Q(f_j, f_k) - f_j tau0]),
+ *              Q = sqrt((f0 + f_j)^2 - (c f_k / (2V))^2), tau0 = 2 range_bin0 / c,
+ *              Rref = R(ref_bin) (the reference range)
+ *   T[k][f'] = S[k] read at f = sqrt((f0 + f')^2 + (c f_k / (2V))^2) - f0 (Stolt mapping) with
+ *              the 8-tap Kaiser(kaiser_beta)-windowed sinc of the RCMC, normalised weights,
+ *              zero outside the sampled band [-Fs/2, Fs/2)
+ *   T       *= exp(-j 2 pi f' 2 (Rref - range_bin0) / c);  img = inverse 2-D DFT (1/(Na Nr)).
+ * Device work: azimuth transform steps, one fused kernel per Doppler row (range FFT, multiply,
+ * Stolt mapping from LDS, range IFFT), inverse azimuth steps; echo == img allowed.
+ * RD_ERR_NOT_CONFIGURED on a range-only plan; RD_ERR_INVALID_ARG if ref_bin is outside
+ * [0, Nr) or f0 - Fs/2 <= c PRF / (4 V); RD_ERR_UNSUPPORTED_LENGTH if the largest Stolt shift
+ * (at f' = -Fs/2 and the Doppler band edge) plus 5 samples exceeds Nr/2 (Nr/8 at 16384). */
+rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref_bin, void* stream);
 
 /* Test hook: the azimuth chain with its intermediates exposed.  azfft and rcmc receive the
  * azimuth spectrum S[k][n] and the RCMC output T[k][n], [Na][Nr] with row k = Doppler bin in

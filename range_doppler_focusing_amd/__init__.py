@@ -10,7 +10,7 @@ from __future__ import annotations
 from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
                       make_bp_grid, make_params, rd_azimuth_focus, rd_backproject, rd_bp_grid,
                       rd_corner_turn, rd_debug_azimuth_stages, rd_debug_line_fft,
-                      rd_focus, rd_last_error, rd_length_supported, rd_params, rd_plan_create,
+                      rd_focus, rd_last_error, rd_length_supported, rd_omega_k, rd_params, rd_plan_create,
                       rd_plan_destroy, rd_range_compress, rd_status_string)
 
 
@@ -83,6 +83,13 @@ class Plan:
         img = self._empty((self.Na, self.Nr))
         rd_debug_azimuth_stages(self.handle, rc, az, rcmc, img)
         return az, rcmc, img
+
+    def omega_k(self, echo, ref_bin: int, out=None):
+        """omega-k image [Na][Nr] of the raw echo with reference range R(ref_bin) (rd_omega_k)."""
+        self._check(echo, (self.Na, self.Nr))
+        out = self._empty((self.Na, self.Nr)) if out is None else self._check(out, (self.Na, self.Nr))
+        rd_omega_k(self.handle, echo, out, ref_bin)
+        return out
 
     def backproject(self, rc, grid: dict, out=None):
         """Back-projection image [nx][ny] of range-compressed data rc [Na][Nr] (rd_backproject)."""

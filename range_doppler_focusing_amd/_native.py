@@ -26,7 +26,7 @@ RD_WINDOW_HAMMING = 1
 # every symbol the header declares
 EXPORTS = ("rd_length_supported", "rd_plan_create", "rd_plan_destroy", "rd_range_compress",
            "rd_azimuth_focus", "rd_focus", "rd_debug_azimuth_stages", "rd_debug_line_fft",
-           "rd_backproject", "rd_corner_turn", "rd_status_string", "rd_last_error")
+           "rd_backproject", "rd_corner_turn", "rd_omega_k", "rd_status_string", "rd_last_error")
 
 
 class rd_params(ctypes.Structure):
@@ -93,6 +93,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rd_debug_line_fft.restype = ctypes.c_int
     lib.rd_backproject.argtypes = [vp, vp, vp, ctypes.POINTER(rd_bp_grid), vp]
     lib.rd_backproject.restype = ctypes.c_int
+    lib.rd_omega_k.argtypes = [vp, vp, vp, i32, vp]
+    lib.rd_omega_k.restype = ctypes.c_int
     lib.rd_corner_turn.argtypes = [vp, vp, i64, i64, vp]
     lib.rd_corner_turn.restype = ctypes.c_int
     lib.rd_status_string.argtypes = [ctypes.c_int]
@@ -202,6 +204,11 @@ def rd_backproject(plan: int, rc, img, grid, stream=None) -> None:
     _check(load_library().rd_backproject(plan, _addr(rc), _addr(img), ctypes.byref(grid) if grid is not None else None,
                                          _stream(stream, rc, img)),
            "rd_backproject")
+
+
+def rd_omega_k(plan: int, echo, img, ref_bin: int, stream=None) -> None:
+    _check(load_library().rd_omega_k(plan, _addr(echo), _addr(img), int(ref_bin), _stream(stream, echo, img)),
+           "rd_omega_k")
 
 
 def rd_corner_turn(x, y, rows: int, cols: int, stream=None) -> None:

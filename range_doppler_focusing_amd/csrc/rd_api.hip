@@ -63,6 +63,9 @@ struct rd_plan {
   double* rowc = nullptr;    // [Na][4] RCMC shift and filter phase coefficients per Doppler bin
   float2* work = nullptr;    // [Na * Nr] workspace (stage test hook only, allocated on first use)
   rdf::AzRowConst az{};
+  double rd_max_shift = 0.0;  // largest RCMC shift (samples); must stay below margin - 5
+  int wk_halo = -1;     // omega-k: zero samples staged after a row (-1: geometry not supported)
+  int wk_grid = 0;      // omega-k row-stage grid
 };
 
 namespace {
@@ -349,6 +352,14 @@ rd_status run_rows(rd_plan* P, const float2* src, float2* dst, bool filter, hipS
   return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, P->cached, s), "RCMC launch");
 }
 
+rd_status check_rcmc_margin(const rd_plan* P) {
+  if (std::floor(P->rd_max_shift) + 5 > double(P->rops->margin))
+    return fail(RD_ERR_UNSUPPORTED_LENGTH,
+                "range migration of %.1f samples exceeds the %d-sample margin built for Nr=%d",
+                P->rd_max_shift, P->rops->margin - 5, P->p.Nr);
+  return RD_OK;
+}
+
 rd_status run_azimuth(rd_plan* P, const float2* rc, float2* img, hipStream_t s) {
   // rc is read only by the first step, so img may alias it
   rd_status st;
@@ -516,11 +527,24 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     }
     // taps reach floor(shift) + 4 samples past the output (one more for rounding differences
     // between this bound and the kernel's float64 shift)
-    if (std::floor(max_shift) + 5 > double(rops->margin))
-      return bail(fail(RD_ERR_UNSUPPORTED_LENGTH,
-                       "range migration of %.1f samples exceeds the %d-sample margin built for Nr=%d",
-                       max_shift, rops->margin - 5, p.Nr));
-    P->az.halo = int(std::floor(max_shift)) + 5;
+    // (a plan whose migration exceeds the RCMC margin still serves omega-k and back-projection;
+    // the range-Doppler entry points report it)
+    P->rd_max_shift = max_shift;
+    P->az.halo = std::min(int(std::floor(max_shift)) + 5, rops->margin);
+    // omega-k: the Stolt shift (sqrt(a^2 + b^2) - a) / df is largest at the lowest range
+    // frequency a = f0 - Fs/2 and the Doppler band edge b = c PRF / (4 V); the mapping needs
+    // a > b there (a real wavenumber at every sample)
+    {
+      const double df = p.fs_hz / p.Nr;
+      const double amin = p.carrier_hz - double(p.Nr / 2) * df;
+      const double bmax = kC * p.prf_hz / (4.0 * p.velocity_mps);
+      if (rops->omega_k_rows && amin > bmax) {
+        P->wk_halo = int(std::floor((std::sqrt(amin * amin + bmax * bmax) - amin) / df)) + 5;
+        int occ = 0;
+        if (rops->occupancy_wk(&occ) != hipSuccess) return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
+        P->wk_grid = persistent_grid(occ, P->cus, Na, rops->lpw);
+      }
+    }
     if ((st = upload(&P->tw_A, roots_table(P->A), "azimuth step twiddles")) != RD_OK) return bail(st);
     if ((st = upload(&P->tw_B, roots_table(P->B), "azimuth step twiddles")) != RD_OK) return bail(st);
     if ((st = upload(&P->rowc, rowc, "azimuth row coefficients")) != RD_OK) return bail(st);
@@ -567,6 +591,7 @@ rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* s
   rd_status st = check_call(plan);
   if (st != RD_OK) return st;
   if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if ((st = check_rcmc_margin(plan)) != RD_OK) return st;
   if (!aligned8(rc) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "rc and img must be non-NULL and 8-byte aligned");
   const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
   if (partial_overlap(rc, img, bytes)) return fail(RD_ERR_INVALID_ARG, "rc and img overlap without being equal");
@@ -578,6 +603,7 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
   rd_status st = check_call(plan);
   if (st != RD_OK) return st;
   if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if ((st = check_rcmc_margin(plan)) != RD_OK) return st;
   if (!aligned8(echo) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "echo and img must be non-NULL and 8-byte aligned");
   const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
   if (partial_overlap(echo, img, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and img overlap without being equal");
@@ -588,11 +614,55 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
   return run_azimuth(plan, I, I, s);
 }
 
+rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref_bin, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  const rd_params& p = plan->p;
+  if (ref_bin < 0 || ref_bin >= p.Nr) return fail(RD_ERR_INVALID_ARG, "ref_bin=%d must be in [0, Nr=%d)", ref_bin, p.Nr);
+  if (!plan->rops->omega_k_rows) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no omega-k row stage for Nr=%d", p.Nr);
+  if (plan->wk_halo < 0)
+    return fail(RD_ERR_INVALID_ARG, "f0 - Fs/2 must exceed c PRF / (4 V) for the Stolt mapping");
+  if (plan->wk_halo > plan->rops->wk_cap)
+    return fail(RD_ERR_UNSUPPORTED_LENGTH, "Stolt shift of %d samples exceeds the %d-sample margin built for Nr=%d",
+                plan->wk_halo - 5, plan->rops->wk_cap - 5, p.Nr);
+  if (!aligned8(echo) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "echo and img must be non-NULL and 8-byte aligned");
+  const size_t bytes = size_t(p.Na) * p.Nr * sizeof(rd_c64);
+  if (partial_overlap(echo, img, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and img overlap without being equal");
+  rdf::OkConst c{};
+  c.f0 = p.carrier_hz;
+  c.df = p.fs_hz / p.Nr;
+  c.inv_df = p.Nr / p.fs_hz;
+  c.bstep = kC * p.prf_hz / (2.0 * p.velocity_mps * p.Na);
+  const double r_ref = p.range_bin0_m + ref_bin * plan->dr;
+  c.k1 = 2.0 * r_ref / kC;
+  const double turns = c.k1 * p.carrier_hz;
+  c.k0 = turns - std::floor(turns);
+  c.ref = ref_bin;
+  c.A = plan->A;
+  c.B = plan->B;
+  c.halo = plan->wk_halo;
+  c.inv_na = float(1.0 / double(p.Na));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* I = reinterpret_cast<float2*>(img);
+  // the azimuth transform first (the 2-D transform's order is free), then one row stage per
+  // Doppler row, then the inverse azimuth transform; echo is read only by the first step
+  if ((st = run_col(plan, reinterpret_cast<const float2*>(echo), I, true, true, s)) != RD_OK) return st;
+  if ((st = run_col(plan, I, I, true, false, s)) != RD_OK) return st;
+  if ((st = check_hip(plan->rops->omega_k_rows(I, I, plan->H, plan->tw_r, c, plan->az.w, p.Na, plan->wk_grid,
+                                               plan->cached, s),
+                      "omega-k row stage launch")) != RD_OK)
+    return st;
+  if ((st = run_col(plan, I, I, false, false, s)) != RD_OK) return st;
+  return run_col(plan, I, I, false, true, s);
+}
+
 rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft, rd_c64* rcmc,
                                   rd_c64* img, void* stream) {
   rd_status st = check_call(plan);
   if (st != RD_OK) return st;
   if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if ((st = check_rcmc_margin(plan)) != RD_OK) return st;
   if (!aligned8(rc) || !aligned8(azfft) || !aligned8(rcmc) || !aligned8(img))
     return fail(RD_ERR_INVALID_ARG, "all buffers must be non-NULL and 8-byte aligned");
   const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);

@@ -576,6 +576,174 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
 }
 
 // ------------------------------------------------------------------------------------------
+// omega-k row stage (nxmr.cn/news/101525 §3, §3.2): one workgroup group per Doppler row of the
+// azimuth-transformed echo.  The row is read rotated by the reference bin, transformed along
+// range in registers, multiplied by H times the reference function, staged in LDS in centred
+// frequency order, read back through the Stolt mapping with the 8-tap interpolator, inverse
+// transformed, and stored rotated back.  The two rotations are the exact forms of the linear
+// phase terms exp(+-j 2 pi f 2 (Rref - range_bin0) / c) of the reference function and of the
+// registration that follows the mapping (f 2 (Rref - range_bin0) / c = js ref / Nr).
+template <int N>
+struct OkRow {
+  using C = LineCfg<N>;
+  static constexpr int CAP = N >= 16384 ? N / 8 : N / 2;  // zero samples staged after a row
+  static constexpr int STG = 3 + N + CAP;                  // staging: 3 zeros, the row, CAP zeros
+  static constexpr int REG = C::LDS > STG ? C::LDS : STG;  // per line: transform scratch / staging
+};
+
+// line I/O rotated by rot (0 <= rot < N): slot e of the line holds sample (e + rot) mod N
+template <int N, int T, int R, int AUX>
+__device__ __forceinline__ void load_line_rot(float2* v, const LineIO& io, int elem0, int tid, int rot) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int r = dft_input_order<R>(i);
+        int e = j + r * G::NB + rot;
+        e -= e >= N ? N : 0;
+        v[b * R + r] = __builtin_bit_cast(
+            float2, __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, uint32_t(elem0 + e) * 8u, 0, AUX));
+      }
+    }
+  }
+}
+template <int N, int T, int R, int AUX>
+__device__ __forceinline__ void store_line_rot(const float2* v, const LineIO& io, int elem0, int tid, int rot) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        int e = j + r * G::NB + rot;
+        e -= e >= N ? N : 0;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, v[b * R + r]), io.rsrc,
+                                              uint32_t(elem0 + e) * 8u, 0, AUX);
+      }
+    }
+  }
+}
+
+template <int N, int AUX>
+__global__ void __launch_bounds__(LineCfg<N>::WG)
+    k_omega_k_row(const float2* in, float2* out, const float2* __restrict__ H,
+                  const float2* __restrict__ tw, OkConst c, RcmcPoly w, int64_t rows) {
+  using C = LineCfg<N>;
+  using L = typename C::Fwd;
+  static_assert(std::is_same<typename C::Fwd, typename C::Inv>::value, "needs Fwd == Inv");
+  constexpr int T = C::T;
+  constexpr int R0 = ListInfo<L>::first;
+  static_assert(R0 == ListInfo<L>::last, "palindromic radix list: spectrum layout = inverse input layout");
+  using G = Geom<N, T, R0>;
+  using TC = TwCache<N, T, 1, L>;
+  constexpr int REG = OkRow<N>::REG;
+  __shared__ float2 lds[C::LPW * REG + (TC::LDS > 0 ? TC::LDS : 1)];
+  const int grp = threadIdx.x / T;
+  const int tid = threadIdx.x - grp * T;
+  float2* my = lds + grp * REG;
+  TC twc;
+  twc.load_all(tw, lds + C::LPW * REG, tid, threadIdx.x, C::WG);
+  if constexpr (C::WAVE && TC::LDS > 0) __syncthreads();
+  twc.touch_all();
+  const int na = c.A * c.B;
+  for (int64_t l0 = int64_t(blockIdx.x) * C::LPW; l0 < rows; l0 += int64_t(gridDim.x) * C::LPW) {
+    const int64_t row = l0 + grp < rows ? l0 + grp : rows - 1;  // lines past the end: loads read
+                                                                 // zero, stores are dropped
+    const int k = int(row / c.B) + c.A * int(row % c.B);
+    const double b = double(2 * k < na ? k : k - na) * c.bstep;
+    const double b2 = b * b;
+    float2 v[C::P];
+    const LineIO io_in(in, N, l0, C::LPW, rows);
+    load_line_rot<N, T, R0, AUX>(v, io_in, grp * N, tid, c.ref);
+    PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
+    // v = X[kx] H[kx] exp(j 2 pi (k0 - k1 (a - Q))) / Na at range bin kx = j + r NB,
+    // a = f0 + js df, Q = sqrt(a^2 - b^2) (float64: the phase reaches ~1e4 turns)
+#pragma unroll
+    for (int bb = 0; bb < G::B; ++bb) {
+      const int j = tid + bb * T;
+      if (G::live(j)) {
+#pragma unroll
+        for (int r = 0; r < R0; ++r) {
+          const int kx = j + r * G::NB;
+          const int js = 2 * kx < N ? kx : kx - N;
+          const double a = c.f0 + double(js) * c.df;
+          const double q = sqrt(fma(a, a, -b2));
+          double t = fma(-c.k1, a - q, c.k0);
+          t -= rint(t);
+          float sn, cs;
+          sincospif(2.0f * float(t), &sn, &cs);
+          const float2 h = H[kx];
+          const float2 z = make_float2((h.x * cs - h.y * sn) * c.inv_na, (h.x * sn + h.y * cs) * c.inv_na);
+          v[bb * R0 + r] = cmul(v[bb * R0 + r], z);
+        }
+      }
+    }
+    __syncthreads();  // the forward transform's last reads of this line's scratch are done
+    // staging: my[3 + u] = spectrum at centred position u = (kx + N/2) mod N, zero around it
+#pragma unroll
+    for (int bb = 0; bb < G::B; ++bb) {
+      const int j = tid + bb * T;
+      if (G::live(j)) {
+#pragma unroll
+        for (int r = 0; r < R0; ++r) {
+          int u = j + r * G::NB + N / 2;
+          u -= u >= N ? N : 0;
+          my[3 + u] = v[bb * R0 + r];
+        }
+      }
+    }
+    if (tid < 3) my[tid] = make_float2(0.f, 0.f);
+    for (int i = tid; i < c.halo; i += T) my[3 + N + i] = make_float2(0.f, 0.f);
+    __syncthreads();
+    // Stolt mapping: output at centred position u reads the staged spectrum at
+    // x = u + (sqrt(a'^2 + b^2) - a') / df, a' = f0 + (u - N/2) df; x >= u and x <= N - 1 + halo - 5
+#pragma unroll
+    for (int bb = 0; bb < G::B; ++bb) {
+      const int j = tid + bb * T;
+      if (G::live(j)) {
+#pragma unroll
+        for (int r = 0; r < R0; ++r) {
+          int u = j + r * G::NB + N / 2;
+          u -= u >= N ? N : 0;
+          const double a = c.f0 + double(u - N / 2) * c.df;
+          const double x = double(u) + (sqrt(fma(a, a, b2)) - a) * c.inv_df;
+          const double fl = floor(x);
+          const float xf = float(x - fl) - 0.5f;
+          const float y = xf * xf;
+          const float2* tap = my + int(fl);  // tap t reads centred sample fl + t - 3
+          float2 acc = make_float2(0.f, 0.f);
+          float es = 0.f;
+#pragma unroll
+          for (int q = 0; q < kRcmcTaps / 2; ++q) {
+            float e = w.even[q][kRcmcDeg / 2];
+#pragma unroll
+            for (int mm = kRcmcDeg / 2 - 1; mm >= 0; --mm) e = fmaf(e, y, w.even[q][mm]);
+            float o = w.odd[q][kRcmcDeg / 2 - 1];
+#pragma unroll
+            for (int mm = kRcmcDeg / 2 - 2; mm >= 0; --mm) o = fmaf(o, y, w.odd[q][mm]);
+            const float wa = fmaf(xf, o, e);
+            const float wb = fmaf(-xf, o, e);
+            const float2 sa = tap[3 - q], sb = tap[4 + q];
+            acc.x = fmaf(wa, sa.x, fmaf(wb, sb.x, acc.x));
+            acc.y = fmaf(wa, sa.y, fmaf(wb, sb.y, acc.y));
+            es += e;
+          }
+          const float sc = 0.5f * __builtin_amdgcn_rcpf(es);
+          v[bb * R0 + r] = make_float2(acc.x * sc, acc.y * sc);
+        }
+      }
+    }
+    // (the inverse transform's first exchange begins with a barrier: the staging reads are done)
+    PassesCached<N, T, +1, 1, L, C::WAVE>::run(v, my, twc, tid);
+    store_line_rot<N, T, R0, AUX>(v, LineIO(out, N, l0, C::LPW, rows), grp * N, tid, c.ref);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Corner turn out[c][r] = in[r][c] of a row-major [rows][cols] complex array (the transpose
 // between range lines and azimuth lines in cf-1.com/news/2323550 §5.1-§5.2 and the padded
 // shared-memory tiles of nxmr.cn/news/101525 §2.2.1).  A workgroup moves one 64 x 64 tile:
@@ -851,6 +1019,27 @@ hipError_t launch_rcmc_mf(const float2* in, float2* out, const AzRowConst& c, in
 }
 
 template <int N>
+hipError_t launch_omega_k_rows(const float2* in, float2* out, const float2* H, const float2* tw,
+                               const OkConst& c, const RcmcPoly& w, int64_t rows, int grid,
+                               int cached, hipStream_t s) {
+  if (c.halo < 0 || c.halo > OkRow<N>::CAP || c.ref < 0 || c.ref >= N) return hipErrorInvalidValue;
+  const int64_t wgs = (rows + LineCfg<N>::LPW - 1) / LineCfg<N>::LPW;
+  if (grid <= 0 || grid > wgs) grid = int(wgs);
+  if (cached)
+    hipLaunchKernelGGL((k_omega_k_row<N, kAuxCached>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, H, tw,
+                       c, w, rows);
+  else
+    hipLaunchKernelGGL((k_omega_k_row<N, kAuxStream>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, H, tw,
+                       c, w, rows);
+  return hipGetLastError();
+}
+
+template <int N>
+hipError_t occupancy_wk(int* wgs) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(wgs, k_omega_k_row<N, kAuxCached>, LineCfg<N>::WG, 0);
+}
+
+template <int N>
 int rc_tab_len() {
   if constexpr (N == 4096 && RD_RC_4096) return kRc4096Tab;
   return 0;
@@ -866,11 +1055,12 @@ constexpr LineOps make_ops() {
   if constexpr (sym) {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
                    &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>, &rc_tab_len<N>,
-                   &rc_tab_fill<N>, &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
+                   &rc_tab_fill<N>, &launch_rcmc_mf<N>, RowStage<N>::MARGIN,
+                   &launch_omega_k_rows<N>, &occupancy_wk<N>, OkRow<N>::CAP};
   } else {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
                    &occupancy<N>, nullptr, nullptr, &rc_tab_len<N>, &rc_tab_fill<N>,
-                   &launch_rcmc_mf<N>, RowStage<N>::MARGIN};
+                   &launch_rcmc_mf<N>, RowStage<N>::MARGIN, nullptr, nullptr, 0};
   }
 }
 

@@ -30,6 +30,22 @@ struct AzRowConst {
   RcmcPoly w;
 };
 
+// omega-k: range FFT, range filter x reference function, Stolt interpolation and range IFFT of
+// one Doppler row (the row's azimuth transform done before, its inverse after).  Frequencies
+// in Hz, times in s; range bin js (signed, FFT order) lies at js df.
+struct OkConst {
+  double f0;      // carrier
+  double df;      // range-frequency bin spacing Fs / Nr
+  double inv_df;  // Nr / Fs
+  double bstep;   // c PRF / (2 V Na): Doppler bin kk (signed) has b = kk bstep
+  double k1;      // 2 Rref / c
+  double k0;      // fractional part of 2 Rref f0 / c (turns)
+  int ref;        // reference range bin: the line is read rotated by ref and stored back
+  int A, B;       // Na = A B; row r holds Doppler bin (r / B) + A (r % B)
+  int halo;       // zero samples staged after the row: floor(max Stolt shift) + 5 <= wk_cap
+  float inv_na;   // 1 / Na (the inverse azimuth transform's scale)
+};
+
 struct LineOps {
   int n;       // transform length
   int wg;      // threads per workgroup
@@ -64,6 +80,13 @@ struct LineOps {
   hipError_t (*rcmc_mf)(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
                         int grid, int cached, hipStream_t s);
   int margin;
+  // omega-k row stage over `rows` Doppler rows (in == out allowed); wk_cap = the largest halo
+  // the kernel stages, occupancy_wk = its workgroups per CU
+  hipError_t (*omega_k_rows)(const float2* in, float2* out, const float2* H, const float2* tw,
+                             const OkConst& c, const RcmcPoly& w, int64_t rows, int grid,
+                             int cached, hipStream_t s);
+  hipError_t (*occupancy_wk)(int* wgs);
+  int wk_cap;
 };
 
 // nullptr if the length has no built transform

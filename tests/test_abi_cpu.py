@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     import range_doppler_focusing_amd as rdf
     lib = rdf.load_library()
     declared = header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 13
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(rdf.EXPORTS) == declared
@@ -141,3 +141,4 @@ def test_backproject_rejects_a_null_plan_before_any_launch():
     lib = rdf.load_library()
     g = rdf.make_bp_grid(nx=4, ny=4, x0_m=0.0, dx_m=1.0, r0_m=1000.0, dr_m=1.0)
     assert lib.rd_backproject(None, 1 << 20, 1 << 30, ctypes.byref(g), None) == -1
+    assert lib.rd_omega_k(None, 1 << 20, 1 << 30, 0, None) == -1
