@@ -163,7 +163,7 @@ def main():
                     help="seconds of untimed running before each warm-up (0 for counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
-    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp", "pad"], default=None,
+    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp", "pad", "wk"], default=None,
                     help="run one workload only (for profiling)")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the 8192 x 6000 and 16384 x 16384 workloads")
@@ -232,6 +232,44 @@ def main():
         torch.cuda.empty_cache()
     px = fcfg.Na * fcfg.Nr
     mpx = px / (focus_ms * 1e-3) / 1e6 if focus_ms else None
+
+    # ---------------------------------------------------------------- omega-k
+    wk = None
+    if args.only in (None, "wk") and not args.no_focus:
+        wk = []
+        for wcfg, steps in ((fcfg, max(10, args.steps // 2)), (C5, 5)):
+            ref = int(round((wcfg.r_ref_m - wcfg.range_bin0_m) / wcfg.dr))
+            big = wcfg.Na * wcfg.Nr > 4096 * 4096
+            nrot = 1 if big else ROTATE
+            if big:
+                xs = [gpu_noise(torch, (wcfg.Na, wcfg.Nr), wcfg.seed)]
+            else:
+                x0 = torch.from_numpy(cached_scene(wcfg).echo).to("cuda")
+                xs = [x0] + [x0.clone() for _ in range(nrot - 1)]
+            ys = [torch.empty_like(xs[0]) for _ in range(nrot)]
+            wplan = rdf.Plan(**wcfg.plan_params())
+            ms = time_steps(torch, lambda i: rdf.rd_omega_k(wplan.handle, xs[i % nrot], ys[i % nrot], ref, stream),
+                            steps, 2, stream)
+            wplan.close()
+            del xs, ys
+            torch.cuda.empty_cache()
+            m = wcfg.Na * wcfg.Nr / (ms * 1e-3) / 1e6
+            rec = {"workload": f"omega-k focusing (rd_omega_k), {wcfg.Na} x {wcfg.Nr} complex64, reference bin {ref}",
+                   "ms_per_step": round(ms, 4), "steps": steps, "value": round(m, 1), "unit": "Mpixel/s",
+                   "roofline_frac_80B_per_px": round(m * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4),
+                   "data": "seeded complex Gaussian noise on the device" if big else
+                           "synthetic scene (seeded point targets + clutter)"}
+            if not big and not args.no_cpu and args.only is None:
+                # the oracle on the first 1024 pulses of the same geometry (a quarter of the scene)
+                from oracle import rd_oracle as O
+                sub = wcfg.with_(Na=1024)
+                t0 = time.perf_counter()
+                O.omega_k(cached_scene(wcfg).echo[:1024], sub.plan_params(), ref)
+                tw = time.perf_counter() - t0
+                rec["cpu_baseline"] = {"value": round(1024 * wcfg.Nr / tw / 1e6, 4), "unit": "Mpixel/s",
+                                       "cores": 1, "kind": "oracle",
+                                       "sample": f"1024 pulses x {wcfg.Nr} of the same geometry, one run ({tw:.1f} s)"}
+            wk.append(rec)
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -399,6 +437,7 @@ def main():
             "roofline_frac_32B_per_px": round(mpx * 1e6 * 32 / (HBM_PEAK_GBS * 1e9), 4),
             "stages": stage_ms,
             "cpu_baseline": cpu_focus},
+        "omega_k": wk,
         "other_workloads": large,
         "vendor_fft_comparison": vendor,
         "kernel_source_sha1": src_hash,

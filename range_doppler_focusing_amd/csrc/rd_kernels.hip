@@ -628,6 +628,19 @@ __device__ __forceinline__ void store_line_rot(const float2* v, const LineIO& io
   }
 }
 
+// sqrt of a positive normal double (the wavenumbers here are ~1e18..1e21 Hz^2): the hardware
+// reciprocal square root refined by one Newton-Raphson step in Goldschmidt form and a final
+// residual correction, which leaves an error of a few ulp (the library form adds range scaling
+// and special-case handling that these arguments never need).
+__device__ __forceinline__ double sqrt_pos(double x) {
+  const double y = __builtin_amdgcn_rsq(x);
+  double s = x * y, h = 0.5 * y;
+  const double e = fma(-h, s, 0.5);
+  s = fma(s, e, s);
+  h = fma(h, e, h);
+  return fma(fma(-s, s, x), h, s);
+}
+
 template <int N, int AUX>
 __global__ void __launch_bounds__(LineCfg<N>::WG)
     k_omega_k_row(const float2* in, float2* out, const float2* __restrict__ H,
@@ -671,11 +684,10 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
           const int kx = j + r * G::NB;
           const int js = 2 * kx < N ? kx : kx - N;
           const double a = c.f0 + double(js) * c.df;
-          const double q = sqrt(fma(a, a, -b2));
-          double t = fma(-c.k1, a - q, c.k0);
-          t -= rint(t);
-          float sn, cs;
-          sincospif(2.0f * float(t), &sn, &cs);
+          const double q = sqrt_pos(fma(a, a, -b2));
+          const double t = fma(-c.k1, a - q, c.k0);
+          const float f = float(t - floor(t));     // hardware sin/cos take turns
+          const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
           const float2 h = H[kx];
           const float2 z = make_float2((h.x * cs - h.y * sn) * c.inv_na, (h.x * sn + h.y * cs) * c.inv_na);
           v[bb * R0 + r] = cmul(v[bb * R0 + r], z);
@@ -710,7 +722,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
           int u = j + r * G::NB + N / 2;
           u -= u >= N ? N : 0;
           const double a = c.f0 + double(u - N / 2) * c.df;
-          const double x = double(u) + (sqrt(fma(a, a, b2)) - a) * c.inv_df;
+          const double x = double(u) + (sqrt_pos(fma(a, a, b2)) - a) * c.inv_df;
           const double fl = floor(x);
           const float xf = float(x - fl) - 0.5f;
           const float y = xf * xf;
