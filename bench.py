@@ -163,7 +163,7 @@ def main():
                     help="seconds of untimed running before each warm-up (0 for counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
-    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp", "pad", "wk"], default=None,
+    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp", "pad", "wk", "f16"], default=None,
                     help="run one workload only (for profiling)")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the 8192 x 6000 and 16384 x 16384 workloads")
@@ -313,6 +313,28 @@ def main():
                 rec.update({"value": round(m, 1), "unit": "Mpixel/s",
                             "roofline_frac_80B_per_px": round(m * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4)})
             large.append(rec)
+
+    # ---------------------------------------------------------------- binary16 storage
+    if (args.only in (None, "large", "f16")) and not args.no_large:
+        large = large or []
+        sc = cached_scene(cfg)
+        e16 = torch.from_numpy(sc.echo).to("cuda").view(torch.float32).to(torch.float16).view(cfg.Na, cfg.Nr, 2)
+        ins = [e16] + [e16.clone() for _ in range(ROTATE - 1)]
+        outs = [torch.empty_like(e16) for _ in range(ROTATE)]
+        plan = rdf.Plan(**cfg.plan_params())
+        ms = time_steps(torch, lambda i: rdf.rd_range_compress_f16(plan.handle, ins[i % ROTATE], outs[i % ROTATE], stream),
+                        args.steps, args.warmup, stream)
+        plan.close()
+        del ins, outs, e16
+        torch.cuda.empty_cache()
+        b16 = 2 * cfg.Na * cfg.Nr * 4
+        gbs = b16 / (ms * 1e-3) / 1e9
+        large.append({"workload": "range compression with binary16 storage (rd_range_compress_f16), "
+                                  f"{cfg.Na} x {cfg.Nr}, float32 arithmetic, same chirp as the headline",
+                      "ms_per_step": round(ms, 4), "steps": args.steps, "value": round(gbs, 1), "unit": "GB/s",
+                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "samples_per_s": round(cfg.Na * cfg.Nr / (ms * 1e-3), 1),
+                      "data": "the headline scene rounded to binary16"})
 
     # ---------------------------------------------------------------- a line length with no built transform
     if (args.only in (None, "large", "pad")) and not args.no_large:

@@ -49,6 +49,13 @@ typedef struct {
   float re, im;
 } rd_c64;
 
+/* Interleaved complex sample in IEEE 754 binary16 (half precision): the bit patterns of the
+ * real and imaginary parts, 4 bytes a sample (cf-1.com/news/2323550 §7: FP16 storage with FP32
+ * arithmetic). */
+typedef struct {
+  uint16_t re, im;
+} rd_c32h;
+
 typedef enum {
   RD_OK = 0,
   RD_ERR_INVALID_ARG = -1,        /* bad pointer, size, alignment, aliasing or parameter   */
@@ -123,6 +130,16 @@ rd_status rd_plan_destroy(rd_plan* plan);
  * spectrum by the M-point spectrum of the reversed, conjugated replica, and stores outputs
  * [L - 1, L - 1 + Nr) of the inverse transform.  The line is still read and written once. */
 rd_status rd_range_compress(rd_plan* plan, const rd_c64* echo, rd_c64* rc, void* stream);
+
+/* rd_range_compress with binary16 storage (cf-1.com/news/2323550 §7: FP16 storage, FP32
+ * arithmetic): echo and rc are [Na][Nr] rd_c32h.  Each sample is converted exactly to float32 on
+ * load, the whole line is processed in float32 as in rd_range_compress (same filter, same
+ * transforms), and each output is rounded to the nearest binary16 value (ties to even) on
+ * store; magnitudes beyond 65504 become infinities.  HBM traffic is 8 bytes a sample instead of
+ * 16.  echo == rc (in place) is allowed; other overlap is an error.  Pointers must be 4-byte
+ * aligned.  RD_ERR_UNSUPPORTED_LENGTH if Nr has no built transform (the padded form of
+ * rd_range_compress has no binary16 variant). */
+rd_status rd_range_compress_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* rc, void* stream);
 
 /* Azimuth processing of range-compressed data rc [Na][Nr] into the focused image img
  * [Na][Nr] (cf-1.com/news/2323550 §2.1, §5.1; nxmr.cn/news/101525 §2.2):

@@ -11,7 +11,7 @@ from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_
                       make_bp_grid, make_params, rd_azimuth_focus, rd_backproject, rd_bp_grid,
                       rd_corner_turn, rd_debug_azimuth_stages, rd_debug_line_fft,
                       rd_focus, rd_last_error, rd_length_supported, rd_omega_k, rd_params, rd_plan_create,
-                      rd_plan_destroy, rd_range_compress, rd_status_string)
+                      rd_plan_destroy, rd_range_compress, rd_range_compress_f16, rd_status_string)
 
 
 class Plan:
@@ -83,6 +83,20 @@ class Plan:
         img = self._empty((self.Na, self.Nr))
         rd_debug_azimuth_stages(self.handle, rc, az, rcmc, img)
         return az, rcmc, img
+
+    def range_compress_f16(self, echo, out=None):
+        """Range compression with binary16 storage: echo and the result are float16 tensors
+        [Na][Nr][2] (real, imaginary), float32 arithmetic inside (rd_range_compress_f16)."""
+        import torch
+        shape = (self.Na, self.Nr, 2)
+        if tuple(echo.shape) != shape:
+            raise ValueError(f"echo must have shape {shape}")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float16, device=echo.device)
+        elif tuple(out.shape) != shape:
+            raise ValueError(f"out must have shape {shape}")
+        rd_range_compress_f16(self.handle, echo, out)
+        return out
 
     def omega_k(self, echo, ref_bin: int, out=None):
         """omega-k image [Na][Nr] of the raw echo with reference range R(ref_bin) (rd_omega_k)."""

@@ -25,6 +25,7 @@ RD_WINDOW_HAMMING = 1
 
 # every symbol the header declares
 EXPORTS = ("rd_length_supported", "rd_plan_create", "rd_plan_destroy", "rd_range_compress",
+           "rd_range_compress_f16",
            "rd_azimuth_focus", "rd_focus", "rd_debug_azimuth_stages", "rd_debug_line_fft",
            "rd_backproject", "rd_corner_turn", "rd_omega_k", "rd_status_string", "rd_last_error")
 
@@ -87,6 +88,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [vp, vp, vp, vp]
         f.restype = ctypes.c_int
+    lib.rd_range_compress_f16.argtypes = [vp, vp, vp, vp]
+    lib.rd_range_compress_f16.restype = ctypes.c_int
     lib.rd_debug_azimuth_stages.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.rd_debug_azimuth_stages.restype = ctypes.c_int
     lib.rd_debug_line_fft.argtypes = [vp, i32, i32, vp, vp, i64, vp]
@@ -121,6 +124,18 @@ def _addr(x) -> int:
         return x
     if not x.is_contiguous():
         raise ValueError("tensor must be contiguous")
+    return x.data_ptr()
+
+
+def _addr_half(x) -> int:
+    """Device address of a binary16 tensor [..., 2] (real, imaginary last) or an integer address."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    import torch
+    if x.dtype != torch.float16 or x.shape[-1] != 2 or not x.is_contiguous():
+        raise ValueError("binary16 data must be a contiguous float16 tensor with a last dimension of 2")
     return x.data_ptr()
 
 
@@ -165,6 +180,11 @@ def rd_plan_destroy(plan: int) -> None:
 def rd_range_compress(plan: int, echo, rc, stream=None) -> None:
     _check(load_library().rd_range_compress(plan, _addr(echo), _addr(rc), _stream(stream, echo, rc)),
            "rd_range_compress")
+
+
+def rd_range_compress_f16(plan: int, echo, rc, stream=None) -> None:
+    _check(load_library().rd_range_compress_f16(plan, _addr_half(echo), _addr_half(rc), _stream(stream, echo, rc)),
+           "rd_range_compress_f16")
 
 
 def rd_azimuth_focus(plan: int, rc, img, stream=None) -> None:

@@ -527,6 +527,62 @@ __device__ __forceinline__ void store_line(const float2* v, const LineIO& io, in
   }
 }
 
+// binary16 line storage: interleaved complex, 4 bytes a sample (real, imaginary), float32 in
+// registers.  Loads convert exactly; stores round to nearest even (the IEEE conversion: values
+// beyond the binary16 range become infinities).  Same resource scheme as LineIO.
+typedef _Float16 rdf_h2 __attribute__((ext_vector_type(2)));
+struct LineIOh {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ LineIOh(const void* base, int N, int64_t first, int count, int64_t total) {
+    int64_t n = total - first;
+    n = n < 0 ? 0 : (n > count ? count : n);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(base)) + first * N * 4, 0, int(n * N * 4), kBufDword3);
+  }
+};
+
+__device__ __forceinline__ float2 h2_to_f2(unsigned int u) {
+  const rdf_h2 h = __builtin_bit_cast(rdf_h2, u);
+  return make_float2(float(h.x), float(h.y));
+}
+__device__ __forceinline__ unsigned int f2_to_h2(float2 v) {
+  rdf_h2 h;
+  h.x = static_cast<_Float16>(v.x);
+  h.y = static_cast<_Float16>(v.y);
+  return __builtin_bit_cast(unsigned int, h);
+}
+
+template <int N, int T, int R, int AUX = kBufNonTemporal>
+__device__ __forceinline__ void load_line_h(float2* v, const LineIOh& io, int elem0, int tid) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int r = dft_input_order<R>(i);
+        v[b * R + r] = h2_to_f2(__builtin_amdgcn_raw_buffer_load_b32(io.rsrc, (elem0 + j) * 4, r * G::NB * 4, AUX));
+      }
+    }
+  }
+}
+
+template <int N, int T, int R, int AUX = kBufNonTemporal>
+__device__ __forceinline__ void store_line_h(const float2* v, const LineIOh& io, int elem0, int tid) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(f2_to_h2(v[b * R + r]), io.rsrc, (elem0 + j) * 4,
+                                              r * G::NB * 4, AUX);
+    }
+  }
+}
+
 // Zero-padded line I/O: a line of n_line < N samples (consecutive lines n_line apart) enters an
 // N-point transform, and the outputs at positions [skip, skip + n_line) of the transform are
 // stored as the line.  An access that falls outside its window gets an offset past the

@@ -66,6 +66,7 @@ struct rd_plan {
   double rd_max_shift = 0.0;  // largest RCMC shift (samples); must stay below margin - 5
   int wk_halo = -1;     // omega-k: zero samples staged after a row (-1: geometry not supported)
   int wk_grid = 0;      // omega-k row-stage grid
+  int f16_grid = 0;     // grid of the binary16-storage range kernel (0: not available)
 };
 
 namespace {
@@ -289,6 +290,7 @@ rd_status check_call(rd_plan* plan) {
 }
 
 bool aligned8(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // [a, a + n) and [b, b + n) overlap but are not the same buffer
 bool partial_overlap(const void* a, const void* b, size_t n) {
@@ -498,6 +500,11 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
       P->rc_variant = 1;
       P->rc_grid = persistent_grid(occ, P->cus, p.Na, rops->lpw);
     }
+    if (rops->range_compress_f16 && !pad_m) {
+      int occ16 = 0;
+      if (rops->occupancy_f16(&occ16) != hipSuccess) return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
+      P->f16_grid = persistent_grid(occ16, P->cus, p.Na, rops->lpw);
+    }
     const char* g = std::getenv("RD_RC_GRID");  // workgroups of the range kernel (tuning)
     if (g && std::atoi(g) > 0) P->rc_grid = std::atoi(g);
   }
@@ -585,6 +592,19 @@ rd_status rd_range_compress(rd_plan* plan, const rd_c64* echo, rd_c64* rc, void*
   if (partial_overlap(echo, rc, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and rc overlap without being equal");
   return run_range_compress(plan, reinterpret_cast<const float2*>(echo),
                             reinterpret_cast<float2*>(rc), false, static_cast<hipStream_t>(stream));
+}
+
+rd_status rd_range_compress_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* rc, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (plan->f16_grid <= 0)
+    return fail(RD_ERR_UNSUPPORTED_LENGTH, "binary16 storage needs a built transform of length Nr=%d", plan->p.Nr);
+  if (!aligned4(echo) || !aligned4(rc)) return fail(RD_ERR_INVALID_ARG, "echo and rc must be non-NULL and 4-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c32h);
+  if (partial_overlap(echo, rc, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and rc overlap without being equal");
+  return check_hip(plan->rops->range_compress_f16(echo, rc, plan->H, plan->tw_r, plan->rc_tab, plan->p.Na,
+                                                  plan->f16_grid, static_cast<hipStream_t>(stream)),
+                   "binary16 range compression launch");
 }
 
 rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* stream) {

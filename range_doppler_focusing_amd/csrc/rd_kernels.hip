@@ -121,36 +121,43 @@ __device__ __forceinline__ void filter_multiply(float2* v, const float2* h,
 }
 
 // Line I/O of the range kernels: natural (n_line == N) or zero-padded (PAD, see below).
-template <int N, bool PAD>
-__device__ __forceinline__ void rc_load(float2* v, const float2* in, int64_t l0, int64_t lines, int grp,
+template <int N, bool PAD, bool HALF>
+__device__ __forceinline__ void rc_load(float2* v, const void* in, int64_t l0, int64_t lines, int grp,
                                         int tid, int n_line, int skip) {
   using C = LineCfg<N>;
   constexpr int R0 = ListInfo<typename C::Fwd>::first;
+  static_assert(!(PAD && HALF), "binary16 storage has no padded form");
+  const float2* src = static_cast<const float2*>(in);
   if constexpr (PAD)
-    load_line_pad<N, C::T, R0>(v, LineIO(in, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
+    load_line_pad<N, C::T, R0>(v, LineIO(src, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
                                n_line + skip);
+  else if constexpr (HALF)
+    load_line_h<N, C::T, R0>(v, LineIOh(in, N, l0, C::LPW, lines), grp * N, tid);
   else
-    load_line<N, C::T, R0>(v, LineIO(in, N, l0, C::LPW, lines), grp * N, tid);
+    load_line<N, C::T, R0>(v, LineIO(src, N, l0, C::LPW, lines), grp * N, tid);
 }
-template <int N, bool PAD, int SAUX>
-__device__ __forceinline__ void rc_store(const float2* v, float2* out, int64_t l0, int64_t lines, int grp,
+template <int N, bool PAD, bool HALF, int SAUX>
+__device__ __forceinline__ void rc_store(const float2* v, void* out, int64_t l0, int64_t lines, int grp,
                                          int tid, int n_line, int skip) {
   using C = LineCfg<N>;
   constexpr int R0 = ListInfo<typename C::Fwd>::first;
+  float2* dst = static_cast<float2*>(out);
   if constexpr (PAD)
-    store_line_pad<N, C::T, R0, SAUX>(v, LineIO(out, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
+    store_line_pad<N, C::T, R0, SAUX>(v, LineIO(dst, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
                                       skip);
+  else if constexpr (HALF)
+    store_line_h<N, C::T, R0, SAUX>(v, LineIOh(out, N, l0, C::LPW, lines), grp * N, tid);
   else
-    store_line<N, C::T, R0, SAUX>(v, LineIO(out, N, l0, C::LPW, lines), grp * N, tid);
+    store_line<N, C::T, R0, SAUX>(v, LineIO(dst, N, l0, C::LPW, lines), grp * N, tid);
 }
 
 // PAD: lines of n_line < N samples (any length): each is extended periodically by skip samples
 // and zero-padded to N; with the plan's filter (the N-point spectrum of the reversed, conjugated
 // replica of skip + 1 samples) the N-point circular convolution holds the length-n_line circular
 // correlation at positions [skip, skip + n_line), exactly when N >= n_line + skip.
-template <int N, bool PF, int SAUX, bool PAD = false>
+template <int N, bool PF, int SAUX, bool PAD = false, bool HALF = false>
 __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
-    k_range_compress_pf(const float2* in, float2* out, const float2* __restrict__ H,
+    k_range_compress_pf(const void* in, void* out, const float2* __restrict__ H,
                         const float2* __restrict__ tw, int64_t lines, int n_line, int skip) {
   using C = LineCfg<N>;
   using L = typename C::Fwd;
@@ -168,7 +175,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   // the table reads instead of following them.
   float2 nxt[C::P];
   if constexpr (PF)
-    rc_load<N, PAD>(nxt, in, int64_t(blockIdx.x) * C::LPW, lines, grp, tid, n_line, skip);
+    rc_load<N, PAD, HALF>(nxt, in, int64_t(blockIdx.x) * C::LPW, lines, grp, tid, n_line, skip);
   TC twc;
   twc.load_all(tw, lds + C::LPW * C::LDS, tid, threadIdx.x, C::WG);
   // (the first pass's barrier orders the LDS twiddle table before its first use, unless a line's
@@ -186,15 +193,15 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     if constexpr (PF) {
 #pragma unroll
       for (int i = 0; i < C::P; ++i) v[i] = nxt[i];
-      if constexpr (!LATE) rc_load<N, PAD>(nxt, in, l0 + stride, lines, grp, tid, n_line, skip);
+      if constexpr (!LATE) rc_load<N, PAD, HALF>(nxt, in, l0 + stride, lines, grp, tid, n_line, skip);
     } else {
-      rc_load<N, PAD>(v, in, l0, lines, grp, tid, n_line, skip);
+      rc_load<N, PAD, HALF>(v, in, l0, lines, grp, tid, n_line, skip);
     }
     PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
     filter_multiply<N>(v, h, opaque(H), tid);
-    if constexpr (LATE) rc_load<N, PAD>(nxt, in, l0 + stride, lines, grp, tid, n_line, skip);
+    if constexpr (LATE) rc_load<N, PAD, HALF>(nxt, in, l0 + stride, lines, grp, tid, n_line, skip);
     PassesCached<N, T, +1, 1, L, C::WAVE>::run(v, my, twc, tid);
-    rc_store<N, PAD, SAUX>(v, out, l0, lines, grp, tid, n_line, skip);
+    rc_store<N, PAD, HALF, SAUX>(v, out, l0, lines, grp, tid, n_line, skip);
     // Wait for the prefetch here, where the stores just issued are younger than it and need not
     // complete; a wait at the loop head would merge with the loop entry and drain the stores.
     if constexpr (PF) touch<C::P>(nxt);
@@ -229,9 +236,9 @@ void rc4096_tab_fill(const float2* H, const float2*, float2* out) {
     for (int t = 0; t < 256; ++t) out[r * 256 + t] = H[(t >> 4) + 16 * (t & 15) + 256 * r];
 }
 
-template <int SAUX>
+template <int SAUX, bool HALF = false>
 __global__ void __launch_bounds__(256, 3)
-    k_range_compress_4096(const float2* in, float2* out, const float2* __restrict__ tab,
+    k_range_compress_4096(const void* in, void* out, const float2* __restrict__ tab,
                           int64_t lines) {
   constexpr int N = 4096, T = 256, REG = 272;
   __shared__ float2 lds[16 * REG + 15 * 16];
@@ -241,8 +248,15 @@ __global__ void __launch_bounds__(256, 3)
   const int64_t stride = gridDim.x;
   // The first line's loads go out before the table loads, so the line's HBM latency overlaps
   // the table reads instead of following them.
+  // line I/O: float32 or binary16 storage
+  auto load = [&](float2* dst, int64_t line) {
+    if constexpr (HALF)
+      load_line_h<N, T, 16>(dst, LineIOh(in, N, line, 1, lines), 0, t);
+    else
+      load_line<N, T, 16>(dst, LineIO(static_cast<const float2*>(in), N, line, 1, lines), 0, t);
+  };
   float2 nxt[16];
-  load_line<N, T, 16>(nxt, LineIO(in, N, blockIdx.x, 1, lines), 0, t);
+  load(nxt, blockIdx.x);
   // The filter is first used at the first line's multiply, so the wait for it lands there (in
   // later lines that wait also covers the previous line's stores, which are complete by then).
   float2 h[16];   // H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l)
@@ -257,7 +271,7 @@ __global__ void __launch_bounds__(256, 3)
     float2 v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = nxt[i];
-    load_line<N, T, 16>(nxt, LineIO(in, N, line + stride, 1, lines), 0, t);
+    load(nxt, line + stride);
     // ---- forward
     Dft<16, -1>::run(v);
 #pragma unroll
@@ -321,7 +335,10 @@ __global__ void __launch_bounds__(256, 3)
       v[k] = cmul(v[k], w);
     }
     Dft<16, +1>::run(v);
-    store_line<N, T, 16, SAUX>(v, LineIO(out, N, line, 1, lines), 0, t);
+    if constexpr (HALF)
+      store_line_h<N, T, 16, SAUX>(v, LineIOh(out, N, line, 1, lines), 0, t);
+    else
+      store_line<N, T, 16, SAUX>(v, LineIO(static_cast<float2*>(out), N, line, 1, lines), 0, t);
     touch<16>(nxt);
   }
 }
@@ -1007,6 +1024,29 @@ hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const fl
   return hipGetLastError();
 }
 
+// binary16 storage (4 bytes a sample in and out), float32 arithmetic: the same kernels with
+// 32-bit line I/O; streaming stores
+template <int N>
+hipError_t launch_rc_f16(const void* in, void* out, const float2* H, const float2* tw, const float2* tab,
+                         int64_t lines, int grid, hipStream_t s) {
+  constexpr bool PF = RD_RC_PREFETCH && LineCfg<N>::PF;
+  if constexpr (N == 4096 && RD_RC_4096) {
+    hipLaunchKernelGGL((k_range_compress_4096<kAuxStream, true>), dim3(grid), dim3(256), 0, s, in, out, tab, lines);
+  } else {
+    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream, false, true>), dim3(grid), dim3(LineCfg<N>::WG), 0,
+                       s, in, out, H, tw, lines, N, 0);
+  }
+  return hipGetLastError();
+}
+
+template <int N>
+hipError_t occupancy_f16(int* rc) {
+  if constexpr (N == 4096 && RD_RC_4096)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_4096<kAuxStream, true>, 256, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream, false, true>, LineCfg<N>::WG, 0);
+}
+
 template <int N>
 hipError_t occupancy_pf(int* rc, int pad) {
   if (pad)
@@ -1068,11 +1108,12 @@ constexpr LineOps make_ops() {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
                    &occupancy<N>, &launch_rc_pf<N>, &occupancy_pf<N>, &rc_tab_len<N>,
                    &rc_tab_fill<N>, &launch_rcmc_mf<N>, RowStage<N>::MARGIN,
-                   &launch_omega_k_rows<N>, &occupancy_wk<N>, OkRow<N>::CAP};
+                   &launch_omega_k_rows<N>, &occupancy_wk<N>, OkRow<N>::CAP, &launch_rc_f16<N>,
+                   &occupancy_f16<N>};
   } else {
     return LineOps{N, LineCfg<N>::WG, LineCfg<N>::LPW, &launch_rc<N>, &launch_fft<N>,
                    &occupancy<N>, nullptr, nullptr, &rc_tab_len<N>, &rc_tab_fill<N>,
-                   &launch_rcmc_mf<N>, RowStage<N>::MARGIN, nullptr, nullptr, 0};
+                   &launch_rcmc_mf<N>, RowStage<N>::MARGIN, nullptr, nullptr, 0, nullptr, nullptr};
   }
 }
 

@@ -19,19 +19,19 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="librdfocus.so n
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rd_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(rd_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
     import range_doppler_focusing_amd as rdf
     lib = rdf.load_library()
     declared = header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(rdf.EXPORTS) == declared
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
-    exported = set(re.findall(r" T (rd_[a-z_]+)$", out, flags=re.M))
+    exported = set(re.findall(r" T (rd_[a-z0-9_]+)$", out, flags=re.M))
     assert set(declared) <= exported
 
 
@@ -142,3 +142,4 @@ def test_backproject_rejects_a_null_plan_before_any_launch():
     g = rdf.make_bp_grid(nx=4, ny=4, x0_m=0.0, dx_m=1.0, r0_m=1000.0, dr_m=1.0)
     assert lib.rd_backproject(None, 1 << 20, 1 << 30, ctypes.byref(g), None) == -1
     assert lib.rd_omega_k(None, 1 << 20, 1 << 30, 0, None) == -1
+    assert lib.rd_range_compress_f16(None, 1 << 20, 1 << 30, None) == -1

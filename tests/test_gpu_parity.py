@@ -199,6 +199,89 @@ def test_range_compression_any_length_large(torch_dev, rdf):
     assert k == 333 == int(np.argmax(np.abs(ref[list(rows).index(5)])))
 
 
+# ------------------------------------------------------------------------------ binary16 storage
+def to_half(x):
+    """complex array -> float16 [..., 2] (real, imaginary), rounded to nearest even."""
+    return np.stack([x.real, x.imag], axis=-1).astype(np.float16)
+
+
+def from_half(h):
+    return h[..., 0].astype(np.float64) + 1j * h[..., 1].astype(np.float64)
+
+
+def check_half(got, ref):
+    """The binary16-storage bar: every stored component lies within half a binary16 ulp of the
+    float64 result (the rounding on store) plus the float32 arithmetic's error (1e-5 of the
+    RMS); and the relative L2 error is at most 4e-4 (the RMS of a round-to-nearest error is
+    about 2^-11 / sqrt(3) = 2.8e-4 of the magnitude)."""
+    g = got.astype(np.float64)
+    r = np.stack([ref.real, ref.imag], axis=-1)
+    ulp = np.spacing(np.abs(r).astype(np.float16)).astype(np.float64)
+    rms = np.sqrt(np.mean(np.abs(ref) ** 2))
+    excess = np.abs(g - r) - (0.5 * ulp * (1 + 2.0 ** -10) + 1e-5 * rms)
+    assert excess.max() <= 0, f"worst excess {excess.max():.3g} at {np.unravel_index(np.argmax(excess), excess.shape)}"
+    err = M.rel_l2(from_half(got), ref)
+    assert err <= 4e-4
+    return err
+
+
+@pytest.mark.parametrize("n", LENGTHS)
+@pytest.mark.parametrize("lines", [1, 37])
+def test_range_compression_f16_every_length(torch_dev, rdf, n, lines):
+    """binary16 storage, every built length: each output is the float64 result rounded to
+    binary16; in place bit-identical to out of place."""
+    torch = torch_dev
+    rng = np.random.default_rng(3000 + n + lines)
+    fs = 120e6
+    params = dict(Na=lines, Nr=n, pulse_s=(n // 3) / fs, bandwidth_hz=90e6, fs_hz=fs,
+                  range_window=int(n % 3 == 0))
+    echo = to_half(rng.standard_normal((lines, n)) + 1j * rng.standard_normal((lines, n)))
+    log(f"[range f16] n={n} lines={lines}")
+    with rdf.Plan(**params) as plan:
+        x = torch.from_numpy(echo).to("cuda")
+        rc = plan.range_compress_f16(x).cpu().numpy()
+        plan.range_compress_f16(x, out=x)
+        torch.cuda.synchronize()
+        assert np.array_equal(x.cpu().numpy().view(np.uint16), rc.view(np.uint16))
+    err = check_half(rc, O.range_compress(from_half(echo), params))
+    log(f"[range f16] n={n} lines={lines} rel-L2 {err:.2e}")
+
+
+def test_range_compression_f16_workload(torch_dev, rdf):
+    """The 4096 x 4096 range-compression scene stored in binary16, against the oracle on the
+    same binary16 input; target peaks where the float64 result has them."""
+    torch = torch_dev
+    cfg = C2
+    sc = make_scene(cfg)
+    echo = to_half(sc.echo)
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        rc = plan.range_compress_f16(torch.from_numpy(echo).to("cuda")).cpu().numpy()
+    ref = O.range_compress(from_half(echo), cfg.plan_params())
+    err = check_half(rc, ref)
+    log(f"[range f16] 4096 x 4096 rel-L2 {err:.2e}")
+    got = from_half(rc)
+    for m in (0, cfg.Na // 2, cfg.Na - 1):
+        for (_, n) in sc.targets:
+            assert int(np.argmax(np.abs(got[m, n - 4:n + 5]))) == 4 == int(np.argmax(np.abs(ref[m, n - 4:n + 5])))
+
+
+def test_range_compression_f16_error_paths(torch_dev, rdf):
+    torch = torch_dev
+    with rdf.Plan(Na=4, Nr=1200, pulse_s=400 / 120e6, bandwidth_hz=100e6, fs_hz=120e6) as plan:
+        x = torch.zeros((4, 1200, 2), dtype=torch.float16, device="cuda")
+        with pytest.raises(rdf.RdError) as ei:      # padded lengths have no binary16 form
+            plan.range_compress_f16(x)
+        assert ei.value.status == -2
+    with rdf.Plan(Na=4, Nr=256, pulse_s=100 / 120e6, bandwidth_hz=100e6, fs_hz=120e6) as plan:
+        x = torch.zeros((4, 256, 2), dtype=torch.float16, device="cuda")
+        with pytest.raises(rdf.RdError) as ei:
+            rdf.rd_range_compress_f16(plan.handle, x.data_ptr() + 2, x)
+        assert ei.value.status == -1
+        with pytest.raises(rdf.RdError) as ei:      # partial overlap
+            rdf.rd_range_compress_f16(plan.handle, x, x.data_ptr() + 4)
+        assert ei.value.status == -1
+
+
 def test_range_compression_table_variant(torch_dev, rdf, monkeypatch):
     """The table-twiddle kernel (selected by RD_RC_VARIANT=table) meets the same bar."""
     torch = torch_dev
