@@ -62,6 +62,11 @@ def read_traffic(path: str, src_hash: str):
 SETTLE_S = 0.3
 
 
+def note(msg: str) -> None:
+    """A progress line on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def time_steps(torch, fn, steps: int, warmup: int, stream):
     """ms per step over exactly `steps` calls, after `warmup` untimed calls.  Before those, the
     step runs for SETTLE_S seconds (untimed, in long batches): the GPU's clocks ramp up over the
@@ -201,6 +206,8 @@ def main():
         torch.cuda.empty_cache()
     rc_bytes = 2 * cfg.Na * cfg.Nr * 8
     rc_gbs = rc_bytes / (rc_ms * 1e-3) / 1e9 if rc_ms else None
+    if rc_ms:
+        note(f"range compression 4096 x 4096: {rc_ms * 1e3:.1f} us")
 
     # ---------------------------------------------------------------- full chain
     fcfg = C3
@@ -232,6 +239,8 @@ def main():
         torch.cuda.empty_cache()
     px = fcfg.Na * fcfg.Nr
     mpx = px / (focus_ms * 1e-3) / 1e6 if focus_ms else None
+    if focus_ms:
+        note(f"rd_focus 4096 x 4096: {focus_ms * 1e3:.1f} us")
 
     # ---------------------------------------------------------------- omega-k
     wk = None
@@ -270,6 +279,7 @@ def main():
                                        "cores": 1, "kind": "oracle",
                                        "sample": f"1024 pulses x {wcfg.Nr} of the same geometry, one run ({tw:.1f} s)"}
             wk.append(rec)
+            note(f"omega-k {wcfg.Na} x {wcfg.Nr}: {ms * 1e3:.1f} us")
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -277,6 +287,7 @@ def main():
     if not args.no_cpu and args.only is None:
         cores = 1  # NumPy's FFT and the oracle's array code run on one thread
         t, runs = cpu_oracle_rc(cfg, cached_scene(cfg).echo)
+        note(f"oracle range compression: {t:.2f} s per run")
         cpu = {"value": rc_bytes / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
                "sample": f"whole 4096x4096 range compression, median of {runs} runs "
                          f"({t:.2f} s each, ~{t * runs:.0f} s of CPU work)"}
@@ -313,6 +324,7 @@ def main():
                 rec.update({"value": round(m, 1), "unit": "Mpixel/s",
                             "roofline_frac_80B_per_px": round(m * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4)})
             large.append(rec)
+            note(f"{rec['workload']}: {ms * 1e3:.1f} us")
 
     # ---------------------------------------------------------------- binary16 storage
     if (args.only in (None, "large", "f16")) and not args.no_large:
@@ -335,6 +347,7 @@ def main():
                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                       "samples_per_s": round(cfg.Na * cfg.Nr / (ms * 1e-3), 1),
                       "data": "the headline scene rounded to binary16"})
+        note(f"binary16 range compression: {ms * 1e3:.1f} us")
 
     # ---------------------------------------------------------------- a line length with no built transform
     if (args.only in (None, "large", "pad")) and not args.no_large:
@@ -366,6 +379,7 @@ def main():
                                    "cores": 1, "kind": "oracle",
                                    "sample": f"all {na} lines, one run ({tc:.2f} s)"}
         large.append(rec)
+        note(f"padded range compression 16384 x 1200: {ms * 1e3:.1f} us")
         del x, y
         torch.cuda.empty_cache()
 
@@ -383,6 +397,7 @@ def main():
                           "ms_per_step": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
                           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                           "data": "seeded complex Gaussian noise on the device"})
+            note(f"corner turn {rows} x {cols}: {ms * 1e3:.1f} us")
             del xs, ys
             torch.cuda.empty_cache()
 
@@ -419,6 +434,7 @@ def main():
                                    "cores": 1, "kind": "oracle",
                                    "sample": f"32 x 32 pixels x {bcfg.Na} pulses, one run ({tb:.1f} s)"}
         large.append(rec)
+        note(f"back-projection: {ms:.2f} ms")
         del rc, img
         torch.cuda.empty_cache()
 
