@@ -218,7 +218,8 @@ rd_status rd_backproject(rd_plan* plan, const rd_c64* rc, rd_c64* img, const rd_
  * row-major complex array in[rows][cols] (for example [Na][Nr] -> [Nr][Na]); out is [cols][rows].
  * Device pointers, 8-byte aligned, owned by the caller; the two buffers must not overlap (out of
  * place only).  rows = 0 or cols = 0 is a no-op.  RD_ERR_INVALID_ARG for negative sizes,
- * rows > 65535 * 64, rows * cols > 2^40, or bad or overlapping pointers.  No plan is needed:
+ * rows * cols > 2^40, more than 2^31 - 1 tiles of 64 x 64, or bad or overlapping pointers.
+ * The work is 64 x 64 tiles through LDS on a persistent grid.  No plan is needed:
  * the work runs on the current device.  rd_focus does not use it (its azimuth transforms run
  * in place on [Na][Nr]); it serves callers that want the azimuth-major layout. */
 rd_status rd_corner_turn(const rd_c64* in, rd_c64* out, int64_t rows, int64_t cols, void* stream);

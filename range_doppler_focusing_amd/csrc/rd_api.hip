@@ -787,10 +787,10 @@ rd_status rd_corner_turn(const rd_c64* in, rd_c64* out, int64_t rows, int64_t co
                          void* stream) {
   if (rows < 0 || cols < 0) return fail(RD_ERR_INVALID_ARG, "rows and cols must be >= 0");
   if (rows == 0 || cols == 0) return RD_OK;
-  if (rows > int64_t(65535) * 64)
-    return fail(RD_ERR_INVALID_ARG, "rows=%lld exceeds the %d-row limit", (long long)rows, 65535 * 64);
   if (cols > (int64_t(1) << 40) / rows)
     return fail(RD_ERR_INVALID_ARG, "rows * cols exceeds 2^40 elements");
+  if (((rows + 63) / 64) * ((cols + 63) / 64) > int64_t(0x7fffffff))
+    return fail(RD_ERR_INVALID_ARG, "more than 2^31 - 1 tiles of 64 x 64");
   if (!aligned8(in) || !aligned8(out)) return fail(RD_ERR_INVALID_ARG, "in and out must be non-NULL and 8-byte aligned");
   const size_t bytes = size_t(rows) * size_t(cols) * sizeof(rd_c64);
   const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(out);

@@ -786,54 +786,90 @@ constexpr int kTurnTile = 64, kTurnPitch = 65;
 typedef float rdf_v2f __attribute__((ext_vector_type(2)));
 
 template <int AUX>
-__global__ void __launch_bounds__(256)
-    k_corner_turn(const float2* __restrict__ in, float2* __restrict__ out, int64_t rows,
-                  int64_t cols) {
-  __shared__ float2 tile[kTurnTile * kTurnPitch];
-  const int64_t c0 = int64_t(blockIdx.x) * kTurnTile, r0 = int64_t(blockIdx.y) * kTurnTile;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  {
-    const int64_t c = c0 + lane;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int rr = w + 4 * k;
-      const int64_t r = r0 + rr;
-      float2 v = make_float2(0.f, 0.f);
-      if (r < rows && c < cols) {
-        const rdf_v2f* src = reinterpret_cast<const rdf_v2f*>(in + r * cols + c);
-        const rdf_v2f x = AUX ? __builtin_nontemporal_load(src) : *src;
-        v = make_float2(x.x, x.y);
-      }
-      tile[rr * kTurnPitch + lane] = v;
-    }
-  }
-  __syncthreads();
-  const int64_t r = r0 + lane;
+__device__ __forceinline__ void turn_load(float2* v, const float2* __restrict__ in, int64_t rows, int64_t cols,
+                                          int64_t r0, int64_t c0, int lane, int w) {
+  const int64_t c = c0 + lane;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int cc = w + 4 * k;
-    const int64_t c = c0 + cc;
-    if (c < cols && r < rows) {
-      rdf_v2f* dst = reinterpret_cast<rdf_v2f*>(out + c * rows + r);
-      const float2 t = tile[lane * kTurnPitch + cc];
-      const rdf_v2f v = {t.x, t.y};
-      if (AUX)
-        __builtin_nontemporal_store(v, dst);
-      else
-        *dst = v;
+    const int64_t r = r0 + w + 4 * k;
+    float2 x = make_float2(0.f, 0.f);
+    if (r < rows && c < cols) {
+      const rdf_v2f* src = reinterpret_cast<const rdf_v2f*>(in + r * cols + c);
+      const rdf_v2f y = AUX ? __builtin_nontemporal_load(src) : *src;
+      x = make_float2(y.x, y.y);
     }
+    v[k] = x;
+  }
+}
+
+// Persistent form: workgroup b moves tiles b, b + G, b + 2G, ... (row-major tile order), and the
+// next tile's loads are issued as soon as the current tile is in LDS, so they are in flight
+// during the transposed reads and the stores (loads and stores complete in order, so the wait
+// for the prefetch does not wait for the stores).
+template <int AUX>
+__global__ void __launch_bounds__(256)
+    k_corner_turn(const float2* __restrict__ in, float2* __restrict__ out, int64_t rows,
+                  int64_t cols, int tiles_x, int tiles) {
+  __shared__ float2 tile[kTurnTile * kTurnPitch];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float2 cur[16];
+  int t = blockIdx.x;
+  if (t < tiles) {
+    const int ty = t / tiles_x;
+    turn_load<AUX>(cur, in, rows, cols, int64_t(ty) * kTurnTile, int64_t(t - ty * tiles_x) * kTurnTile, lane, w);
+  }
+  for (; t < tiles; t += gridDim.x) {
+    const int ty = t / tiles_x;
+    const int64_t r0 = int64_t(ty) * kTurnTile, c0 = int64_t(t - ty * tiles_x) * kTurnTile;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tile[(w + 4 * k) * kTurnPitch + lane] = cur[k];
+    __syncthreads();
+    const int tn = t + int(gridDim.x);
+    if (tn < tiles) {
+      const int tyn = tn / tiles_x;
+      turn_load<AUX>(cur, in, rows, cols, int64_t(tyn) * kTurnTile, int64_t(tn - tyn * tiles_x) * kTurnTile,
+                     lane, w);
+    }
+    const int64_t r = r0 + lane;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int cc = w + 4 * k;
+      const int64_t c = c0 + cc;
+      if (c < cols && r < rows) {
+        rdf_v2f* dst = reinterpret_cast<rdf_v2f*>(out + c * rows + r);
+        const float2 v = tile[lane * kTurnPitch + cc];
+        const rdf_v2f y = {v.x, v.y};
+        if (AUX)
+          __builtin_nontemporal_store(y, dst);
+        else
+          *dst = y;
+      }
+    }
+    __syncthreads();  // the tile's LDS reads are done before the next tile is written
   }
 }
 
 hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64_t cols,
                               int streaming, hipStream_t s) {
   const int64_t gx = (cols + kTurnTile - 1) / kTurnTile, gy = (rows + kTurnTile - 1) / kTurnTile;
-  if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
-  const dim3 grid{unsigned(gx), unsigned(gy), 1u};
+  if (gx * gy > 0x7fffffff) return hipErrorInvalidValue;
+  const int tiles = int(gx * gy);
+  // persistent grid: the resident workgroups of the whole device (queried once per device)
+  static int resident[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (resident[dev] == 0) {
+    int occ = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_corner_turn<1>, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    resident[dev] = (occ > 0 ? occ : 1) * (cus > 0 ? cus : 1);
+  }
+  const int grid = tiles < resident[dev] ? tiles : resident[dev];
   if (streaming)
-    hipLaunchKernelGGL(k_corner_turn<1>, grid, dim3(256), 0, s, in, out, rows, cols);
+    hipLaunchKernelGGL(k_corner_turn<1>, dim3(grid), dim3(256), 0, s, in, out, rows, cols, int(gx), tiles);
   else
-    hipLaunchKernelGGL(k_corner_turn<0>, grid, dim3(256), 0, s, in, out, rows, cols);
+    hipLaunchKernelGGL(k_corner_turn<0>, dim3(grid), dim3(256), 0, s, in, out, rows, cols, int(gx), tiles);
   return hipGetLastError();
 }
 

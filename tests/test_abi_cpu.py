@@ -114,8 +114,10 @@ def test_corner_turn_argument_errors_return_before_any_launch():
     assert lib.rd_corner_turn(0, b, 7, 7, None) == -1
     assert lib.rd_corner_turn(a + 4, b, 7, 7, None) == -1
     assert lib.rd_corner_turn(a, a + 8, 7, 7, None) == -1          # overlapping buffers
-    assert lib.rd_corner_turn(a, b, 65535 * 64 + 1, 1, None) == -1  # beyond the tile grid
-    assert "overlap" in lib.rd_last_error().decode() or "rows" in lib.rd_last_error().decode()
+    assert lib.rd_corner_turn(a, b, 1, 1 << 37, None) == -1         # 2^31 tiles of 64 x 64
+    assert "tiles" in lib.rd_last_error().decode()
+    assert lib.rd_corner_turn(a, b, 1 << 21, 1 << 20, None) == -1    # beyond 2^40 elements
+    assert "2^40" in lib.rd_last_error().decode()
 
 
 def test_bp_grid_layout_matches_c():
