@@ -81,8 +81,8 @@ enum { RD_WINDOW_RECT = 0, RD_WINDOW_HAMMING = 1 };
  * samples outside the line taken as 0. */
 typedef struct {
   int32_t Na;            /* pulses (azimuth lines) >= 1; full-chain plans: see below         */
-  int32_t Nr;            /* range samples per pulse: a supported transform length, or on a   *
-                          * range-only plan any length 1..8192 (see rd_range_compress)       */
+  int32_t Nr;            /* range samples per pulse: a supported transform length, or any    *
+                          * length 1..8192 (see rd_range_compress, rd_length_supported)      */
   double pulse_s;        /* Tp  > 0                                                          */
   double bandwidth_hz;   /* B   > 0 (chirp rate +B/Tp)                                       */
   double fs_hz;          /* Fs  > 0; requires L <= Nr                                        */
@@ -99,13 +99,15 @@ typedef struct {
 typedef struct rd_plan rd_plan;
 
 /* Returns 1 if `n` is a transform length the library builds (256..16384 powers of two, and
- * 6000 = 2^4 * 3 * 5^3), else 0.  Range-only plans also accept any other Nr in 1..8192 (range
- * compression then runs as a zero-padded convolution, see rd_range_compress).  Full-chain
- * plans also need Na a power of two in [256, 16384] and Na*Nr*8 < 4 GiB (checked by
- * rd_plan_create).  The range-Doppler entry points (rd_azimuth_focus, rd_focus and the stage
- * hook) further need a range migration R(n)(1/D_k - 1)/dr below Nr/8 - 5 samples over the
- * whole Doppler band; beyond it they return RD_ERR_UNSUPPORTED_LENGTH, while the plan still
- * serves rd_omega_k and rd_backproject. */
+ * 6000 = 2^4 * 3 * 5^3), else 0.  Plans also accept any other Nr in 1..8192: range compression
+ * then runs as a zero-padded convolution (see rd_range_compress) and the RCMC of the
+ * range-Doppler chain on rows of that length; rd_omega_k and rd_debug_line_fft along range need
+ * a built length.  Full-chain plans also need Na a power of two in [256, 16384] and
+ * Na*Nr*8 < 4 GiB (checked by rd_plan_create).  The range-Doppler entry points
+ * (rd_azimuth_focus, rd_focus and the stage hook) further need a range migration
+ * R(n)(1/D_k - 1)/dr below Nr/8 - 5 samples (1019 samples at lengths with no built transform)
+ * over the whole Doppler band; beyond it they return RD_ERR_UNSUPPORTED_LENGTH, while the plan
+ * still serves rd_omega_k and rd_backproject. */
 int rd_length_supported(int32_t n);
 
 /* Validates `params`, builds the matched filter H (float64 -> float32), the twiddle and
@@ -122,7 +124,7 @@ rd_status rd_plan_destroy(rd_plan* plan);
  * HBM once and written once.  echo == rc (in place) is allowed; other overlap is an error.
  * Any line length: nxmr.cn/news/101525 §4.1 names Nr = 1200 as a usual airborne length and
  * §5.1 asks for transforms of lengths that are not powers of two.  Where Nr has no built
- * transform (range-only plans, Nr <= 8192), the same length-Nr circular correlation
+ * transform (Nr <= 8192), the same length-Nr circular correlation
  *   rc[m][n] = sum_i echo[m][(n + i) mod Nr] conj(h[i])
  * is computed exactly (up to float32 rounding) as one zero-padded circular convolution of
  * length M = the smallest power of two >= max(256, Nr + L - 1): the kernel reads the line,

@@ -50,7 +50,9 @@ struct rd_plan {
   const rdf::LineOps* aops = nullptr;  // azimuth-length kernels
   int rc_variant = 0;   // 0 table loads, 1 register-cached (pf)
   int pad_m = 0;        // > 0: Nr has no built transform; range compression runs as a zero-padded
-                        // circular convolution of length pad_m >= Nr + L - 1 (power of two)
+                        // circular convolution of length pad_m >= Nr + L - 1 (power of two), and
+                        // RCMC runs on rows of run-time length
+  int rcmc_margin = 0;  // samples the RCMC kernel stages after a chunk (shifts up to margin - 5)
   int cached = 0;       // image passes use ordinary (cacheable) accesses: image fits the cache
   int rc_grid = 0;      // persistent grid of the range kernels
   int A = 0, B = 0;     // Na = A B: strided and block steps of the azimuth transform
@@ -351,14 +353,16 @@ rd_status run_col(rd_plan* P, const float2* src, float2* dst, bool forward, bool
 rd_status run_rows(rd_plan* P, const float2* src, float2* dst, bool filter, hipStream_t s) {
   rdf::AzRowConst c = P->az;
   c.filter = filter ? 1 : 0;
+  if (P->pad_m)
+    return check_hip(rdf::launch_rcmc_mf_any(src, dst, c, P->p.Na, P->p.Nr, P->cached, s), "RCMC launch");
   return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, P->cached, s), "RCMC launch");
 }
 
 rd_status check_rcmc_margin(const rd_plan* P) {
-  if (std::floor(P->rd_max_shift) + 5 > double(P->rops->margin))
+  if (std::floor(P->rd_max_shift) + 5 > double(P->rcmc_margin))
     return fail(RD_ERR_UNSUPPORTED_LENGTH,
                 "range migration of %.1f samples exceeds the %d-sample margin built for Nr=%d",
-                P->rd_max_shift, P->rops->margin - 5, P->p.Nr);
+                P->rd_max_shift, P->rcmc_margin - 5, P->p.Nr);
   return RD_OK;
 }
 
@@ -421,9 +425,9 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   const rdf::LineOps* rops = rdf::line_ops(p.Nr);
   int pad_m = 0;
   if (!rops) {
-    // any line length up to 8192 on a range-only plan: zero-padded convolution of length
-    // M = the smallest built power of two >= Nr + L - 1
-    if (all_az) return fail(RD_ERR_UNSUPPORTED_LENGTH, "full-chain plans need a built transform of length Nr=%d", p.Nr);
+    // any line length up to 8192: range compression as a zero-padded convolution of length
+    // M = the smallest built power of two >= Nr + L - 1 (the azimuth steps and the RCMC take the
+    // row length at run time)
     if (p.Nr > 8192) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length Nr=%d is built, and Nr > 8192", p.Nr);
     pad_m = 256;
     while (pad_m < p.Nr + int(Lf) - 1) pad_m *= 2;
@@ -462,6 +466,7 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   P->azimuth = all_az;
   P->rops = rops;
   P->pad_m = pad_m;
+  P->rcmc_margin = pad_m ? rdf::rcmc_any_margin() : rops->margin;
   P->aops = aops;
   if (hipDeviceGetAttribute(&P->cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     P->cus = 256;
@@ -537,7 +542,7 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     // (a plan whose migration exceeds the RCMC margin still serves omega-k and back-projection;
     // the range-Doppler entry points report it)
     P->rd_max_shift = max_shift;
-    P->az.halo = std::min(int(std::floor(max_shift)) + 5, rops->margin);
+    P->az.halo = std::min(int(std::floor(max_shift)) + 5, P->rcmc_margin);
     // omega-k: the Stolt shift (sqrt(a^2 + b^2) - a) / df is largest at the lowest range
     // frequency a = f0 - Fs/2 and the Doppler band edge b = c PRF / (4 V); the mapping needs
     // a > b there (a real wavenumber at every sample)
@@ -545,7 +550,7 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
       const double df = p.fs_hz / p.Nr;
       const double amin = p.carrier_hz - double(p.Nr / 2) * df;
       const double bmax = kC * p.prf_hz / (4.0 * p.velocity_mps);
-      if (rops->omega_k_rows && amin > bmax) {
+      if (rops->omega_k_rows && !pad_m && amin > bmax) {
         P->wk_halo = int(std::floor((std::sqrt(amin * amin + bmax * bmax) - amin) / df)) + 5;
         int occ = 0;
         if (rops->occupancy_wk(&occ) != hipSuccess) return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
@@ -640,7 +645,8 @@ rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref
   if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
   const rd_params& p = plan->p;
   if (ref_bin < 0 || ref_bin >= p.Nr) return fail(RD_ERR_INVALID_ARG, "ref_bin=%d must be in [0, Nr=%d)", ref_bin, p.Nr);
-  if (!plan->rops->omega_k_rows) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no omega-k row stage for Nr=%d", p.Nr);
+  if (!plan->rops->omega_k_rows || plan->pad_m)
+    return fail(RD_ERR_UNSUPPORTED_LENGTH, "omega-k needs a built transform of length Nr=%d", p.Nr);
   if (plan->wk_halo < 0)
     return fail(RD_ERR_INVALID_ARG, "f0 - Fs/2 must exceed c PRF / (4 V) for the Stolt mapping");
   if (plan->wk_halo > plan->rops->wk_cap)

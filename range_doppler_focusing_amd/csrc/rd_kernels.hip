@@ -472,47 +472,64 @@ struct RowStage {
   static constexpr int WG = T * LPW;
   static constexpr int MARGIN = N / 8;       // staged samples after a chunk (shift + 5 <= MARGIN)
   static constexpr int LEN = 3 + CH + MARGIN;
+  static constexpr int P = LineCfg<N>::P;    // registers per thread for a chunk
+};
+// Rows of any length (given at run time): 1024-sample chunks with up to 1024 staged samples
+// after each; the row's buffer resource reads zero past its end and drops stores there.
+template <>
+struct RowStage<0> {
+  static constexpr int CH = 1024;
+  static constexpr int CHUNKS = 0;  // run time
+  static constexpr int T = 256;
+  static constexpr int LPW = 1;
+  static constexpr int WG = T * LPW;
+  static constexpr int MARGIN = 1024;
+  static constexpr int LEN = 3 + CH + MARGIN;
+  static constexpr int P = CH / T;
 };
 
 template <int N, int AUX>
 __global__ void __launch_bounds__(RowStage<N>::WG)
-    k_rcmc_mf(const float2* in, float2* out, AzRowConst c, int64_t rows) {
+    k_rcmc_mf(const float2* in, float2* out, AzRowConst c, int64_t rows, int n_rt) {
   using RS = RowStage<N>;
+  constexpr bool RT = RS::CHUNKS == 0;        // row length n_rt at run time
+  const int nl = RT ? n_rt : N;              // samples per row
+  const int chunks = RT ? (n_rt + RS::CH - 1) / RS::CH : RS::CHUNKS;
   constexpr int T = RS::T;
   constexpr int CH = RS::CH;
   constexpr int R0 = CH / T;  // each thread holds chunk samples j + r T, r < CH/T
-  static_assert(CH % T == 0 && R0 <= LineCfg<N>::P, "row layout");
+  static_assert(CH % T == 0 && R0 <= RS::P, "row layout");
   using G = Geom<CH, T, R0>;
   __shared__ float2 lds[RS::LPW * RS::LEN];
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * RS::LEN;
   for (int i = threadIdx.x; i < RS::LPW * RS::LEN; i += RS::WG) lds[i] = make_float2(0.f, 0.f);
-  const int64_t items = rows * RS::CHUNKS;
+  const int64_t items = rows * chunks;
   for (int64_t i0 = int64_t(blockIdx.x) * RS::LPW; i0 < items; i0 += int64_t(gridDim.x) * RS::LPW) {
     const int64_t item = i0 + grp;
     const int64_t it = item < items ? item : items - 1;
-    const int64_t row = it / RS::CHUNKS;
-    const int n0 = int(it % RS::CHUNKS) * CH;
+    const int64_t row = it / chunks;
+    const int n0 = int(it % chunks) * CH;
     const int k = int(row / c.B) + c.A * int(row % c.B);
     const double alpha = c.row[4 * k], beta = c.row[4 * k + 1];
     const double gamma = c.row[4 * k + 2], delta = c.row[4 * k + 3];
-    float2 v[LineCfg<N>::P];
+    float2 v[RS::P];
     // one chunk per group: rows [i0, i0 + LPW) when a row is one chunk, else the item's row
     const LineIO src = RS::CHUNKS == 1 ? LineIO(in, N, i0, RS::LPW, rows)
-                                       : LineIO(in, N, item < items ? row : rows, 1, rows);
+                                       : LineIO(in, nl, item < items ? row : rows, 1, rows);
     const int e0 = RS::CHUNKS == 1 ? grp * N : n0;
     load_line<CH, T, R0, AUX>(v, src, e0, tid);
     float2 pre = make_float2(0.f, 0.f);
     int hs = -1;  // this thread's first halo slot, if any
-    if constexpr (RS::CHUNKS > 1) {
+    if constexpr (RS::CHUNKS != 1) {
       // the 3 samples before the chunk and c.halo after it (zero outside the row); the first
       // pass of them is loaded with the chunk, before the barrier
       const int i = tid;
       if (i < 3 + c.halo) {
         const int sidx = i < 3 ? n0 - 3 + i : n0 + CH + (i - 3);
         hs = i < 3 ? i : 3 + CH + (i - 3);
-        if (sidx >= 0 && sidx < N)
+        if (sidx >= 0 && sidx < nl)
           pre = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, sidx * 8, 0, AUX));
       }
     }
@@ -525,11 +542,11 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
         for (int r = 0; r < R0; ++r) my[3 + j + r * G::NB] = v[b * R0 + r];
       }
     }
-    if constexpr (RS::CHUNKS > 1) {
+    if constexpr (RS::CHUNKS != 1) {
       if (hs >= 0) my[hs] = pre;
       for (int i = tid + T; i < 3 + c.halo; i += T) {  // halos longer than one pass
         const int sidx = n0 + CH + (i - 3);
-        my[3 + CH + (i - 3)] = sidx < N ? __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+        my[3 + CH + (i - 3)] = sidx < nl ? __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
                                                  src.rsrc, sidx * 8, 0, AUX))
                                         : make_float2(0.f, 0.f);
       }
@@ -587,7 +604,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
       }
     }
     const LineIO dst = RS::CHUNKS == 1 ? LineIO(out, N, i0, RS::LPW, rows)
-                                       : LineIO(out, N, item < items ? row : rows, 1, rows);
+                                       : LineIO(out, nl, item < items ? row : rows, 1, rows);
     store_line<CH, T, R0, AUX>(v, dst, e0, tid);
   }
 }
@@ -1100,9 +1117,9 @@ hipError_t launch_rcmc_mf(const float2* in, float2* out, const AzRowConst& c, in
   const int64_t wgs = (rows * RowStage<N>::CHUNKS + RowStage<N>::LPW - 1) / RowStage<N>::LPW;
   if (grid <= 0 || grid > wgs) grid = int(wgs);
   if (cached)
-    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxCached>), dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows);
+    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxCached>), dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows, N);
   else
-    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxStream>), dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows);
+    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxStream>), dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows, N);
   return hipGetLastError();
 }
 
@@ -1126,6 +1143,23 @@ template <int N>
 hipError_t occupancy_wk(int* wgs) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(wgs, k_omega_k_row<N, kAuxCached>, LineCfg<N>::WG, 0);
 }
+
+// RCMC + azimuth filter over rows of n samples, any n >= 1 (run-time length; shifts up to
+// RowStage<0>::MARGIN - 5)
+hipError_t launch_rcmc_mf_any(const float2* in, float2* out, const AzRowConst& c, int64_t rows, int n,
+                              int cached, hipStream_t s) {
+  using RS = RowStage<0>;
+  if (n <= 0 || c.halo < 0 || c.halo > RS::MARGIN) return hipErrorInvalidValue;
+  const int64_t items = rows * ((n + RS::CH - 1) / RS::CH);
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  const int grid = int(items);
+  if (cached)
+    hipLaunchKernelGGL((k_rcmc_mf<0, kAuxCached>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
+  else
+    hipLaunchKernelGGL((k_rcmc_mf<0, kAuxStream>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
+  return hipGetLastError();
+}
+int rcmc_any_margin() { return RowStage<0>::MARGIN; }
 
 template <int N>
 int rc_tab_len() {

@@ -97,6 +97,12 @@ struct LineOps {
 // nullptr if the length has no built transform
 const LineOps* line_ops(int n);
 
+// RCMC + azimuth filter over rows of any length n (1024-sample chunks; halo up to
+// rcmc_any_margin(), so shifts up to rcmc_any_margin() - 5); in == out allowed
+hipError_t launch_rcmc_mf_any(const float2* in, float2* out, const AzRowConst& c, int64_t rows, int n,
+                              int cached, hipStream_t s);
+int rcmc_any_margin();
+
 // In-place four-step azimuth transforms on [rows][cols]; see rd_kernels.hip.
 struct ColStep {
   int L;          // transform length of this step

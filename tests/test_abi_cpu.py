@@ -76,7 +76,7 @@ def good_params(**kw):
     (dict(range_window=7), -1), (dict(flags=1), -1),
     (dict(pulse_s=1e-3), -1),                       # replica longer than the line
     (dict(prf_hz=0.0), -1),                         # half-configured azimuth
-    (dict(Nr=4000), -2), (dict(Na=3000), -2),       # no transform of that length
+    (dict(Nr=9000), -2), (dict(Na=3000), -2),       # no transform of that length, none padded
     (dict(Nr=9000, carrier_hz=0.0, prf_hz=0.0, velocity_mps=0.0), -2),  # range-only, beyond 8192
     (dict(rcmc_taps=6), -1), (dict(kaiser_beta=-1.0), -1),
     (dict(velocity_mps=1.0), -1),                   # Doppler band beyond 2V/lambda

@@ -24,6 +24,14 @@ LONG_MIGRATION = SceneConfig(
     fs_hz=120e6, window="rect", n_targets=4, noise_power=0.01, seed=12, carrier_hz=1.3e9,
     prf_hz=800.0, velocity_mps=150.0, r_ref_m=8000.0, sep_range=9, sep_az=64)
 
+# full-chain scenes at line lengths with no built transform (padded range compression, RCMC on
+# rows of run-time length in 1024-sample chunks with a ragged last chunk)
+RD_1200 = C3.with_(name="rd_1024x1200", Na=1024, Nr=1200, pulse_s=1e-6, n_targets=4)
+RD_3001 = SceneConfig(
+    name="rd_2048x3001_large_migration", Na=2048, Nr=3001, pulse_s=2e-6, bandwidth_hz=100e6,
+    fs_hz=120e6, window="rect", n_targets=3, noise_power=0.01, seed=13, carrier_hz=1.0e9,
+    prf_hz=600.0, velocity_mps=200.0, r_ref_m=3000.0, sep_range=9, sep_az=100)
+
 STAGE_TOL = 1e-5
 IMAGE_TOL = 1e-4
 LENGTHS = (256, 512, 1024, 2048, 4096, 8192, 16384, 6000)
@@ -327,7 +335,7 @@ def check_targets(img, ref_img, targets):
                 assert abs(a - b) <= 0.1, (m, n, axis, key)
 
 
-@pytest.mark.parametrize("cfg", [C1, C3, LONG_MIGRATION], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, C3, LONG_MIGRATION, RD_1200, RD_3001], ids=lambda c: c.name)
 def test_focus_every_stage(torch_dev, rdf, cfg):
     torch = torch_dev
     sc, ref = scene_and_stages(cfg)
@@ -509,6 +517,11 @@ def test_omega_k_error_paths(torch_dev, rdf):
                 call(x)
             assert ei.value.status == -2
         plan.omega_k(x, 0)                              # the same plan still serves omega-k
+    with rdf.Plan(**RD_1200.plan_params()) as plan:   # no built range transform
+        x = torch.zeros((RD_1200.Na, RD_1200.Nr), dtype=torch.complex64, device="cuda")
+        with pytest.raises(rdf.RdError) as ei:
+            plan.omega_k(x, 0)
+        assert ei.value.status == -2
     with rdf.Plan(**LONG_MIGRATION.plan_params()) as plan:   # Stolt shift beyond the staged margin
         x = torch.zeros((LONG_MIGRATION.Na, LONG_MIGRATION.Nr), dtype=torch.complex64, device="cuda")
         with pytest.raises(rdf.RdError) as ei:
