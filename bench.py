@@ -382,6 +382,23 @@ def main():
         note(f"padded range compression 16384 x 1200: {ms * 1e3:.1f} us")
         del x, y
         torch.cuda.empty_cache()
+        # range-Doppler focusing at that line length (the 4096-pulse airborne geometry with a
+        # 1 us pulse): padded range compression, azimuth steps, RCMC on 1200-sample rows
+        acfg = fcfg.with_(Nr=1200, pulse_s=1e-6)
+        x = gpu_noise(torch, (acfg.Na, acfg.Nr), 32)
+        y = torch.empty_like(x)
+        plan = rdf.Plan(**acfg.plan_params())
+        ms = time_steps(torch, lambda i: rdf.rd_focus(plan.handle, x, y, stream), 50, 3, stream)
+        plan.close()
+        m = acfg.Na * acfg.Nr / (ms * 1e-3) / 1e6
+        large.append({"workload": f"full RD focusing at a line length with no built transform, {acfg.Na} x {acfg.Nr} "
+                                  "complex64 (9.6 GHz, 1 us / 300 MHz at 360 MHz, PRF 1.5 kHz, 150 m/s, 10 km)",
+                      "ms_per_step": round(ms, 4), "steps": 50, "value": round(m, 1), "unit": "Mpixel/s",
+                      "roofline_frac_80B_per_px": round(m * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4),
+                      "data": "seeded complex Gaussian noise on the device (timing is data-independent)"})
+        note(f"rd_focus {acfg.Na} x {acfg.Nr}: {ms * 1e3:.1f} us")
+        del x, y
+        torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- corner turn
     if (args.only in (None, "large", "turn")) and not args.no_large:
