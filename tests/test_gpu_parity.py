@@ -599,6 +599,26 @@ def test_backproject_small_grids(torch_dev, rdf, monkeypatch, variant):
         assert M.peak_near(gimg, m, n) == M.peak_near(img, m, n)
 
 
+def test_backproject_any_line_length(torch_dev, rdf):
+    """Back-projection on a plan whose line length (1200) has no built transform, on 64 x 64
+    grids around two targets: the same complex64 range-compressed input on both sides."""
+    torch = torch_dev
+    cfg = RD_1200
+    sc, ref = scene_and_stages(cfg)
+    rc = ref["rc"].astype(np.complex64)
+    p = cfg.plan_params()
+    with rdf.Plan(**p) as plan:
+        rcd = dev(torch, rc)
+        for (m, n) in sc.targets[:2]:
+            g = focus_grid(cfg, m - 32, n - 32, 64, 64)
+            got = plan.backproject(rcd, g).cpu().numpy()
+            want = O.backproject(rc, p, g)
+            err = M.rel_l2(got, want)
+            log(f"[bp] {cfg.name} around ({m}, {n}) rel-L2 {err:.2e}")
+            assert err <= BP_TOL
+            assert M.peak_near(got, 32, 32) == M.peak_near(want, 32, 32)
+
+
 def test_backproject_large_grid_sampled(torch_dev, rdf):
     """4096 pulses onto a 1024 x 1024 grid of the 4096 x 4096 airborne scene (the workload the
     bench times): sampled pixels against the oracle computed pixel by pixel, and every target in
