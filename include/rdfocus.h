@@ -171,7 +171,8 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
  * Device work: azimuth transform steps, one fused kernel per Doppler row (range FFT, multiply,
  * Stolt mapping from LDS, range IFFT), inverse azimuth steps; echo == img allowed.
  * RD_ERR_NOT_CONFIGURED on a range-only plan; RD_ERR_INVALID_ARG if ref_bin is outside
- * [0, Nr) or f0 - Fs/2 <= c PRF / (4 V); RD_ERR_UNSUPPORTED_LENGTH if the largest Stolt shift
+ * [0, Nr) or f0 - Fs/2 <= c PRF / (4 V); RD_ERR_UNSUPPORTED_LENGTH if Nr has no built
+ * transform (see rd_length_supported), or if the largest Stolt shift
  * (at f' = -Fs/2 and the Doppler band edge) plus 5 samples exceeds Nr/2 (Nr/8 at 16384). */
 rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref_bin, void* stream);
 

@@ -130,7 +130,7 @@ hipError_t launch_backproject(const float2* rc, float2* img, const BpConst& c, i
                               hipStream_t s);
 
 // out[c][r] = in[r][c] for a row-major [rows][cols] array (streaming: non-temporal accesses);
-// hipErrorInvalidValue if the tile grid does not fit (rows > 65535 * 64)
+// hipErrorInvalidValue beyond 2^31 - 1 tiles of 64 x 64
 hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64_t cols,
                               int streaming, hipStream_t s);
 
