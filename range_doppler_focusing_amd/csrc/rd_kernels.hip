@@ -704,8 +704,13 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     const double b = double(2 * k < na ? k : k - na) * c.bstep;
     const double b2 = b * b;
     float2 v[C::P];
+    // The rotation is hidden from the compiler once per row, so the rotated offsets are formed
+    // where they are used instead of being hoisted out of the loop (32 registers for the whole
+    // kernel otherwise).
+    int rot = c.ref;
+    asm volatile("" : "+s"(rot));
     const LineIO io_in(in, N, l0, C::LPW, rows);
-    load_line_rot<N, T, R0, AUX>(v, io_in, grp * N, tid, c.ref);
+    load_line_rot<N, T, R0, AUX>(v, io_in, grp * N, tid, rot);
     PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
     // v = X[kx] H[kx] exp(j 2 pi (k0 - k1 (a - Q))) / Na at range bin kx = j + r NB,
     // a = f0 + js df, Q = sqrt(a^2 - b^2) (float64: the phase reaches ~1e4 turns)
@@ -785,7 +790,8 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     }
     // (the inverse transform's first exchange begins with a barrier: the staging reads are done)
     PassesCached<N, T, +1, 1, L, C::WAVE>::run(v, my, twc, tid);
-    store_line_rot<N, T, R0, AUX>(v, LineIO(out, N, l0, C::LPW, rows), grp * N, tid, c.ref);
+    asm volatile("" : "+s"(rot));
+    store_line_rot<N, T, R0, AUX>(v, LineIO(out, N, l0, C::LPW, rows), grp * N, tid, rot);
   }
 }
 
