@@ -59,6 +59,22 @@ def read_traffic(path: str, src_hash: str):
         return None
 
 
+def read_chain_traffic(path: str, src_hash: str):
+    """Calibrated HBM KiB per launch of each kernel of the focusing chains, from the committed
+    counter summary (a markdown table), if it was taken on the current kernel source; else None."""
+    try:
+        text = open(path).read()
+        if f"kernel_source_sha1: {src_hash}." not in text:
+            return None
+        head = next(l for l in text.splitlines() if l.startswith("| counter |"))
+        row = next(l for l in text.splitlines() if l.startswith("| HBM KiB (calibrated) |"))
+        names = [c.strip() for c in head.strip("|").split("|")][1:]
+        vals = [float(c) for c in row.strip("|").split("|")[1:]]
+        return {n: v for n, v in zip(names, vals)}
+    except (OSError, StopIteration, ValueError):
+        return None
+
+
 SETTLE_S = 0.3
 
 
@@ -229,8 +245,12 @@ def main():
         rc_alone_ms = time_steps(torch, lambda i: rdf.rd_range_compress(fplan.handle, fins[i % ROTATE],
                                                                         fouts[i % ROTATE], stream),
                                  max(10, args.steps // 2), args.warmup, stream)
+        img_bytes = fcfg.Na * fcfg.Nr * 8
         stage_ms = {"rd_range_compress_ms": round(rc_alone_ms, 4),
+                    "rd_range_compress_GBps": round(2 * img_bytes / (rc_alone_ms * 1e-3) / 1e9, 1),
                     "rd_azimuth_focus_ms": round(az_ms, 4),
+                    # four azimuth transform steps and the RCMC pass: five sweeps of 16 B a pixel
+                    "rd_azimuth_focus_GBps_80B_per_px": round(10 * img_bytes / (az_ms * 1e-3) / 1e9, 1),
                     "note": "each half timed on its own from an HBM-resident input; inside rd_focus "
                             "the range-compressed image stays in the Infinity Cache for the azimuth "
                             "passes, so the chain takes less than the sum"}
@@ -491,6 +511,8 @@ def main():
             "roofline_frac_80B_per_px": round(mpx * 1e6 * 80 / (HBM_PEAK_GBS * 1e9), 4),
             "roofline_frac_32B_per_px": round(mpx * 1e6 * 32 / (HBM_PEAK_GBS * 1e9), 4),
             "stages": stage_ms,
+            "hbm_kib_per_kernel_launch": read_chain_traffic(
+                os.path.join(ROOT, "profiles", "rd_chain_4096x4096_counters.md"), src_hash),
             "cpu_baseline": cpu_focus},
         "omega_k": wk,
         "other_workloads": large,
