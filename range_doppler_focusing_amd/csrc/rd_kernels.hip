@@ -474,14 +474,15 @@ struct RowStage {
   static constexpr int LEN = 3 + CH + MARGIN;
   static constexpr int P = LineCfg<N>::P;    // registers per thread for a chunk
 };
-// Rows of any length (given at run time): 1024-sample chunks with up to 1024 staged samples
-// after each; the row's buffer resource reads zero past its end and drops stores there.
+// Rows of any length (given at run time): 512-sample chunks (two per workgroup) with up to 1024
+// staged samples after each; the row's buffer resource reads zero past its end and drops stores
+// there.
 template <>
 struct RowStage<0> {
-  static constexpr int CH = 1024;
+  static constexpr int CH = 512;
   static constexpr int CHUNKS = 0;  // run time
-  static constexpr int T = 256;
-  static constexpr int LPW = 1;
+  static constexpr int T = 128;
+  static constexpr int LPW = 2;
   static constexpr int WG = T * LPW;
   static constexpr int MARGIN = 1024;
   static constexpr int LEN = 3 + CH + MARGIN;
@@ -1157,8 +1158,9 @@ hipError_t launch_rcmc_mf_any(const float2* in, float2* out, const AzRowConst& c
   using RS = RowStage<0>;
   if (n <= 0 || c.halo < 0 || c.halo > RS::MARGIN) return hipErrorInvalidValue;
   const int64_t items = rows * ((n + RS::CH - 1) / RS::CH);
-  if (items > 0x7fffffff) return hipErrorInvalidValue;
-  const int grid = int(items);
+  const int64_t wgs = (items + RS::LPW - 1) / RS::LPW;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  const int grid = int(wgs);
   if (cached)
     hipLaunchKernelGGL((k_rcmc_mf<0, kAuxCached>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
   else

@@ -97,7 +97,7 @@ struct LineOps {
 // nullptr if the length has no built transform
 const LineOps* line_ops(int n);
 
-// RCMC + azimuth filter over rows of any length n (1024-sample chunks; halo up to
+// RCMC + azimuth filter over rows of any length n (512-sample chunks; halo up to
 // rcmc_any_margin(), so shifts up to rcmc_any_margin() - 5); in == out allowed
 hipError_t launch_rcmc_mf_any(const float2* in, float2* out, const AzRowConst& c, int64_t rows, int n,
                               int cached, hipStream_t s);
