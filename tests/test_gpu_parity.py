@@ -290,6 +290,35 @@ def test_range_compression_f16_error_paths(torch_dev, rdf):
         assert ei.value.status == -1
 
 
+def test_range_compression_random_sweep(torch_dev, rdf):
+    """40 seeded random cases: line length 1..8192 (built or not), replica length 1..n, 1..40
+    lines, either window, float32 or (where a transform of that length is built) binary16
+    storage; each against the oracle on the same input."""
+    torch = torch_dev
+    rng = np.random.default_rng(4242)
+    fs = 120e6
+    for case in range(40):
+        n = int(rng.choice([int(rng.integers(1, 8193)), int(rng.choice(LENGTHS[:-2] + (6000,)))]))
+        L = int(rng.integers(1, n + 1))
+        lines = int(rng.integers(1, 41))
+        params = dict(Na=lines, Nr=n, pulse_s=L / fs, bandwidth_hz=float(rng.uniform(20e6, 110e6)), fs_hz=fs,
+                      range_window=int(rng.integers(0, 2)))
+        assert O.replica_length(params) == L
+        half = rdf.rd_length_supported(n) and rng.random() < 0.3
+        x = rng.standard_normal((lines, n)) + 1j * rng.standard_normal((lines, n))
+        log(f"[sweep] case {case}: n={n} L={L} lines={lines} window={params['range_window']} half={half}")
+        with rdf.Plan(**params) as plan:
+            if half:
+                e16 = to_half(x)
+                got = plan.range_compress_f16(torch.from_numpy(e16).to("cuda")).cpu().numpy()
+                check_half(got, O.range_compress(from_half(e16), params))
+            else:
+                x64 = x.astype(np.complex64)
+                got = plan.range_compress(dev(torch, x64)).cpu().numpy()
+                err = M.rel_l2(got, O.range_compress(x64, params))
+                assert err <= STAGE_TOL, (case, n, L, lines, err)
+
+
 def test_range_compression_table_variant(torch_dev, rdf, monkeypatch):
     """The table-twiddle kernel (selected by RD_RC_VARIANT=table) meets the same bar."""
     torch = torch_dev
