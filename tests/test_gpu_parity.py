@@ -751,3 +751,33 @@ def test_entry_points_replay_from_a_captured_graph(torch_dev, rdf):
             assert torch.equal(rc, rc_e) and torch.equal(img, img_e) and torch.equal(wk, wk_e), i
         log("[graph] 4 replays bit-identical to eager")
         del g
+
+
+def test_two_plans_on_two_streams_concurrently(torch_dev, rdf):
+    """Two plans driven from two streams at once (range compression of one scene while another is
+    focused, then omega-k): plans share no mutable device state, so each result equals the one
+    computed alone."""
+    torch = torch_dev
+    sa, sb = make_scene(C2.with_(Na=512)), make_scene(C1)
+    ref_bin = int(round((C1.r_ref_m - C1.range_bin0_m) / C1.dr))
+    with rdf.Plan(**C2.with_(Na=512).plan_params()) as pa, rdf.Plan(**C1.plan_params()) as pb:
+        ea, eb = dev(torch, sa.echo), dev(torch, sb.echo)
+        rc_alone, img_alone, wk_alone = pa.range_compress(ea), pb.focus(eb), pb.omega_k(eb, ref_bin)
+        torch.cuda.synchronize()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        outs = []
+        for _ in range(3):
+            rc, img, wk = torch.empty_like(ea), torch.empty_like(eb), torch.empty_like(eb)
+            s1.wait_stream(torch.cuda.current_stream())
+            s2.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s1):
+                for _ in range(4):
+                    rdf.rd_range_compress(pa.handle, ea, rc, s1)
+            with torch.cuda.stream(s2):
+                rdf.rd_focus(pb.handle, eb, img, s2)
+                rdf.rd_omega_k(pb.handle, eb, wk, ref_bin, s2)
+            outs.append((rc, img, wk))
+        torch.cuda.synchronize()
+        for rc, img, wk in outs:
+            assert torch.equal(rc, rc_alone) and torch.equal(img, img_alone) and torch.equal(wk, wk_alone)
+    log("[streams] concurrent results equal the ones computed alone")
