@@ -746,7 +746,14 @@ struct Passes<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
 // lane addresses (every workgroup at once) was measured to cost microseconds per launch.
 template <int N>
 __device__ __forceinline__ float2 root_of(int m) {
-  static_assert(N % 4 == 0, "quadrant reduction needs N divisible by 4");
+  if constexpr (N % 4 != 0) {
+    // no exact quadrants: reduce m to (-N/2, N/2], so the argument of sincospi is in (-1, 1]
+    m %= N;
+    if (2 * m > N) m -= N;
+    float sn, cs;
+    sincospif(float(2 * m) / float(N), &sn, &cs);
+    return make_float2(cs, -sn);
+  }
   m %= N;
   const int q = (4 * m) / N;
   const int r = m - q * (N / 4);
@@ -1038,6 +1045,7 @@ struct ColCfg;
   };
 
 using L_16 = IntList<16>;
+using L_5_5 = IntList<5, 5>;
 using L_16_2 = IntList<16, 2>;
 using L_2_16 = IntList<2, 16>;
 using L_16_4 = IntList<16, 4>;
@@ -1050,6 +1058,7 @@ RDF_COL_CFG(32, L_16_2, L_2_16)
 RDF_COL_CFG(64, L_16_4, L_4_16)
 RDF_COL_CFG(128, L_16_8, L_8_16)
 RDF_COL_CFG(256, L_16_16, L_16_16)
+RDF_COL_CFG(25, L_5_5, L_5_5)
 
 #undef RDF_COL_CFG
 

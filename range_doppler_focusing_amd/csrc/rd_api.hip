@@ -301,6 +301,15 @@ bool partial_overlap(const void* a, const void* b, size_t n) {
   return x != y && x < y + n && y < x + n;
 }
 
+// Azimuth lengths of full-chain plans: the two steps of the transform must be built column
+// lengths (16, 32, 64, 128 and 25).
+bool azimuth_pow2(int na) { return na >= 256 && na <= 16384 && (na & (na - 1)) == 0; }
+bool azimuth_five(int na) {
+  if (na % 25 != 0) return false;
+  const int a = na / 25;
+  return a >= 16 && a <= 128 && (a & (a - 1)) == 0;
+}
+
 int persistent_grid(int occ, int cus, int64_t lines, int lpw) {
   const int64_t need = (lines + lpw - 1) / lpw;
   const int64_t resident = int64_t(occ > 0 ? occ : 1) * int64_t(cus > 0 ? cus : 1);
@@ -436,11 +445,11 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   }
   const rdf::LineOps* aops = nullptr;
   if (all_az) {
-    aops = rdf::line_ops(p.Na);
-    if (!aops) return fail(RD_ERR_UNSUPPORTED_LENGTH, "no transform of length Na=%d is built", p.Na);
-    if (p.Na < 256 || p.Na > 16384 || (p.Na & (p.Na - 1)) != 0)
+    aops = rdf::line_ops(p.Na);  // (only the line-transform test hook needs one)
+    if (!azimuth_pow2(p.Na) && !azimuth_five(p.Na))
       return fail(RD_ERR_UNSUPPORTED_LENGTH,
-                  "full-chain plans need Na a power of two in [256, 16384] (Na=%d)", p.Na);
+                  "full-chain plans need Na a power of two in [256, 16384] or 25 * 2^k in [400, 3200] (Na=%d)",
+                  p.Na);
     if (int64_t(p.Na) * p.Nr * 8 > int64_t(0xFFFFFFF0))
       return fail(RD_ERR_INVALID_ARG, "full-chain plans need Na*Nr*8 < 4 GiB");
     if (p.rcmc_taps != 8)
@@ -519,10 +528,16 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   if (all_az) {
     const int Na = p.Na;
     const double lam = kC / p.carrier_hz;
-    // Na = A B with A the largest power of two <= sqrt(Na)
-    P->A = 1;
-    while (P->A * P->A * 4 <= Na) P->A *= 2;
-    P->B = Na / P->A;
+    // Na = A B: A the largest power of two <= sqrt(Na) for powers of two; else A = Na / 25,
+    // B = 25 (both steps are built column transform lengths)
+    if (azimuth_five(Na)) {
+      P->A = Na / 25;
+      P->B = 25;
+    } else {
+      P->A = 1;
+      while (P->A * P->A * 4 <= Na) P->A *= 2;
+      P->B = Na / P->A;
+    }
     std::vector<double> rowc(size_t(Na) * 4);
     double max_shift = 0.0;
     for (int k = 0; k < Na; ++k) {

@@ -409,9 +409,11 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
   twc.load_all(tw, lds + C::COLS * C::LDS, tid, threadIdx.x, C::WG);
   const int g = blockIdx.x / cg.chunks;
   if (cg.twiddle && threadIdx.x < L) {
-    // exact argument: (g t mod Na) / Na, Na a power of two; read after the passes' barriers
+    // exact argument: (g t mod Na) / Na; read after the passes' barriers
+    const int gt = g * int(threadIdx.x);
+    const int m = (cg.na & (cg.na - 1)) == 0 ? gt & (cg.na - 1) : gt % cg.na;
     float sn, cs;
-    sincospif(float((g * int(threadIdx.x)) & (cg.na - 1)) * (2.0f / float(cg.na)), &sn, &cs);
+    sincospif(float(m) * (2.0f / float(cg.na)), &sn, &cs);
     step_tw[threadIdx.x] = make_float2(cs, DIR > 0 ? sn : -sn);
   }
   const int64_t c = int64_t(blockIdx.x - g * cg.chunks) * 64 + col;
@@ -1243,6 +1245,7 @@ hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, con
     case 32: return launch_col<32>(in, out, tw_L, st, cols, na, cached, s);
     case 64: return launch_col<64>(in, out, tw_L, st, cols, na, cached, s);
     case 128: return launch_col<128>(in, out, tw_L, st, cols, na, cached, s);
+    case 25: return launch_col<25>(in, out, tw_L, st, cols, na, cached, s);
     default: return hipErrorInvalidValue;
   }
 }

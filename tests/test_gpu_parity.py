@@ -32,6 +32,11 @@ RD_3001 = SceneConfig(
     fs_hz=120e6, window="rect", n_targets=3, noise_power=0.01, seed=13, carrier_hz=1.0e9,
     prf_hz=600.0, velocity_mps=200.0, r_ref_m=3000.0, sep_range=9, sep_az=100)
 
+# azimuth lengths that are not powers of two (Na = 32 x 25): the image size of the airborne
+# test in nxmr.cn/news/101525 §5.3 (1200 range samples x 800 pulses), and an omega-k case
+RD_800 = C3.with_(name="rd_800x1200", Na=800, Nr=1200, pulse_s=1e-6, n_targets=4)
+WK_800 = C3.with_(name="wk_800x1024", Na=800, Nr=1024, pulse_s=1e-6, n_targets=3)
+
 STAGE_TOL = 1e-5
 IMAGE_TOL = 1e-4
 LENGTHS = (256, 512, 1024, 2048, 4096, 8192, 16384, 6000)
@@ -364,7 +369,7 @@ def check_targets(img, ref_img, targets):
                 assert abs(a - b) <= 0.1, (m, n, axis, key)
 
 
-@pytest.mark.parametrize("cfg", [C1, C3, LONG_MIGRATION, RD_1200, RD_3001], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, C3, LONG_MIGRATION, RD_1200, RD_3001, RD_800], ids=lambda c: c.name)
 def test_focus_every_stage(torch_dev, rdf, cfg):
     torch = torch_dev
     sc, ref = scene_and_stages(cfg)
@@ -454,7 +459,7 @@ def wk_ref_bin(cfg) -> int:
     return int(round((cfg.r_ref_m - cfg.range_bin0_m) / cfg.dr))
 
 
-@pytest.mark.parametrize("cfg", [C1, WK_BIG, WK_C3AZ, WK_6000], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, WK_BIG, WK_C3AZ, WK_6000, WK_800], ids=lambda c: c.name)
 def test_omega_k_matches_oracle(torch_dev, rdf, cfg):
     """rd_omega_k against the oracle at the scene's reference bin and at bin 0; in place gives
     the same bits; targets at the oracle's pixels with the same PSLR / ISLR."""
