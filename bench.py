@@ -419,6 +419,22 @@ def main():
         note(f"rd_focus {acfg.Na} x {acfg.Nr}: {ms * 1e3:.1f} us")
         del x, y
         torch.cuda.empty_cache()
+        # the image size of the pages' airborne test (1200 range samples x 800 pulses): neither
+        # length is a power of two (800 = 32 x 25 azimuth steps, 1200 padded range compression)
+        ocfg = fcfg.with_(Na=800, Nr=1200, pulse_s=1e-6)
+        x = gpu_noise(torch, (ocfg.Na, ocfg.Nr), 33)
+        y = torch.empty_like(x)
+        plan = rdf.Plan(**ocfg.plan_params())
+        ms = time_steps(torch, lambda i: rdf.rd_focus(plan.handle, x, y, stream), 100, 3, stream)
+        plan.close()
+        large.append({"workload": f"full RD focusing of a {ocfg.Nr} x {ocfg.Na} image (range x azimuth; no power-of-two "
+                                  "length), 9.6 GHz, 1 us / 300 MHz at 360 MHz, PRF 1.5 kHz, 150 m/s, 10 km",
+                      "ms_per_step": round(ms, 4), "steps": 100, "value": round(1e3 / ms, 1), "unit": "images/s",
+                      "mpixel_per_s": round(ocfg.Na * ocfg.Nr / (ms * 1e-3) / 1e6, 1),
+                      "data": "seeded complex Gaussian noise on the device (timing is data-independent)"})
+        note(f"rd_focus {ocfg.Na} x {ocfg.Nr}: {ms * 1e3:.1f} us")
+        del x, y
+        torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- corner turn
     if (args.only in (None, "large", "turn")) and not args.no_large:
