@@ -1,13 +1,20 @@
 // Focusing kernels for gfx950.
 //
-// Range compression (cf-1.com/news/2323550 §3.1; nxmr.cn/news/101525 §2.1): one workgroup per
-// range line (or LPW short lines), whole line resident in LDS/VGPRs, so each sample crosses HBM
-// once in and once out.  The grid is persistent: workgroups loop over lines, which keeps H and
-// the twiddles hot in the CU's cache and avoids a launch tail of one-line workgroups.
+// Range compression (cf-1.com/news/2323550 §3.1; nxmr.cn/news/101525 §2.1): each range line is
+// transformed, multiplied by H and inverse transformed in one kernel with the whole line in
+// registers and LDS, so each sample crosses HBM once in and once out.  Persistent grids:
+// workgroups loop over lines with the next line prefetched into registers.  Variants: the
+// 4096-sample DIF/DIT kernel, the register-cached kernel for the other built lengths, the
+// zero-padded form for any length up to 8192, and binary16 line storage.
 //
-// Azimuth processing (cf-1.com/news/2323550 §5.1): corner turn to [Nr][Na], per-row FFT, RCMC
-// along the range axis (nxmr.cn/news/101525 §2.2: a workgroup covers contiguous range rows so
-// neighbouring rows are reused from cache), azimuth filter multiply fused with the inverse FFT.
+// Azimuth processing (cf-1.com/news/2323550 §5.1; nxmr.cn/news/101525 §2.2) in place on
+// [Na][Nr], with no corner turn: the azimuth transform as strided and block column steps, RCMC
+// fused with the azimuth filter per Doppler row from LDS, and the inverse column steps.
+// omega-k (nxmr.cn/news/101525 §3) reuses the column steps around one fused row stage.
+// Also here: the corner turn (an entry point of its own), back-projection
+// (framerc.cn/news/4459478), and the line-transform test hook.
+#include <atomic>
+
 #include "fft_core.hpp"
 #include "rd_kernels.hpp"
 
@@ -883,17 +890,20 @@ hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64
   if (gx * gy > 0x7fffffff) return hipErrorInvalidValue;
   const int tiles = int(gx * gy);
   // persistent grid: the resident workgroups of the whole device (queried once per device)
-  static int resident[64] = {0};
+  // (several host threads may race to fill an entry: they store the same value)
+  static std::atomic<int> resident[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (resident[dev] == 0) {
+  int res = resident[dev].load(std::memory_order_relaxed);
+  if (res == 0) {
     int occ = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_corner_turn<1>, 256, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidValue;
-    resident[dev] = (occ > 0 ? occ : 1) * (cus > 0 ? cus : 1);
+    res = (occ > 0 ? occ : 1) * (cus > 0 ? cus : 1);
+    resident[dev].store(res, std::memory_order_relaxed);
   }
-  const int grid = tiles < resident[dev] ? tiles : resident[dev];
+  const int grid = tiles < res ? tiles : res;
   if (streaming)
     hipLaunchKernelGGL(k_corner_turn<1>, dim3(grid), dim3(256), 0, s, in, out, rows, cols, int(gx), tiles);
   else
