@@ -55,12 +55,13 @@ def wavelength(params) -> float:
 # transform e^{-j...} unnormalised, inverse with 1/N (NumPy convention).
 # ----------------------------------------------------------------------------------------------
 def replica_window(L: int, kind: int) -> np.ndarray:
-    """0 = rectangular, 1 = symmetric Hamming 0.54 - 0.46 cos(2 pi n / (L-1)).
+    """0 = rectangular, 1 = symmetric Hamming 0.54 - 0.46 cos(2 pi n / (L-1)); a one-sample
+    Hamming window (where the formula is 0/0) is [1], the usual convention.
 
     [BP-GPU] §3.1: an unweighted matched filter has about -13 dB sidelobes; Hamming lowers them
     at the cost of a 1.3-1.5x wider mainlobe.  The window is applied to the replica."""
     n = np.arange(L, dtype=np.float64)
-    if kind == 0:
+    if kind == 0 or (kind == 1 and L == 1):
         return np.ones(L)
     if kind == 1:
         return 0.54 - 0.46 * np.cos(2.0 * np.pi * n / (L - 1))

@@ -118,6 +118,12 @@ def test_replica_is_windowed_up_chirp():
     assert C4.replica_len == 1758 and C3.replica_len == 1800 and C1.replica_len == 240
 
 
+@pytest.mark.parametrize("L", [1, 2, 3, 12, 1200, 1758])
+def test_hamming_window_is_the_symmetric_library_window(L):
+    np.testing.assert_allclose(O.replica_window(L, 1), np.hamming(L), rtol=0, atol=1e-15)
+    assert np.array_equal(O.replica_window(L, 0), np.ones(L))
+
+
 @pytest.mark.parametrize("cfg", [C1, C2, C3, C4], ids=lambda c: c.name)
 def test_compressed_chirp_matches_closed_forms(cfg):
     n0 = min(17, cfg.Nr - cfg.replica_len)
