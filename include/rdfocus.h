@@ -141,8 +141,7 @@ rd_status rd_range_compress(rd_plan* plan, const rd_c64* echo, rd_c64* rc, void*
  * transforms), and each output is rounded to the nearest binary16 value (ties to even) on
  * store; magnitudes beyond 65504 become infinities.  HBM traffic is 8 bytes a sample instead of
  * 16.  echo == rc (in place) is allowed; other overlap is an error.  Pointers must be 4-byte
- * aligned.  RD_ERR_UNSUPPORTED_LENGTH if Nr has no built transform (the padded form of
- * rd_range_compress has no binary16 variant). */
+ * aligned.  Every line length rd_range_compress takes is supported (the padded form too). */
 rd_status rd_range_compress_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* rc, void* stream);
 
 /* Azimuth processing of range-compressed data rc [Na][Nr] into the focused image img

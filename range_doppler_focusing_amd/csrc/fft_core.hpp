@@ -630,6 +630,45 @@ __device__ __forceinline__ void store_line_pad(const float2* v, const LineIO& io
   }
 }
 
+// binary16 forms of the padded line I/O above (4-byte elements; same windows)
+template <int N, int T, int R, int AUX = kBufNonTemporal>
+__device__ __forceinline__ void load_line_pad_h(float2* v, const LineIOh& io, int elem0, int tid,
+                                                int n_line, int n_ext) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int r = dft_input_order<R>(i);
+        const int e = j + r * G::NB;
+        const int w = e < n_line ? e : e - n_line;
+        const uint32_t off = e < n_ext ? uint32_t(elem0 + w) * 4u : kBufOff;
+        v[b * R + r] = h2_to_f2(__builtin_amdgcn_raw_buffer_load_b32(io.rsrc, off, 0, AUX));
+      }
+    }
+  }
+}
+
+template <int N, int T, int R, int AUX = kBufNonTemporal>
+__device__ __forceinline__ void store_line_pad_h(const float2* v, const LineIOh& io, int elem0, int tid,
+                                                 int n_line, int skip) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int o = j + r * G::NB - skip;
+        const uint32_t off = uint32_t(o) < uint32_t(n_line) ? uint32_t(elem0 + o) * 4u : kBufOff;
+        __builtin_amdgcn_raw_buffer_store_b32(f2_to_h2(v[b * R + r]), io.rsrc, off, 0, AUX);
+      }
+    }
+  }
+}
+
 // Reads of the pass after the exchange keyed NS (the product of the radices before it).
 template <int N, int T, int R, int NS>
 __device__ __forceinline__ void load_lds(float2* v, const float2* lds, int tid) {

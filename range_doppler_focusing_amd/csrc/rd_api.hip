@@ -514,9 +514,10 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
       P->rc_variant = 1;
       P->rc_grid = persistent_grid(occ, P->cus, p.Na, rops->lpw);
     }
-    if (rops->range_compress_f16 && !pad_m) {
+    if (rops->range_compress_f16) {
       int occ16 = 0;
-      if (rops->occupancy_f16(&occ16) != hipSuccess) return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
+      if (rops->occupancy_f16(&occ16, pad_m ? 1 : 0) != hipSuccess)
+        return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
       P->f16_grid = persistent_grid(occ16, P->cus, p.Na, rops->lpw);
     }
     const char* g = std::getenv("RD_RC_GRID");  // workgroups of the range kernel (tuning)
@@ -618,12 +619,13 @@ rd_status rd_range_compress_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* rc,
   rd_status st = check_call(plan);
   if (st != RD_OK) return st;
   if (plan->f16_grid <= 0)
-    return fail(RD_ERR_UNSUPPORTED_LENGTH, "binary16 storage needs a built transform of length Nr=%d", plan->p.Nr);
+    return fail(RD_ERR_UNSUPPORTED_LENGTH, "no binary16 range kernel for Nr=%d", plan->p.Nr);
   if (!aligned4(echo) || !aligned4(rc)) return fail(RD_ERR_INVALID_ARG, "echo and rc must be non-NULL and 4-byte aligned");
   const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c32h);
   if (partial_overlap(echo, rc, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and rc overlap without being equal");
   return check_hip(plan->rops->range_compress_f16(echo, rc, plan->H, plan->tw_r, plan->rc_tab, plan->p.Na,
-                                                  plan->f16_grid, static_cast<hipStream_t>(stream)),
+                                                  plan->f16_grid, plan->p.Nr, plan->pad_m ? plan->L - 1 : 0,
+                                                  static_cast<hipStream_t>(stream)),
                    "binary16 range compression launch");
 }
 

@@ -133,9 +133,11 @@ __device__ __forceinline__ void rc_load(float2* v, const void* in, int64_t l0, i
                                         int tid, int n_line, int skip) {
   using C = LineCfg<N>;
   constexpr int R0 = ListInfo<typename C::Fwd>::first;
-  static_assert(!(PAD && HALF), "binary16 storage has no padded form");
   const float2* src = static_cast<const float2*>(in);
-  if constexpr (PAD)
+  if constexpr (PAD && HALF)
+    load_line_pad_h<N, C::T, R0>(v, LineIOh(in, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
+                                 n_line + skip);
+  else if constexpr (PAD)
     load_line_pad<N, C::T, R0>(v, LineIO(src, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
                                n_line + skip);
   else if constexpr (HALF)
@@ -149,7 +151,10 @@ __device__ __forceinline__ void rc_store(const float2* v, void* out, int64_t l0,
   using C = LineCfg<N>;
   constexpr int R0 = ListInfo<typename C::Fwd>::first;
   float2* dst = static_cast<float2*>(out);
-  if constexpr (PAD)
+  if constexpr (PAD && HALF)
+    store_line_pad_h<N, C::T, R0, SAUX>(v, LineIOh(out, n_line, l0, C::LPW, lines), grp * n_line, tid,
+                                        n_line, skip);
+  else if constexpr (PAD)
     store_line_pad<N, C::T, R0, SAUX>(v, LineIO(dst, n_line, l0, C::LPW, lines), grp * n_line, tid, n_line,
                                       skip);
   else if constexpr (HALF)
@@ -1102,8 +1107,14 @@ hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const fl
 // 32-bit line I/O; streaming stores
 template <int N>
 hipError_t launch_rc_f16(const void* in, void* out, const float2* H, const float2* tw, const float2* tab,
-                         int64_t lines, int grid, hipStream_t s) {
+                         int64_t lines, int grid, int n_line, int skip, hipStream_t s) {
   constexpr bool PF = RD_RC_PREFETCH && LineCfg<N>::PF;
+  if (n_line != N) {
+    if (n_line <= 0 || skip < 0 || skip >= n_line || n_line + skip > N) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream, true, true>), dim3(grid), dim3(LineCfg<N>::WG), 0,
+                       s, in, out, H, tw, lines, n_line, skip);
+    return hipGetLastError();
+  }
   if constexpr (N == 4096 && RD_RC_4096) {
     hipLaunchKernelGGL((k_range_compress_4096<kAuxStream, true>), dim3(grid), dim3(256), 0, s, in, out, tab, lines);
   } else {
@@ -1114,7 +1125,10 @@ hipError_t launch_rc_f16(const void* in, void* out, const float2* H, const float
 }
 
 template <int N>
-hipError_t occupancy_f16(int* rc) {
+hipError_t occupancy_f16(int* rc, int pad) {
+  if (pad)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream, true, true>, LineCfg<N>::WG, 0);
   if constexpr (N == 4096 && RD_RC_4096)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_4096<kAuxStream, true>, 256, 0);
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(

@@ -88,10 +88,11 @@ struct LineOps {
   hipError_t (*occupancy_wk)(int* wgs);
   int wk_cap;
   // range compression with binary16 line storage (4 bytes a sample in and out, float32
-  // arithmetic; tab as for range_compress_pf) and its occupancy
+  // arithmetic; tab, n_line and skip as for range_compress_pf) and its occupancy
   hipError_t (*range_compress_f16)(const void* in, void* out, const float2* H, const float2* tw,
-                                   const float2* tab, int64_t lines, int grid, hipStream_t s);
-  hipError_t (*occupancy_f16)(int* wgs);
+                                   const float2* tab, int64_t lines, int grid, int n_line, int skip,
+                                   hipStream_t s);
+  hipError_t (*occupancy_f16)(int* wgs, int pad);
 };
 
 // nullptr if the length has no built transform

@@ -278,13 +278,27 @@ def test_range_compression_f16_workload(torch_dev, rdf):
             assert int(np.argmax(np.abs(got[m, n - 4:n + 5]))) == 4 == int(np.argmax(np.abs(ref[m, n - 4:n + 5])))
 
 
+@pytest.mark.parametrize("n,L", [(1, 1), (1200, 400), (1201, 1201), (5000, 1666), (8191, 2730)],
+                         ids=lambda v: str(v))
+def test_range_compression_f16_any_length(torch_dev, rdf, n, L):
+    """binary16 storage at line lengths with no built transform (the padded form)."""
+    torch = torch_dev
+    rng = np.random.default_rng(5000 + n)
+    fs = 120e6
+    params = dict(Na=37, Nr=n, pulse_s=L / fs, bandwidth_hz=90e6, fs_hz=fs, range_window=1)
+    echo = to_half(rng.standard_normal((37, n)) + 1j * rng.standard_normal((37, n)))
+    with rdf.Plan(**params) as plan:
+        x = torch.from_numpy(echo).to("cuda")
+        rc = plan.range_compress_f16(x).cpu().numpy()
+        plan.range_compress_f16(x, out=x)
+        torch.cuda.synchronize()
+        assert np.array_equal(x.cpu().numpy().view(np.uint16), rc.view(np.uint16))
+    err = check_half(rc, O.range_compress(from_half(echo), params))
+    log(f"[range f16] any length n={n} L={L} rel-L2 {err:.2e}")
+
+
 def test_range_compression_f16_error_paths(torch_dev, rdf):
     torch = torch_dev
-    with rdf.Plan(Na=4, Nr=1200, pulse_s=400 / 120e6, bandwidth_hz=100e6, fs_hz=120e6) as plan:
-        x = torch.zeros((4, 1200, 2), dtype=torch.float16, device="cuda")
-        with pytest.raises(rdf.RdError) as ei:      # padded lengths have no binary16 form
-            plan.range_compress_f16(x)
-        assert ei.value.status == -2
     with rdf.Plan(Na=4, Nr=256, pulse_s=100 / 120e6, bandwidth_hz=100e6, fs_hz=120e6) as plan:
         x = torch.zeros((4, 256, 2), dtype=torch.float16, device="cuda")
         with pytest.raises(rdf.RdError) as ei:
@@ -297,8 +311,8 @@ def test_range_compression_f16_error_paths(torch_dev, rdf):
 
 def test_range_compression_random_sweep(torch_dev, rdf):
     """40 seeded random cases: line length 1..8192 (built or not), replica length 1..n, 1..40
-    lines, either window, float32 or (where a transform of that length is built) binary16
-    storage; each against the oracle on the same input."""
+    lines, either window, float32 or binary16 storage; each against the oracle on the same
+    input."""
     torch = torch_dev
     rng = np.random.default_rng(4242)
     fs = 120e6
@@ -309,7 +323,7 @@ def test_range_compression_random_sweep(torch_dev, rdf):
         params = dict(Na=lines, Nr=n, pulse_s=L / fs, bandwidth_hz=float(rng.uniform(20e6, 110e6)), fs_hz=fs,
                       range_window=int(rng.integers(0, 2)))
         assert O.replica_length(params) == L
-        half = rdf.rd_length_supported(n) and rng.random() < 0.3
+        half = rng.random() < 0.3
         x = rng.standard_normal((lines, n)) + 1j * rng.standard_normal((lines, n))
         log(f"[sweep] case {case}: n={n} L={L} lines={lines} window={params['range_window']} half={half}")
         with rdf.Plan(**params) as plan:
