@@ -412,6 +412,8 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
   constexpr int RI = ListInfo<LST>::first;
   constexpr int RO = ListInfo<LST>::last;
   using TC = TwCache<L, T, 1, LST>;
+  static_assert(Geom<L, T, RI>::FULL && Geom<L, T, RO>::FULL,
+                "the column loads and stores below assume every lane's butterflies are live");
   __shared__ float2 lds[C::COLS * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
   __shared__ float2 step_tw[L];  // inter-step twiddles W_Na^{DIR g t}, t < L
   const int col = threadIdx.x & 63;
