@@ -55,7 +55,14 @@ struct rd_plan {
   int rcmc_margin = 0;  // samples the RCMC kernel stages after a chunk (shifts up to margin - 5)
   int cached = 0;       // image passes use ordinary (cacheable) accesses: image fits the cache
   int rc_grid = 0;      // persistent grid of the range kernels
-  int A = 0, B = 0;     // Na = A B: strided and block steps of the azimuth transform
+  int A = 0, B = 0;     // Doppler row order after the forward azimuth transform: row r holds bin
+                        // r / B + A (r % B) (digit order of the two steps; A = 1, B = Na when the
+                        // transform is the Bluestein form, whose output is in natural order)
+  int ca = 0, cb = 0;   // the column transform steps: lengths ca (strided) and cb (block)
+  int col_n = 0;        // their transform length ca cb: Na, or M for the Bluestein form
+  int bs_m = 0;         // > 0: the azimuth transform is Bluestein's, through columns of length M
+  float2* bs_ws = nullptr;   // [M][Nr] Bluestein workspace
+  float2* bs_fb = nullptr;   // [2][M] spectra of the two chirps / M, in the column steps' row order
   float2* H = nullptr;       // [Nr] conj(FFT(h)) / Nr
   float2* tw_r = nullptr;    // [Nr] e^{-j 2 pi k / Nr}
   float2* rc_tab = nullptr;  // per-thread constants of the range kernel (null if it has none)
@@ -87,6 +94,8 @@ void free_plan(rd_plan* p) {
   (void)hipFree(p->tw_B);
   (void)hipFree(p->rowc);
   (void)hipFree(p->work);
+  (void)hipFree(p->bs_ws);
+  (void)hipFree(p->bs_fb);
   delete p;
 }
 
@@ -203,6 +212,35 @@ std::vector<float2> padded_filter(const rd_params& p, int L, int M) {
   return out;
 }
 
+// Spectra of the Bluestein chirps for an azimuth DFT of length Na through columns of length M:
+// b[n] = exp(-sign j pi n^2 / Na) for |n| < Na, placed circularly (b[M - n] = b[n]), zero
+// elsewhere; B = FFT_M(b) / M (the 1/M of the inverse column transform folded in), evaluated in
+// float64 and rounded once, forward (sign -1) then inverse (sign +1), each in the column steps'
+// output row order (row r holds bin r / cb + ca (r % cb)).
+std::vector<float2> bluestein_spectra(int na, int m, int ca, int cb) {
+  std::vector<float2> out(static_cast<size_t>(2 * m));
+  for (int d = 0; d < 2; ++d) {
+    const double sign = d == 0 ? -1.0 : 1.0;
+    std::vector<double> re(size_t(m), 0.0), im(size_t(m), 0.0);
+    for (int n = 0; n < na; ++n) {
+      const int64_t q = (int64_t(n) * n) % (2 * int64_t(na));
+      const double ph = -sign * M_PI * double(q) / double(na);
+      re[size_t(n)] = std::cos(ph);
+      im[size_t(n)] = std::sin(ph);
+      if (n > 0) {
+        re[size_t(m - n)] = re[size_t(n)];
+        im[size_t(m - n)] = im[size_t(n)];
+      }
+    }
+    fft_pow2(re, im);
+    for (int r = 0; r < m; ++r) {
+      const int bin = r / cb + ca * (r % cb);
+      out[size_t(d * m + r)] = make_float2(float(re[size_t(bin)] / m), float(im[size_t(bin)] / m));
+    }
+  }
+  return out;
+}
+
 // RCMC tap weights (nxmr.cn/news/101525 §2.2 interpolates the migrated range; the 8-tap
 // Kaiser-windowed sinc is the interpolator).  For fraction f in [0, 1) the output reads samples
 // floor(x) - 3 .. floor(x) + 4 with weights w_j = sinc(f - j) K(f - j) / sum, K the Kaiser
@@ -304,6 +342,18 @@ bool partial_overlap(const void* a, const void* b, size_t n) {
 // Azimuth lengths of full-chain plans: the two steps of the transform must be built column
 // lengths (16, 32, 64, 128 and 25).
 bool azimuth_pow2(int na) { return na >= 256 && na <= 16384 && (na & (na - 1)) == 0; }
+// column transform length of the Bluestein form: a power of two >= 2 Na - 1 (at least 256)
+int bluestein_m(int na) {
+  int m = 256;
+  while (m < 2 * na - 1) m *= 2;
+  return m;
+}
+// Na = A B with A the largest power of two <= sqrt(Na) (Na a power of two >= 256)
+void pow2_split(int n, int* a, int* b) {
+  *a = 1;
+  while (*a * *a * 4 <= n) *a *= 2;
+  *b = n / *a;
+}
 bool azimuth_five(int na) {
   if (na % 25 != 0) return false;
   const int a = na / 25;
@@ -336,16 +386,16 @@ rdf::ColStep col_step(const rd_plan* P, bool forward, bool strided) {
   rdf::ColStep st{};
   st.dir = forward ? -1 : +1;
   if (strided) {
-    st.L = P->A;
+    st.L = P->ca;
     st.base_mul = 1;
-    st.stride = P->B;
-    st.sets = P->B;
+    st.stride = P->cb;
+    st.sets = P->cb;
     st.twiddle = forward ? 1 : 0;
   } else {
-    st.L = P->B;
-    st.base_mul = P->B;
+    st.L = P->cb;
+    st.base_mul = P->cb;
     st.stride = 1;
-    st.sets = P->A;
+    st.sets = P->ca;
     st.twiddle = forward ? 0 : 1;
   }
   return st;
@@ -354,9 +404,43 @@ rdf::ColStep col_step(const rd_plan* P, bool forward, bool strided) {
 rd_status run_col(rd_plan* P, const float2* src, float2* dst, bool forward, bool strided,
                   hipStream_t s) {
   const rdf::ColStep st = col_step(P, forward, strided);
-  return check_hip(rdf::launch_col_fft(src, dst, strided ? P->tw_A : P->tw_B, st, P->p.Nr, P->p.Na,
+  return check_hip(rdf::launch_col_fft(src, dst, strided ? P->tw_A : P->tw_B, st, P->p.Nr, P->col_n,
                                        P->cached, s),
                    "azimuth transform launch");
+}
+
+// Bluestein form of an azimuth DFT of length Na (sign -1 forward, +1 inverse unnormalised):
+// X[k] = c[k] sum_m (x[m] c[m]) conj(c[k - m]) with c[n] = exp(sign j pi n^2 / Na), the sum a
+// linear convolution done as a length-M circular one (M >= 2 Na - 1) by the column steps.
+rd_status run_bluestein(rd_plan* P, const float2* src, float2* dst, int sign, hipStream_t s) {
+  const int Na = P->p.Na, M = P->bs_m;
+  const int64_t Nr = P->p.Nr;
+  float2* W = P->bs_ws;
+  rd_status st;
+  if ((st = check_hip(rdf::launch_chirp_rows(src, W, Nr, Na, M, Na, sign, s), "chirp launch")) != RD_OK) return st;
+  if ((st = run_col(P, W, W, true, true, s)) != RD_OK) return st;
+  if ((st = run_col(P, W, W, true, false, s)) != RD_OK) return st;
+  if ((st = check_hip(rdf::launch_scale_rows(W, P->bs_fb + (sign < 0 ? 0 : M), Nr, M, s), "scale launch")) != RD_OK)
+    return st;
+  if ((st = run_col(P, W, W, false, false, s)) != RD_OK) return st;
+  if ((st = run_col(P, W, W, false, true, s)) != RD_OK) return st;
+  return check_hip(rdf::launch_chirp_rows(W, dst, Nr, Na, Na, Na, sign, s), "chirp launch");
+}
+
+// The azimuth transform: src [Na][Nr] (pulses) -> dst, row r holding Doppler bin r / B + A (r % B)
+rd_status az_forward(rd_plan* P, const float2* src, float2* dst, hipStream_t s) {
+  if (P->bs_m) return run_bluestein(P, src, dst, -1, s);
+  rd_status st;
+  if ((st = run_col(P, src, dst, true, true, s)) != RD_OK) return st;
+  return run_col(P, dst, dst, true, false, s);
+}
+
+// Its inverse (unnormalised; 1/Na is folded into the row stage), in place, back to pulse order
+rd_status az_inverse(rd_plan* P, float2* io, hipStream_t s) {
+  if (P->bs_m) return run_bluestein(P, io, io, +1, s);
+  rd_status st;
+  if ((st = run_col(P, io, io, false, false, s)) != RD_OK) return st;
+  return run_col(P, io, io, false, true, s);
 }
 
 rd_status run_rows(rd_plan* P, const float2* src, float2* dst, bool filter, hipStream_t s) {
@@ -378,11 +462,9 @@ rd_status check_rcmc_margin(const rd_plan* P) {
 rd_status run_azimuth(rd_plan* P, const float2* rc, float2* img, hipStream_t s) {
   // rc is read only by the first step, so img may alias it
   rd_status st;
-  if ((st = run_col(P, rc, img, true, true, s)) != RD_OK) return st;
-  if ((st = run_col(P, img, img, true, false, s)) != RD_OK) return st;
+  if ((st = az_forward(P, rc, img, s)) != RD_OK) return st;
   if ((st = run_rows(P, img, img, true, s)) != RD_OK) return st;
-  if ((st = run_col(P, img, img, false, false, s)) != RD_OK) return st;
-  return run_col(P, img, img, false, true, s);
+  return az_inverse(P, img, s);
 }
 
 }  // namespace
@@ -446,12 +528,13 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   const rdf::LineOps* aops = nullptr;
   if (all_az) {
     aops = rdf::line_ops(p.Na);  // (only the line-transform test hook needs one)
-    if (!azimuth_pow2(p.Na) && !azimuth_five(p.Na))
+    const bool bluestein = !azimuth_pow2(p.Na) && !azimuth_five(p.Na);
+    if (bluestein && (p.Na < 16 || p.Na > 8192))
       return fail(RD_ERR_UNSUPPORTED_LENGTH,
-                  "full-chain plans need Na a power of two in [256, 16384] or 25 * 2^k in [400, 3200] (Na=%d)",
-                  p.Na);
-    if (int64_t(p.Na) * p.Nr * 8 > int64_t(0xFFFFFFF0))
-      return fail(RD_ERR_INVALID_ARG, "full-chain plans need Na*Nr*8 < 4 GiB");
+                  "full-chain plans need Na a power of two in [256, 16384], 25 * 2^k in [400, 3200], or "
+                  "16..8192 for the Bluestein form (Na=%d)", p.Na);
+    if (int64_t(bluestein ? bluestein_m(p.Na) : p.Na) * p.Nr * 8 > int64_t(0xFFFFFFF0))
+      return fail(RD_ERR_INVALID_ARG, "full-chain plans need Na*Nr*8 (M*Nr*8 for the Bluestein form) < 4 GiB");
     if (p.rcmc_taps != 8)
       return fail(RD_ERR_INVALID_ARG, "rcmc_taps=%d: only the 8-tap interpolator is built", p.rcmc_taps);
     if (!(p.kaiser_beta >= 0.0 && p.kaiser_beta <= 12.0))
@@ -532,13 +615,20 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     // Na = A B: A the largest power of two <= sqrt(Na) for powers of two; else A = Na / 25,
     // B = 25 (both steps are built column transform lengths)
     if (azimuth_five(Na)) {
-      P->A = Na / 25;
-      P->B = 25;
+      P->ca = Na / 25;
+      P->cb = 25;
+      P->col_n = Na;
+    } else if (azimuth_pow2(Na)) {
+      pow2_split(Na, &P->ca, &P->cb);
+      P->col_n = Na;
     } else {
-      P->A = 1;
-      while (P->A * P->A * 4 <= Na) P->A *= 2;
-      P->B = Na / P->A;
+      // Bluestein: columns of length M; the transform's output rows are in natural order
+      P->bs_m = bluestein_m(Na);
+      pow2_split(P->bs_m, &P->ca, &P->cb);
+      P->col_n = P->bs_m;
     }
+    P->A = P->bs_m ? 1 : P->ca;
+    P->B = P->bs_m ? Na : P->cb;
     std::vector<double> rowc(size_t(Na) * 4);
     double max_shift = 0.0;
     for (int k = 0; k < Na; ++k) {
@@ -573,8 +663,16 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
         P->wk_grid = persistent_grid(occ, P->cus, Na, rops->lpw);
       }
     }
-    if ((st = upload(&P->tw_A, roots_table(P->A), "azimuth step twiddles")) != RD_OK) return bail(st);
-    if ((st = upload(&P->tw_B, roots_table(P->B), "azimuth step twiddles")) != RD_OK) return bail(st);
+    if ((st = upload(&P->tw_A, roots_table(P->ca), "azimuth step twiddles")) != RD_OK) return bail(st);
+    if ((st = upload(&P->tw_B, roots_table(P->cb), "azimuth step twiddles")) != RD_OK) return bail(st);
+    if (P->bs_m) {
+      if ((st = upload(&P->bs_fb, bluestein_spectra(Na, P->bs_m, P->ca, P->cb), "Bluestein chirp spectra")) != RD_OK)
+        return bail(st);
+      if (hipMalloc(&P->bs_ws, size_t(P->bs_m) * size_t(p.Nr) * sizeof(float2)) != hipSuccess) {
+        P->bs_ws = nullptr;
+        return bail(fail(RD_ERR_OUT_OF_MEMORY, "hipMalloc of the Bluestein workspace failed"));
+      }
+    }
     if ((st = upload(&P->rowc, rowc, "azimuth row coefficients")) != RD_OK) return bail(st);
     P->az.row = P->rowc;
     P->az.A = P->A;
@@ -690,14 +788,12 @@ rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref
   float2* I = reinterpret_cast<float2*>(img);
   // the azimuth transform first (the 2-D transform's order is free), then one row stage per
   // Doppler row, then the inverse azimuth transform; echo is read only by the first step
-  if ((st = run_col(plan, reinterpret_cast<const float2*>(echo), I, true, true, s)) != RD_OK) return st;
-  if ((st = run_col(plan, I, I, true, false, s)) != RD_OK) return st;
+  if ((st = az_forward(plan, reinterpret_cast<const float2*>(echo), I, s)) != RD_OK) return st;
   if ((st = check_hip(plan->rops->omega_k_rows(I, I, plan->H, plan->tw_r, c, plan->az.w, p.Na, plan->wk_grid,
                                                plan->cached, s),
                       "omega-k row stage launch")) != RD_OK)
     return st;
-  if ((st = run_col(plan, I, I, false, false, s)) != RD_OK) return st;
-  return run_col(plan, I, I, false, true, s);
+  return az_inverse(plan, I, s);
 }
 
 rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft, rd_c64* rcmc,
@@ -727,8 +823,7 @@ rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft
   float2* I = reinterpret_cast<float2*>(img);
   float2* W = plan->work;
   const int64_t Nr = plan->p.Nr;
-  if ((st = run_col(plan, reinterpret_cast<const float2*>(rc), I, true, true, s)) != RD_OK) return st;
-  if ((st = run_col(plan, I, I, true, false, s)) != RD_OK) return st;
+  if ((st = az_forward(plan, reinterpret_cast<const float2*>(rc), I, s)) != RD_OK) return st;
   if ((st = run_rows(plan, I, W, false, s)) != RD_OK) return st;  // RCMC alone
   if ((st = check_hip(rdf::launch_row_unpermute(I, reinterpret_cast<float2*>(azfft), plan->A, plan->B,
                                                 Nr, s), "row order launch")) != RD_OK)
@@ -737,8 +832,7 @@ rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft
                                                 Nr, s), "row order launch")) != RD_OK)
     return st;
   if ((st = run_rows(plan, I, I, true, s)) != RD_OK) return st;
-  if ((st = run_col(plan, I, I, false, false, s)) != RD_OK) return st;
-  return run_col(plan, I, I, false, true, s);
+  return az_inverse(plan, I, s);
 }
 
 rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const rd_c64* in,

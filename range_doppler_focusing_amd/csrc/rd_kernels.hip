@@ -1276,6 +1276,50 @@ hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, con
   }
 }
 
+// Bluestein (chirp-z) transforms along the azimuth axis (nxmr.cn/news/101525 §5.1: any length):
+// the two elementwise row passes.  out[r][c] = in[r][c] exp(sign j pi r^2 / na) for r < rows_in
+// and 0 for rows_in <= r < rows_out (r^2 reduced modulo 2 na in integers, so the argument of
+// sincospi is exact and below 2); io[r][c] *= f[r].
+__global__ void __launch_bounds__(256)
+    k_chirp_rows(const float2* __restrict__ in, float2* __restrict__ out, int64_t cols, int rows_in, int na,
+                 int sign) {
+  const int r = blockIdx.y;
+  const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (c >= cols) return;
+  float2 v = make_float2(0.f, 0.f);
+  if (r < rows_in) {
+    const int64_t q = (int64_t(r) * r) % (2 * int64_t(na));
+    float sn, cs;
+    sincospif(float(q) / float(na), &sn, &cs);
+    v = cmul(in[int64_t(r) * cols + c], make_float2(cs, sign > 0 ? sn : -sn));
+  }
+  out[int64_t(r) * cols + c] = v;
+}
+
+__global__ void __launch_bounds__(256)
+    k_scale_rows(float2* __restrict__ io, const float2* __restrict__ f, int64_t cols) {
+  const int r = blockIdx.y;
+  const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (c < cols) io[int64_t(r) * cols + c] = cmul(io[int64_t(r) * cols + c], f[r]);
+}
+
+hipError_t launch_chirp_rows(const float2* in, float2* out, int64_t cols, int rows_in, int rows_out, int na,
+                             int sign, hipStream_t s) {
+  const int64_t gx = (cols + 255) / 256;
+  if (gx > 0x7fffffff || rows_out <= 0 || rows_out > 65535 || rows_in > rows_out || na <= 0)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_chirp_rows, dim3(unsigned(gx), unsigned(rows_out)), dim3(256), 0, s, in, out, cols, rows_in,
+                     na, sign);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_rows(float2* io, const float2* f, int64_t cols, int rows, hipStream_t s) {
+  const int64_t gx = (cols + 255) / 256;
+  if (gx > 0x7fffffff || rows <= 0 || rows > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_scale_rows, dim3(unsigned(gx), unsigned(rows)), dim3(256), 0, s, io, f, cols);
+  return hipGetLastError();
+}
+
 hipError_t launch_row_unpermute(const float2* in, float2* out, int A, int B, int64_t cols,
                                 hipStream_t s) {
   hipLaunchKernelGGL(k_row_unpermute, dim3(unsigned(A * B)), dim3(256), 0, s, in, out, A, B, cols);

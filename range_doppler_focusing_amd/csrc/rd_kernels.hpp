@@ -136,6 +136,10 @@ hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64
                               int streaming, hipStream_t s);
 
 // out[k] = in[(k % A) B + k / A] for rows of `cols` samples: Doppler-digit row order to natural
+// Bluestein row passes (see rd_kernels.hip): chirp multiply with zero fill, and a per-row scale
+hipError_t launch_chirp_rows(const float2* in, float2* out, int64_t cols, int rows_in, int rows_out, int na,
+                             int sign, hipStream_t s);
+hipError_t launch_scale_rows(float2* io, const float2* f, int64_t cols, int rows, hipStream_t s);
 hipError_t launch_row_unpermute(const float2* in, float2* out, int A, int B, int64_t cols,
                                 hipStream_t s);
 

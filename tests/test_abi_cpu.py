@@ -76,8 +76,8 @@ def good_params(**kw):
     (dict(range_window=7), -1), (dict(flags=1), -1),
     (dict(pulse_s=1e-3), -1),                       # replica longer than the line
     (dict(prf_hz=0.0), -1),                         # half-configured azimuth
-    (dict(Nr=9000), -2), (dict(Na=3000), -2),       # no transform of that length, none padded
-    (dict(Na=6400), -2), (dict(Na=375), -2),        # azimuth: 25 * 256, 15 * 25 (no column steps)
+    (dict(Nr=9000), -2), (dict(Na=9000), -2),       # no transform of that length, none padded
+    (dict(Na=12), -2),                              # azimuth below the Bluestein form's range
     (dict(Nr=9000, carrier_hz=0.0, prf_hz=0.0, velocity_mps=0.0), -2),  # range-only, beyond 8192
     (dict(rcmc_taps=6), -1), (dict(kaiser_beta=-1.0), -1),
     (dict(velocity_mps=1.0), -1),                   # Doppler band beyond 2V/lambda

@@ -36,6 +36,9 @@ RD_3001 = SceneConfig(
 # test in nxmr.cn/news/101525 §5.3 (1200 range samples x 800 pulses), and an omega-k case
 RD_800 = C3.with_(name="rd_800x1200", Na=800, Nr=1200, pulse_s=1e-6, n_targets=4)
 WK_800 = C3.with_(name="wk_800x1024", Na=800, Nr=1024, pulse_s=1e-6, n_targets=3)
+# azimuth lengths through the Bluestein form: 1000 = 2^3 5^3, and the prime 997
+RD_1000 = C3.with_(name="rd_1000x1024", Na=1000, Nr=1024, pulse_s=1e-6, n_targets=3)
+WK_997 = C3.with_(name="wk_997x1024", Na=997, Nr=1024, pulse_s=1e-6, n_targets=3)
 
 STAGE_TOL = 1e-5
 IMAGE_TOL = 1e-4
@@ -383,7 +386,8 @@ def check_targets(img, ref_img, targets):
                 assert abs(a - b) <= 0.1, (m, n, axis, key)
 
 
-@pytest.mark.parametrize("cfg", [C1, C3, LONG_MIGRATION, RD_1200, RD_3001, RD_800], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, C3, LONG_MIGRATION, RD_1200, RD_3001, RD_800, RD_1000, WK_997],
+                         ids=lambda c: c.name)
 def test_focus_every_stage(torch_dev, rdf, cfg):
     torch = torch_dev
     sc, ref = scene_and_stages(cfg)
@@ -473,7 +477,7 @@ def wk_ref_bin(cfg) -> int:
     return int(round((cfg.r_ref_m - cfg.range_bin0_m) / cfg.dr))
 
 
-@pytest.mark.parametrize("cfg", [C1, WK_BIG, WK_C3AZ, WK_6000, WK_800], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, WK_BIG, WK_C3AZ, WK_6000, WK_800, WK_997], ids=lambda c: c.name)
 def test_omega_k_matches_oracle(torch_dev, rdf, cfg):
     """rd_omega_k against the oracle at the scene's reference bin and at bin 0; in place gives
     the same bits; targets at the oracle's pixels with the same PSLR / ISLR."""
