@@ -435,6 +435,21 @@ def main():
         note(f"rd_focus {ocfg.Na} x {ocfg.Nr}: {ms * 1e3:.1f} us")
         del x, y
         torch.cuda.empty_cache()
+        # a prime azimuth length: the Bluestein form of the azimuth transform (M = 2048)
+        pcfg = fcfg.with_(Na=997, Nr=1024, pulse_s=1e-6)
+        x = gpu_noise(torch, (pcfg.Na, pcfg.Nr), 34)
+        y = torch.empty_like(x)
+        plan = rdf.Plan(**pcfg.plan_params())
+        ms = time_steps(torch, lambda i: rdf.rd_focus(plan.handle, x, y, stream), 100, 3, stream)
+        plan.close()
+        large.append({"workload": f"full RD focusing with a prime azimuth length (Bluestein form), {pcfg.Na} x {pcfg.Nr} "
+                                  "complex64, 9.6 GHz, 1 us / 300 MHz at 360 MHz, PRF 1.5 kHz, 150 m/s, 10 km",
+                      "ms_per_step": round(ms, 4), "steps": 100,
+                      "value": round(pcfg.Na * pcfg.Nr / (ms * 1e-3) / 1e6, 1), "unit": "Mpixel/s",
+                      "data": "seeded complex Gaussian noise on the device (timing is data-independent)"})
+        note(f"rd_focus {pcfg.Na} x {pcfg.Nr}: {ms * 1e3:.1f} us")
+        del x, y
+        torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- corner turn
     if (args.only in (None, "large", "turn")) and not args.no_large:

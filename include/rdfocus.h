@@ -103,9 +103,11 @@ typedef struct rd_plan rd_plan;
  * 6000 = 2^4 * 3 * 5^3), else 0.  Plans also accept any other Nr in 1..8192: range compression
  * then runs as a zero-padded convolution (see rd_range_compress) and the RCMC of the
  * range-Doppler chain on rows of that length; rd_omega_k and rd_debug_line_fft along range need
- * a built length.  Full-chain plans also need Na a power of two in [256, 16384] or
- * 25 * 2^k in [400, 3200] (nxmr.cn/news/101525 §5.3 images 1200 x 800), and Na*Nr*8 < 4 GiB
- * (checked by rd_plan_create).  The range-Doppler entry points
+ * a built length.  Full-chain plans also need Na a power of two in [256, 16384], 25 * 2^k in
+ * [400, 3200] (nxmr.cn/news/101525 §5.3 images 1200 x 800), or any other Na in [16, 8192]: the
+ * azimuth transform then takes the Bluestein (chirp-z) form of §5.1 through column transforms
+ * of length M = the smallest power of two >= max(256, 2 Na - 1), with a plan-owned workspace of
+ * M*Nr*8 bytes; and Na*Nr*8 (M*Nr*8) < 4 GiB (checked by rd_plan_create).  The range-Doppler entry points
  * (rd_azimuth_focus, rd_focus and the stage hook) further need a range migration
  * R(n)(1/D_k - 1)/dr below Nr/8 - 5 samples (1019 samples at lengths with no built transform)
  * over the whole Doppler band; beyond it they return RD_ERR_UNSUPPORTED_LENGTH, while the plan
