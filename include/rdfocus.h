@@ -159,6 +159,23 @@ rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* s
  * allowed.  RD_ERR_NOT_CONFIGURED on a range-only plan. */
 rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream);
 
+/* rd_focus with binary16 storage of the echo, of every intermediate and of the image
+ * (cf-1.com/news/2323550 §7: FP16 storage, FP32 arithmetic): echo and img are [Na][Nr]
+ * rd_c32h and the chain runs in place in img.  Every kernel converts its input exactly to
+ * float32, computes as rd_focus does, and rounds its output to the nearest binary16 value (ties
+ * to even).  The unnormalised azimuth sums of rd_focus grow with Na (a point target's image
+ * peak is about L times the number of pulses that see it) and would leave the binary16 range
+ * (65504), so here each azimuth transform step is scaled by 1/(its length), the forward and the
+ * inverse transform each by 1/Na in all, and the row stage omits its 1/Na:
+ *   img_f16 = img / Na,  img = rd_focus's image of the same echo,
+ * and no intermediate exceeds the largest magnitude of the range-compressed data.  Magnitudes
+ * beyond 65504 still become infinities.  HBM traffic is 8 bytes a sample per pass instead of 16
+ * (the Bluestein form's workspace stays float32).  echo == img is allowed; other overlap is an
+ * error; pointers must be 4-byte aligned.  Every plan rd_focus takes is supported.
+ * RD_ERR_NOT_CONFIGURED on a range-only plan; RD_ERR_UNSUPPORTED_LENGTH where rd_focus would
+ * refuse the plan (range migration beyond the RCMC margin). */
+rd_status rd_focus_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, void* stream);
+
 /* omega-k focusing with Stolt interpolation (nxmr.cn/news/101525 §3: the migration correction
  * becomes a frequency-domain mapping; forward and inverse 2-D transforms and two large complex
  * multiplies; §3.2: a phase built from the range and Doppler frequencies).  Raw echo [Na][Nr]

@@ -10,7 +10,7 @@ from __future__ import annotations
 from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
                       make_bp_grid, make_params, rd_azimuth_focus, rd_backproject, rd_bp_grid,
                       rd_corner_turn, rd_debug_azimuth_stages, rd_debug_line_fft,
-                      rd_focus, rd_last_error, rd_length_supported, rd_omega_k, rd_params, rd_plan_create,
+                      rd_focus, rd_focus_f16, rd_last_error, rd_length_supported, rd_omega_k, rd_params, rd_plan_create,
                       rd_plan_destroy, rd_range_compress, rd_range_compress_f16, rd_status_string)
 
 
@@ -84,18 +84,29 @@ class Plan:
         rd_debug_azimuth_stages(self.handle, rc, az, rcmc, img)
         return az, rcmc, img
 
+    def _half_pair(self, x, out):
+        import torch
+        shape = (self.Na, self.Nr, 2)
+        if tuple(x.shape) != shape:
+            raise ValueError(f"input must have shape {shape}")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float16, device=x.device)
+        elif tuple(out.shape) != shape:
+            raise ValueError(f"out must have shape {shape}")
+        return out
+
     def range_compress_f16(self, echo, out=None):
         """Range compression with binary16 storage: echo and the result are float16 tensors
         [Na][Nr][2] (real, imaginary), float32 arithmetic inside (rd_range_compress_f16)."""
-        import torch
-        shape = (self.Na, self.Nr, 2)
-        if tuple(echo.shape) != shape:
-            raise ValueError(f"echo must have shape {shape}")
-        if out is None:
-            out = torch.empty(shape, dtype=torch.float16, device=echo.device)
-        elif tuple(out.shape) != shape:
-            raise ValueError(f"out must have shape {shape}")
+        out = self._half_pair(echo, out)
         rd_range_compress_f16(self.handle, echo, out)
+        return out
+
+    def focus_f16(self, echo, out=None):
+        """Focusing with binary16 storage of echo, intermediates and image (float16 tensors
+        [Na][Nr][2]); the image is rd_focus's image divided by Na (rd_focus_f16)."""
+        out = self._half_pair(echo, out)
+        rd_focus_f16(self.handle, echo, out)
         return out
 
     def omega_k(self, echo, ref_bin: int, out=None):

@@ -26,7 +26,7 @@ RD_WINDOW_HAMMING = 1
 # every symbol the header declares
 EXPORTS = ("rd_length_supported", "rd_plan_create", "rd_plan_destroy", "rd_range_compress",
            "rd_range_compress_f16",
-           "rd_azimuth_focus", "rd_focus", "rd_debug_azimuth_stages", "rd_debug_line_fft",
+           "rd_azimuth_focus", "rd_focus", "rd_focus_f16", "rd_debug_azimuth_stages", "rd_debug_line_fft",
            "rd_backproject", "rd_corner_turn", "rd_omega_k", "rd_status_string", "rd_last_error")
 
 
@@ -90,6 +90,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.rd_range_compress_f16.argtypes = [vp, vp, vp, vp]
     lib.rd_range_compress_f16.restype = ctypes.c_int
+    lib.rd_focus_f16.argtypes = [vp, vp, vp, vp]
+    lib.rd_focus_f16.restype = ctypes.c_int
     lib.rd_debug_azimuth_stages.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.rd_debug_azimuth_stages.restype = ctypes.c_int
     lib.rd_debug_line_fft.argtypes = [vp, i32, i32, vp, vp, i64, vp]
@@ -195,6 +197,11 @@ def rd_azimuth_focus(plan: int, rc, img, stream=None) -> None:
 def rd_focus(plan: int, echo, img, stream=None) -> None:
     _check(load_library().rd_focus(plan, _addr(echo), _addr(img), _stream(stream, echo, img)),
            "rd_focus")
+
+
+def rd_focus_f16(plan: int, echo, img, stream=None) -> None:
+    _check(load_library().rd_focus_f16(plan, _addr_half(echo), _addr_half(img), _stream(stream, echo, img)),
+           "rd_focus_f16")
 
 
 def rd_debug_azimuth_stages(plan: int, rc, azfft, rcmc, img, stream=None) -> None:

@@ -379,6 +379,12 @@ rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, bool cha
                    "range compression launch");
 }
 
+rd_status run_range_compress_f16(rd_plan* P, const void* in, void* out, bool chained, hipStream_t s) {
+  return check_hip(P->rops->range_compress_f16(in, out, P->H, P->tw_r, P->rc_tab, P->p.Na, P->f16_grid,
+                                               chained ? P->cached : 0, P->p.Nr, P->pad_m ? P->L - 1 : 0, s),
+                   "binary16 range compression launch");
+}
+
 // Azimuth processing in place on [Na][Nr] (no corner turns):
 //   forward transform, strided step (reads `src`, writes `dst`) then block step;
 //   RCMC + filter per Doppler row; inverse transform, block step then strided step.
@@ -401,9 +407,13 @@ rdf::ColStep col_step(const rd_plan* P, bool forward, bool strided) {
   return st;
 }
 
-rd_status run_col(rd_plan* P, const float2* src, float2* dst, bool forward, bool strided,
+// half: binary16 storage, each step scaled by 1 / (its length) so that no intermediate exceeds
+// the largest magnitude of the step's input (the binary16 range ends at 65504)
+rd_status run_col(rd_plan* P, const void* src, void* dst, bool forward, bool strided, bool half,
                   hipStream_t s) {
-  const rdf::ColStep st = col_step(P, forward, strided);
+  rdf::ColStep st = col_step(P, forward, strided);
+  st.half = half ? 1 : 0;
+  st.scale = 1.0f / float(st.L);
   return check_hip(rdf::launch_col_fft(src, dst, strided ? P->tw_A : P->tw_B, st, P->p.Nr, P->col_n,
                                        P->cached, s),
                    "azimuth transform launch");
@@ -412,43 +422,52 @@ rd_status run_col(rd_plan* P, const float2* src, float2* dst, bool forward, bool
 // Bluestein form of an azimuth DFT of length Na (sign -1 forward, +1 inverse unnormalised):
 // X[k] = c[k] sum_m (x[m] c[m]) conj(c[k - m]) with c[n] = exp(sign j pi n^2 / Na), the sum a
 // linear convolution done as a length-M circular one (M >= 2 Na - 1) by the column steps.
-rd_status run_bluestein(rd_plan* P, const float2* src, float2* dst, int sign, hipStream_t s) {
+// half: src and dst in binary16 (the workspace stays float32) and the result scaled by 1 / Na.
+rd_status run_bluestein(rd_plan* P, const void* src, void* dst, int sign, bool half, hipStream_t s) {
   const int Na = P->p.Na, M = P->bs_m;
   const int64_t Nr = P->p.Nr;
   float2* W = P->bs_ws;
+  const int h = half ? 1 : 0;
   rd_status st;
-  if ((st = check_hip(rdf::launch_chirp_rows(src, W, Nr, Na, M, Na, sign, s), "chirp launch")) != RD_OK) return st;
-  if ((st = run_col(P, W, W, true, true, s)) != RD_OK) return st;
-  if ((st = run_col(P, W, W, true, false, s)) != RD_OK) return st;
+  if ((st = check_hip(rdf::launch_chirp_rows(src, W, Nr, Na, M, Na, sign, h, 0, 1.0f, s), "chirp launch")) != RD_OK)
+    return st;
+  if ((st = run_col(P, W, W, true, true, false, s)) != RD_OK) return st;
+  if ((st = run_col(P, W, W, true, false, false, s)) != RD_OK) return st;
   if ((st = check_hip(rdf::launch_scale_rows(W, P->bs_fb + (sign < 0 ? 0 : M), Nr, M, s), "scale launch")) != RD_OK)
     return st;
-  if ((st = run_col(P, W, W, false, false, s)) != RD_OK) return st;
-  if ((st = run_col(P, W, W, false, true, s)) != RD_OK) return st;
-  return check_hip(rdf::launch_chirp_rows(W, dst, Nr, Na, Na, Na, sign, s), "chirp launch");
+  if ((st = run_col(P, W, W, false, false, false, s)) != RD_OK) return st;
+  if ((st = run_col(P, W, W, false, true, false, s)) != RD_OK) return st;
+  return check_hip(rdf::launch_chirp_rows(W, dst, Nr, Na, Na, Na, sign, 0, h, half ? 1.0f / float(Na) : 1.0f, s),
+                   "chirp launch");
 }
 
 // The azimuth transform: src [Na][Nr] (pulses) -> dst, row r holding Doppler bin r / B + A (r % B)
-rd_status az_forward(rd_plan* P, const float2* src, float2* dst, hipStream_t s) {
-  if (P->bs_m) return run_bluestein(P, src, dst, -1, s);
+// (half: binary16 storage, transform scaled by 1 / Na)
+rd_status az_forward(rd_plan* P, const void* src, void* dst, bool half, hipStream_t s) {
+  if (P->bs_m) return run_bluestein(P, src, dst, -1, half, s);
   rd_status st;
-  if ((st = run_col(P, src, dst, true, true, s)) != RD_OK) return st;
-  return run_col(P, dst, dst, true, false, s);
+  if ((st = run_col(P, src, dst, true, true, half, s)) != RD_OK) return st;
+  return run_col(P, dst, dst, true, false, half, s);
 }
 
-// Its inverse (unnormalised; 1/Na is folded into the row stage), in place, back to pulse order
-rd_status az_inverse(rd_plan* P, float2* io, hipStream_t s) {
-  if (P->bs_m) return run_bluestein(P, io, io, +1, s);
+// Its inverse, in place, back to pulse order: unnormalised (1/Na is folded into the row stage),
+// or with binary16 storage scaled by 1 / Na like the forward transform
+rd_status az_inverse(rd_plan* P, void* io, bool half, hipStream_t s) {
+  if (P->bs_m) return run_bluestein(P, io, io, +1, half, s);
   rd_status st;
-  if ((st = run_col(P, io, io, false, false, s)) != RD_OK) return st;
-  return run_col(P, io, io, false, true, s);
+  if ((st = run_col(P, io, io, false, false, half, s)) != RD_OK) return st;
+  return run_col(P, io, io, false, true, half, s);
 }
 
-rd_status run_rows(rd_plan* P, const float2* src, float2* dst, bool filter, hipStream_t s) {
+// RCMC and (filter) the azimuth filter per Doppler row; half: binary16 rows, whose forward
+// transform already carries 1 / Na
+rd_status run_rows(rd_plan* P, const void* src, void* dst, bool filter, bool half, hipStream_t s) {
   rdf::AzRowConst c = P->az;
   c.filter = filter ? 1 : 0;
+  if (half) c.inv_na = 1.0f;
   if (P->pad_m)
-    return check_hip(rdf::launch_rcmc_mf_any(src, dst, c, P->p.Na, P->p.Nr, P->cached, s), "RCMC launch");
-  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, P->cached, s), "RCMC launch");
+    return check_hip(rdf::launch_rcmc_mf_any(src, dst, c, P->p.Na, P->p.Nr, P->cached, half, s), "RCMC launch");
+  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, P->cached, half, s), "RCMC launch");
 }
 
 rd_status check_rcmc_margin(const rd_plan* P) {
@@ -459,12 +478,12 @@ rd_status check_rcmc_margin(const rd_plan* P) {
   return RD_OK;
 }
 
-rd_status run_azimuth(rd_plan* P, const float2* rc, float2* img, hipStream_t s) {
+rd_status run_azimuth(rd_plan* P, const void* rc, void* img, bool half, hipStream_t s) {
   // rc is read only by the first step, so img may alias it
   rd_status st;
-  if ((st = az_forward(P, rc, img, s)) != RD_OK) return st;
-  if ((st = run_rows(P, img, img, true, s)) != RD_OK) return st;
-  return az_inverse(P, img, s);
+  if ((st = az_forward(P, rc, img, half, s)) != RD_OK) return st;
+  if ((st = run_rows(P, img, img, true, half, s)) != RD_OK) return st;
+  return az_inverse(P, img, half, s);
 }
 
 }  // namespace
@@ -721,10 +740,7 @@ rd_status rd_range_compress_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* rc,
   if (!aligned4(echo) || !aligned4(rc)) return fail(RD_ERR_INVALID_ARG, "echo and rc must be non-NULL and 4-byte aligned");
   const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c32h);
   if (partial_overlap(echo, rc, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and rc overlap without being equal");
-  return check_hip(plan->rops->range_compress_f16(echo, rc, plan->H, plan->tw_r, plan->rc_tab, plan->p.Na,
-                                                  plan->f16_grid, plan->p.Nr, plan->pad_m ? plan->L - 1 : 0,
-                                                  static_cast<hipStream_t>(stream)),
-                   "binary16 range compression launch");
+  return run_range_compress_f16(plan, echo, rc, false, static_cast<hipStream_t>(stream));
 }
 
 rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* stream) {
@@ -735,8 +751,7 @@ rd_status rd_azimuth_focus(rd_plan* plan, const rd_c64* rc, rd_c64* img, void* s
   if (!aligned8(rc) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "rc and img must be non-NULL and 8-byte aligned");
   const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
   if (partial_overlap(rc, img, bytes)) return fail(RD_ERR_INVALID_ARG, "rc and img overlap without being equal");
-  return run_azimuth(plan, reinterpret_cast<const float2*>(rc), reinterpret_cast<float2*>(img),
-                     static_cast<hipStream_t>(stream));
+  return run_azimuth(plan, rc, img, false, static_cast<hipStream_t>(stream));
 }
 
 rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream) {
@@ -751,7 +766,22 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
   float2* I = reinterpret_cast<float2*>(img);
   st = run_range_compress(plan, reinterpret_cast<const float2*>(echo), I, true, s);
   if (st != RD_OK) return st;
-  return run_azimuth(plan, I, I, s);
+  return run_azimuth(plan, I, I, false, s);
+}
+
+rd_status rd_focus_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if (plan->f16_grid <= 0)
+    return fail(RD_ERR_UNSUPPORTED_LENGTH, "no binary16 range kernel for Nr=%d", plan->p.Nr);
+  if ((st = check_rcmc_margin(plan)) != RD_OK) return st;
+  if (!aligned4(echo) || !aligned4(img)) return fail(RD_ERR_INVALID_ARG, "echo and img must be non-NULL and 4-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c32h);
+  if (partial_overlap(echo, img, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and img overlap without being equal");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_range_compress_f16(plan, echo, img, true, s)) != RD_OK) return st;
+  return run_azimuth(plan, img, img, true, s);
 }
 
 rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref_bin, void* stream) {
@@ -788,12 +818,12 @@ rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref
   float2* I = reinterpret_cast<float2*>(img);
   // the azimuth transform first (the 2-D transform's order is free), then one row stage per
   // Doppler row, then the inverse azimuth transform; echo is read only by the first step
-  if ((st = az_forward(plan, reinterpret_cast<const float2*>(echo), I, s)) != RD_OK) return st;
+  if ((st = az_forward(plan, echo, I, false, s)) != RD_OK) return st;
   if ((st = check_hip(plan->rops->omega_k_rows(I, I, plan->H, plan->tw_r, c, plan->az.w, p.Na, plan->wk_grid,
                                                plan->cached, s),
                       "omega-k row stage launch")) != RD_OK)
     return st;
-  return az_inverse(plan, I, s);
+  return az_inverse(plan, I, false, s);
 }
 
 rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft, rd_c64* rcmc,
@@ -823,16 +853,16 @@ rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft
   float2* I = reinterpret_cast<float2*>(img);
   float2* W = plan->work;
   const int64_t Nr = plan->p.Nr;
-  if ((st = az_forward(plan, reinterpret_cast<const float2*>(rc), I, s)) != RD_OK) return st;
-  if ((st = run_rows(plan, I, W, false, s)) != RD_OK) return st;  // RCMC alone
+  if ((st = az_forward(plan, rc, I, false, s)) != RD_OK) return st;
+  if ((st = run_rows(plan, I, W, false, false, s)) != RD_OK) return st;  // RCMC alone
   if ((st = check_hip(rdf::launch_row_unpermute(I, reinterpret_cast<float2*>(azfft), plan->A, plan->B,
                                                 Nr, s), "row order launch")) != RD_OK)
     return st;
   if ((st = check_hip(rdf::launch_row_unpermute(W, reinterpret_cast<float2*>(rcmc), plan->A, plan->B,
                                                 Nr, s), "row order launch")) != RD_OK)
     return st;
-  if ((st = run_rows(plan, I, I, true, s)) != RD_OK) return st;
-  return az_inverse(plan, I, s);
+  if ((st = run_rows(plan, I, I, true, false, s)) != RD_OK) return st;
+  return az_inverse(plan, I, false, s);
 }
 
 rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const rd_c64* in,

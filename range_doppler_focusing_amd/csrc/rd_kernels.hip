@@ -175,7 +175,6 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   using L = typename C::Fwd;
   static_assert(std::is_same<typename C::Fwd, typename C::Inv>::value, "needs Fwd == Inv");
   constexpr int T = C::T;
-  constexpr int R0 = ListInfo<L>::first;
   using TC = TwCache<N, T, 1, L>;
   constexpr bool LATE = PF && PfLate<N>::value && !C::HREG;
   __shared__ float2 lds[C::LPW * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
@@ -392,7 +391,9 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
 //   inverse step 1 (block):    for each k1, DFT_B^-1 over rows B k1 + k2, then x W_Na^{-m2 k1}
 //   inverse step 2 (strided):  for each m2, DFT_A^-1 over rows B k1 + m2 -> row B m1 + m2.
 // A workgroup takes one row set (L rows) x 64 columns; each lane owns one column, so every
-// global access of a wave is one contiguous 512-byte row segment.  In place (out may equal in).
+// global access of a wave is one contiguous 512-byte row segment (256 bytes with binary16
+// storage, whose steps also scale every output by `scale` to keep the values in range).  In
+// place (out may equal in).
 struct ColGeom {
   int64_t cols;      // row length (elements)
   int base_mul;      // first row of row set g = g * base_mul
@@ -400,12 +401,12 @@ struct ColGeom {
   int chunks;        // column chunks of 64
   int na;            // total transform length (for the inter-step twiddle), power of two
   int twiddle;       // multiply output t by W_Na^{DIR g t} after the transform
+  float scale;       // binary16 storage only: every output times scale
 };
 
-template <int L, int DIR, int AUX>
+template <int L, int DIR, int AUX, bool HALF = false>
 __global__ void __launch_bounds__(ColCfg<L>::WG)
-    k_col_fft(const float2* in, float2* out, const float2* __restrict__ tw, ColGeom cg,
-              uint32_t bytes) {
+    k_col_fft(const void* in, void* out, const float2* __restrict__ tw, ColGeom cg, uint32_t bytes) {
   using C = ColCfg<L>;
   using LST = typename std::conditional<(DIR < 0), typename C::Fwd, typename C::Inv>::type;
   constexpr int T = C::T;
@@ -436,10 +437,11 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
   // below 4 GiB).  Lanes past the last column read the last column and store nothing.  (The
   // same offsets split into a per-lane base and a wave-uniform scalar part measured ~5% slower
   // on the 16384-row steps.)
-  const uint32_t base = uint32_t((int64_t(g) * cg.base_mul * cg.cols + (live ? c : cg.cols - 1)) * 8);
-  const uint32_t rowstep = uint32_t(int64_t(cg.stride) * cg.cols * 8);
+  constexpr int ES = HALF ? 4 : 8;  // bytes per element
+  const uint32_t base = uint32_t((int64_t(g) * cg.base_mul * cg.cols + (live ? c : cg.cols - 1)) * ES);
+  const uint32_t rowstep = uint32_t(int64_t(cg.stride) * cg.cols * ES);
   const __amdgpu_buffer_rsrc_t rin =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(in), 0, int(bytes), kBufDword3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(in), 0, int(bytes), kBufDword3);
   const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(out, 0, int(bytes), kBufDword3);
   float2 v[C::P];
   {
@@ -448,9 +450,13 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
     for (int b = 0; b < G::B; ++b) {
       const int j = tid + b * T;
 #pragma unroll
-      for (int r = 0; r < RI; ++r)
-        v[b * RI + r] = __builtin_bit_cast(
-            float2, __builtin_amdgcn_raw_buffer_load_b64(rin, base + uint32_t(j + r * G::NB) * rowstep, 0, AUX));
+      for (int r = 0; r < RI; ++r) {
+        const uint32_t off = base + uint32_t(j + r * G::NB) * rowstep;
+        if constexpr (HALF)
+          v[b * RI + r] = h2_to_f2(__builtin_amdgcn_raw_buffer_load_b32(rin, off, 0, AUX));
+        else
+          v[b * RI + r] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rin, off, 0, AUX));
+      }
     }
   }
   PassesCached<L, T, DIR, 1, LST>::run(v, my, twc, tid);
@@ -463,9 +469,12 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
       for (int r = 0; r < RO; ++r) {
         float2 x = v[b * RO + r];
         if (cg.twiddle) x = cmul(x, step_tw[j + r * G::NB]);
-        if (live)
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout,
-                                                base + uint32_t(j + r * G::NB) * rowstep, 0, AUX);
+        const uint32_t off = base + uint32_t(j + r * G::NB) * rowstep;
+        if constexpr (HALF) {
+          if (live) __builtin_amdgcn_raw_buffer_store_b32(f2_to_h2(cscale(x, cg.scale)), rout, off, 0, AUX);
+        } else {
+          if (live) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, x), rout, off, 0, AUX);
+        }
       }
     }
   }
@@ -478,7 +487,8 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
 // Rows up to 4096 samples are one chunk, staged between zero margins written once; longer rows
 // split into 4096-sample chunks, which keeps the staging buffer small enough for several
 // workgroups per CU.  Shift and filter phase are formed in float64 (the phase reaches ~1e7 rad)
-// and reduced before they are taken to float32.
+// and reduced before they are taken to float32.  HALF: binary16 rows (4 bytes a sample) in and
+// out, float32 arithmetic.
 template <int N>
 struct RowStage {
   static constexpr int CH = (N > 4096 && N % 4096 == 0) ? 4096 : N;  // outputs per chunk
@@ -505,9 +515,48 @@ struct RowStage<0> {
   static constexpr int P = CH / T;
 };
 
-template <int N, int AUX>
+// row I/O of the row stage: float32 or binary16 storage
+template <bool HALF>
+struct RowIO;
+template <>
+struct RowIO<false> {
+  using IO = LineIO;
+  __device__ static IO make(const void* b, int n, int64_t first, int count, int64_t total) {
+    return LineIO(static_cast<const float2*>(b), n, first, count, total);
+  }
+  template <int AUX>
+  __device__ static float2 one(const IO& io, int i) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, i * 8, 0, AUX));
+  }
+  template <int N, int T, int R, int AUX>
+  __device__ static void load(float2* v, const IO& io, int e0, int tid) { load_line<N, T, R, AUX>(v, io, e0, tid); }
+  template <int N, int T, int R, int AUX>
+  __device__ static void store(const float2* v, const IO& io, int e0, int tid) {
+    store_line<N, T, R, AUX>(v, io, e0, tid);
+  }
+};
+template <>
+struct RowIO<true> {
+  using IO = LineIOh;
+  __device__ static IO make(const void* b, int n, int64_t first, int count, int64_t total) {
+    return LineIOh(b, n, first, count, total);
+  }
+  template <int AUX>
+  __device__ static float2 one(const IO& io, int i) {
+    return h2_to_f2(__builtin_amdgcn_raw_buffer_load_b32(io.rsrc, i * 4, 0, AUX));
+  }
+  template <int N, int T, int R, int AUX>
+  __device__ static void load(float2* v, const IO& io, int e0, int tid) { load_line_h<N, T, R, AUX>(v, io, e0, tid); }
+  template <int N, int T, int R, int AUX>
+  __device__ static void store(const float2* v, const IO& io, int e0, int tid) {
+    store_line_h<N, T, R, AUX>(v, io, e0, tid);
+  }
+};
+
+template <int N, int AUX, bool HALF = false>
 __global__ void __launch_bounds__(RowStage<N>::WG)
-    k_rcmc_mf(const float2* in, float2* out, AzRowConst c, int64_t rows, int n_rt) {
+    k_rcmc_mf(const void* in, void* out, AzRowConst c, int64_t rows, int n_rt) {
+  using RIO = RowIO<HALF>;
   using RS = RowStage<N>;
   constexpr bool RT = RS::CHUNKS == 0;        // row length n_rt at run time
   const int nl = RT ? n_rt : N;              // samples per row
@@ -533,10 +582,10 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
     const double gamma = c.row[4 * k + 2], delta = c.row[4 * k + 3];
     float2 v[RS::P];
     // one chunk per group: rows [i0, i0 + LPW) when a row is one chunk, else the item's row
-    const LineIO src = RS::CHUNKS == 1 ? LineIO(in, N, i0, RS::LPW, rows)
-                                       : LineIO(in, nl, item < items ? row : rows, 1, rows);
+    const typename RIO::IO src = RS::CHUNKS == 1 ? RIO::make(in, N, i0, RS::LPW, rows)
+                                                 : RIO::make(in, nl, item < items ? row : rows, 1, rows);
     const int e0 = RS::CHUNKS == 1 ? grp * N : n0;
-    load_line<CH, T, R0, AUX>(v, src, e0, tid);
+    RIO::template load<CH, T, R0, AUX>(v, src, e0, tid);
     float2 pre = make_float2(0.f, 0.f);
     int hs = -1;  // this thread's first halo slot, if any
     if constexpr (RS::CHUNKS != 1) {
@@ -546,8 +595,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
       if (i < 3 + c.halo) {
         const int sidx = i < 3 ? n0 - 3 + i : n0 + CH + (i - 3);
         hs = i < 3 ? i : 3 + CH + (i - 3);
-        if (sidx >= 0 && sidx < nl)
-          pre = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(src.rsrc, sidx * 8, 0, AUX));
+        if (sidx >= 0 && sidx < nl) pre = RIO::template one<AUX>(src, sidx);
       }
     }
     __syncthreads();  // the previous chunk's taps have been read
@@ -563,9 +611,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
       if (hs >= 0) my[hs] = pre;
       for (int i = tid + T; i < 3 + c.halo; i += T) {  // halos longer than one pass
         const int sidx = n0 + CH + (i - 3);
-        my[3 + CH + (i - 3)] = sidx < nl ? __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                 src.rsrc, sidx * 8, 0, AUX))
-                                        : make_float2(0.f, 0.f);
+        my[3 + CH + (i - 3)] = sidx < nl ? RIO::template one<AUX>(src, sidx) : make_float2(0.f, 0.f);
       }
     }
     __syncthreads();
@@ -620,9 +666,9 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
         }
       }
     }
-    const LineIO dst = RS::CHUNKS == 1 ? LineIO(out, N, i0, RS::LPW, rows)
-                                       : LineIO(out, nl, item < items ? row : rows, 1, rows);
-    store_line<CH, T, R0, AUX>(v, dst, e0, tid);
+    const typename RIO::IO dst = RS::CHUNKS == 1 ? RIO::make(out, N, i0, RS::LPW, rows)
+                                                 : RIO::make(out, nl, item < items ? row : rows, 1, rows);
+    RIO::template store<CH, T, R0, AUX>(v, dst, e0, tid);
   }
 }
 
@@ -1107,22 +1153,28 @@ hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const fl
 
 // binary16 storage (4 bytes a sample in and out), float32 arithmetic: the same kernels with
 // 32-bit line I/O; streaming stores
+template <int N, int SAUX>
+void launch_rc_f16_aux(const void* in, void* out, const float2* H, const float2* tw, const float2* tab,
+                       int64_t lines, int grid, int n_line, int skip, hipStream_t s) {
+  constexpr bool PF = RD_RC_PREFETCH && LineCfg<N>::PF;
+  if (n_line != N)
+    hipLaunchKernelGGL((k_range_compress_pf<N, PF, SAUX, true, true>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in,
+                       out, H, tw, lines, n_line, skip);
+  else if constexpr (N == 4096 && RD_RC_4096)
+    hipLaunchKernelGGL((k_range_compress_4096<SAUX, true>), dim3(grid), dim3(256), 0, s, in, out, tab, lines);
+  else
+    hipLaunchKernelGGL((k_range_compress_pf<N, PF, SAUX, false, true>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in,
+                       out, H, tw, lines, N, 0);
+}
+
 template <int N>
 hipError_t launch_rc_f16(const void* in, void* out, const float2* H, const float2* tw, const float2* tab,
-                         int64_t lines, int grid, int n_line, int skip, hipStream_t s) {
-  constexpr bool PF = RD_RC_PREFETCH && LineCfg<N>::PF;
-  if (n_line != N) {
-    if (n_line <= 0 || skip < 0 || skip >= n_line || n_line + skip > N) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream, true, true>), dim3(grid), dim3(LineCfg<N>::WG), 0,
-                       s, in, out, H, tw, lines, n_line, skip);
-    return hipGetLastError();
-  }
-  if constexpr (N == 4096 && RD_RC_4096) {
-    hipLaunchKernelGGL((k_range_compress_4096<kAuxStream, true>), dim3(grid), dim3(256), 0, s, in, out, tab, lines);
-  } else {
-    hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxStream, false, true>), dim3(grid), dim3(LineCfg<N>::WG), 0,
-                       s, in, out, H, tw, lines, N, 0);
-  }
+                         int64_t lines, int grid, int cached, int n_line, int skip, hipStream_t s) {
+  if (n_line != N && (n_line <= 0 || skip < 0 || skip >= n_line || n_line + skip > N)) return hipErrorInvalidValue;
+  if (cached)
+    launch_rc_f16_aux<N, kAuxCached>(in, out, H, tw, tab, lines, grid, n_line, skip, s);
+  else
+    launch_rc_f16_aux<N, kAuxStream>(in, out, H, tw, tab, lines, grid, n_line, skip, s);
   return hipGetLastError();
 }
 
@@ -1149,14 +1201,17 @@ hipError_t occupancy_pf(int* rc, int pad) {
 }
 
 template <int N>
-hipError_t launch_rcmc_mf(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
-                          int grid, int cached, hipStream_t s) {
+hipError_t launch_rcmc_mf(const void* in, void* out, const AzRowConst& c, int64_t rows, int grid,
+                          int cached, int half, hipStream_t s) {
   const int64_t wgs = (rows * RowStage<N>::CHUNKS + RowStage<N>::LPW - 1) / RowStage<N>::LPW;
   if (grid <= 0 || grid > wgs) grid = int(wgs);
-  if (cached)
-    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxCached>), dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows, N);
+  const dim3 g(grid), b(RowStage<N>::WG);
+  if (half)
+    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxCached, true>), g, b, 0, s, in, out, c, rows, N);
+  else if (cached)
+    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxCached>), g, b, 0, s, in, out, c, rows, N);
   else
-    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxStream>), dim3(grid), dim3(RowStage<N>::WG), 0, s, in, out, c, rows, N);
+    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxStream>), g, b, 0, s, in, out, c, rows, N);
   return hipGetLastError();
 }
 
@@ -1183,15 +1238,17 @@ hipError_t occupancy_wk(int* wgs) {
 
 // RCMC + azimuth filter over rows of n samples, any n >= 1 (run-time length; shifts up to
 // RowStage<0>::MARGIN - 5)
-hipError_t launch_rcmc_mf_any(const float2* in, float2* out, const AzRowConst& c, int64_t rows, int n,
-                              int cached, hipStream_t s) {
+hipError_t launch_rcmc_mf_any(const void* in, void* out, const AzRowConst& c, int64_t rows, int n,
+                              int cached, int half, hipStream_t s) {
   using RS = RowStage<0>;
   if (n <= 0 || c.halo < 0 || c.halo > RS::MARGIN) return hipErrorInvalidValue;
   const int64_t items = rows * ((n + RS::CH - 1) / RS::CH);
   const int64_t wgs = (items + RS::LPW - 1) / RS::LPW;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   const int grid = int(wgs);
-  if (cached)
+  if (half)
+    hipLaunchKernelGGL((k_rcmc_mf<0, kAuxCached, true>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
+  else if (cached)
     hipLaunchKernelGGL((k_rcmc_mf<0, kAuxCached>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
   else
     hipLaunchKernelGGL((k_rcmc_mf<0, kAuxStream>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
@@ -1236,13 +1293,16 @@ const LineOps* line_ops(int n) {
 }
 
 template <int L, int DIR, int AUX>
-void launch_col3(const float2* in, float2* out, const float2* tw_L, const ColGeom& cg, dim3 grid,
-                 uint32_t bytes, hipStream_t s) {
-  hipLaunchKernelGGL((k_col_fft<L, DIR, AUX>), grid, dim3(ColCfg<L>::WG), 0, s, in, out, tw_L, cg, bytes);
+void launch_col3(const void* in, void* out, const float2* tw_L, const ColGeom& cg, dim3 grid,
+                 uint32_t bytes, int half, hipStream_t s) {
+  if (half)
+    hipLaunchKernelGGL((k_col_fft<L, DIR, AUX, true>), grid, dim3(ColCfg<L>::WG), 0, s, in, out, tw_L, cg, bytes);
+  else
+    hipLaunchKernelGGL((k_col_fft<L, DIR, AUX>), grid, dim3(ColCfg<L>::WG), 0, s, in, out, tw_L, cg, bytes);
 }
 
 template <int L>
-hipError_t launch_col(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
+hipError_t launch_col(const void* in, void* out, const float2* tw_L, const ColStep& st,
                       int64_t cols, int na, int cached, hipStream_t s) {
   ColGeom cg;
   cg.cols = cols;
@@ -1251,20 +1311,21 @@ hipError_t launch_col(const float2* in, float2* out, const float2* tw_L, const C
   cg.chunks = int((cols + 63) / 64);
   cg.na = na;
   cg.twiddle = st.twiddle;
-  const uint64_t bytes = uint64_t(na) * uint64_t(cols) * 8u;
+  cg.scale = st.scale;
+  const uint64_t bytes = uint64_t(na) * uint64_t(cols) * (st.half ? 4u : 8u);
   if (bytes > 0xFFFFFFF0ull) return hipErrorInvalidValue;
   const dim3 grid(unsigned(int64_t(st.sets) * cg.chunks));
   if (st.dir < 0) {
-    if (cached) launch_col3<L, -1, kAuxCached>(in, out, tw_L, cg, grid, uint32_t(bytes), s);
-    else launch_col3<L, -1, kAuxStream>(in, out, tw_L, cg, grid, uint32_t(bytes), s);
+    if (cached) launch_col3<L, -1, kAuxCached>(in, out, tw_L, cg, grid, uint32_t(bytes), st.half, s);
+    else launch_col3<L, -1, kAuxStream>(in, out, tw_L, cg, grid, uint32_t(bytes), st.half, s);
   } else {
-    if (cached) launch_col3<L, +1, kAuxCached>(in, out, tw_L, cg, grid, uint32_t(bytes), s);
-    else launch_col3<L, +1, kAuxStream>(in, out, tw_L, cg, grid, uint32_t(bytes), s);
+    if (cached) launch_col3<L, +1, kAuxCached>(in, out, tw_L, cg, grid, uint32_t(bytes), st.half, s);
+    else launch_col3<L, +1, kAuxStream>(in, out, tw_L, cg, grid, uint32_t(bytes), st.half, s);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
+hipError_t launch_col_fft(const void* in, void* out, const float2* tw_L, const ColStep& st,
                           int64_t cols, int na, int cached, hipStream_t s) {
   switch (st.L) {
     case 16: return launch_col<16>(in, out, tw_L, st, cols, na, cached, s);
@@ -1277,23 +1338,30 @@ hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, con
 }
 
 // Bluestein (chirp-z) transforms along the azimuth axis (nxmr.cn/news/101525 §5.1: any length):
-// the two elementwise row passes.  out[r][c] = in[r][c] exp(sign j pi r^2 / na) for r < rows_in
-// and 0 for rows_in <= r < rows_out (r^2 reduced modulo 2 na in integers, so the argument of
-// sincospi is exact and below 2); io[r][c] *= f[r].
+// the two elementwise row passes.  out[r][c] = scale in[r][c] exp(sign j pi r^2 / na) for
+// r < rows_in and 0 for rows_in <= r < rows_out (r^2 reduced modulo 2 na in integers, so the
+// argument of sincospi is exact and below 2); io[r][c] *= f[r].  HIN / HOUT: binary16 storage
+// of the input / output (the image side of a binary16 chain; the workspace stays float32).
+template <bool HIN, bool HOUT>
 __global__ void __launch_bounds__(256)
-    k_chirp_rows(const float2* __restrict__ in, float2* __restrict__ out, int64_t cols, int rows_in, int na,
-                 int sign) {
+    k_chirp_rows(const void* __restrict__ in, void* __restrict__ out, int64_t cols, int rows_in, int na,
+                 int sign, float scale) {
   const int r = blockIdx.y;
   const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (c >= cols) return;
+  const int64_t e = int64_t(r) * cols + c;
   float2 v = make_float2(0.f, 0.f);
   if (r < rows_in) {
     const int64_t q = (int64_t(r) * r) % (2 * int64_t(na));
     float sn, cs;
     sincospif(float(q) / float(na), &sn, &cs);
-    v = cmul(in[int64_t(r) * cols + c], make_float2(cs, sign > 0 ? sn : -sn));
+    const float2 x = HIN ? h2_to_f2(static_cast<const unsigned int*>(in)[e]) : static_cast<const float2*>(in)[e];
+    v = cmul(x, make_float2(cs * scale, (sign > 0 ? sn : -sn) * scale));
   }
-  out[int64_t(r) * cols + c] = v;
+  if constexpr (HOUT)
+    static_cast<unsigned int*>(out)[e] = f2_to_h2(v);
+  else
+    static_cast<float2*>(out)[e] = v;
 }
 
 __global__ void __launch_bounds__(256)
@@ -1303,13 +1371,18 @@ __global__ void __launch_bounds__(256)
   if (c < cols) io[int64_t(r) * cols + c] = cmul(io[int64_t(r) * cols + c], f[r]);
 }
 
-hipError_t launch_chirp_rows(const float2* in, float2* out, int64_t cols, int rows_in, int rows_out, int na,
-                             int sign, hipStream_t s) {
+hipError_t launch_chirp_rows(const void* in, void* out, int64_t cols, int rows_in, int rows_out, int na,
+                             int sign, int hin, int hout, float scale, hipStream_t s) {
   const int64_t gx = (cols + 255) / 256;
-  if (gx > 0x7fffffff || rows_out <= 0 || rows_out > 65535 || rows_in > rows_out || na <= 0)
+  if (gx > 0x7fffffff || rows_out <= 0 || rows_out > 65535 || rows_in > rows_out || na <= 0 || (hin && hout))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_chirp_rows, dim3(unsigned(gx), unsigned(rows_out)), dim3(256), 0, s, in, out, cols, rows_in,
-                     na, sign);
+  const dim3 g{static_cast<uint32_t>(gx), static_cast<uint32_t>(rows_out)}, b{256};
+  if (hin)
+    hipLaunchKernelGGL((k_chirp_rows<true, false>), g, b, 0, s, in, out, cols, rows_in, na, sign, scale);
+  else if (hout)
+    hipLaunchKernelGGL((k_chirp_rows<false, true>), g, b, 0, s, in, out, cols, rows_in, na, sign, scale);
+  else
+    hipLaunchKernelGGL((k_chirp_rows<false, false>), g, b, 0, s, in, out, cols, rows_in, na, sign, scale);
   return hipGetLastError();
 }
 

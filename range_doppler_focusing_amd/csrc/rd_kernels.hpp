@@ -77,8 +77,9 @@ struct LineOps {
   // RCMC + azimuth filter over rows of this length (in == out allowed; grid 0 = one workgroup
   // per staged chunk); margin = samples staged after a chunk, so the largest shift the kernel
   // accepts is margin - 5
-  hipError_t (*rcmc_mf)(const float2* in, float2* out, const AzRowConst& c, int64_t rows,
-                        int grid, int cached, hipStream_t s);
+  // (half: binary16 rows, 4 bytes a sample, float32 arithmetic; ordinary stores)
+  hipError_t (*rcmc_mf)(const void* in, void* out, const AzRowConst& c, int64_t rows, int grid,
+                        int cached, int half, hipStream_t s);
   int margin;
   // omega-k row stage over `rows` Doppler rows (in == out allowed); wk_cap = the largest halo
   // the kernel stages, occupancy_wk = its workgroups per CU
@@ -88,10 +89,10 @@ struct LineOps {
   hipError_t (*occupancy_wk)(int* wgs);
   int wk_cap;
   // range compression with binary16 line storage (4 bytes a sample in and out, float32
-  // arithmetic; tab, n_line and skip as for range_compress_pf) and its occupancy
+  // arithmetic; tab, cached, n_line and skip as for range_compress_pf) and its occupancy
   hipError_t (*range_compress_f16)(const void* in, void* out, const float2* H, const float2* tw,
-                                   const float2* tab, int64_t lines, int grid, int n_line, int skip,
-                                   hipStream_t s);
+                                   const float2* tab, int64_t lines, int grid, int cached, int n_line,
+                                   int skip, hipStream_t s);
   hipError_t (*occupancy_f16)(int* wgs, int pad);
 };
 
@@ -99,9 +100,10 @@ struct LineOps {
 const LineOps* line_ops(int n);
 
 // RCMC + azimuth filter over rows of any length n (512-sample chunks; halo up to
-// rcmc_any_margin(), so shifts up to rcmc_any_margin() - 5); in == out allowed
-hipError_t launch_rcmc_mf_any(const float2* in, float2* out, const AzRowConst& c, int64_t rows, int n,
-                              int cached, hipStream_t s);
+// rcmc_any_margin(), so shifts up to rcmc_any_margin() - 5); in == out allowed; half as for
+// LineOps::rcmc_mf
+hipError_t launch_rcmc_mf_any(const void* in, void* out, const AzRowConst& c, int64_t rows, int n,
+                              int cached, int half, hipStream_t s);
 int rcmc_any_margin();
 
 // In-place four-step azimuth transforms on [rows][cols]; see rd_kernels.hip.
@@ -112,9 +114,11 @@ struct ColStep {
   int stride;     // row stride within a set
   int sets;       // number of row sets
   int twiddle;    // apply the inter-step twiddle W_Na^{dir g t}
+  int half;       // binary16 storage (4 bytes a sample), float32 arithmetic
+  float scale;    // binary16 storage only: every output times scale
 };
 // cached: ordinary loads and stores (image held by the Infinity Cache), else non-temporal
-hipError_t launch_col_fft(const float2* in, float2* out, const float2* tw_L, const ColStep& st,
+hipError_t launch_col_fft(const void* in, void* out, const float2* tw_L, const ColStep& st,
                           int64_t cols, int na, int cached, hipStream_t s);
 
 // Back-projection constants (see k_backproject): pixel (i, j) lies at along-track x0 + i dx and
@@ -137,8 +141,9 @@ hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64
 
 // out[k] = in[(k % A) B + k / A] for rows of `cols` samples: Doppler-digit row order to natural
 // Bluestein row passes (see rd_kernels.hip): chirp multiply with zero fill, and a per-row scale
-hipError_t launch_chirp_rows(const float2* in, float2* out, int64_t cols, int rows_in, int rows_out, int na,
-                             int sign, hipStream_t s);
+// hin / hout: binary16 input / output (not both); scale multiplies every output
+hipError_t launch_chirp_rows(const void* in, void* out, int64_t cols, int rows_in, int rows_out, int na,
+                             int sign, int hin, int hout, float scale, hipStream_t s);
 hipError_t launch_scale_rows(float2* io, const float2* f, int64_t cols, int rows, hipStream_t s);
 hipError_t launch_row_unpermute(const float2* in, float2* out, int A, int B, int64_t cols,
                                 hipStream_t s);

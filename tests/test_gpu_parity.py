@@ -428,6 +428,83 @@ def test_focus_in_place_and_noiseless_targets(torch_dev, rdf):
         assert M.peak_near(gi, m, n) == (m, n)
 
 
+# Binary16 storage through the whole chain: six stored stages (range compression, two forward
+# and two inverse azimuth steps, the row stage; the Bluestein form's workspace stays float32),
+# each rounding to nearest with a relative error of at most 2^-11 per component in the normal
+# range.  Every later stage is a scaled unitary map (column DFT / L, twiddles, phase-only
+# filter) or the normalised interpolator, so the errors add at most linearly:
+# rel-L2 <= 6 * 2^-11 = 2.9e-3.  The oracle takes the same binary16 echo.
+F16_CHAIN_TOL = 3e-3
+
+
+def check_targets_near(img, ref_img, targets, rel):
+    """Target peaks of an image whose stored values carry a relative error up to `rel`: where
+    the oracle's peak is flat (neighbours within `rel` of its maximum), any of those pixels is a
+    correct argmax, so the image's peak must be a pixel whose oracle magnitude is within `rel` of
+    the oracle's maximum.  PSLR is compared at the oracle's peak.  ISLR is not: its mainlobe ends
+    at the first nulls, which are shallow on weakly focused (short-aperture) targets, and an
+    error of a few 1e-4 can move the null the measurement picks and with it a large share of
+    energy between mainlobe and sidelobes."""
+    for (m, n) in targets:
+        pk, pr = M.peak_near(img, m, n), M.peak_near(ref_img, m, n)
+        assert abs(ref_img[pk]) >= (1 - rel) * abs(ref_img[pr]), (m, n, pk, pr)
+        got, want = M.point_target(img, *pr), M.point_target(ref_img, *pr)
+        for axis in ("range", "azimuth"):
+            a, b = got[axis]["pslr_db"], want[axis]["pslr_db"]
+            if not (np.isinf(a) and a == b):
+                assert abs(a - b) <= 0.1, (m, n, axis)
+
+
+RD_6000 = C3.with_(name="rd_512x6000", Na=512, Nr=6000, n_targets=4)
+
+
+@pytest.mark.parametrize("cfg", [C1, C3, LONG_MIGRATION, RD_1200, RD_800, WK_997, RD_6000], ids=lambda c: c.name)
+def test_focus_f16(torch_dev, rdf, cfg):
+    """rd_focus_f16: the image divided by Na, against the oracle on the binary16 echo; target
+    peaks and sidelobe ratios as the oracle's; in place bit-identical to out of place."""
+    torch = torch_dev
+    sc = make_scene(cfg)
+    echo = to_half(sc.echo)
+    log(f"[focus f16] {cfg.name}")
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        x = torch.from_numpy(echo).to("cuda")
+        img = plan.focus_f16(x).cpu().numpy()
+        plan.focus_f16(x, out=x)
+        torch.cuda.synchronize()
+        assert np.array_equal(x.cpu().numpy().view(np.uint16), img.view(np.uint16))
+    assert np.isfinite(img.astype(np.float32)).all()
+    log(f"[oracle] {cfg.name}: focusing the binary16 echo on the CPU")
+    ref = O.focus(from_half(echo), cfg.plan_params()) / cfg.Na
+    got = from_half(img)
+    err = M.rel_l2(got, ref)
+    log(f"[focus f16] {cfg.name} img rel-L2 {err:.2e}")
+    assert err <= F16_CHAIN_TOL
+    if cfg is not LONG_MIGRATION:
+        check_targets_near(got, ref, sc.targets, F16_CHAIN_TOL)
+
+
+def test_focus_f16_error_paths(torch_dev, rdf):
+    torch = torch_dev
+    x = torch.zeros((4, 256, 2), dtype=torch.float16, device="cuda")
+    with rdf.Plan(Na=4, Nr=256, pulse_s=100 / 120e6, bandwidth_hz=100e6, fs_hz=120e6) as plan:
+        with pytest.raises(rdf.RdError) as ei:      # range-only plan
+            plan.focus_f16(x)
+        assert ei.value.status == -6
+    with rdf.Plan(**C1.plan_params()) as plan:
+        y = torch.zeros((C1.Na, C1.Nr, 2), dtype=torch.float16, device="cuda")
+        for a, b in ((y.data_ptr() + 2, y), (y, y.data_ptr() + 4)):   # misaligned; partial overlap
+            with pytest.raises(rdf.RdError) as ei:
+                rdf.rd_focus_f16(plan.handle, a, b)
+            assert ei.value.status == -1
+    # 512-sample rows: the migration (~77 samples) exceeds the RCMC margin built for that length
+    with rdf.Plan(**C3.with_(Nr=512, pulse_s=1e-6).plan_params()) as plan:
+        z = torch.zeros((C3.Na, 512, 2), dtype=torch.float16, device="cuda")
+        with pytest.raises(rdf.RdError) as ei:
+            plan.focus_f16(z)
+        assert ei.value.status == -2
+    torch.cuda.synchronize()
+
+
 def test_focus_large_sampled_range_bins(torch_dev, rdf):
     torch = torch_dev
     cfg = C5
@@ -460,6 +537,39 @@ def test_focus_large_sampled_range_bins(torch_dev, rdf):
         a = M.point_target(sub_g, m, 16, axes=("azimuth",))["azimuth"]
         b = M.point_target(sub_r, m, 16, axes=("azimuth",))["azimuth"]
         assert abs(a["pslr_db"] - b["pslr_db"]) <= 0.1 and abs(a["islr_db"] - b["islr_db"]) <= 0.1
+
+
+def test_focus_f16_large_sampled_range_bins(torch_dev, rdf):
+    """rd_focus_f16 on the 16384 x 16384 scene (128-point column steps, chunked rows), against
+    the oracle on the binary16 echo at sampled range bins."""
+    torch = torch_dev
+    cfg = C5
+    log("[focus f16] 16384 x 16384: echo")
+    sc = cached_scene(cfg)
+    tg = sorted(sc.targets, key=lambda t: t[1])
+    bins = sorted(set(range(tg[1][1] - 16, tg[1][1] + 17)) | {0, cfg.Nr // 3, cfg.Nr - 1})
+    echo = to_half(sc.echo)
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        x = torch.from_numpy(echo).to("cuda")
+        plan.focus_f16(x, out=x)
+        torch.cuda.synchronize()
+        got = from_half(x[:, torch.tensor(bins, device="cuda")].cpu().numpy())
+        del x
+    torch.cuda.empty_cache()
+    log("[focus f16] 16384 x 16384: oracle on sampled range bins")
+    ref, ref_bins = O.focus_columns(from_half(echo), cfg.plan_params(), bins)
+    del echo
+    assert list(ref_bins) == bins
+    ref = ref / cfg.Na
+    err = M.rel_l2(got, ref)
+    log(f"[focus f16] 16384 sampled rel-L2 {err:.2e}")
+    assert err <= F16_CHAIN_TOL
+    m, n = tg[1]
+    col = {b: i for i, b in enumerate(bins)}
+    sub_g = got[:, [col[b] for b in range(n - 16, n + 17)]]
+    sub_r = ref[:, [col[b] for b in range(n - 16, n + 17)]]
+    pk, pr = M.peak_near(sub_g, m, 16), M.peak_near(sub_r, m, 16)
+    assert pr == (m, 16) and abs(sub_r[pk]) >= (1 - F16_CHAIN_TOL) * abs(sub_r[pr])
 
 
 # ------------------------------------------------------------------------------ omega-k
