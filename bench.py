@@ -368,6 +368,27 @@ def main():
                       "samples_per_s": round(cfg.Na * cfg.Nr / (ms * 1e-3), 1),
                       "data": "the headline scene rounded to binary16"})
         note(f"binary16 range compression: {ms * 1e3:.1f} us")
+        # the whole range-Doppler chain with binary16 storage: 4096 x 4096 airborne scene and
+        # the 16384 x 16384 scene (five sweeps of 8 B a pixel in the pages' model: 40 B/px)
+        for zcfg, steps in ((fcfg, max(10, args.steps // 2)), (C5, max(5, args.steps // 20))):
+            zs = cached_scene(zcfg)
+            z16 = torch.from_numpy(zs.echo).to("cuda").view(torch.float32).to(torch.float16).view(zcfg.Na, zcfg.Nr, 2)
+            rot = ROTATE if zcfg is fcfg else 2
+            ins = [z16] + [z16.clone() for _ in range(rot - 1)]
+            outs = [torch.empty_like(z16) for _ in range(rot)]
+            plan = rdf.Plan(**zcfg.plan_params())
+            ms = time_steps(torch, lambda i: rdf.rd_focus_f16(plan.handle, ins[i % rot], outs[i % rot], stream),
+                            steps, args.warmup, stream)
+            plan.close()
+            del ins, outs, z16
+            torch.cuda.empty_cache()
+            mp = zcfg.Na * zcfg.Nr / (ms * 1e-3) / 1e6
+            large.append({"workload": f"full RD focusing with binary16 storage (rd_focus_f16), {zcfg.Na} x {zcfg.Nr}, "
+                                      "float32 arithmetic, image / Na",
+                          "ms_per_step": round(ms, 4), "steps": steps, "value": round(mp, 1), "unit": "Mpixel/s",
+                          "roofline_frac_40B_per_px": round(mp * 1e6 * 40 / (HBM_PEAK_GBS * 1e9), 4),
+                          "data": "the focusing scene rounded to binary16"})
+            note(f"rd_focus_f16 {zcfg.Na} x {zcfg.Nr}: {ms * 1e3:.1f} us")
 
     # ---------------------------------------------------------------- a line length with no built transform
     if (args.only in (None, "large", "pad")) and not args.no_large:
