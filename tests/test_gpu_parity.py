@@ -505,6 +505,36 @@ def test_focus_f16_error_paths(torch_dev, rdf):
     torch.cuda.synchronize()
 
 
+def test_focus_random_sweep(torch_dev, rdf):
+    """12 seeded random scenes on the 4096 x 4096 scene's platform (1 us pulse): azimuth lengths
+    that are powers of two, 25 * 2^k, or anything else in [200, 1100] (the Bluestein form), and
+    range lengths in [700, 2048] (built or padded); each through rd_focus and rd_focus_f16
+    against the oracle on the same input, with every target's peak a valid argmax."""
+    torch = torch_dev
+    rng = np.random.default_rng(777)
+    for i in range(12):
+        kind = i % 3
+        na = int(rng.choice([256, 512, 1024])) if kind == 0 else (
+            int(rng.choice([400, 800])) if kind == 1 else int(rng.integers(200, 1101)))
+        nr = int(rng.choice([1024, 2048])) if i % 4 == 0 else int(rng.integers(700, 2049))
+        cfg = C3.with_(name=f"sweep_{i}_{na}x{nr}", Na=na, Nr=nr, pulse_s=1e-6, n_targets=2, seed=300 + i)
+        sc = make_scene(cfg)
+        e16 = to_half(sc.echo)
+        log(f"[focus sweep] {cfg.name}")
+        with rdf.Plan(**cfg.plan_params()) as plan:
+            img = plan.focus(dev(torch, sc.echo)).cpu().numpy()
+            h = from_half(plan.focus_f16(torch.from_numpy(e16).to("cuda")).cpu().numpy())
+        ref = O.focus(sc.echo, cfg.plan_params())
+        ref16 = O.focus(from_half(e16), cfg.plan_params()) / na
+        e32, eh = M.rel_l2(img, ref), M.rel_l2(h, ref16)
+        log(f"[focus sweep] {cfg.name} rel-L2 float32 {e32:.2e} binary16 {eh:.2e}")
+        assert e32 <= IMAGE_TOL and eh <= F16_CHAIN_TOL, (cfg.name, e32, eh)
+        for got, want, rel in ((img, ref, IMAGE_TOL), (h, ref16, F16_CHAIN_TOL)):
+            for (m, n) in sc.targets:
+                pk, pr = M.peak_near(got, m, n), M.peak_near(want, m, n)
+                assert abs(want[pk]) >= (1 - rel) * abs(want[pr]), (cfg.name, m, n, pk, pr)
+
+
 def test_focus_large_sampled_range_bins(torch_dev, rdf):
     torch = torch_dev
     cfg = C5
