@@ -177,6 +177,14 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
  * refuse the plan (range migration beyond the RCMC margin). */
 rd_status rd_focus_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, void* stream);
 
+/* The azimuth half of rd_focus_f16 (cf-1.com/news/2323550 §7): range-compressed data rc
+ * [Na][Nr] rd_c32h to img [Na][Nr] rd_c32h, img = (rd_azimuth_focus's image of the same rc) / Na,
+ * with the same binary16 storage and scaling of every intermediate.  rd_focus_f16 equals
+ * rd_range_compress_f16 followed by this call, bit for bit.  rc == img is allowed; other overlap
+ * is an error; pointers must be 4-byte aligned.  RD_ERR_NOT_CONFIGURED on a range-only plan;
+ * RD_ERR_UNSUPPORTED_LENGTH where rd_azimuth_focus would refuse the plan. */
+rd_status rd_azimuth_focus_f16(rd_plan* plan, const rd_c32h* rc, rd_c32h* img, void* stream);
+
 /* omega-k focusing with Stolt interpolation (nxmr.cn/news/101525 §3: the migration correction
  * becomes a frequency-domain mapping; forward and inverse 2-D transforms and two large complex
  * multiplies; §3.2: a phase built from the range and Doppler frequencies).  Raw echo [Na][Nr]

@@ -220,6 +220,15 @@ def focus(echo: np.ndarray, params) -> np.ndarray:
     return focus_stages(echo, params)["img"]
 
 
+def azimuth_focus(rc: np.ndarray, params) -> np.ndarray:
+    """The chain's azimuth half on range-compressed data rc [Na][Nr]: the same steps as
+    focus_stages after its range compression."""
+    n = np.arange(_p(params, "Nr"))
+    S = azimuth_fft(rc)
+    R = rcmc(S, rcmc_shift(params, n), _p(params, "rcmc_taps"), _p(params, "kaiser_beta"))
+    return azimuth_ifft(R * azimuth_matched_filter(params, n))
+
+
 def focus_columns(echo: np.ndarray, params, out_bins, block_rows: int = 1024):
     """Image columns img[:, out_bins] from the same definitions, for scenes too large to focus
     whole.  Range compression runs line by line and keeps only the range bins that the RCMC of

@@ -10,7 +10,7 @@ from __future__ import annotations
 from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
                       make_bp_grid, make_params, rd_azimuth_focus, rd_backproject, rd_bp_grid,
                       rd_corner_turn, rd_debug_azimuth_stages, rd_debug_line_fft,
-                      rd_focus, rd_focus_f16, rd_last_error, rd_length_supported, rd_omega_k, rd_params, rd_plan_create,
+                      rd_azimuth_focus_f16, rd_focus, rd_focus_f16, rd_last_error, rd_length_supported, rd_omega_k, rd_params, rd_plan_create,
                       rd_plan_destroy, rd_range_compress, rd_range_compress_f16, rd_status_string)
 
 
@@ -100,6 +100,12 @@ class Plan:
         [Na][Nr][2] (real, imaginary), float32 arithmetic inside (rd_range_compress_f16)."""
         out = self._half_pair(echo, out)
         rd_range_compress_f16(self.handle, echo, out)
+        return out
+
+    def azimuth_focus_f16(self, rc, out=None):
+        """Azimuth half of focus_f16 on binary16 range-compressed data (rd_azimuth_focus_f16)."""
+        out = self._half_pair(rc, out)
+        rd_azimuth_focus_f16(self.handle, rc, out)
         return out
 
     def focus_f16(self, echo, out=None):

@@ -769,6 +769,17 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
   return run_azimuth(plan, I, I, false, s);
 }
 
+rd_status rd_azimuth_focus_f16(rd_plan* plan, const rd_c32h* rc, rd_c32h* img, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if ((st = check_rcmc_margin(plan)) != RD_OK) return st;
+  if (!aligned4(rc) || !aligned4(img)) return fail(RD_ERR_INVALID_ARG, "rc and img must be non-NULL and 4-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c32h);
+  if (partial_overlap(rc, img, bytes)) return fail(RD_ERR_INVALID_ARG, "rc and img overlap without being equal");
+  return run_azimuth(plan, rc, img, true, static_cast<hipStream_t>(stream));
+}
+
 rd_status rd_focus_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, void* stream) {
   rd_status st = check_call(plan);
   if (st != RD_OK) return st;

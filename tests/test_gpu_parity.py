@@ -505,6 +505,28 @@ def test_focus_f16_error_paths(torch_dev, rdf):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("cfg", [C1, C3, RD_1200, WK_997], ids=lambda c: c.name)
+def test_azimuth_focus_f16(torch_dev, rdf, cfg):
+    """rd_azimuth_focus_f16 on binary16 range-compressed data (the oracle's, rounded) against the
+    oracle's azimuth half of the same data, divided by Na (five stored stages, within the
+    six-stage bound); rd_focus_f16 equals rd_range_compress_f16 followed by it, bit for bit."""
+    torch = torch_dev
+    sc = make_scene(cfg)
+    p = cfg.plan_params()
+    rc16 = to_half(O.range_compress(sc.echo, p))
+    with rdf.Plan(**p) as plan:
+        img = plan.azimuth_focus_f16(torch.from_numpy(rc16).to("cuda")).cpu().numpy()
+        x = torch.from_numpy(to_half(sc.echo)).to("cuda")
+        a = plan.focus_f16(x)
+        b = plan.azimuth_focus_f16(plan.range_compress_f16(x))
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = O.azimuth_focus(from_half(rc16), p) / cfg.Na
+    err = M.rel_l2(from_half(img), ref)
+    log(f"[azimuth f16] {cfg.name} rel-L2 {err:.2e}")
+    assert err <= F16_CHAIN_TOL
+
+
 def test_focus_random_sweep(torch_dev, rdf):
     """12 seeded random scenes on the 4096 x 4096 scene's platform (1 us pulse): azimuth lengths
     that are powers of two, 25 * 2^k, or anything else in [200, 1100] (the Bluestein form), and

@@ -287,6 +287,19 @@ def test_sampled_columns_equal_whole_image(c3az):
     np.testing.assert_allclose(cols, st["img"][:, got_bins], atol=1e-12 * np.abs(st["img"]).max())
 
 
+def test_azimuth_half_composes_with_range_compression_to_the_chain(c3az):
+    """azimuth_focus(range_compress(echo)) is the whole chain's image, and the azimuth half is
+    linear in its input (a scaled and a summed input give the scaled and summed images)."""
+    sc, st = c3az
+    p = C3_AZ.plan_params()
+    img = O.azimuth_focus(st["rc"], p)
+    np.testing.assert_allclose(img, st["img"], atol=1e-12 * np.abs(st["img"]).max())
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(st["rc"].shape) + 1j * rng.standard_normal(st["rc"].shape)
+    lin = O.azimuth_focus((2 - 1j) * st["rc"] + x, p)
+    np.testing.assert_allclose(lin, (2 - 1j) * img + O.azimuth_focus(x, p), atol=1e-10 * np.abs(lin).max())
+
+
 def test_metrics_ignore_a_linear_phase_ramp():
     p, x = single_chirp(C3, 0, 17)
     rc = O.range_compress(x, p)[0]
