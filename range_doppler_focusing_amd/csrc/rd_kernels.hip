@@ -1206,8 +1206,10 @@ hipError_t launch_rcmc_mf(const void* in, void* out, const AzRowConst& c, int64_
   const int64_t wgs = (rows * RowStage<N>::CHUNKS + RowStage<N>::LPW - 1) / RowStage<N>::LPW;
   if (grid <= 0 || grid > wgs) grid = int(wgs);
   const dim3 g(grid), b(RowStage<N>::WG);
-  if (half)
+  if (half && cached)
     hipLaunchKernelGGL((k_rcmc_mf<N, kAuxCached, true>), g, b, 0, s, in, out, c, rows, N);
+  else if (half)
+    hipLaunchKernelGGL((k_rcmc_mf<N, kAuxStream, true>), g, b, 0, s, in, out, c, rows, N);
   else if (cached)
     hipLaunchKernelGGL((k_rcmc_mf<N, kAuxCached>), g, b, 0, s, in, out, c, rows, N);
   else
@@ -1246,8 +1248,10 @@ hipError_t launch_rcmc_mf_any(const void* in, void* out, const AzRowConst& c, in
   const int64_t wgs = (items + RS::LPW - 1) / RS::LPW;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   const int grid = int(wgs);
-  if (half)
+  if (half && cached)
     hipLaunchKernelGGL((k_rcmc_mf<0, kAuxCached, true>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
+  else if (half)
+    hipLaunchKernelGGL((k_rcmc_mf<0, kAuxStream, true>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
   else if (cached)
     hipLaunchKernelGGL((k_rcmc_mf<0, kAuxCached>), dim3(grid), dim3(RS::WG), 0, s, in, out, c, rows, n);
   else

@@ -77,7 +77,7 @@ struct LineOps {
   // RCMC + azimuth filter over rows of this length (in == out allowed; grid 0 = one workgroup
   // per staged chunk); margin = samples staged after a chunk, so the largest shift the kernel
   // accepts is margin - 5
-  // (half: binary16 rows, 4 bytes a sample, float32 arithmetic; ordinary stores)
+  // (half: binary16 rows, 4 bytes a sample, float32 arithmetic)
   hipError_t (*rcmc_mf)(const void* in, void* out, const AzRowConst& c, int64_t rows, int grid,
                         int cached, int half, hipStream_t s);
   int margin;
