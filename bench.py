@@ -389,6 +389,26 @@ def main():
                           "roofline_frac_40B_per_px": round(mp * 1e6 * 40 / (HBM_PEAK_GBS * 1e9), 4),
                           "data": "the focusing scene rounded to binary16"})
             note(f"rd_focus_f16 {zcfg.Na} x {zcfg.Nr}: {ms * 1e3:.1f} us")
+        # omega-k with binary16 storage on the 4096 x 4096 airborne scene
+        ref = int(round((fcfg.r_ref_m - fcfg.range_bin0_m) / fcfg.dr))
+        z16 = torch.from_numpy(cached_scene(fcfg).echo).to("cuda").view(torch.float32).to(torch.float16).view(
+            fcfg.Na, fcfg.Nr, 2)
+        ins = [z16] + [z16.clone() for _ in range(ROTATE - 1)]
+        outs = [torch.empty_like(z16) for _ in range(ROTATE)]
+        plan = rdf.Plan(**fcfg.plan_params())
+        steps = max(10, args.steps // 2)
+        ms = time_steps(torch, lambda i: rdf.rd_omega_k_f16(plan.handle, ins[i % ROTATE], outs[i % ROTATE], ref, stream),
+                        steps, args.warmup, stream)
+        plan.close()
+        del ins, outs, z16
+        torch.cuda.empty_cache()
+        mp = fcfg.Na * fcfg.Nr / (ms * 1e-3) / 1e6
+        large.append({"workload": f"omega-k focusing with binary16 storage (rd_omega_k_f16), {fcfg.Na} x {fcfg.Nr}, "
+                                  f"float32 arithmetic, image / Na, reference bin {ref}",
+                      "ms_per_step": round(ms, 4), "steps": steps, "value": round(mp, 1), "unit": "Mpixel/s",
+                      "roofline_frac_40B_per_px": round(mp * 1e6 * 40 / (HBM_PEAK_GBS * 1e9), 4),
+                      "data": "the focusing scene rounded to binary16"})
+        note(f"rd_omega_k_f16 {fcfg.Na} x {fcfg.Nr}: {ms * 1e3:.1f} us")
 
     # ---------------------------------------------------------------- a line length with no built transform
     if (args.only in (None, "large", "pad")) and not args.no_large:

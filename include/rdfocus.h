@@ -205,6 +205,15 @@ rd_status rd_azimuth_focus_f16(rd_plan* plan, const rd_c32h* rc, rd_c32h* img, v
  * (at f' = -Fs/2 and the Doppler band edge) plus 5 samples exceeds Nr/2 (Nr/8 at 16384). */
 rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref_bin, void* stream);
 
+/* rd_omega_k with binary16 storage of the echo, of every intermediate and of the image
+ * (cf-1.com/news/2323550 §7: FP16 storage, FP32 arithmetic): echo and img are [Na][Nr] rd_c32h,
+ * the chain runs in place in img, every kernel converts its input exactly to float32 and
+ * rounds its output to the nearest binary16 value (ties to even).  As in rd_focus_f16, each
+ * azimuth transform step is scaled by 1/(its length) and the row stage omits its 1/Na, so
+ *   img_f16 = img / Na,  img = rd_omega_k's image of the same echo and ref_bin.
+ * Arguments, conditions and errors as rd_omega_k, with 4-byte alignment. */
+rd_status rd_omega_k_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, int32_t ref_bin, void* stream);
+
 /* Test hook: the azimuth chain with its intermediates exposed.  azfft and rcmc receive the
  * azimuth spectrum S[k][n] and the RCMC output T[k][n], [Na][Nr] with row k = Doppler bin in
  * FFT order; img receives the image [Na][Nr].  azfft, rcmc and img must be distinct from each

@@ -10,7 +10,7 @@ from __future__ import annotations
 from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
                       make_bp_grid, make_params, rd_azimuth_focus, rd_backproject, rd_bp_grid,
                       rd_corner_turn, rd_debug_azimuth_stages, rd_debug_line_fft,
-                      rd_azimuth_focus_f16, rd_focus, rd_focus_f16, rd_last_error, rd_length_supported, rd_omega_k, rd_params, rd_plan_create,
+                      rd_azimuth_focus_f16, rd_focus, rd_focus_f16, rd_last_error, rd_length_supported, rd_omega_k, rd_omega_k_f16, rd_params, rd_plan_create,
                       rd_plan_destroy, rd_range_compress, rd_range_compress_f16, rd_status_string)
 
 
@@ -120,6 +120,13 @@ class Plan:
         self._check(echo, (self.Na, self.Nr))
         out = self._empty((self.Na, self.Nr)) if out is None else self._check(out, (self.Na, self.Nr))
         rd_omega_k(self.handle, echo, out, ref_bin)
+        return out
+
+    def omega_k_f16(self, echo, ref_bin: int, out=None):
+        """omega-k with binary16 storage (float16 tensors [Na][Nr][2]); the image is rd_omega_k's
+        divided by Na (rd_omega_k_f16)."""
+        out = self._half_pair(echo, out)
+        rd_omega_k_f16(self.handle, echo, out, ref_bin)
         return out
 
     def backproject(self, rc, grid: dict, out=None):

@@ -27,7 +27,7 @@ RD_WINDOW_HAMMING = 1
 EXPORTS = ("rd_length_supported", "rd_plan_create", "rd_plan_destroy", "rd_range_compress",
            "rd_range_compress_f16",
            "rd_azimuth_focus", "rd_focus", "rd_focus_f16", "rd_azimuth_focus_f16", "rd_debug_azimuth_stages", "rd_debug_line_fft",
-           "rd_backproject", "rd_corner_turn", "rd_omega_k", "rd_status_string", "rd_last_error")
+           "rd_backproject", "rd_corner_turn", "rd_omega_k", "rd_omega_k_f16", "rd_status_string", "rd_last_error")
 
 
 class rd_params(ctypes.Structure):
@@ -94,6 +94,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rd_focus_f16.restype = ctypes.c_int
     lib.rd_azimuth_focus_f16.argtypes = [vp, vp, vp, vp]
     lib.rd_azimuth_focus_f16.restype = ctypes.c_int
+    lib.rd_omega_k_f16.argtypes = [vp, vp, vp, ctypes.c_int32, vp]
+    lib.rd_omega_k_f16.restype = ctypes.c_int
     lib.rd_debug_azimuth_stages.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.rd_debug_azimuth_stages.restype = ctypes.c_int
     lib.rd_debug_line_fft.argtypes = [vp, i32, i32, vp, vp, i64, vp]
@@ -209,6 +211,11 @@ def rd_focus_f16(plan: int, echo, img, stream=None) -> None:
 def rd_azimuth_focus_f16(plan: int, rc, img, stream=None) -> None:
     _check(load_library().rd_azimuth_focus_f16(plan, _addr_half(rc), _addr_half(img), _stream(stream, rc, img)),
            "rd_azimuth_focus_f16")
+
+
+def rd_omega_k_f16(plan: int, echo, img, ref_bin: int, stream=None) -> None:
+    _check(load_library().rd_omega_k_f16(plan, _addr_half(echo), _addr_half(img), int(ref_bin),
+                                         _stream(stream, echo, img)), "rd_omega_k_f16")
 
 
 def rd_debug_azimuth_stages(plan: int, rc, azfft, rcmc, img, stream=None) -> None:

@@ -486,6 +486,50 @@ rd_status run_azimuth(rd_plan* P, const void* rc, void* img, bool half, hipStrea
   return az_inverse(P, img, half, s);
 }
 
+// omega-k: the azimuth transform first (the 2-D transform's order is free), then one row stage
+// per Doppler row, then the inverse azimuth transform; echo is read only by the first step.
+// half: binary16 storage of echo, intermediates and image (the azimuth steps scaled by 1/L, the
+// row stage without its 1/Na: the image divided by Na)
+rd_status run_omega_k(rd_plan* plan, const void* echo, void* img, int32_t ref_bin, bool half, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  const rd_params& p = plan->p;
+  if (ref_bin < 0 || ref_bin >= p.Nr) return fail(RD_ERR_INVALID_ARG, "ref_bin=%d must be in [0, Nr=%d)", ref_bin, p.Nr);
+  if (!plan->rops->omega_k_rows || plan->pad_m)
+    return fail(RD_ERR_UNSUPPORTED_LENGTH, "omega-k needs a built transform of length Nr=%d", p.Nr);
+  if (plan->wk_halo < 0)
+    return fail(RD_ERR_INVALID_ARG, "f0 - Fs/2 must exceed c PRF / (4 V) for the Stolt mapping");
+  if (plan->wk_halo > plan->rops->wk_cap)
+    return fail(RD_ERR_UNSUPPORTED_LENGTH, "Stolt shift of %d samples exceeds the %d-sample margin built for Nr=%d",
+                plan->wk_halo - 5, plan->rops->wk_cap - 5, p.Nr);
+  if (half ? !aligned4(echo) || !aligned4(img) : !aligned8(echo) || !aligned8(img))
+    return fail(RD_ERR_INVALID_ARG, "echo and img must be non-NULL and %d-byte aligned", half ? 4 : 8);
+  const size_t bytes = size_t(p.Na) * p.Nr * (half ? sizeof(rd_c32h) : sizeof(rd_c64));
+  if (partial_overlap(echo, img, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and img overlap without being equal");
+  rdf::OkConst c{};
+  c.f0 = p.carrier_hz;
+  c.df = p.fs_hz / p.Nr;
+  c.inv_df = p.Nr / p.fs_hz;
+  c.bstep = kC * p.prf_hz / (2.0 * p.velocity_mps * p.Na);
+  const double r_ref = p.range_bin0_m + ref_bin * plan->dr;
+  c.k1 = 2.0 * r_ref / kC;
+  const double turns = c.k1 * p.carrier_hz;
+  c.k0 = turns - std::floor(turns);
+  c.ref = ref_bin;
+  c.A = plan->A;
+  c.B = plan->B;
+  c.halo = plan->wk_halo;
+  c.inv_na = half ? 1.0f : float(1.0 / double(p.Na));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = az_forward(plan, echo, img, half, s)) != RD_OK) return st;
+  if ((st = check_hip(plan->rops->omega_k_rows(img, img, plan->H, plan->tw_r, c, plan->az.w, p.Na, plan->wk_grid,
+                                               plan->cached, half ? 1 : 0, s),
+                      "omega-k row stage launch")) != RD_OK)
+    return st;
+  return az_inverse(plan, img, half, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -796,45 +840,11 @@ rd_status rd_focus_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, void* s
 }
 
 rd_status rd_omega_k(rd_plan* plan, const rd_c64* echo, rd_c64* img, int32_t ref_bin, void* stream) {
-  rd_status st = check_call(plan);
-  if (st != RD_OK) return st;
-  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
-  const rd_params& p = plan->p;
-  if (ref_bin < 0 || ref_bin >= p.Nr) return fail(RD_ERR_INVALID_ARG, "ref_bin=%d must be in [0, Nr=%d)", ref_bin, p.Nr);
-  if (!plan->rops->omega_k_rows || plan->pad_m)
-    return fail(RD_ERR_UNSUPPORTED_LENGTH, "omega-k needs a built transform of length Nr=%d", p.Nr);
-  if (plan->wk_halo < 0)
-    return fail(RD_ERR_INVALID_ARG, "f0 - Fs/2 must exceed c PRF / (4 V) for the Stolt mapping");
-  if (plan->wk_halo > plan->rops->wk_cap)
-    return fail(RD_ERR_UNSUPPORTED_LENGTH, "Stolt shift of %d samples exceeds the %d-sample margin built for Nr=%d",
-                plan->wk_halo - 5, plan->rops->wk_cap - 5, p.Nr);
-  if (!aligned8(echo) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "echo and img must be non-NULL and 8-byte aligned");
-  const size_t bytes = size_t(p.Na) * p.Nr * sizeof(rd_c64);
-  if (partial_overlap(echo, img, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and img overlap without being equal");
-  rdf::OkConst c{};
-  c.f0 = p.carrier_hz;
-  c.df = p.fs_hz / p.Nr;
-  c.inv_df = p.Nr / p.fs_hz;
-  c.bstep = kC * p.prf_hz / (2.0 * p.velocity_mps * p.Na);
-  const double r_ref = p.range_bin0_m + ref_bin * plan->dr;
-  c.k1 = 2.0 * r_ref / kC;
-  const double turns = c.k1 * p.carrier_hz;
-  c.k0 = turns - std::floor(turns);
-  c.ref = ref_bin;
-  c.A = plan->A;
-  c.B = plan->B;
-  c.halo = plan->wk_halo;
-  c.inv_na = float(1.0 / double(p.Na));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float2* I = reinterpret_cast<float2*>(img);
-  // the azimuth transform first (the 2-D transform's order is free), then one row stage per
-  // Doppler row, then the inverse azimuth transform; echo is read only by the first step
-  if ((st = az_forward(plan, echo, I, false, s)) != RD_OK) return st;
-  if ((st = check_hip(plan->rops->omega_k_rows(I, I, plan->H, plan->tw_r, c, plan->az.w, p.Na, plan->wk_grid,
-                                               plan->cached, s),
-                      "omega-k row stage launch")) != RD_OK)
-    return st;
-  return az_inverse(plan, I, false, s);
+  return run_omega_k(plan, echo, img, ref_bin, false, stream);
+}
+
+rd_status rd_omega_k_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, int32_t ref_bin, void* stream) {
+  return run_omega_k(plan, echo, img, ref_bin, true, stream);
 }
 
 rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft, rd_c64* rcmc,

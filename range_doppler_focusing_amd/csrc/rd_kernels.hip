@@ -689,8 +689,9 @@ struct OkRow {
 };
 
 // line I/O rotated by rot (0 <= rot < N): slot e of the line holds sample (e + rot) mod N
-template <int N, int T, int R, int AUX>
-__device__ __forceinline__ void load_line_rot(float2* v, const LineIO& io, int elem0, int tid, int rot) {
+// (HALF: binary16 storage through a LineIOh resource)
+template <int N, int T, int R, int AUX, bool HALF = false, class IO>
+__device__ __forceinline__ void load_line_rot(float2* v, const IO& io, int elem0, int tid, int rot) {
   using G = Geom<N, T, R>;
 #pragma unroll
   for (int b = 0; b < G::B; ++b) {
@@ -701,14 +702,17 @@ __device__ __forceinline__ void load_line_rot(float2* v, const LineIO& io, int e
         const int r = dft_input_order<R>(i);
         int e = j + r * G::NB + rot;
         e -= e >= N ? N : 0;
-        v[b * R + r] = __builtin_bit_cast(
-            float2, __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, uint32_t(elem0 + e) * 8u, 0, AUX));
+        if constexpr (HALF)
+          v[b * R + r] = h2_to_f2(__builtin_amdgcn_raw_buffer_load_b32(io.rsrc, uint32_t(elem0 + e) * 4u, 0, AUX));
+        else
+          v[b * R + r] = __builtin_bit_cast(
+              float2, __builtin_amdgcn_raw_buffer_load_b64(io.rsrc, uint32_t(elem0 + e) * 8u, 0, AUX));
       }
     }
   }
 }
-template <int N, int T, int R, int AUX>
-__device__ __forceinline__ void store_line_rot(const float2* v, const LineIO& io, int elem0, int tid, int rot) {
+template <int N, int T, int R, int AUX, bool HALF = false, class IO>
+__device__ __forceinline__ void store_line_rot(const float2* v, const IO& io, int elem0, int tid, int rot) {
   using G = Geom<N, T, R>;
 #pragma unroll
   for (int b = 0; b < G::B; ++b) {
@@ -718,8 +722,11 @@ __device__ __forceinline__ void store_line_rot(const float2* v, const LineIO& io
       for (int r = 0; r < R; ++r) {
         int e = j + r * G::NB + rot;
         e -= e >= N ? N : 0;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, v[b * R + r]), io.rsrc,
-                                              uint32_t(elem0 + e) * 8u, 0, AUX);
+        if constexpr (HALF)
+          __builtin_amdgcn_raw_buffer_store_b32(f2_to_h2(v[b * R + r]), io.rsrc, uint32_t(elem0 + e) * 4u, 0, AUX);
+        else
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, v[b * R + r]), io.rsrc,
+                                                uint32_t(elem0 + e) * 8u, 0, AUX);
       }
     }
   }
@@ -738,10 +745,11 @@ __device__ __forceinline__ double sqrt_pos(double x) {
   return fma(fma(-s, s, x), h, s);
 }
 
-template <int N, int AUX>
+template <int N, int AUX, bool HALF = false>
 __global__ void __launch_bounds__(LineCfg<N>::WG)
-    k_omega_k_row(const float2* in, float2* out, const float2* __restrict__ H,
+    k_omega_k_row(const void* in, void* out, const float2* __restrict__ H,
                   const float2* __restrict__ tw, OkConst c, RcmcPoly w, int64_t rows) {
+  using RIO = RowIO<HALF>;
   using C = LineCfg<N>;
   using L = typename C::Fwd;
   static_assert(std::is_same<typename C::Fwd, typename C::Inv>::value, "needs Fwd == Inv");
@@ -774,8 +782,8 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     constexpr bool TIGHT = N <= 512 || N == 6000 || N >= 16384;
     int rot = c.ref;
     if constexpr (TIGHT) asm volatile("" : "+s"(rot));
-    const LineIO io_in(in, N, l0, C::LPW, rows);
-    load_line_rot<N, T, R0, AUX>(v, io_in, grp * N, tid, rot);
+    const typename RIO::IO io_in = RIO::make(in, N, l0, C::LPW, rows);
+    load_line_rot<N, T, R0, AUX, HALF>(v, io_in, grp * N, tid, rot);
     PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
     // v = X[kx] H[kx] exp(j 2 pi (k0 - k1 (a - Q))) / Na at range bin kx = j + r NB,
     // a = f0 + js df, Q = sqrt(a^2 - b^2) (float64: the phase reaches ~1e4 turns)
@@ -856,7 +864,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     // (the inverse transform's first exchange begins with a barrier: the staging reads are done)
     PassesCached<N, T, +1, 1, L, C::WAVE>::run(v, my, twc, tid);
     if constexpr (TIGHT) asm volatile("" : "+s"(rot));
-    store_line_rot<N, T, R0, AUX>(v, LineIO(out, N, l0, C::LPW, rows), grp * N, tid, rot);
+    store_line_rot<N, T, R0, AUX, HALF>(v, RIO::make(out, N, l0, C::LPW, rows), grp * N, tid, rot);
   }
 }
 
@@ -1218,13 +1226,19 @@ hipError_t launch_rcmc_mf(const void* in, void* out, const AzRowConst& c, int64_
 }
 
 template <int N>
-hipError_t launch_omega_k_rows(const float2* in, float2* out, const float2* H, const float2* tw,
+hipError_t launch_omega_k_rows(const void* in, void* out, const float2* H, const float2* tw,
                                const OkConst& c, const RcmcPoly& w, int64_t rows, int grid,
-                               int cached, hipStream_t s) {
+                               int cached, int half, hipStream_t s) {
   if (c.halo < 0 || c.halo > OkRow<N>::CAP || c.ref < 0 || c.ref >= N) return hipErrorInvalidValue;
   const int64_t wgs = (rows + LineCfg<N>::LPW - 1) / LineCfg<N>::LPW;
   if (grid <= 0 || grid > wgs) grid = int(wgs);
-  if (cached)
+  if (half && cached)
+    hipLaunchKernelGGL((k_omega_k_row<N, kAuxCached, true>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, H,
+                       tw, c, w, rows);
+  else if (half)
+    hipLaunchKernelGGL((k_omega_k_row<N, kAuxStream, true>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, H,
+                       tw, c, w, rows);
+  else if (cached)
     hipLaunchKernelGGL((k_omega_k_row<N, kAuxCached>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in, out, H, tw,
                        c, w, rows);
   else

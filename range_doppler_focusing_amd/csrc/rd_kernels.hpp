@@ -83,9 +83,10 @@ struct LineOps {
   int margin;
   // omega-k row stage over `rows` Doppler rows (in == out allowed); wk_cap = the largest halo
   // the kernel stages, occupancy_wk = its workgroups per CU
-  hipError_t (*omega_k_rows)(const float2* in, float2* out, const float2* H, const float2* tw,
+  // (half: binary16 rows, float32 arithmetic)
+  hipError_t (*omega_k_rows)(const void* in, void* out, const float2* H, const float2* tw,
                              const OkConst& c, const RcmcPoly& w, int64_t rows, int grid,
-                             int cached, hipStream_t s);
+                             int cached, int half, hipStream_t s);
   hipError_t (*occupancy_wk)(int* wgs);
   int wk_cap;
   // range compression with binary16 line storage (4 bytes a sample in and out, float32

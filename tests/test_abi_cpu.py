@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     import range_doppler_focusing_amd as rdf
     lib = rdf.load_library()
     declared = header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(rdf.EXPORTS) == declared
@@ -148,3 +148,4 @@ def test_backproject_rejects_a_null_plan_before_any_launch():
     assert lib.rd_range_compress_f16(None, 1 << 20, 1 << 30, None) == -1
     assert lib.rd_focus_f16(None, 1 << 20, 1 << 30, None) == -1
     assert lib.rd_azimuth_focus_f16(None, 1 << 20, 1 << 30, None) == -1
+    assert lib.rd_omega_k_f16(None, 1 << 20, 1 << 30, 0, None) == -1

@@ -743,6 +743,35 @@ def test_omega_k_error_paths(torch_dev, rdf):
         assert ei.value.status == -2
 
 
+@pytest.mark.parametrize("cfg", [C1, C3, WK_C3AZ, WK_6000, WK_800, WK_997], ids=lambda c: c.name)
+def test_omega_k_f16(torch_dev, rdf, cfg):
+    """rd_omega_k_f16: the image divided by Na against the oracle on the same binary16 echo
+    (five stored stages: two forward azimuth steps, the row stage, two inverse steps; within the
+    six-stage bound), target peaks valid; in place bit-identical to out of place."""
+    torch = torch_dev
+    sc = make_scene(cfg)
+    rb = wk_ref_bin(cfg)
+    e16 = to_half(sc.echo)
+    log(f"[omega-k f16] {cfg.name}")
+    with rdf.Plan(**cfg.plan_params()) as plan:
+        x = torch.from_numpy(e16).to("cuda")
+        img = plan.omega_k_f16(x, rb).cpu().numpy()
+        plan.omega_k_f16(x, rb, out=x)
+        torch.cuda.synchronize()
+        assert np.array_equal(x.cpu().numpy().view(np.uint16), img.view(np.uint16))
+        with pytest.raises(rdf.RdError) as ei:      # misaligned
+            rdf.rd_omega_k_f16(plan.handle, x.data_ptr() + 2, x, rb)
+        assert ei.value.status == -1
+    ref = O.omega_k(from_half(e16), cfg.plan_params(), rb) / cfg.Na
+    got = from_half(img)
+    err = M.rel_l2(got, ref)
+    log(f"[omega-k f16] {cfg.name} rel-L2 {err:.2e}")
+    assert err <= F16_CHAIN_TOL
+    for (m, n) in sc.targets:
+        pk, pr = M.peak_near(got, m, n), M.peak_near(ref, m, n)
+        assert abs(ref[pk]) >= (1 - F16_CHAIN_TOL) * abs(ref[pr]), (m, n, pk, pr)
+
+
 # ------------------------------------------------------------------------------ corner turn
 @pytest.mark.parametrize("rows,cols", [(256, 256), (4096, 4096), (37, 1000), (1, 5), (5, 1),
                                        (65, 63), (8192, 6000), (64, 16384)])
