@@ -9,8 +9,11 @@
 //
 // Azimuth processing (cf-1.com/news/2323550 §5.1; nxmr.cn/news/101525 §2.2) in place on
 // [Na][Nr], with no corner turn: the azimuth transform as strided and block column steps, RCMC
-// fused with the azimuth filter per Doppler row from LDS, and the inverse column steps.
-// omega-k (nxmr.cn/news/101525 §3) reuses the column steps around one fused row stage.
+// fused with the azimuth filter per Doppler row from LDS, and the inverse column steps.  Other
+// azimuth lengths take the Bluestein form (nxmr.cn/news/101525 §5.1): chirp passes around
+// column steps of a power-of-two length.  omega-k (nxmr.cn/news/101525 §3) reuses the column
+// steps around one fused row stage.  The column steps, both row stages and the chirp passes
+// also have binary16-storage variants (cf-1.com/news/2323550 §7), float32 arithmetic inside.
 // Also here: the corner turn (an entry point of its own), back-projection
 // (framerc.cn/news/4459478), and the line-transform test hook.
 #include <atomic>
