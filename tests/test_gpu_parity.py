@@ -934,8 +934,8 @@ def test_error_paths_on_device(torch_dev, rdf):
 
 # ------------------------------------------------------------------------------ graph capture
 def test_entry_points_replay_from_a_captured_graph(torch_dev, rdf):
-    """rd_range_compress, rd_focus, rd_focus_f16 and rd_omega_k allocate nothing and issue no
-    memsets per call, so they can be captured into a HIP graph: each of several replays, with
+    """rd_range_compress, rd_focus, rd_focus_f16, rd_omega_k and rd_omega_k_f16 allocate nothing
+    and issue no memsets per call, so they can be captured into a HIP graph: each of several replays, with
     eager work and synchronisation between them, gives the eager result bit for bit."""
     torch = torch_dev
     cfg = C1
@@ -945,9 +945,9 @@ def test_entry_points_replay_from_a_captured_graph(torch_dev, rdf):
         echo = dev(torch, sc.echo)
         e16 = torch.from_numpy(to_half(sc.echo)).to("cuda")
         rc_e, img_e, wk_e = plan.range_compress(echo), plan.focus(echo), plan.omega_k(echo, ref_bin)
-        h_e = plan.focus_f16(e16)
+        h_e, hw_e = plan.focus_f16(e16), plan.omega_k_f16(e16, ref_bin)
         rc, img, wk = torch.empty_like(echo), torch.empty_like(echo), torch.empty_like(echo)
-        h = torch.empty_like(e16)
+        h, hw = torch.empty_like(e16), torch.empty_like(e16)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):                 # warm the capture stream
@@ -960,14 +960,16 @@ def test_entry_points_replay_from_a_captured_graph(torch_dev, rdf):
             plan.focus(echo, out=img)
             plan.focus_f16(e16, out=h)
             plan.omega_k(echo, ref_bin, out=wk)
+            plan.omega_k_f16(e16, ref_bin, out=hw)
         for i in range(4):
-            rc.zero_(), img.zero_(), wk.zero_(), h.zero_()
+            rc.zero_(), img.zero_(), wk.zero_(), h.zero_(), hw.zero_()
             _ = (echo * (i + 1)).sum()                # eager work between replays
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(rc, rc_e) and torch.equal(img, img_e) and torch.equal(wk, wk_e), i
             assert torch.equal(h.view(torch.int16), h_e.view(torch.int16)), i
+            assert torch.equal(hw.view(torch.int16), hw_e.view(torch.int16)), i
         log("[graph] 4 replays bit-identical to eager")
         del g
 
