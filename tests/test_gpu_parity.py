@@ -2,6 +2,10 @@
 
 Bars: relative L2 <= 1e-5 per stage and <= 1e-4 for the focused image; target peak indices
 identical to the oracle's; PSLR / ISLR of every target within 0.1 dB of the oracle's.
+Binary16 storage has its own tier against the oracle on the same binary16 input: range
+compression within half a binary16 ulp (+1e-5 of the RMS) per stored component and rel-L2 <=
+4e-4; the focusing chains rel-L2 <= 3e-3 (six stored roundings of at most 2^-11 each), peaks a
+valid argmax within that error, PSLR within 0.1 dB.
 Sizes: the five workloads at their full sizes (the 16384 x 16384 scene on sampled lines and
 range bins, which the oracle computes one by one), plus ragged line counts and every built
 transform length for the line FFT.
