@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 import tempfile
 
 import pytest
@@ -149,3 +150,12 @@ def test_backproject_rejects_a_null_plan_before_any_launch():
     assert lib.rd_focus_f16(None, 1 << 20, 1 << 30, None) == -1
     assert lib.rd_azimuth_focus_f16(None, 1 << 20, 1 << 30, None) == -1
     assert lib.rd_omega_k_f16(None, 1 << 20, 1 << 30, 0, None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The path runs on one GPU: bench.py --gpus N with N > 1 exits with a message, before any
+    device work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
