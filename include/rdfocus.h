@@ -222,6 +222,17 @@ rd_status rd_omega_k_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, int32
 rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft, rd_c64* rcmc,
                                   rd_c64* img, void* stream);
 
+/* Test hook: the row stage of the range-Doppler chain on its own (cf-1.com/news/2323550 §5.1:
+ * RCMC by sinc interpolation and the azimuth filter; nxmr.cn/news/101525 §2.2: the migrated
+ * slant range along each range line of the range-Doppler domain).  in and out are [Na][Nr] with
+ * row k holding Doppler bin k (FFT order) and range along the row:
+ *   out[k][n] = sum_{j=-3..4} w_j in[k][floor(x)+j],  x = n + R(n) (1/D_k - 1)/dr
+ * (the RCMC of rd_azimuth_focus), times exp(+j 4 pi R(n) D_k / lambda) / Na if filter != 0.
+ * The chain runs this stage in place, so in == out is allowed (and gives the same bits as out of
+ * place); other overlap is an error.  RD_ERR_NOT_CONFIGURED on a range-only plan;
+ * RD_ERR_UNSUPPORTED_LENGTH where rd_azimuth_focus refuses the plan. */
+rd_status rd_debug_rcmc(rd_plan* plan, const rd_c64* in, rd_c64* out, int32_t filter, void* stream);
+
 /* Test hook: `lines` independent transforms of length Na (axis = 0) or Nr (axis = 1), from
  * in[lines][len] to out[lines][len] (in == out allowed): forward if inverse == 0, else the
  * inverse including 1/len.  Uses the same LDS-resident transform as the focusing kernels. */

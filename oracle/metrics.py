@@ -27,6 +27,25 @@ def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.sqrt(np.sum(np.abs(a - b) ** 2)) / den) if den > 0 else float(np.sqrt(np.sum(np.abs(a) ** 2)))
 
 
+def line_errors(a: np.ndarray, b: np.ndarray, axis: int) -> np.ndarray:
+    """Relative L2 error of every line of a 2-D array against the reference b: line i along
+    `axis` (axis=1: rows, axis=0: columns) gives ||a_i - b_i|| / max(||b_i||, RMS(b) sqrt(len_i)),
+    i.e. the line's own relative error, or its error relative to an average line where the
+    line holds less than average energy.  A defect confined to a few rows or columns, which a
+    whole-array norm dilutes by the square root of the line count, shows at full size here."""
+    a = np.asarray(a, dtype=np.complex128)
+    b = np.asarray(b, dtype=np.complex128)
+    num = np.sqrt(np.sum(np.abs(a - b) ** 2, axis=axis))
+    own = np.sqrt(np.sum(np.abs(b) ** 2, axis=axis))
+    avg = np.sqrt(np.mean(np.abs(b) ** 2) * b.shape[axis])
+    return num / np.maximum(own, avg) if avg > 0 else num
+
+
+def worst_line_errors(a: np.ndarray, b: np.ndarray) -> tuple:
+    """(worst row error, worst column error) of line_errors."""
+    return float(line_errors(a, b, 1).max()), float(line_errors(a, b, 0).max())
+
+
 def peak_near(img: np.ndarray, m: int, n: int, radius: int = 16) -> tuple:
     """(row, col) of the largest |img| within +-radius of (m, n), circular in both axes;
     ties resolve to the first in row-major order of the scanned window."""

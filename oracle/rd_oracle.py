@@ -5,8 +5,10 @@ test suite, the package's smoke check and the benchmark's CPU-baseline leg may i
 library itself never calls it and shares no code, table or constant generator with it.
 
 Every function is the textbook definition of its step, written for a reader to check by eye:
-no blocking, fusion or reordering beyond what the definition states.  NumPy's FFT is used as a
-library primitive.  All arithmetic is float64 / complex128; the raw echo is upcast on entry.
+no blocking, fusion or reordering beyond what the definition states.  SciPy's FFT is used as a
+library primitive, with as many worker threads as the process may use (``workers()``); a
+transform's value does not depend on the thread count beyond rounding.  All arithmetic is
+float64 / complex128; the raw echo is upcast on entry.
 
 Page references (the source pages, by site and section):
   [SAR-GPU]  nxmr.cn/news/101525 -- "ultra-high-resolution airborne SAR imaging on GPU"
@@ -19,11 +21,34 @@ model, azimuth filter form) are stated at each function.
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
+import scipy.fft
 from scipy.special import i0 as bessel_i0
 
 C_LIGHT = 299_792_458.0
+
+
+def workers() -> int:
+    """Threads the FFTs may use: the CPUs this process may run on, capped by OMP_NUM_THREADS
+    where that is set (a machine's share of cores can be smaller than its CPU count)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return max(1, min(n, cap) if cap > 0 else n)
+
+
+def fft(x, axis=-1):
+    """Forward DFT X[k] = sum_n x[n] e^{-j 2 pi k n / N} along `axis` (unnormalised)."""
+    return scipy.fft.fft(x, axis=axis, workers=workers())
+
+
+def ifft(x, axis=-1):
+    """Inverse DFT x[n] = (1/N) sum_k X[k] e^{+j 2 pi k n / N} along `axis`."""
+    return scipy.fft.ifft(x, axis=axis, workers=workers())
 
 
 # ----------------------------------------------------------------------------------------------
@@ -84,14 +109,14 @@ def matched_filter(params) -> np.ndarray:
     if rep.size > Nr:
         raise ValueError("replica longer than the range line")
     h[:rep.size] = rep
-    return np.conj(np.fft.fft(h))
+    return np.conj(fft(h))
 
 
 def range_compress(echo: np.ndarray, params) -> np.ndarray:
     """rc[m] = IFFT(FFT(echo[m]) * H) for every line m (circular correlation with the replica)."""
     H = matched_filter(params)
     x = np.asarray(echo, dtype=np.complex128)
-    return np.fft.ifft(np.fft.fft(x, axis=1) * H[None, :], axis=1)
+    return ifft(fft(x, axis=1) * H[None, :], axis=1)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -108,7 +133,7 @@ def corner_turn(x: np.ndarray) -> np.ndarray:
 
 def azimuth_fft(rc: np.ndarray) -> np.ndarray:
     """S[k][n] = sum_m rc[m][n] e^{-j 2 pi k m / Na}: forward DFT down every range bin."""
-    return np.fft.fft(rc, axis=0)
+    return fft(rc, axis=0)
 
 
 def doppler_freqs(params) -> np.ndarray:
@@ -129,13 +154,15 @@ def bin_range(params, n) -> np.ndarray:
     return _p(params, "range_bin0_m") + np.asarray(n, dtype=np.float64) * range_spacing(params)
 
 
-def rcmc_shift(params, n) -> np.ndarray:
-    """Delta[k][i] = R(n_i) (1/D_k - 1) / dr  (samples), for range bins n.
+def rcmc_shift(params, n, k=None) -> np.ndarray:
+    """Delta[k][i] = R(n_i) (1/D_k - 1) / dr  (samples), for range bins n and Doppler bins k
+    (all of them by default).
 
     A target at closest range R0 appears at range R0 / D_k in Doppler bin k, so output bin n
     reads the input at x = n + Delta.  Evaluated as R u / (D (1 + D)) / dr, which equals
     R (1/D - 1) / dr without the cancellation of 1/D - 1 near D = 1."""
     D = migration_factor(params)
+    D = D if k is None else D[np.asarray(k)]
     u = 1.0 - D * D
     q = u / (D * (1.0 + D))
     return bin_range(params, n)[None, :] * q[:, None] / range_spacing(params)
@@ -184,20 +211,22 @@ def rcmc(S: np.ndarray, shift: np.ndarray, taps: int = 8, beta: float = 2.5,
     return acc / wsum
 
 
-def azimuth_matched_filter(params, n) -> np.ndarray:
-    """Haz[k][i] = exp(+j 4 pi R(n_i) D_k / lambda).
+def azimuth_matched_filter(params, n, k=None) -> np.ndarray:
+    """Haz[k][i] = exp(+j 4 pi R(n_i) D_k / lambda) for range bins n and Doppler bins k (all of
+    them by default).
 
     After RCMC a target at R0 carries the range-Doppler phase exp(-j 4 pi R0 D_k / lambda)
     (stationary phase of the hyperbolic history); the filter removes it.  Phase-only,
     range-dependent, unwindowed."""
     D = migration_factor(params)
+    D = D if k is None else D[np.asarray(k)]
     phase = 4.0 * np.pi * bin_range(params, n)[None, :] * D[:, None] / wavelength(params)
     return np.exp(1j * phase)
 
 
 def azimuth_ifft(Z: np.ndarray) -> np.ndarray:
     """img[m][n] = (1/Na) sum_k Z[k][n] e^{+j 2 pi k m / Na}."""
-    return np.fft.ifft(Z, axis=0)
+    return ifft(Z, axis=0)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -229,11 +258,12 @@ def azimuth_focus(rc: np.ndarray, params) -> np.ndarray:
     return azimuth_ifft(R * azimuth_matched_filter(params, n))
 
 
-def focus_columns(echo: np.ndarray, params, out_bins, block_rows: int = 1024):
+def focus_columns(echo: np.ndarray, params, out_bins, block_rows: int = 1024, stages: bool = False):
     """Image columns img[:, out_bins] from the same definitions, for scenes too large to focus
     whole.  Range compression runs line by line and keeps only the range bins that the RCMC of
     the requested outputs reads; azimuth FFT, RCMC, filter and IFFT then run on those columns.
-    Returns (columns [Na][len(bins)], bins) with bins = sorted unique out_bins."""
+    Returns (columns [Na][len(bins)], bins) with bins = sorted unique out_bins; with stages,
+    (dict of the rc, azfft, rcmc and img columns at those bins, bins) instead."""
     Na, Nr = _p(params, "Na"), _p(params, "Nr")
     taps = _p(params, "rcmc_taps")
     out_bins = np.asarray(sorted(set(int(b) for b in out_bins)))
@@ -249,7 +279,11 @@ def focus_columns(echo: np.ndarray, params, out_bins, block_rows: int = 1024):
         rc_cols[m0:m0 + block_rows] = blk[:, in_bins]
     S = azimuth_fft(rc_cols)
     R = rcmc(S, shift, taps, _p(params, "kaiser_beta"), out_bins=out_bins, in_bins=in_bins, Nr=Nr)
-    return azimuth_ifft(R * azimuth_matched_filter(params, out_bins)), out_bins
+    img = azimuth_ifft(R * azimuth_matched_filter(params, out_bins))
+    if not stages:
+        return img, out_bins
+    at = np.searchsorted(in_bins, out_bins)     # every output bin is among the input bins
+    return {"rc": rc_cols[:, at], "azfft": S[:, at], "rcmc": R, "img": img}, out_bins
 
 
 # ----------------------------------------------------------------------------------------------
@@ -374,7 +408,7 @@ def omega_k_stages(echo: np.ndarray, params, ref_bin: int) -> dict:
     img   : inverse 2-D DFT (1/(Na Nr))"""
     Nr = _p(params, "Nr")
     x = np.asarray(echo, dtype=np.complex128)
-    spec = np.fft.fft(np.fft.fft(x, axis=1), axis=0)
+    spec = fft(fft(x, axis=1), axis=0)
     rfm = spec * matched_filter(params)[None, :] * reference_function(params, ref_bin)
     centred = np.fft.fftshift(rfm, axes=1)
     T = rcmc(centred, stolt_shift(params), _p(params, "rcmc_taps"), _p(params, "kaiser_beta"))
@@ -382,7 +416,7 @@ def omega_k_stages(echo: np.ndarray, params, ref_bin: int) -> dict:
     shift_m = float(bin_range(params, ref_bin)) - _p(params, "range_bin0_m")
     T = T * np.exp(-2j * np.pi * fp * (2.0 * shift_m / C_LIGHT))[None, :]
     stolt = np.fft.ifftshift(T, axes=1)
-    img = np.fft.ifft(np.fft.ifft(stolt, axis=1), axis=0)
+    img = ifft(ifft(stolt, axis=1), axis=0)
     return {"spec": spec, "rfm": rfm, "stolt": stolt, "img": img}
 
 

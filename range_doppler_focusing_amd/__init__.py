@@ -10,7 +10,7 @@ from __future__ import annotations
 from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
                       make_bp_grid, make_params, rd_azimuth_focus, rd_azimuth_focus_f16,
                       rd_backproject, rd_bp_grid, rd_corner_turn, rd_debug_azimuth_stages,
-                      rd_debug_line_fft, rd_focus, rd_focus_f16, rd_last_error, rd_length_supported,
+                      rd_debug_line_fft, rd_debug_rcmc, rd_focus, rd_focus_f16, rd_last_error, rd_length_supported,
                       rd_omega_k, rd_omega_k_f16, rd_params, rd_plan_create, rd_plan_destroy,
                       rd_range_compress, rd_range_compress_f16, rd_status_string)
 
@@ -84,6 +84,14 @@ class Plan:
         img = self._empty((self.Na, self.Nr))
         rd_debug_azimuth_stages(self.handle, rc, az, rcmc, img)
         return az, rcmc, img
+
+    def rcmc_stage(self, x, filter: bool = True, out=None):
+        """The chain's row stage alone on x [Na][Nr] with row k = Doppler bin k (FFT order): RCMC,
+        and the azimuth filter with 1/Na if `filter` (rd_debug_rcmc); out may be x (in place)."""
+        self._check(x, (self.Na, self.Nr))
+        out = self._empty((self.Na, self.Nr)) if out is None else self._check(out, (self.Na, self.Nr))
+        rd_debug_rcmc(self.handle, x, out, int(filter))
+        return out
 
     def _half_pair(self, x, out):
         import torch

@@ -1,9 +1,13 @@
 """ctypes declarations of the C ABI in include/rdfocus.h (argument marshalling only).
 
 Every function here has the name of the C entry point it calls.  Device buffers are passed as
-torch tensors (complex64, contiguous, on the plan's device) or raw integer addresses; the stream
-defaults to torch's current stream on the tensor's device.  There is no CPU fallback: if the
-library is missing, loading fails with an error.
+torch tensors or raw integer addresses.  A tensor is checked before its address is taken: it must
+be contiguous, on the GPU the call runs on (the plan's device), complex64 (float16 [..., 2] for
+binary16 storage) and hold at least the samples the call reads or writes (Na * Nr for a plan
+created here); a failed check raises ValueError and nothing reaches the library.  Integer
+addresses are the explicit unchecked path.  The stream defaults to torch's current stream on the
+tensor's device.  There is no CPU fallback: if the library is missing, loading fails with an
+error.
 """
 from __future__ import annotations
 
@@ -26,7 +30,8 @@ RD_WINDOW_HAMMING = 1
 # every symbol the header declares
 EXPORTS = ("rd_length_supported", "rd_plan_create", "rd_plan_destroy", "rd_range_compress",
            "rd_range_compress_f16",
-           "rd_azimuth_focus", "rd_focus", "rd_focus_f16", "rd_azimuth_focus_f16", "rd_debug_azimuth_stages", "rd_debug_line_fft",
+           "rd_azimuth_focus", "rd_focus", "rd_focus_f16", "rd_azimuth_focus_f16", "rd_debug_azimuth_stages",
+           "rd_debug_rcmc", "rd_debug_line_fft",
            "rd_backproject", "rd_corner_turn", "rd_omega_k", "rd_omega_k_f16", "rd_status_string", "rd_last_error")
 
 
@@ -98,6 +103,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rd_omega_k_f16.restype = ctypes.c_int
     lib.rd_debug_azimuth_stages.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.rd_debug_azimuth_stages.restype = ctypes.c_int
+    lib.rd_debug_rcmc.argtypes = [vp, vp, vp, i32, vp]
+    lib.rd_debug_rcmc.restype = ctypes.c_int
     lib.rd_debug_line_fft.argtypes = [vp, i32, i32, vp, vp, i64, vp]
     lib.rd_debug_line_fft.restype = ctypes.c_int
     lib.rd_backproject.argtypes = [vp, vp, vp, ctypes.POINTER(rd_bp_grid), vp]
@@ -122,27 +129,64 @@ def _check(status: int, func: str) -> int:
     return status
 
 
-def _addr(x) -> int:
-    """Device address of a tensor (complex64, contiguous) or an integer address."""
-    if x is None:
-        return 0
-    if isinstance(x, int):
-        return x
-    if not x.is_contiguous():
-        raise ValueError("tensor must be contiguous")
-    return x.data_ptr()
+# Live plans created through this module: handle -> (Na, Nr, device index), so that tensor
+# arguments can be checked against the sizes and the device the C call will use.
+_plans: dict = {}
 
 
-def _addr_half(x) -> int:
-    """Device address of a binary16 tensor [..., 2] (real, imaginary last) or an integer address."""
-    if x is None:
-        return 0
-    if isinstance(x, int):
-        return x
+def _plan_geom(plan):
+    """(Na, Nr, device index) of a plan created here, or None (then sizes are not checked)."""
+    return _plans.get(plan) if isinstance(plan, int) else None
+
+
+def _tensor_addr(x, name: str, half: bool, elems, device) -> int:
+    """Device address of tensor x after checking it: a contiguous tensor on the GPU (on `device`
+    when given), complex64 -- or, with half, float16 with a last dimension of 2 (real,
+    imaginary) -- holding at least `elems` complex samples when given."""
     import torch
-    if x.dtype != torch.float16 or x.shape[-1] != 2 or not x.is_contiguous():
-        raise ValueError("binary16 data must be a contiguous float16 tensor with a last dimension of 2")
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor or an integer device address")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got one on {x.device})")
+    if device is not None and x.device.index != device:
+        raise ValueError(f"{name} is on cuda:{x.device.index} but the call runs on cuda:{device}")
+    if half:
+        if x.dtype != torch.float16 or x.dim() == 0 or x.shape[-1] != 2:
+            raise ValueError(f"{name}: binary16 data must be a float16 tensor with a last dimension of 2")
+    elif x.dtype != torch.complex64:
+        raise ValueError(f"{name} must be complex64 (got {x.dtype})")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = x.numel() // 2 if half else x.numel()
+    if elems is not None and have < elems:
+        raise ValueError(f"{name} holds {have} complex samples; the call needs {elems}")
     return x.data_ptr()
+
+
+def _addr(x, name: str = "buffer", elems=None, device=None) -> int:
+    """Device address of a complex64 tensor (checked: GPU, device, contiguity, at least `elems`
+    samples) or an integer address (passed through unchecked)."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return _tensor_addr(x, name, False, elems, device)
+
+
+def _addr_half(x, name: str = "buffer", elems=None, device=None) -> int:
+    """Device address of a binary16 tensor [..., 2] (real, imaginary last; checked like _addr) or
+    an integer address (unchecked)."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return _tensor_addr(x, name, True, elems, device)
+
+
+def _image_args(plan):
+    """(elems, device) for a [Na][Nr] buffer of `plan` (None, None for an unknown plan)."""
+    g = _plan_geom(plan)
+    return (None, None) if g is None else (g[0] * g[1], g[2])
 
 
 def _stream(stream, *tensors) -> int:
@@ -176,57 +220,88 @@ def rd_plan_create(params: rd_params | dict) -> int:
         params = make_params(**params)
     h = ctypes.c_void_p()
     _check(load_library().rd_plan_create(ctypes.byref(params), ctypes.byref(h)), "rd_plan_create")
+    import torch
+    _plans[h.value] = (int(params.Na), int(params.Nr), torch.cuda.current_device())
     return h.value
 
 
 def rd_plan_destroy(plan: int) -> None:
-    _check(load_library().rd_plan_destroy(plan), "rd_plan_destroy")
+    try:
+        _check(load_library().rd_plan_destroy(plan), "rd_plan_destroy")
+    finally:
+        _plans.pop(plan, None)
 
 
 def rd_range_compress(plan: int, echo, rc, stream=None) -> None:
-    _check(load_library().rd_range_compress(plan, _addr(echo), _addr(rc), _stream(stream, echo, rc)),
+    n, d = _image_args(plan)
+    _check(load_library().rd_range_compress(plan, _addr(echo, "echo", n, d), _addr(rc, "rc", n, d),
+                                            _stream(stream, echo, rc)),
            "rd_range_compress")
 
 
 def rd_range_compress_f16(plan: int, echo, rc, stream=None) -> None:
-    _check(load_library().rd_range_compress_f16(plan, _addr_half(echo), _addr_half(rc), _stream(stream, echo, rc)),
+    n, d = _image_args(plan)
+    _check(load_library().rd_range_compress_f16(plan, _addr_half(echo, "echo", n, d), _addr_half(rc, "rc", n, d),
+                                                _stream(stream, echo, rc)),
            "rd_range_compress_f16")
 
 
 def rd_azimuth_focus(plan: int, rc, img, stream=None) -> None:
-    _check(load_library().rd_azimuth_focus(plan, _addr(rc), _addr(img), _stream(stream, rc, img)),
+    n, d = _image_args(plan)
+    _check(load_library().rd_azimuth_focus(plan, _addr(rc, "rc", n, d), _addr(img, "img", n, d),
+                                           _stream(stream, rc, img)),
            "rd_azimuth_focus")
 
 
 def rd_focus(plan: int, echo, img, stream=None) -> None:
-    _check(load_library().rd_focus(plan, _addr(echo), _addr(img), _stream(stream, echo, img)),
+    n, d = _image_args(plan)
+    _check(load_library().rd_focus(plan, _addr(echo, "echo", n, d), _addr(img, "img", n, d),
+                                   _stream(stream, echo, img)),
            "rd_focus")
 
 
 def rd_focus_f16(plan: int, echo, img, stream=None) -> None:
-    _check(load_library().rd_focus_f16(plan, _addr_half(echo), _addr_half(img), _stream(stream, echo, img)),
+    n, d = _image_args(plan)
+    _check(load_library().rd_focus_f16(plan, _addr_half(echo, "echo", n, d), _addr_half(img, "img", n, d),
+                                       _stream(stream, echo, img)),
            "rd_focus_f16")
 
 
 def rd_azimuth_focus_f16(plan: int, rc, img, stream=None) -> None:
-    _check(load_library().rd_azimuth_focus_f16(plan, _addr_half(rc), _addr_half(img), _stream(stream, rc, img)),
+    n, d = _image_args(plan)
+    _check(load_library().rd_azimuth_focus_f16(plan, _addr_half(rc, "rc", n, d), _addr_half(img, "img", n, d),
+                                               _stream(stream, rc, img)),
            "rd_azimuth_focus_f16")
 
 
 def rd_omega_k_f16(plan: int, echo, img, ref_bin: int, stream=None) -> None:
-    _check(load_library().rd_omega_k_f16(plan, _addr_half(echo), _addr_half(img), int(ref_bin),
+    n, d = _image_args(plan)
+    _check(load_library().rd_omega_k_f16(plan, _addr_half(echo, "echo", n, d), _addr_half(img, "img", n, d),
+                                         int(ref_bin),
                                          _stream(stream, echo, img)), "rd_omega_k_f16")
 
 
 def rd_debug_azimuth_stages(plan: int, rc, azfft, rcmc, img, stream=None) -> None:
-    _check(load_library().rd_debug_azimuth_stages(plan, _addr(rc), _addr(azfft), _addr(rcmc),
-                                                  _addr(img), _stream(stream, rc, img)),
+    n, d = _image_args(plan)
+    _check(load_library().rd_debug_azimuth_stages(plan, _addr(rc, "rc", n, d), _addr(azfft, "azfft", n, d),
+                                                  _addr(rcmc, "rcmc", n, d), _addr(img, "img", n, d),
+                                                  _stream(stream, rc, img)),
            "rd_debug_azimuth_stages")
 
 
+def rd_debug_rcmc(plan: int, x, y, filter: int, stream=None) -> None:
+    n, d = _image_args(plan)
+    _check(load_library().rd_debug_rcmc(plan, _addr(x, "in", n, d), _addr(y, "out", n, d), int(filter),
+                                        _stream(stream, x, y)),
+           "rd_debug_rcmc")
+
+
 def rd_debug_line_fft(plan: int, axis: int, inverse: int, x, y, lines: int, stream=None) -> None:
-    _check(load_library().rd_debug_line_fft(plan, int(axis), int(inverse), _addr(x), _addr(y),
-                                            int(lines), _stream(stream, x, y)),
+    g = _plan_geom(plan)
+    n = None if g is None or int(axis) not in (0, 1) or int(lines) < 0 else int(lines) * g[int(axis)]
+    d = None if g is None else g[2]
+    _check(load_library().rd_debug_line_fft(plan, int(axis), int(inverse), _addr(x, "in", n, d),
+                                            _addr(y, "out", n, d), int(lines), _stream(stream, x, y)),
            "rd_debug_line_fft")
 
 
@@ -242,18 +317,27 @@ def make_bp_grid(**kw) -> rd_bp_grid:
 def rd_backproject(plan: int, rc, img, grid, stream=None) -> None:
     if isinstance(grid, dict):
         grid = make_bp_grid(**grid)
-    _check(load_library().rd_backproject(plan, _addr(rc), _addr(img), ctypes.byref(grid) if grid is not None else None,
+    n, d = _image_args(plan)
+    npx = None if grid is None or grid.nx < 0 or grid.ny < 0 else int(grid.nx) * int(grid.ny)
+    _check(load_library().rd_backproject(plan, _addr(rc, "rc", n, d), _addr(img, "img", npx, d),
+                                         ctypes.byref(grid) if grid is not None else None,
                                          _stream(stream, rc, img)),
            "rd_backproject")
 
 
 def rd_omega_k(plan: int, echo, img, ref_bin: int, stream=None) -> None:
-    _check(load_library().rd_omega_k(plan, _addr(echo), _addr(img), int(ref_bin), _stream(stream, echo, img)),
+    n, d = _image_args(plan)
+    _check(load_library().rd_omega_k(plan, _addr(echo, "echo", n, d), _addr(img, "img", n, d), int(ref_bin),
+                                     _stream(stream, echo, img)),
            "rd_omega_k")
 
 
 def rd_corner_turn(x, y, rows: int, cols: int, stream=None) -> None:
-    _check(load_library().rd_corner_turn(_addr(x), _addr(y), int(rows), int(cols), _stream(stream, x, y)),
+    n = int(rows) * int(cols) if int(rows) >= 0 and int(cols) >= 0 else None
+    import torch
+    d = torch.cuda.current_device() if not isinstance(x, int) or not isinstance(y, int) else None
+    _check(load_library().rd_corner_turn(_addr(x, "in", n, d), _addr(y, "out", n, d), int(rows), int(cols),
+                                         _stream(stream, x, y)),
            "rd_corner_turn")
 
 

@@ -459,15 +459,20 @@ rd_status az_inverse(rd_plan* P, void* io, bool half, hipStream_t s) {
   return run_col(P, io, io, false, true, half, s);
 }
 
+// The row stage with the constants c (rows in c's Doppler order); in place allowed
+rd_status run_rows_c(rd_plan* P, const void* src, void* dst, const rdf::AzRowConst& c, bool half, hipStream_t s) {
+  if (P->pad_m)
+    return check_hip(rdf::launch_rcmc_mf_any(src, dst, c, P->p.Na, P->p.Nr, P->cached, half, s), "RCMC launch");
+  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, P->cached, half, s), "RCMC launch");
+}
+
 // RCMC and (filter) the azimuth filter per Doppler row; half: binary16 rows, whose forward
 // transform already carries 1 / Na
 rd_status run_rows(rd_plan* P, const void* src, void* dst, bool filter, bool half, hipStream_t s) {
   rdf::AzRowConst c = P->az;
   c.filter = filter ? 1 : 0;
   if (half) c.inv_na = 1.0f;
-  if (P->pad_m)
-    return check_hip(rdf::launch_rcmc_mf_any(src, dst, c, P->p.Na, P->p.Nr, P->cached, half, s), "RCMC launch");
-  return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, P->cached, half, s), "RCMC launch");
+  return run_rows_c(P, src, dst, c, half, s);
 }
 
 rd_status check_rcmc_margin(const rd_plan* P) {
@@ -884,6 +889,21 @@ rd_status rd_debug_azimuth_stages(rd_plan* plan, const rd_c64* rc, rd_c64* azfft
     return st;
   if ((st = run_rows(plan, I, I, true, false, s)) != RD_OK) return st;
   return az_inverse(plan, I, false, s);
+}
+
+rd_status rd_debug_rcmc(rd_plan* plan, const rd_c64* in, rd_c64* out, int32_t filter, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if ((st = check_rcmc_margin(plan)) != RD_OK) return st;
+  if (!aligned8(in) || !aligned8(out)) return fail(RD_ERR_INVALID_ARG, "in and out must be non-NULL and 8-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
+  if (partial_overlap(in, out, bytes)) return fail(RD_ERR_INVALID_ARG, "in and out overlap without being equal");
+  rdf::AzRowConst c = plan->az;
+  c.filter = filter ? 1 : 0;
+  c.A = 1;  // row k holds Doppler bin k
+  c.B = plan->p.Na;
+  return run_rows_c(plan, in, out, c, false, static_cast<hipStream_t>(stream));
 }
 
 rd_status rd_debug_line_fft(rd_plan* plan, int32_t axis, int32_t inverse, const rd_c64* in,

@@ -489,23 +489,26 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
 // samples after it, zero outside the row) is staged in LDS, so every tap is a plain LDS read.
 // Rows up to 4096 samples are one chunk, staged between zero margins written once; longer rows
 // split into 4096-sample chunks, which keeps the staging buffer small enough for several
-// workgroups per CU.  Shift and filter phase are formed in float64 (the phase reaches ~1e7 rad)
-// and reduced before they are taken to float32.  HALF: binary16 rows (4 bytes a sample) in and
-// out, float32 arithmetic.
+// workgroups per CU.  The chunks of one row are processed in order by one thread group, which
+// makes the stage safe in place (out == in): a chunk's window reads only samples at or after
+// its own start from memory (nothing this group has stored yet, and no other group touches the
+// row), and the 3 samples before it come from the previous chunk's staged input in LDS.  Shift
+// and filter phase are formed in float64 (the phase reaches ~1e7 rad) and reduced before they
+// are taken to float32.  HALF: binary16 rows (4 bytes a sample) in and out, float32 arithmetic.
 template <int N>
 struct RowStage {
   static constexpr int CH = (N > 4096 && N % 4096 == 0) ? 4096 : N;  // outputs per chunk
   static constexpr int CHUNKS = N / CH;
-  static constexpr int T = CHUNKS == 1 ? LineCfg<N>::T : 256;          // threads per chunk
-  static constexpr int LPW = CHUNKS == 1 ? LineCfg<N>::LPW : 1;        // chunks per workgroup
+  static constexpr int T = CHUNKS == 1 ? LineCfg<N>::T : 256;          // threads per row
+  static constexpr int LPW = CHUNKS == 1 ? LineCfg<N>::LPW : 1;        // rows per workgroup
   static constexpr int WG = T * LPW;
   static constexpr int MARGIN = N / 8;       // staged samples after a chunk (shift + 5 <= MARGIN)
   static constexpr int LEN = 3 + CH + MARGIN;
   static constexpr int P = LineCfg<N>::P;    // registers per thread for a chunk
 };
-// Rows of any length (given at run time): 512-sample chunks (two per workgroup) with up to 1024
-// staged samples after each; the row's buffer resource reads zero past its end and drops stores
-// there.
+// Rows of any length (given at run time): 512-sample chunks with up to 1024 staged samples after
+// each, two rows per workgroup; the row's buffer resource reads zero past its end and drops
+// stores there.
 template <>
 struct RowStage<0> {
   static constexpr int CH = 512;
@@ -556,6 +559,65 @@ struct RowIO<true> {
   }
 };
 
+// The outputs of one staged chunk (starting at row sample n0) into v: thread tid computes chunk
+// positions j + r NB (the layout of the chunk's loads and stores).
+template <int CH, int T, int R0>
+__device__ __forceinline__ void rcmc_chunk(float2* v, const float2* my, const AzRowConst& c, int n0,
+                                           double alpha, double beta, double gamma, double delta, int tid) {
+  using G = Geom<CH, T, R0>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+      // filter phasor exp(j 2 pi (gamma + n delta)) for n = n0 + j + r NB: exact at r = 0
+      // (phase reduced in float64), then advanced by the exact step rotation
+      float2 z = make_float2(1.f, 0.f), rot = make_float2(1.f, 0.f);
+      if (c.filter) {
+        const double c0 = gamma + double(n0 + j) * delta;
+        const double c1 = double(G::NB) * delta;
+        float sn, cs;
+        sincospif(2.0f * float(c0 - rint(c0)), &sn, &cs);
+        z = make_float2(cs * c.inv_na, sn * c.inv_na);
+        sincospif(2.0f * float(c1 - rint(c1)), &sn, &cs);
+        rot = make_float2(cs, sn);
+      }
+#pragma unroll
+      for (int r = 0; r < R0; ++r) {
+        const int m = j + r * G::NB;  // position in the chunk
+        const double x = alpha + double(n0 + m) * beta;
+        const double fl = floor(x);
+        const float xf = float(x - fl) - 0.5f;
+        const float y = xf * xf;
+        const float2* tap = my + (m + int(fl));  // tap t reads sample n0 + m + fl + t - 3
+        float2 acc = make_float2(0.f, 0.f);
+        float es = 0.f;  // sum of the even parts: the weights sum to 2 es
+#pragma unroll
+        for (int q = 0; q < kRcmcTaps / 2; ++q) {
+          float e = c.w.even[q][kRcmcDeg / 2];
+#pragma unroll
+          for (int mm = kRcmcDeg / 2 - 1; mm >= 0; --mm) e = fmaf(e, y, c.w.even[q][mm]);
+          float o = c.w.odd[q][kRcmcDeg / 2 - 1];
+#pragma unroll
+          for (int mm = kRcmcDeg / 2 - 2; mm >= 0; --mm) o = fmaf(o, y, c.w.odd[q][mm]);
+          const float wa = fmaf(xf, o, e);    // tap j = -q   (t = 3 - q)
+          const float wb = fmaf(-xf, o, e);   // tap j = 1 + q (t = 4 + q)
+          const float2 sa = tap[3 - q], sb = tap[4 + q];
+          acc.x = fmaf(wa, sa.x, fmaf(wb, sb.x, acc.x));
+          acc.y = fmaf(wa, sa.y, fmaf(wb, sb.y, acc.y));
+          es += e;
+        }
+        const float sc = 0.5f * __builtin_amdgcn_rcpf(es);
+        float2 o = make_float2(acc.x * sc, acc.y * sc);
+        if (c.filter) {
+          o = cmul(o, z);
+          z = cmul(z, rot);
+        }
+        v[b * R0 + r] = o;
+      }
+    }
+  }
+}
+
 template <int N, int AUX, bool HALF = false>
 __global__ void __launch_bounds__(RowStage<N>::WG)
     k_rcmc_mf(const void* in, void* out, AzRowConst c, int64_t rows, int n_rt) {
@@ -574,104 +636,70 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * RS::LEN;
   for (int i = threadIdx.x; i < RS::LPW * RS::LEN; i += RS::WG) lds[i] = make_float2(0.f, 0.f);
-  const int64_t items = rows * chunks;
-  for (int64_t i0 = int64_t(blockIdx.x) * RS::LPW; i0 < items; i0 += int64_t(gridDim.x) * RS::LPW) {
-    const int64_t item = i0 + grp;
-    const int64_t it = item < items ? item : items - 1;
-    const int64_t row = it / chunks;
-    const int n0 = int(it % chunks) * CH;
+  // one row per thread group: rows [r0, r0 + LPW) per workgroup pass
+  for (int64_t r0 = int64_t(blockIdx.x) * RS::LPW; r0 < rows; r0 += int64_t(gridDim.x) * RS::LPW) {
+    const bool live_row = r0 + grp < rows;
+    const int64_t row = live_row ? r0 + grp : rows - 1;
     const int k = int(row / c.B) + c.A * int(row % c.B);
     const double alpha = c.row[4 * k], beta = c.row[4 * k + 1];
     const double gamma = c.row[4 * k + 2], delta = c.row[4 * k + 3];
     float2 v[RS::P];
-    // one chunk per group: rows [i0, i0 + LPW) when a row is one chunk, else the item's row
-    const typename RIO::IO src = RS::CHUNKS == 1 ? RIO::make(in, N, i0, RS::LPW, rows)
-                                                 : RIO::make(in, nl, item < items ? row : rows, 1, rows);
-    const int e0 = RS::CHUNKS == 1 ? grp * N : n0;
-    RIO::template load<CH, T, R0, AUX>(v, src, e0, tid);
-    float2 pre = make_float2(0.f, 0.f);
-    int hs = -1;  // this thread's first halo slot, if any
-    if constexpr (RS::CHUNKS != 1) {
-      // the 3 samples before the chunk and c.halo after it (zero outside the row); the first
-      // pass of them is loaded with the chunk, before the barrier
-      const int i = tid;
-      if (i < 3 + c.halo) {
-        const int sidx = i < 3 ? n0 - 3 + i : n0 + CH + (i - 3);
-        hs = i < 3 ? i : 3 + CH + (i - 3);
-        if (sidx >= 0 && sidx < nl) pre = RIO::template one<AUX>(src, sidx);
-      }
-    }
-    __syncthreads();  // the previous chunk's taps have been read
+    if constexpr (RS::CHUNKS == 1) {
+      // the whole row is the chunk; the zero margins around it are never written
+      RIO::template load<CH, T, R0, AUX>(v, RIO::make(in, N, r0, RS::LPW, rows), grp * N, tid);
+      __syncthreads();  // the previous row's taps have been read
 #pragma unroll
-    for (int b = 0; b < G::B; ++b) {
-      const int j = tid + b * T;
-      if (G::live(j)) {
+      for (int b = 0; b < G::B; ++b) {
+        const int j = tid + b * T;
+        if (G::live(j)) {
 #pragma unroll
-        for (int r = 0; r < R0; ++r) my[3 + j + r * G::NB] = v[b * R0 + r];
-      }
-    }
-    if constexpr (RS::CHUNKS != 1) {
-      if (hs >= 0) my[hs] = pre;
-      for (int i = tid + T; i < 3 + c.halo; i += T) {  // halos longer than one pass
-        const int sidx = n0 + CH + (i - 3);
-        my[3 + CH + (i - 3)] = sidx < nl ? RIO::template one<AUX>(src, sidx) : make_float2(0.f, 0.f);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < G::B; ++b) {
-      const int j = tid + b * T;
-      if (G::live(j)) {
-        // filter phasor exp(j 2 pi (gamma + n delta)) for n = n0 + j + r NB: exact at r = 0
-        // (phase reduced in float64), then advanced by the exact step rotation
-        float2 z = make_float2(1.f, 0.f), rot = make_float2(1.f, 0.f);
-        if (c.filter) {
-          const double c0 = gamma + double(n0 + j) * delta;
-          const double c1 = double(G::NB) * delta;
-          float sn, cs;
-          sincospif(2.0f * float(c0 - rint(c0)), &sn, &cs);
-          z = make_float2(cs * c.inv_na, sn * c.inv_na);
-          sincospif(2.0f * float(c1 - rint(c1)), &sn, &cs);
-          rot = make_float2(cs, sn);
-        }
-#pragma unroll
-        for (int r = 0; r < R0; ++r) {
-          const int m = j + r * G::NB;  // position in the chunk
-          const double x = alpha + double(n0 + m) * beta;
-          const double fl = floor(x);
-          const float xf = float(x - fl) - 0.5f;
-          const float y = xf * xf;
-          const float2* tap = my + (m + int(fl));  // tap t reads sample n0 + m + fl + t - 3
-          float2 acc = make_float2(0.f, 0.f);
-          float es = 0.f;  // sum of the even parts: the weights sum to 2 es
-#pragma unroll
-          for (int q = 0; q < kRcmcTaps / 2; ++q) {
-            float e = c.w.even[q][kRcmcDeg / 2];
-#pragma unroll
-            for (int mm = kRcmcDeg / 2 - 1; mm >= 0; --mm) e = fmaf(e, y, c.w.even[q][mm]);
-            float o = c.w.odd[q][kRcmcDeg / 2 - 1];
-#pragma unroll
-            for (int mm = kRcmcDeg / 2 - 2; mm >= 0; --mm) o = fmaf(o, y, c.w.odd[q][mm]);
-            const float wa = fmaf(xf, o, e);    // tap j = -q   (t = 3 - q)
-            const float wb = fmaf(-xf, o, e);   // tap j = 1 + q (t = 4 + q)
-            const float2 sa = tap[3 - q], sb = tap[4 + q];
-            acc.x = fmaf(wa, sa.x, fmaf(wb, sb.x, acc.x));
-            acc.y = fmaf(wa, sa.y, fmaf(wb, sb.y, acc.y));
-            es += e;
-          }
-          const float sc = 0.5f * __builtin_amdgcn_rcpf(es);
-          float2 o = make_float2(acc.x * sc, acc.y * sc);
-          if (c.filter) {
-            o = cmul(o, z);
-            z = cmul(z, rot);
-          }
-          v[b * R0 + r] = o;
+          for (int r = 0; r < R0; ++r) my[3 + j + r * G::NB] = v[b * R0 + r];
         }
       }
+      __syncthreads();
+      rcmc_chunk<CH, T, R0>(v, my, c, 0, alpha, beta, gamma, delta, tid);
+      RIO::template store<CH, T, R0, AUX>(v, RIO::make(out, N, r0, RS::LPW, rows), grp * N, tid);
+    } else {
+      // rows past the end: an empty resource (loads read zero, stores are dropped)
+      const typename RIO::IO src = RIO::make(in, nl, live_row ? row : rows, 1, rows);
+      const typename RIO::IO dst = RIO::make(out, nl, live_row ? row : rows, 1, rows);
+      for (int ch = 0; ch < chunks; ++ch) {
+        const int n0 = ch * CH;
+        RIO::template load<CH, T, R0, AUX>(v, src, n0, tid);
+        // Window edges: slots 0..2 hold the 3 samples before the chunk -- zero before the row,
+        // else the previous chunk's last 3 input samples, still staged at my[CH..CH+2] (read
+        // before the barrier below, after which the slots are overwritten); slots after the
+        // chunk hold the first `halo` samples that follow it (zero past the row), the first
+        // pass of them loaded with the chunk.
+        float2 pre = make_float2(0.f, 0.f);
+        int hs = -1;  // this thread's window slot, if any
+        if (tid < 3) {
+          hs = tid;
+          if (ch > 0) pre = my[CH + tid];
+        } else if (tid < 3 + c.halo) {
+          const int sidx = n0 + CH + (tid - 3);
+          hs = CH + tid;
+          if (sidx < nl) pre = RIO::template one<AUX>(src, sidx);
+        }
+        __syncthreads();  // the previous chunk's taps and edge samples have been read
+#pragma unroll
+        for (int b = 0; b < G::B; ++b) {
+          const int j = tid + b * T;
+          if (G::live(j)) {
+#pragma unroll
+            for (int r = 0; r < R0; ++r) my[3 + j + r * G::NB] = v[b * R0 + r];
+          }
+        }
+        if (hs >= 0) my[hs] = pre;
+        for (int i = tid + T; i < 3 + c.halo; i += T) {  // halos longer than one pass
+          const int sidx = n0 + CH + (i - 3);
+          my[CH + i] = sidx < nl ? RIO::template one<AUX>(src, sidx) : make_float2(0.f, 0.f);
+        }
+        __syncthreads();
+        rcmc_chunk<CH, T, R0>(v, my, c, n0, alpha, beta, gamma, delta, tid);
+        RIO::template store<CH, T, R0, AUX>(v, dst, n0, tid);
+      }
     }
-    const typename RIO::IO dst = RS::CHUNKS == 1 ? RIO::make(out, N, i0, RS::LPW, rows)
-                                                 : RIO::make(out, nl, item < items ? row : rows, 1, rows);
-    RIO::template store<CH, T, R0, AUX>(v, dst, e0, tid);
   }
 }
 
@@ -1214,7 +1242,7 @@ hipError_t occupancy_pf(int* rc, int pad) {
 template <int N>
 hipError_t launch_rcmc_mf(const void* in, void* out, const AzRowConst& c, int64_t rows, int grid,
                           int cached, int half, hipStream_t s) {
-  const int64_t wgs = (rows * RowStage<N>::CHUNKS + RowStage<N>::LPW - 1) / RowStage<N>::LPW;
+  const int64_t wgs = (rows + RowStage<N>::LPW - 1) / RowStage<N>::LPW;  // one row per thread group
   if (grid <= 0 || grid > wgs) grid = int(wgs);
   const dim3 g(grid), b(RowStage<N>::WG);
   if (half && cached)
@@ -1261,8 +1289,7 @@ hipError_t launch_rcmc_mf_any(const void* in, void* out, const AzRowConst& c, in
                               int cached, int half, hipStream_t s) {
   using RS = RowStage<0>;
   if (n <= 0 || c.halo < 0 || c.halo > RS::MARGIN) return hipErrorInvalidValue;
-  const int64_t items = rows * ((n + RS::CH - 1) / RS::CH);
-  const int64_t wgs = (items + RS::LPW - 1) / RS::LPW;
+  const int64_t wgs = (rows + RS::LPW - 1) / RS::LPW;  // one row per thread group
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   const int grid = int(wgs);
   if (half && cached)

@@ -74,8 +74,8 @@ struct LineOps {
   // natural-order filter H[n] and roots e^{-j 2 pi k / n} (a permutation, no arithmetic).
   int (*rc_tab_len)();
   void (*rc_tab_fill)(const float2* H, const float2* roots, float2* out);
-  // RCMC + azimuth filter over rows of this length (in == out allowed; grid 0 = one workgroup
-  // per staged chunk); margin = samples staged after a chunk, so the largest shift the kernel
+  // RCMC + azimuth filter over rows of this length (in == out allowed; grid 0 = one row per
+  // thread group, the row's chunks in order); margin = samples staged after a chunk, so the largest shift the kernel
   // accepts is margin - 5
   // (half: binary16 rows, 4 bytes a sample, float32 arithmetic)
   hipError_t (*rcmc_mf)(const void* in, void* out, const AzRowConst& c, int64_t rows, int grid,

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     import range_doppler_focusing_amd as rdf
     lib = rdf.load_library()
     declared = header_functions()
-    assert len(declared) == 17
+    assert len(declared) == 18
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(rdf.EXPORTS) == declared
@@ -138,6 +138,29 @@ def test_bp_grid_layout_matches_c():
         got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
     assert got[0] == ctypes.sizeof(rd_bp_grid)
     assert got[1:] == [getattr(rd_bp_grid, f).offset for f in fields]
+
+
+def test_binding_checks_tensors_before_the_call():
+    """The Python entry points check a tensor argument before taking its address: a host tensor
+    raises ValueError and anything else that is neither a tensor nor an integer address raises
+    TypeError, so nothing reaches the library (the plan handle here is not even a plan).  The
+    dtype, contiguity and size checks are exercised on the GPU."""
+    import torch
+
+    import range_doppler_focusing_amd as rdf
+    x = torch.zeros((4, 256), dtype=torch.complex64)
+    h = torch.zeros((4, 256, 2), dtype=torch.float16)
+    for call in (lambda: rdf.rd_range_compress(1, x, x), lambda: rdf.rd_focus(1, x, x),
+                 lambda: rdf.rd_azimuth_focus(1, x, x), lambda: rdf.rd_omega_k(1, x, x, 0),
+                 lambda: rdf.rd_debug_rcmc(1, x, x, 1), lambda: rdf.rd_debug_line_fft(1, 1, 0, x, x, 4),
+                 lambda: rdf.rd_debug_azimuth_stages(1, x, x, x, x),
+                 lambda: rdf.rd_backproject(1, x, x, dict(nx=2, ny=2, x0_m=0.0, dx_m=1.0, r0_m=1e3, dr_m=1.0)),
+                 lambda: rdf.rd_range_compress_f16(1, h, h), lambda: rdf.rd_focus_f16(1, h, h),
+                 lambda: rdf.rd_azimuth_focus_f16(1, h, h), lambda: rdf.rd_omega_k_f16(1, h, h, 0)):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call()
+    with pytest.raises(TypeError):
+        rdf.rd_range_compress(1, [0.0], 1 << 20)
 
 
 def test_backproject_rejects_a_null_plan_before_any_launch():

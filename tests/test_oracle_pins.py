@@ -199,6 +199,42 @@ def test_rcmc_weights_symmetric_at_half_sample():
     np.testing.assert_allclose(O.kaiser_sinc(0.3 - j, 8, 0.0), np.sinc(0.3 - j), atol=1e-15)
 
 
+def _kaiser_window_error(kernel, beta):
+    """Largest deviation of kernel(t, 8, beta) / sinc(t) from NumPy's M-point Kaiser window
+    (an independent implementation of I0(beta sqrt(1 - (2n/(M-1) - 1)^2)) / I0(beta)) on the
+    grid t = 4 (2n/(M-1) - 1), M = 81, integer t (where sinc vanishes) left out."""
+    M = 81
+    n = np.arange(M)
+    t = 4.0 * (2.0 * n / (M - 1) - 1.0)
+    keep = np.abs(t - np.round(t)) > 1e-9
+    return np.max(np.abs(kernel(t[keep], 8, beta) / np.sinc(t[keep]) - np.kaiser(M, beta)[keep]))
+
+
+@pytest.mark.parametrize("beta", [0.0, 2.5, 8.0])
+def test_rcmc_window_is_the_library_kaiser_window(beta):
+    """The interpolator's window over its 8-tap span is the Kaiser window (the 4096 x 4096
+    airborne scene interpolates its RCMC with an 8-tap Kaiser-windowed sinc), pinned to
+    numpy.kaiser rather than to its own formula."""
+    assert _kaiser_window_error(O.kaiser_sinc, beta) < 1e-12
+
+
+def test_rcmc_window_pin_rejects_plausible_misreadings():
+    """Planted mistakes in the window formula -- the square root dropped, or a half-width of 3.5
+    taps instead of 4 -- fail the pin above (each by far more than its tolerance)."""
+    from scipy.special import i0
+
+    def no_sqrt(t, taps, beta):
+        return np.sinc(t) * i0(beta * np.clip(1.0 - (t / (taps / 2.0)) ** 2, 0.0, None)) / i0(beta)
+
+    def half_width_35(t, taps, beta):
+        arg = np.clip(1.0 - (t / 3.5) ** 2, 0.0, None)
+        return np.sinc(t) * i0(beta * np.sqrt(arg)) / i0(beta)
+
+    for beta in (2.5, 8.0):
+        assert _kaiser_window_error(no_sqrt, beta) > 1e-2
+        assert _kaiser_window_error(half_width_35, beta) > 1e-2
+
+
 def test_rcmc_shift_matches_simulated_range_doppler_migration(big):
     """In Doppler bin k the compressed echo of a target at bin n_t peaks at n_t + Delta(n_t, k);
     the simulator's independent hyperbolic forward model puts it there."""
@@ -285,6 +321,48 @@ def test_sampled_columns_equal_whole_image(c3az):
     cols, got_bins = O.focus_columns(sc.echo, C3_AZ.plan_params(), bins, block_rows=700)
     assert list(got_bins) == sorted(bins)
     np.testing.assert_allclose(cols, st["img"][:, got_bins], atol=1e-12 * np.abs(st["img"]).max())
+
+
+def test_sampled_column_stages_equal_whole_chain_stages(c3az):
+    """focus_columns(stages=True) returns the whole chain's rc, azimuth spectrum, RCMC output and
+    image at the sampled range bins (the sampled C5 parity test compares each stage there)."""
+    sc, st = c3az
+    bins = [0, 1, 2, 255, 256, 300, 508, 509, 510, 511]
+    got, got_bins = O.focus_columns(sc.echo, C3_AZ.plan_params(), bins, block_rows=1000, stages=True)
+    assert list(got_bins) == bins
+    for name in ("rc", "azfft", "rcmc", "img"):
+        ref = st[name][:, bins]
+        np.testing.assert_allclose(got[name], ref, atol=1e-12 * np.abs(ref).max(), err_msg=name)
+
+
+def test_shift_and_filter_at_selected_doppler_bins_are_the_rows_of_the_whole():
+    p = C3_AZ.plan_params()
+    n = np.arange(0, C3_AZ.Nr, 7)
+    k = [0, 5, C3_AZ.Na // 2, C3_AZ.Na - 1]
+    np.testing.assert_array_equal(O.rcmc_shift(p, n, k), O.rcmc_shift(p, n)[k])
+    np.testing.assert_array_equal(O.azimuth_matched_filter(p, n, k), O.azimuth_matched_filter(p, n)[k])
+
+
+def test_line_errors_find_a_defect_that_the_whole_array_norm_dilutes():
+    """A 5e-4 relative error confined to one column of a 4096 x 4096-like array passes a 1e-5
+    bar on the whole-array norm but shows at full size in the column error; uniform rounding
+    noise gives line errors of the order of the global error."""
+    rng = np.random.default_rng(9)
+    ref = rng.standard_normal((1024, 1024)) + 1j * rng.standard_normal((1024, 1024))
+    bad = ref.copy()
+    bad[:, 77] *= 1 + 5e-4
+    assert M.rel_l2(bad, ref) < 1e-5 * 2
+    worst_row, worst_col = M.worst_line_errors(bad, ref)
+    assert abs(worst_col - 5e-4) < 2e-5 and worst_row < 1e-4   # a row holds one bad sample of 1024
+    noisy = ref * (1 + 1e-7 * rng.standard_normal(ref.shape))
+    g = M.rel_l2(noisy, ref)
+    assert max(M.worst_line_errors(noisy, ref)) < 2 * g
+    # a line with almost no energy is measured against an average line, not its own norm
+    quiet = ref.copy()
+    quiet[5] *= 1e-9
+    q2 = quiet.copy()
+    q2[5] += 1e-9
+    assert M.worst_line_errors(q2, quiet)[0] < 1e-8
 
 
 def test_azimuth_half_composes_with_range_compression_to_the_chain(c3az):
