@@ -177,6 +177,20 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
  * refuse the plan (range migration beyond the RCMC margin). */
 rd_status rd_focus_f16(rd_plan* plan, const rd_c32h* echo, rd_c32h* img, void* stream);
 
+/* rd_focus for callers that cannot allocate device memory while they run (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same result as rd_focus,
+ * bit for bit, with the same arguments and errors, and no allocation of any kind (no hipMalloc,
+ * hipFree or allocating library routine).  The one scratch buffer of the chain -- the [M][Nr]
+ * float32 workspace of the Bluestein azimuth form (azimuth lengths that are neither a power of
+ * two nor 25 * 2^k) -- is the library's static device scratch of 64 MiB instead of the plan's
+ * workspace, so plans with M * Nr * 8 > 64 MiB return RD_ERR_INVALID_ARG; other plans use no
+ * scratch.  Every GPU holds one such scratch for the life of the process, shared by every call
+ * on that GPU: calls of rd_focus_noalloc that overlap on one GPU (different streams, or host
+ * threads) race on it and must be serialised by the caller.  Nothing in it needs to start at
+ * zero (each call writes every workspace sample before reading it); it keeps the last call's
+ * contents. */
+rd_status rd_focus_noalloc(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream);
+
 /* The azimuth half of rd_focus_f16 (cf-1.com/news/2323550 §7): range-compressed data rc
  * [Na][Nr] rd_c32h to img [Na][Nr] rd_c32h, img = (rd_azimuth_focus's image of the same rc) / Na,
  * with the same binary16 storage and scaling of every intermediate.  rd_focus_f16 equals

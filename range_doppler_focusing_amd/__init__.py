@@ -10,7 +10,7 @@ from __future__ import annotations
 from ._native import (EXPORTS, RD_WINDOW_HAMMING, RD_WINDOW_RECT, RdError, load_library,  # noqa: F401
                       make_bp_grid, make_params, rd_azimuth_focus, rd_azimuth_focus_f16,
                       rd_backproject, rd_bp_grid, rd_corner_turn, rd_debug_azimuth_stages,
-                      rd_debug_line_fft, rd_debug_rcmc, rd_focus, rd_focus_f16, rd_last_error, rd_length_supported,
+                      rd_debug_line_fft, rd_debug_rcmc, rd_focus, rd_focus_f16, rd_focus_noalloc, rd_last_error, rd_length_supported,
                       rd_omega_k, rd_omega_k_f16, rd_params, rd_plan_create, rd_plan_destroy,
                       rd_range_compress, rd_range_compress_f16, rd_status_string)
 

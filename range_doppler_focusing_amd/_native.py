@@ -30,7 +30,7 @@ RD_WINDOW_HAMMING = 1
 # every symbol the header declares
 EXPORTS = ("rd_length_supported", "rd_plan_create", "rd_plan_destroy", "rd_range_compress",
            "rd_range_compress_f16",
-           "rd_azimuth_focus", "rd_focus", "rd_focus_f16", "rd_azimuth_focus_f16", "rd_debug_azimuth_stages",
+           "rd_azimuth_focus", "rd_focus", "rd_focus_noalloc", "rd_focus_f16", "rd_azimuth_focus_f16", "rd_debug_azimuth_stages",
            "rd_debug_rcmc", "rd_debug_line_fft",
            "rd_backproject", "rd_corner_turn", "rd_omega_k", "rd_omega_k_f16", "rd_status_string", "rd_last_error")
 
@@ -89,7 +89,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.rd_plan_create.restype = ctypes.c_int
     lib.rd_plan_destroy.argtypes = [vp]
     lib.rd_plan_destroy.restype = ctypes.c_int
-    for name in ("rd_range_compress", "rd_azimuth_focus", "rd_focus"):
+    for name in ("rd_range_compress", "rd_azimuth_focus", "rd_focus", "rd_focus_noalloc"):
         f = getattr(lib, name)
         f.argtypes = [vp, vp, vp, vp]
         f.restype = ctypes.c_int
@@ -258,6 +258,13 @@ def rd_focus(plan: int, echo, img, stream=None) -> None:
     _check(load_library().rd_focus(plan, _addr(echo, "echo", n, d), _addr(img, "img", n, d),
                                    _stream(stream, echo, img)),
            "rd_focus")
+
+
+def rd_focus_noalloc(plan: int, echo, img, stream=None) -> None:
+    n, d = _image_args(plan)
+    _check(load_library().rd_focus_noalloc(plan, _addr(echo, "echo", n, d), _addr(img, "img", n, d),
+                                           _stream(stream, echo, img)),
+           "rd_focus_noalloc")
 
 
 def rd_focus_f16(plan: int, echo, img, stream=None) -> None:

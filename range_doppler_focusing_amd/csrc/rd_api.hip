@@ -423,10 +423,9 @@ rd_status run_col(rd_plan* P, const void* src, void* dst, bool forward, bool str
 // X[k] = c[k] sum_m (x[m] c[m]) conj(c[k - m]) with c[n] = exp(sign j pi n^2 / Na), the sum a
 // linear convolution done as a length-M circular one (M >= 2 Na - 1) by the column steps.
 // half: src and dst in binary16 (the workspace stays float32) and the result scaled by 1 / Na.
-rd_status run_bluestein(rd_plan* P, const void* src, void* dst, int sign, bool half, hipStream_t s) {
+rd_status run_bluestein(rd_plan* P, const void* src, void* dst, int sign, bool half, float2* W, hipStream_t s) {
   const int Na = P->p.Na, M = P->bs_m;
   const int64_t Nr = P->p.Nr;
-  float2* W = P->bs_ws;
   const int h = half ? 1 : 0;
   rd_status st;
   if ((st = check_hip(rdf::launch_chirp_rows(src, W, Nr, Na, M, Na, sign, h, 0, 1.0f, s), "chirp launch")) != RD_OK)
@@ -442,9 +441,9 @@ rd_status run_bluestein(rd_plan* P, const void* src, void* dst, int sign, bool h
 }
 
 // The azimuth transform: src [Na][Nr] (pulses) -> dst, row r holding Doppler bin r / B + A (r % B)
-// (half: binary16 storage, transform scaled by 1 / Na)
-rd_status az_forward(rd_plan* P, const void* src, void* dst, bool half, hipStream_t s) {
-  if (P->bs_m) return run_bluestein(P, src, dst, -1, half, s);
+// (half: binary16 storage, transform scaled by 1 / Na; ws: the Bluestein form's [M][Nr] workspace)
+rd_status az_forward(rd_plan* P, const void* src, void* dst, bool half, hipStream_t s, float2* ws = nullptr) {
+  if (P->bs_m) return run_bluestein(P, src, dst, -1, half, ws ? ws : P->bs_ws, s);
   rd_status st;
   if ((st = run_col(P, src, dst, true, true, half, s)) != RD_OK) return st;
   return run_col(P, dst, dst, true, false, half, s);
@@ -452,8 +451,8 @@ rd_status az_forward(rd_plan* P, const void* src, void* dst, bool half, hipStrea
 
 // Its inverse, in place, back to pulse order: unnormalised (1/Na is folded into the row stage),
 // or with binary16 storage scaled by 1 / Na like the forward transform
-rd_status az_inverse(rd_plan* P, void* io, bool half, hipStream_t s) {
-  if (P->bs_m) return run_bluestein(P, io, io, +1, half, s);
+rd_status az_inverse(rd_plan* P, void* io, bool half, hipStream_t s, float2* ws = nullptr) {
+  if (P->bs_m) return run_bluestein(P, io, io, +1, half, ws ? ws : P->bs_ws, s);
   rd_status st;
   if ((st = run_col(P, io, io, false, false, half, s)) != RD_OK) return st;
   return run_col(P, io, io, false, true, half, s);
@@ -483,12 +482,12 @@ rd_status check_rcmc_margin(const rd_plan* P) {
   return RD_OK;
 }
 
-rd_status run_azimuth(rd_plan* P, const void* rc, void* img, bool half, hipStream_t s) {
+rd_status run_azimuth(rd_plan* P, const void* rc, void* img, bool half, hipStream_t s, float2* ws = nullptr) {
   // rc is read only by the first step, so img may alias it
   rd_status st;
-  if ((st = az_forward(P, rc, img, half, s)) != RD_OK) return st;
+  if ((st = az_forward(P, rc, img, half, s, ws)) != RD_OK) return st;
   if ((st = run_rows(P, img, img, true, half, s)) != RD_OK) return st;
-  return az_inverse(P, img, half, s);
+  return az_inverse(P, img, half, s, ws);
 }
 
 // omega-k: the azimuth transform first (the 2-D transform's order is free), then one row stage
@@ -533,6 +532,37 @@ rd_status run_omega_k(rd_plan* plan, const void* echo, void* img, int32_t ref_bi
                       "omega-k row stage launch")) != RD_OK)
     return st;
   return az_inverse(plan, img, half, s);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------- static scratch
+// Workspace of rd_focus_noalloc: a file-scope device array, so that the entry point allocates
+// nothing.  Every GPU the library runs on holds its own copy (at its own address) until the
+// process ends.  Host code never uses the array's name as an address: the device address is
+// looked up once per device with hipGetSymbolAddress and passed to the kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) float2 scratch[kScratchBytes / sizeof(float2)];
+
+namespace {
+
+std::mutex g_scratch_mu;
+float2* g_scratch_ptr[64] = {};  // per device index
+
+// Device address of `scratch` on device `dev`, which must be current (looked up on the first
+// call per device).
+rd_status scratch_address(int dev, float2** out) {
+  if (dev < 0 || dev >= 64) return fail(RD_ERR_DEVICE, "device %d out of range for the static scratch", dev);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(RD_ERR_DEVICE, "hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float2*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return RD_OK;
 }
 
 }  // namespace
@@ -816,6 +846,30 @@ rd_status rd_focus(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream)
   st = run_range_compress(plan, reinterpret_cast<const float2*>(echo), I, true, s);
   if (st != RD_OK) return st;
   return run_azimuth(plan, I, I, false, s);
+}
+
+rd_status rd_focus_noalloc(rd_plan* plan, const rd_c64* echo, rd_c64* img, void* stream) {
+  rd_status st = check_call(plan);
+  if (st != RD_OK) return st;
+  if (!plan->azimuth) return fail(RD_ERR_NOT_CONFIGURED, "range-only plan");
+  if ((st = check_rcmc_margin(plan)) != RD_OK) return st;
+  if (!aligned8(echo) || !aligned8(img)) return fail(RD_ERR_INVALID_ARG, "echo and img must be non-NULL and 8-byte aligned");
+  const size_t bytes = size_t(plan->p.Na) * plan->p.Nr * sizeof(rd_c64);
+  if (partial_overlap(echo, img, bytes)) return fail(RD_ERR_INVALID_ARG, "echo and img overlap without being equal");
+  float2* ws = nullptr;
+  if (plan->bs_m) {
+    const size_t need = size_t(plan->bs_m) * size_t(plan->p.Nr) * sizeof(float2);
+    if (need > kScratchBytes)
+      return fail(RD_ERR_INVALID_ARG,
+                  "the Bluestein workspace of this plan (%zu bytes: M=%d x Nr=%d) exceeds the %zu-byte static scratch",
+                  need, plan->bs_m, plan->p.Nr, kScratchBytes);
+    if ((st = scratch_address(plan->device, &ws)) != RD_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* I = reinterpret_cast<float2*>(img);
+  st = run_range_compress(plan, reinterpret_cast<const float2*>(echo), I, true, s);
+  if (st != RD_OK) return st;
+  return run_azimuth(plan, I, I, false, s, ws);
 }
 
 rd_status rd_azimuth_focus_f16(rd_plan* plan, const rd_c32h* rc, rd_c32h* img, void* stream) {
