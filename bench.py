@@ -109,26 +109,33 @@ def time_steps(torch, fn, steps: int, warmup: int, stream):
 
 
 def cpu_oracle_rc(cfg, echo, budget_s: float = 10.0):
-    """The CPU oracle's range compression of the whole workload (NumPy fp64, one thread),
-    repeated until about `budget_s` seconds of CPU work have run; returns (median s, runs)."""
+    """The CPU oracle's range compression of the whole workload (float64; its FFTs on the
+    oracle's worker threads), repeated until about `budget_s` seconds have run, at least 3 times
+    after a warm-up; returns (median s, runs)."""
     from oracle import rd_oracle as O
     p = cfg.plan_params()
-    O.range_compress(echo[:64], p)
+    O.range_compress(echo, p)          # warm-up (FFT plans, page faults)
     ts = []
     t_start = time.perf_counter()
-    while not ts or (time.perf_counter() - t_start < budget_s and len(ts) < 200):
+    while len(ts) < 3 or (time.perf_counter() - t_start < budget_s and len(ts) < 200):
         t0 = time.perf_counter()
         O.range_compress(echo, p)
         ts.append(time.perf_counter() - t0)
     return statistics.median(ts), len(ts)
 
 
-def cpu_oracle_focus(cfg, echo):
-    """The CPU oracle's whole chain (NumPy fp64, one thread) on the whole scene, one run."""
+def cpu_oracle_focus(cfg, echo, runs: int = 3):
+    """The CPU oracle's whole chain (float64; its FFTs on the oracle's worker threads, the RCMC
+    and filter arithmetic in NumPy on one thread) on the whole scene: one warm-up run, then the
+    median of `runs`; returns (median s, runs)."""
     from oracle import rd_oracle as O
-    t0 = time.perf_counter()
     O.focus_stages(echo, cfg.plan_params())
-    return time.perf_counter() - t0
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        O.focus_stages(echo, cfg.plan_params())
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts), runs
 
 
 def gpu_noise(torch, shape, seed):
@@ -184,8 +191,10 @@ def main():
                     help="seconds of untimed running before each warm-up (0 for counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-focus", action="store_true", help="skip the full-chain measurement")
-    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp", "pad", "wk", "f16"], default=None,
-                    help="run one workload only (for profiling)")
+    ap.add_argument("--only", choices=["rc", "focus", "large", "vendor", "turn", "bp", "pad", "wk", "f16",
+                                       "rc6000", "rc16384", "focus16384"], default=None,
+                    help="run one workload only (for profiling); rc6000 / rc16384 / focus16384: one of the "
+                         "large workloads on its own")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the 8192 x 6000 and 16384 x 16384 workloads")
     args = ap.parse_args()
@@ -296,7 +305,7 @@ def main():
                 O.omega_k(cached_scene(wcfg).echo[:1024], sub.plan_params(), ref)
                 tw = time.perf_counter() - t0
                 rec["cpu_baseline"] = {"value": round(1024 * wcfg.Nr / tw / 1e6, 4), "unit": "Mpixel/s",
-                                       "cores": 1, "kind": "oracle",
+                                       "cores": O.workers(), "kind": "oracle",
                                        "sample": f"1024 pulses x {wcfg.Nr} of the same geometry, one run ({tw:.1f} s)"}
             wk.append(rec)
             note(f"omega-k {wcfg.Na} x {wcfg.Nr}: {ms * 1e3:.1f} us")
@@ -305,22 +314,30 @@ def main():
     cpu = None
     cpu_focus = None
     if not args.no_cpu and args.only is None:
-        cores = 1  # NumPy's FFT and the oracle's array code run on one thread
+        from oracle import rd_oracle as O
+        cores = O.workers()  # the oracle's FFT threads: this process's CPUs, capped by OMP_NUM_THREADS
+        note(f"oracle on {cores} worker threads (host reports {os.cpu_count()} CPUs, "
+             f"{len(os.sched_getaffinity(0))} in this process's affinity set)")
         t, runs = cpu_oracle_rc(cfg, cached_scene(cfg).echo)
         note(f"oracle range compression: {t:.2f} s per run")
         cpu = {"value": rc_bytes / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "sample": f"whole 4096x4096 range compression, median of {runs} runs "
-                         f"({t:.2f} s each, ~{t * runs:.0f} s of CPU work)"}
+               "sample": f"whole 4096x4096 range compression (float64, scipy.fft on {cores} threads), "
+                         f"warm-up then median of {runs} runs ({t:.3f} s each)"}
         if focus_ms:
-            tf = cpu_oracle_focus(fcfg, cached_scene(fcfg).echo)
+            tf, fr = cpu_oracle_focus(fcfg, cached_scene(fcfg).echo)
+            note(f"oracle rd focus: {tf:.2f} s per run")
             cpu_focus = {"value": px / tf / 1e6, "unit": "Mpixel/s", "cores": cores, "kind": "oracle",
-                         "sample": f"whole 4096x4096 rd focus, one run ({tf:.1f} s)"}
+                         "sample": f"whole 4096x4096 rd focus (float64; FFTs on {cores} threads, RCMC and "
+                                   f"filter on one), warm-up then median of {fr} runs ({tf:.2f} s each)"}
 
     # ---------------------------------------------------------------- larger workloads
     large = None
-    if (args.only in (None, "large")) and not args.no_large:
+    single = {"rc6000": (C4, "rc"), "rc16384": (C5, "rc"), "focus16384": (C5, "focus")}
+    if (args.only in (None, "large") or args.only in single) and not args.no_large:
         large = []
         for wcfg, kind, steps in ((C4, "rc", 20), (C5, "rc", 10), (C5, "focus", 5)):
+            if args.only in single and single[args.only] != (wcfg, kind):
+                continue
             x = gpu_noise(torch, (wcfg.Na, wcfg.Nr), wcfg.seed)
             y = torch.empty_like(x)
             plan = rdf.Plan(**wcfg.plan_params())
@@ -437,7 +454,7 @@ def main():
             O.range_compress(xh, pp)
             tc = time.perf_counter() - t0
             rec["cpu_baseline"] = {"value": round(2 * na * nr * 8 / tc / 1e9, 3), "unit": "GB/s",
-                                   "cores": 1, "kind": "oracle",
+                                   "cores": O.workers(), "kind": "oracle",
                                    "sample": f"all {na} lines, one run ({tc:.2f} s)"}
         large.append(rec)
         note(f"padded range compression 16384 x 1200: {ms * 1e3:.1f} us")

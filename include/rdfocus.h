@@ -70,7 +70,10 @@ typedef enum {
  * unweighted filters leave ~-13 dB sidelobes; Hamming lowers them and widens the mainlobe). */
 enum { RD_WINDOW_RECT = 0, RD_WINDOW_HAMMING = 1 };
 
-/* Problem statement.  Range: linear-FM up-chirp of duration pulse_s and bandwidth
+/* Problem statement (nxmr.cn/news/101525 §2.1: the echo float2 [Na][Nr] with Na pulses of Nr
+ * range samples, and a chirp spectrum [Nr] precomputed on the host; §2.2: the platform and
+ * slant-range geometry of RCMC; cf-1.com/news/2323550 §2.1: chirp parameters, range compression
+ * by a matched filter, azimuth processing).  Range: linear-FM up-chirp of duration pulse_s and bandwidth
  * bandwidth_hz sampled at fs_hz; the replica holds L = ceil(pulse_s * fs_hz) samples at
  * indices [0, L) of a range line, h[n] = w[n] exp(j pi (B/Tp) (n/Fs - Tp/2)^2), and
  * H = conj(FFT_Nr(h)) is built in float64 on the host and rounded to float32 once.
@@ -115,7 +118,9 @@ typedef struct rd_plan rd_plan;
 int rd_length_supported(int32_t n);
 
 /* Validates `params`, builds the matched filter H (float64 -> float32), the twiddle and
- * azimuth tables and the workspace on the current HIP device, and returns the plan in *out.
+ * azimuth tables and the workspace on the current HIP device, and returns the plan in *out
+ * (nxmr.cn/news/101525 §2.1: the chirp spectrum is computed once on the host, ahead of the
+ * per-line kernels).  The plan owns its tables; rd_plan_destroy releases them.
  * On error *out is set to NULL and nothing is leaked. */
 rd_status rd_plan_create(const rd_params* params, rd_plan** out);
 

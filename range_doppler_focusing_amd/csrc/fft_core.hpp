@@ -209,42 +209,74 @@ template <int R>
 struct DftSplit {
   static constexpr int A = 1, B = R;
 };
+template <> struct DftSplit<6> { static constexpr int A = 2, B = 3; };
 template <> struct DftSplit<8> { static constexpr int A = 2, B = 4; };
+template <> struct DftSplit<10> { static constexpr int A = 2, B = 5; };
 template <> struct DftSplit<15> { static constexpr int A = 3, B = 5; };
 template <> struct DftSplit<16> { static constexpr int A = 4, B = 4; };
 template <> struct DftSplit<20> { static constexpr int A = 4, B = 5; };
 template <> struct DftSplit<25> { static constexpr int A = 5, B = 5; };
 
-// The i-th input a length-R DFT consumes: a split DFT starts with the A inputs B n1 + 0, then
-// B n1 + 1, ...  Loading a butterfly's inputs in this order lets its first sub-DFT start as soon
-// as the first A loads have returned (memory counters complete in order).
+constexpr int gcd_i(int a, int b) { return b == 0 ? a : gcd_i(b, a % b); }
+// A split with coprime factors runs as a prime-factor (Good-Thomas) DFT: no twiddles.
+template <int R>
+constexpr bool dft_pfa() { return DftSplit<R>::A > 1 && gcd_i(DftSplit<R>::A, DftSplit<R>::B) == 1; }
+
+// The i-th input a length-R DFT consumes: a split DFT starts with the A inputs of its first
+// sub-DFT (B n1 + 0, or (B n1) mod R for a prime-factor split), then those of the second, ...
+// Loading a butterfly's inputs in this order lets its first sub-DFT start as soon as the first A
+// loads have returned (memory counters complete in order).
 template <int R>
 constexpr int dft_input_order(int i) {
-  return DftSplit<R>::A == 1 ? i : DftSplit<R>::B * (i % DftSplit<R>::A) + i / DftSplit<R>::A;
+  constexpr int A = DftSplit<R>::A, B = DftSplit<R>::B;
+  if constexpr (A == 1) return i;
+  else if constexpr (dft_pfa<R>()) return (B * (i % A) + A * (i / A)) % R;
+  else return B * (i % A) + i / A;
 }
+
+template <int A, int B, int DIR>
+__device__ __forceinline__ void dft_pfa_run(float2* v);
 
 template <int R, int DIR>
 struct Dft {
   static_assert(DftSplit<R>::A > 1, "no DFT of this length");
   static __device__ __forceinline__ void run(float2* v) {
-    dft_ct<DftSplit<R>::A, DftSplit<R>::B, DIR>(v);
+    if constexpr (dft_pfa<R>())
+      dft_pfa_run<DftSplit<R>::A, DftSplit<R>::B, DIR>(v);
+    else
+      dft_ct<DftSplit<R>::A, DftSplit<R>::B, DIR>(v);
   }
 };
 
-// Length A*B DFT in registers (one Cooley-Tukey split): input n = B n1 + n2, output
-// k = k1 + A k2; DFT_A over n1, twiddle W_{AB}^{n2 k1}, DFT_B over n2.
+// Length A*B DFT in registers with gcd(A, B) = 1 (Good-Thomas prime-factor algorithm): input
+// n = (B n1 + A n2) mod N, output k the residue with k = k1 (mod A) and k = k2 (mod B).  Then
+// W_N^{n k} = W_A^{n1 k1} W_B^{n2 k2}, so the DFT is DFT_A over n1 followed by DFT_B over n2 with
+// no twiddle multiplies between them; both index maps are compile-time register renamings.
+template <int A, int B>
+struct PfaMap {
+  int in[A * B];   // in[n1 + A n2] = (B n1 + A n2) mod N
+  int out[A * B];  // out[k1 + A k2] = the k in [0, N) with k = k1 (mod A), k = k2 (mod B)
+  constexpr PfaMap() : in(), out() {
+    for (int n2 = 0; n2 < B; ++n2)
+      for (int n1 = 0; n1 < A; ++n1) in[n1 + A * n2] = (B * n1 + A * n2) % (A * B);
+    for (int k = 0; k < A * B; ++k) out[(k % A) + A * (k % B)] = k;
+  }
+};
+template <int A, int B>
+inline constexpr PfaMap<A, B> kPfaMap{};
+
 template <int A, int B, int DIR>
-__device__ __forceinline__ void dft_ct(float2* v) {
+__device__ __forceinline__ void dft_pfa_run(float2* v) {
   constexpr int N = A * B;
   float2 t[N];
 #pragma unroll
   for (int n2 = 0; n2 < B; ++n2) {
     float2 u[A];
 #pragma unroll
-    for (int n1 = 0; n1 < A; ++n1) u[n1] = v[B * n1 + n2];
+    for (int n1 = 0; n1 < A; ++n1) u[n1] = v[kPfaMap<A, B>.in[n1 + A * n2]];
     Dft<A, DIR>::run(u);
 #pragma unroll
-    for (int k1 = 0; k1 < A; ++k1) t[k1 * B + n2] = rot_const<N, DIR>(u[k1], n2 * k1);
+    for (int k1 = 0; k1 < A; ++k1) t[k1 * B + n2] = u[k1];
   }
 #pragma unroll
   for (int k1 = 0; k1 < A; ++k1) {
@@ -253,7 +285,7 @@ __device__ __forceinline__ void dft_ct(float2* v) {
     for (int n2 = 0; n2 < B; ++n2) u[n2] = t[k1 * B + n2];
     Dft<B, DIR>::run(u);
 #pragma unroll
-    for (int k2 = 0; k2 < B; ++k2) v[k1 + A * k2] = u[k2];
+    for (int k2 = 0; k2 < B; ++k2) v[kPfaMap<A, B>.out[k1 + A * k2]] = u[k2];
   }
 }
 
@@ -418,9 +450,19 @@ template <int N, int NS>
 struct XPad {
   static constexpr int P = 1, Q = 16;
 };
+template <> struct XPad<512, 8> { static constexpr int P = 0, Q = 512; };
 template <> struct XPad<1024, 16> { static constexpr int P = 0, Q = 1024; };
 template <> struct XPad<2048, 16> { static constexpr int P = 0, Q = 2048; };
 template <> struct XPad<4096, 16> { static constexpr int P = 0, Q = 4096; };
+template <> struct XPad<8192, 8> { static constexpr int P = 0, Q = 8192; };
+template <> struct XPad<8192, 32> { static constexpr int P = 0, Q = 8192; };
+template <> struct XPad<8192, 256> { static constexpr int P = 0, Q = 8192; };
+// 6000 = 10 * 6 * 10 * 10: periods that divide the exchange strides, so every access stays a
+// per-thread base plus a constant (model: 670 instead of 2707 conflict cycles a line and direction;
+// measured 45.4 M cycles per 8192-line launch with one pad per 16, as the model predicts)
+template <> struct XPad<6000, 1> { static constexpr int P = 1, Q = 200; };
+template <> struct XPad<6000, 10> { static constexpr int P = 2, Q = 300; };
+template <> struct XPad<6000, 60> { static constexpr int P = 4, Q = 600; };
 
 template <int N, int NS>
 __device__ __forceinline__ int xpad(int i) {
@@ -989,8 +1031,9 @@ struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
 
 // ---------------------------------------------------------------------------- line configurations
 // T threads per line (16 points per thread in radix-16 passes), LPW lines per workgroup.  The
-// radix lists are palindromes, so the inverse transform (the list reversed) runs the same passes
-// as the forward one and one twiddle cache serves both.  PF: the range-compression kernel holds
+// forward and inverse transforms run the same list of passes (a list that starts and ends with
+// the same radix: the forward transform's output layout is then the inverse transform's input
+// layout), so one twiddle cache serves both.  PF: the range-compression kernel holds
 // a prefetched second line in registers.  HREG: the filter H is held in registers for the
 // kernel's lifetime (else read from the cached global table per line, all of a thread's filter
 // loads issued together).  TWB: twiddle sets up to TWB bytes live in LDS.  WPE: waves per SIMD
@@ -1000,7 +1043,11 @@ struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
 // multiply.  The long lines (8192, 16384: 512 / 1024 threads, at most 128 registers) need TWD
 // to fit a prefetch; measured on MI355X, prefetch + TWD + LATE is 5-7% faster there than no
 // prefetch.  At 4096, TWD would allow 4 waves per SIMD but its extra multiplies cancel the gain
-// (measured equal), so the full register sets stay.
+// (measured equal), so the full register sets stay.  6000 = 10 * 6 * 10 * 10 on 600 threads (at
+// most 12 points a thread) with the prefetch after the filter multiply and the filter read per
+// line: 142 registers and no spills, against 255 for 20 * 15 * 20 on 400 threads with the filter
+// in registers (measured on MI355X, 8192 lines: 301 against 335 us; the radix-20 butterflies
+// alone need ~80 registers, and every 128-register form of either list spills).
 template <int N>
 struct LineCfg;
 
@@ -1047,7 +1094,8 @@ using L_16_8_16 = IntList<16, 8, 16>;
 using L_16_16_16 = IntList<16, 16, 16>;
 using L_8_4_8_4_8 = IntList<8, 4, 8, 4, 8>;
 using L_8_16_16_8 = IntList<8, 16, 16, 8>;
-using L_20_15_20 = IntList<20, 15, 20>;
+using L_20_15_20 = IntList<20, 15, 20>;  // the earlier 6000-point list (RD_CFG6000 selects it)
+using L_10_6_10_10 = IntList<10, 6, 10, 10>;
 
 RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, 1, false, false)
@@ -1056,7 +1104,12 @@ RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 3, false, false)
 RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, true, false, 8192, 4, true, true)
 RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, true, false, 16384, 1, true, true)
-RDF_LINE_CFG(6000, 400, L_20_15_20, L_20_15_20, true, true, 4096, 1, false, false)
+#ifndef RD_CFG6000
+#define RD_CFG6000 600, L_10_6_10_10, L_10_6_10_10, true, false, 8192, 2, false, true
+#endif
+#define RDF_LINE_CFG_X(...) RDF_LINE_CFG(__VA_ARGS__)
+RDF_LINE_CFG_X(6000, RD_CFG6000)
+#undef RDF_LINE_CFG_X
 
 #undef RDF_LINE_CFG
 

@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
 }
 
 // ------------------------------------------------------------------------------------------
-// Range compression of 4096-sample lines with three barriers per line.  With n = t + 256 n2
+// Range compression of 4096-sample lines with two barriers per line.  With n = t + 256 n2
 // (t = n0 + 16 n1 < 256) and k = k0 + 16 k1 + 256 k2, the forward transform runs in the
 // decimation-in-frequency order
 //   a: DFT16 over n2 -> k0, times W_4096^{t k0}            (thread t = n0 + 16 n1)
@@ -234,7 +234,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
 // decimation-in-time order (c, b, a with conjugate roots, the twiddles before the DFTs), ending
 // with y[t + 256 n2] in thread t.  Steps b -> c and their mirror exchange data only inside a
 // group of 16 lanes (one wave), so they need no workgroup barrier; a -> b and its mirror are
-// workgroup exchanges.  Both directions use the same twiddles: W_4096^{t k0} in registers and
+// workgroup exchanges, one barrier each (two per line).  Both directions use the same twiddles: W_4096^{t k0} in registers and
 // W_256^{n0 k1} in an LDS table.  LDS layout: region g = 0..15 of 272 elements (rows of 256 or
 // 16 x 17, padded so that two 16-lane groups of a half-wave fall on complementary banks):
 // every exchange is free of bank conflicts under the gfx950 geometry (8-byte reads: 32 lanes
@@ -290,7 +290,9 @@ __global__ void __launch_bounds__(256, 3)
     Dft<16, -1>::run(v);
 #pragma unroll
     for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
-    __syncthreads();  // the previous line's last exchange has been read
+    // No barrier before these writes: thread t writes element t of every region, exactly the
+    // elements it alone read in the previous line's last exchange (its LDS accesses execute in
+    // order), and every other access to them lies on the far side of the barriers below.
 #pragma unroll
     for (int k = 0; k < 16; ++k) lds[REG * k + t] = v[k];
     __syncthreads();
@@ -813,6 +815,12 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     constexpr bool TIGHT = N <= 512 || N == 6000 || N >= 16384;
     int rot = c.ref;
     if constexpr (TIGHT) asm volatile("" : "+s"(rot));
+    // At 16384 (1024 threads: at most 128 registers) the per-sample loops below use a copy of
+    // the thread index hidden from the compiler once per row, so the values derived from it
+    // (bin indices in float64, filter addresses) are formed in the row loop rather than hoisted
+    // into registers that then spill.
+    int tid_s = tid;
+    if constexpr (N >= 16384) asm volatile("" : "+v"(tid_s));
     const typename RIO::IO io_in = RIO::make(in, N, l0, C::LPW, rows);
     load_line_rot<N, T, R0, AUX, HALF>(v, io_in, grp * N, tid, rot);
     PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
@@ -820,7 +828,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     // a = f0 + js df, Q = sqrt(a^2 - b^2) (float64: the phase reaches ~1e4 turns)
 #pragma unroll
     for (int bb = 0; bb < G::B; ++bb) {
-      const int j = tid + bb * T;
+      const int j = tid_s + bb * T;
       if (G::live(j)) {
 #pragma unroll
         for (int r = 0; r < R0; ++r) {
@@ -834,6 +842,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
           const float2 h = H[kx];
           const float2 z = make_float2((h.x * cs - h.y * sn) * c.inv_na, (h.x * sn + h.y * cs) * c.inv_na);
           v[bb * R0 + r] = cmul(v[bb * R0 + r], z);
+          if constexpr (TIGHT) group_fence();  // one sample's float64 temporaries at a time
         }
       }
     }
@@ -841,7 +850,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     // staging: my[3 + u] = spectrum at centred position u = (kx + N/2) mod N, zero around it
 #pragma unroll
     for (int bb = 0; bb < G::B; ++bb) {
-      const int j = tid + bb * T;
+      const int j = tid_s + bb * T;
       if (G::live(j)) {
 #pragma unroll
         for (int r = 0; r < R0; ++r) {
@@ -858,7 +867,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
     // x = u + (sqrt(a'^2 + b^2) - a') / df, a' = f0 + (u - N/2) df; x >= u and x <= N - 1 + halo - 5
 #pragma unroll
     for (int bb = 0; bb < G::B; ++bb) {
-      const int j = tid + bb * T;
+      const int j = tid_s + bb * T;
       if (G::live(j)) {
 #pragma unroll
         for (int r = 0; r < R0; ++r) {
@@ -889,6 +898,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
           }
           const float sc = 0.5f * __builtin_amdgcn_rcpf(es);
           v[bb * R0 + r] = make_float2(acc.x * sc, acc.y * sc);
+          if constexpr (TIGHT) group_fence();
         }
       }
     }
