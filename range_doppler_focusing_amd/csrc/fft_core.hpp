@@ -427,13 +427,14 @@ template <class L>
 struct ListInfo;
 template <int R>
 struct ListInfo<IntList<R>> {
-  static constexpr int first = R, last = R, product = R;
+  static constexpr int first = R, last = R, product = R, count = 1;
 };
 template <int R, int R2, int... Rs>
 struct ListInfo<IntList<R, R2, Rs...>> {
   static constexpr int first = R;
   static constexpr int last = ListInfo<IntList<R2, Rs...>>::last;
   static constexpr int product = R * ListInfo<IntList<R2, Rs...>>::product;
+  static constexpr int count = 1 + ListInfo<IntList<R2, Rs...>>::count;
 };
 
 // Exchange layout in LDS.  Measured on gfx950 (SQ_LDS_BANK_CONFLICT on single-pattern
@@ -1005,10 +1006,20 @@ struct TwCache<N, T, NS, IntList<R, R2, Rs...>> : TwCacheBase<N, T, NS, R> {
 template <int N, int T, int DIR, int NS, class L, bool WAVE = false>
 struct PassesCached;
 
+// run2: the double-buffered form.  Consecutive exchanges alternate between two line buffers a and
+// b, so an exchange's writes cannot meet the previous exchange's reads (those complete before the
+// barrier of the exchange in between) and need no barrier before them: one barrier per exchange
+// instead of two.  A caller chaining transforms continues with the buffer the last exchange did
+// not use (see LdsDouble).
 template <int N, int T, int DIR, int NS, int R, bool WAVE>
 struct PassesCached<N, T, DIR, NS, IntList<R>, WAVE> {
   static __device__ __forceinline__ void run(float2* v, float2* lds,
                                              const TwCache<N, T, NS, IntList<R>>& c, int tid) {
+    c.template apply<DIR>(v, tid);
+    butterflies<N, T, R, DIR>(v, tid);
+  }
+  static __device__ __forceinline__ void run2(float2* v, float2*, float2*,
+                                              const TwCache<N, T, NS, IntList<R>>& c, int tid) {
     c.template apply<DIR>(v, tid);
     butterflies<N, T, R, DIR>(v, tid);
   }
@@ -1027,6 +1038,30 @@ struct PassesCached<N, T, DIR, NS, IntList<R, R2, Rs...>, WAVE> {
     load_lds<N, T, R2, NS>(v, lds, tid);
     PassesCached<N, T, DIR, NS * R, IntList<R2, Rs...>, WAVE>::run(v, lds, c.next, tid);
   }
+  static __device__ __forceinline__ void run2(float2* v, float2* a, float2* b,
+                                              const TwCache<N, T, NS, IntList<R, R2, Rs...>>& c,
+                                              int tid) {
+    c.template apply<DIR>(v, tid);
+    butterflies<N, T, R, DIR>(v, tid);
+    store_lds<N, T, R, NS>(v, a, tid);
+    exchange_sync<WAVE>();
+    load_lds<N, T, R2, NS>(v, a, tid);
+    PassesCached<N, T, DIR, NS * R, IntList<R2, Rs...>, WAVE>::run2(v, b, a, c.next, tid);
+  }
+};
+
+// Range compression of a length whose kernel fits only one workgroup per CU may hold two line
+// buffers in LDS and run its exchanges double-buffered (PassesCached::run2).  A transform of
+// `count` passes makes count - 1 exchanges; starting with buffer a, its last exchange used a when
+// that number is odd, so the next transform starts with b (and, the inverse making as many
+// exchanges, the following line's forward transform starts with a again).
+template <int N>
+struct LdsDouble {
+  static constexpr bool value = false;
+};
+template <>
+struct LdsDouble<6000> {
+  static constexpr bool value = true;
 };
 
 // ---------------------------------------------------------------------------- line configurations

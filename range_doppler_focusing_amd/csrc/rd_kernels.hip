@@ -180,10 +180,14 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   constexpr int T = C::T;
   using TC = TwCache<N, T, 1, L>;
   constexpr bool LATE = PF && PfLate<N>::value && !C::HREG;
-  __shared__ float2 lds[C::LPW * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
+  constexpr bool DB = LdsDouble<N>::value;          // two line buffers, one barrier per exchange
+  constexpr int LBUF = C::LDS * (DB ? 2 : 1);
+  constexpr bool SWAP = DB && (ListInfo<L>::count - 1) % 2 == 1;  // inverse starts on buffer b
+  __shared__ float2 lds[C::LPW * LBUF + (TC::LDS > 0 ? TC::LDS : 1)];
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
-  float2* my = lds + grp * C::LDS;
+  float2* my = lds + grp * LBUF;
+  float2* my2 = my + (DB ? C::LDS : 0);
   const int64_t stride = int64_t(gridDim.x) * C::LPW;
   // The first line's loads go out before the table loads, so the line's HBM latency overlaps
   // the table reads instead of following them.
@@ -191,10 +195,10 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   if constexpr (PF)
     rc_load<N, PAD, HALF>(nxt, in, int64_t(blockIdx.x) * C::LPW, lines, grp, tid, n_line, skip);
   TC twc;
-  twc.load_all(tw, lds + C::LPW * C::LDS, tid, threadIdx.x, C::WG);
+  twc.load_all(tw, lds + C::LPW * LBUF, tid, threadIdx.x, C::WG);
   // (the first pass's barrier orders the LDS twiddle table before its first use, unless a line's
-  // exchanges are wave-local: then an explicit barrier does)
-  if constexpr (C::WAVE && TC::LDS > 0) __syncthreads();
+  // exchanges are wave-local or double-buffered: then an explicit barrier does)
+  if constexpr ((C::WAVE || DB) && TC::LDS > 0) __syncthreads();
   float2 h[C::HREG ? filter_regs<N>() : 1];
   if constexpr (C::HREG) load_filter<N>(h, H, tid);
   // Wait for the filter and twiddle registers before the line loop (see touch): a wait for them
@@ -211,10 +215,16 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
     } else {
       rc_load<N, PAD, HALF>(v, in, l0, lines, grp, tid, n_line, skip);
     }
-    PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
+    if constexpr (DB)
+      PassesCached<N, T, -1, 1, L, C::WAVE>::run2(v, my, my2, twc, tid);
+    else
+      PassesCached<N, T, -1, 1, L, C::WAVE>::run(v, my, twc, tid);
     filter_multiply<N>(v, h, opaque(H), tid);
     if constexpr (LATE) rc_load<N, PAD, HALF>(nxt, in, l0 + stride, lines, grp, tid, n_line, skip);
-    PassesCached<N, T, +1, 1, L, C::WAVE>::run(v, my, twc, tid);
+    if constexpr (DB)
+      PassesCached<N, T, +1, 1, L, C::WAVE>::run2(v, SWAP ? my2 : my, SWAP ? my : my2, twc, tid);
+    else
+      PassesCached<N, T, +1, 1, L, C::WAVE>::run(v, my, twc, tid);
     rc_store<N, PAD, HALF, SAUX>(v, out, l0, lines, grp, tid, n_line, skip);
     // Wait for the prefetch here, where the stores just issued are younger than it and need not
     // complete; a wait at the loop head would merge with the loop entry and drain the stores.
