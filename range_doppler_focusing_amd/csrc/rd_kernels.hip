@@ -250,14 +250,25 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
 // every exchange is free of bank conflicts under the gfx950 geometry (8-byte reads: 32 lanes
 // over 64 banks; 8-byte writes: 16 lanes over 32 banks).
 // The filter in the order the threads hold it, so that every wave reads it with contiguous
-// accesses: tab[r 256 + t] = H[g + 16 l + 256 r] (g = t / 16, l = t % 16, r = 0..15).  The
-// twiddles are evaluated in the kernel from exactly reduced arguments instead of being read
-// from a table (start-up table reads by every workgroup at once were measured to cost 2-9 us per
-// launch, most of it for strided reads).
-constexpr int kRc4096Tab = 16 * 256;
-void rc4096_tab_fill(const float2* H, const float2*, float2* out) {
+// accesses: tab[r 256 + t] = H[g + 16 l + 256 r] (g = t / 16, l = t % 16, r = 0..15), followed by
+// the twiddles in the same thread-major order, so every start-up table read is a contiguous wave
+// access (strided start-up table reads by every workgroup at once were measured to cost 2-9 us
+// per launch).
+#ifndef RD_RC4096_TWTAB
+#define RD_RC4096_TWTAB 1
+#endif
+// The twiddles W_4096^{t k} and the W_256 table are read from the same thread-major table
+// (rounded once from float64), not evaluated by every workgroup with sincospi: measured on MI355X
+// 0.3-0.5 us faster per 4096-line launch (RD_RC4096_TWTAB=0 builds the evaluated form).
+constexpr int kRc4096Tab = 16 * 256 + (RD_RC4096_TWTAB ? 16 * 256 : 0);
+void rc4096_tab_fill(const float2* H, const float2* roots, float2* out) {
   for (int r = 0; r < 16; ++r)
     for (int t = 0; t < 256; ++t) out[r * 256 + t] = H[(t >> 4) + 16 * (t & 15) + 256 * r];
+  if (RD_RC4096_TWTAB) {
+    for (int k = 1; k < 16; ++k)
+      for (int t = 0; t < 256; ++t) out[4096 + (k - 1) * 256 + t] = roots[(t * k) & 4095];
+    for (int t = 0; t < 240; ++t) out[4096 + 15 * 256 + t] = roots[16 * (((t & 15) * (t / 16 + 1)) & 255)];
+  }
 }
 
 template <int SAUX, bool HALF = false>
@@ -286,10 +297,16 @@ __global__ void __launch_bounds__(256, 3)
   float2 h[16];   // H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l)
 #pragma unroll
   for (int r = 0; r < 16; ++r) h[r] = tab[r * 256 + t];
-  if (t < 240) tw2[t] = root_of<256>(((t & 15) * (t / 16 + 1)) & 255);
   float2 w1[15];  // W_4096^{t k}, k = 1..15
+  if constexpr (RD_RC4096_TWTAB) {
+    if (t < 240) tw2[t] = tab[4096 + 15 * 256 + t];
 #pragma unroll
-  for (int k = 1; k < 16; ++k) w1[k - 1] = root_of<4096>((t * k) & 4095);
+    for (int k = 1; k < 16; ++k) w1[k - 1] = tab[4096 + (k - 1) * 256 + t];
+  } else {
+    if (t < 240) tw2[t] = root_of<256>(((t & 15) * (t / 16 + 1)) & 255);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) w1[k - 1] = root_of<4096>((t * k) & 4095);
+  }
   __syncthreads();
   for (int64_t line = blockIdx.x; line < lines; line += stride) {
     float2 v[16];
