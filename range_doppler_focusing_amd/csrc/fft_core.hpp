@@ -54,6 +54,11 @@ __device__ __forceinline__ void touch(const float2* v) {
 #pragma unroll
   for (int i = 0; i < K; ++i) asm volatile("" ::"v"(v[i].x), "v"(v[i].y));
 }
+template <int K>
+__device__ __forceinline__ void touch(const unsigned int* v) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) asm volatile("" ::"v"(v[i]));
+}
 
 // ---------------------------------------------------------------------------- compile-time roots
 // cos / sin of 2 pi p / q in double precision, evaluated by the compiler: the angle is reduced
@@ -606,6 +611,24 @@ __device__ __forceinline__ void load_line_h(float2* v, const LineIOh& io, int el
       for (int i = 0; i < R; ++i) {
         const int r = dft_input_order<R>(i);
         v[b * R + r] = h2_to_f2(__builtin_amdgcn_raw_buffer_load_b32(io.rsrc, (elem0 + j) * 4, r * G::NB * 4, AUX));
+      }
+    }
+  }
+}
+
+// The same loads, the samples left packed (real half in the low 16 bits); h2_to_f2 unpacks one.
+template <int N, int T, int R, int AUX = kBufNonTemporal>
+__device__ __forceinline__ void load_line_h_packed(unsigned int* v, const LineIOh& io, int elem0,
+                                                   int tid) {
+  using G = Geom<N, T, R>;
+#pragma unroll
+  for (int b = 0; b < G::B; ++b) {
+    const int j = tid + b * T;
+    if (G::live(j)) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int r = dft_input_order<R>(i);
+        v[b * R + r] = __builtin_amdgcn_raw_buffer_load_b32(io.rsrc, (elem0 + j) * 4, r * G::NB * 4, AUX);
       }
     }
   }

@@ -271,8 +271,17 @@ void rc4096_tab_fill(const float2* H, const float2* roots, float2* out) {
   }
 }
 
+// Occupancy: four workgroups per CU (four waves per SIMD, 1024 workgroups, exactly four lines
+// each at 4096 lines) need at most 128 VGPRs.  Only the line (32 registers) and the twiddles W_4096
+// (30) are live across a whole line; the filter (32) is reloaded from the table every line before
+// stage c, and the next line's prefetch (32) is issued after the filter multiply, so the two never
+// coexist (114 VGPRs; the binary16 form keeps its prefetch packed, 16 registers, and fits in 128
+// without spilling).  Measured on MI355X (kernel trace, 3 x ~5300 launches, alternating
+// on one GPU): 55.1 us per launch against 56.8 us for the three-wave form that held filter and
+// prefetch for the whole line (166 VGPRs); reloading the filter at three waves alone is slower
+// (59-60 us).
 template <int SAUX, bool HALF = false>
-__global__ void __launch_bounds__(256, 3)
+__global__ void __launch_bounds__(256, 4)
     k_range_compress_4096(const void* in, void* out, const float2* __restrict__ tab,
                           int64_t lines) {
   constexpr int N = 4096, T = 256, REG = 272;
@@ -283,20 +292,17 @@ __global__ void __launch_bounds__(256, 3)
   const int64_t stride = gridDim.x;
   // The first line's loads go out before the table loads, so the line's HBM latency overlaps
   // the table reads instead of following them.
-  // line I/O: float32 or binary16 storage
-  auto load = [&](float2* dst, int64_t line) {
+  // line I/O: float32 or binary16 storage.  A binary16 prefetch stays packed (one register a
+  // sample) until it becomes the working line.
+  using Pre = typename std::conditional<HALF, unsigned int, float2>::type;
+  auto load = [&](Pre* dst, int64_t line) {
     if constexpr (HALF)
-      load_line_h<N, T, 16>(dst, LineIOh(in, N, line, 1, lines), 0, t);
+      load_line_h_packed<N, T, 16>(dst, LineIOh(in, N, line, 1, lines), 0, t);
     else
       load_line<N, T, 16>(dst, LineIO(static_cast<const float2*>(in), N, line, 1, lines), 0, t);
   };
-  float2 nxt[16];
+  Pre nxt[16];
   load(nxt, blockIdx.x);
-  // The filter is first used at the first line's multiply, so the wait for it lands there (in
-  // later lines that wait also covers the previous line's stores, which are complete by then).
-  float2 h[16];   // H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l)
-#pragma unroll
-  for (int r = 0; r < 16; ++r) h[r] = tab[r * 256 + t];
   float2 w1[15];  // W_4096^{t k}, k = 1..15
   if constexpr (RD_RC4096_TWTAB) {
     if (t < 240) tw2[t] = tab[4096 + 15 * 256 + t];
@@ -311,8 +317,12 @@ __global__ void __launch_bounds__(256, 3)
   for (int64_t line = blockIdx.x; line < lines; line += stride) {
     float2 v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = nxt[i];
-    load(nxt, line + stride);
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (HALF)
+        v[i] = h2_to_f2(nxt[i]);
+      else
+        v[i] = nxt[i];
+    }
     // ---- forward
     Dft<16, -1>::run(v);
 #pragma unroll
@@ -331,6 +341,15 @@ __global__ void __launch_bounds__(256, 3)
     Dft<16, -1>::run(v);
 #pragma unroll
     for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], tw2[(k - 1) * 16 + l]);
+    // The filter H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l), read from the
+    // cache-resident table once per line, one pass before its use, instead of being held in
+    // registers across lines (see the occupancy note above the kernel).
+    float2 h[16];
+    {
+      const float2* hl = opaque(tab);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) h[r] = hl[r * 256 + t];
+    }
     exchange_sync<true>();
 #pragma unroll
     for (int k = 0; k < 16; ++k) lds[REG * g + 17 * k + l] = v[k];
@@ -344,6 +363,8 @@ __global__ void __launch_bounds__(256, 3)
     // ---- filter (carries 1/N)
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[r] = cmul(v[r], h[r]);
+    // The next line's loads go out here, once the filter registers are free.
+    load(nxt, line + stride);
     // ---- inverse
     Dft<16, +1>::run(v);
     exchange_sync<true>();
