@@ -1,6 +1,12 @@
 """Build the HIP library librdfocus.so in-tree (gfx950), with hipcc.
 
-Usage: python -m range_doppler_focusing_amd.build [--jobs N]
+Usage: python -m range_doppler_focusing_amd.build [--jobs N] [--debug]
+
+--debug builds librdfocus_debug.so instead: RD_DEBUG on (every launch's geometry checked against
+the plan before it runs, refused with RD_ERR_LAUNCH otherwise; each kernel's LDS filled with NaNs
+before first use, so a read of an unwritten element shows up in the output).  Load it with
+RDFOCUS_LIB=<path>.  The host arithmetic also runs under the host sanitizers on the CPU
+(tests/test_host_sanitized.py).
 """
 from __future__ import annotations
 
@@ -14,7 +20,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librdfocus.so")
-SOURCES = ["rd_kernels.hip", "rd_api.hip"]
+SOURCES = ["rd_kernels.hip", "rd_api.hip", "rd_host.cpp"]
 ARCH = os.environ.get("RD_OFFLOAD_ARCH", "gfx950")
 
 # Packed float32 instructions are disabled for every HIP source (they are generated from
@@ -52,7 +58,7 @@ def build(verbose: bool = False, jobs: int = 2, extra_flags=(), out: str | None 
     objs = []
 
     def one(src):
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         msg = _run([hipcc, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and msg.strip():
             print(msg, file=sys.stderr)
@@ -68,8 +74,19 @@ def build(verbose: bool = False, jobs: int = 2, extra_flags=(), out: str | None 
     return lib
 
 
+DEBUG_LIB = os.path.join(HERE, "librdfocus_debug.so")
+
+
+def build_debug(verbose: bool = False, jobs: int = 2) -> str:
+    """The RD_DEBUG variant of the library (see the module docstring)."""
+    return build(verbose=verbose, jobs=jobs, extra_flags=("-DRD_DEBUG=1",), out=DEBUG_LIB)
+
+
 if __name__ == "__main__":
     jobs = 2
     if "--jobs" in sys.argv:
         jobs = int(sys.argv[sys.argv.index("--jobs") + 1])
-    build(verbose=True, jobs=jobs)
+    if "--debug" in sys.argv:
+        build_debug(verbose=True, jobs=jobs)
+    else:
+        build(verbose=True, jobs=jobs)

@@ -45,6 +45,22 @@ __device__ __forceinline__ const T* opaque(const T* p) {
   return p + zero;
 }
 
+// Debug builds (RD_DEBUG) fill a kernel's LDS array with quiet NaNs before first use, so a read of
+// an element that no thread has written shows up as NaN in the output; other builds do nothing.
+template <size_t BYTES>
+__device__ __forceinline__ void debug_poison_lds(void* lds) {
+#ifdef RD_DEBUG
+  const unsigned n = blockDim.x * blockDim.y * blockDim.z;
+  const unsigned t = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
+  unsigned* w = static_cast<unsigned*>(lds);
+  for (unsigned i = t; i < BYTES / 4; i += n) w[i] = 0x7fc00000u;
+  __syncthreads();
+#else
+  (void)lds;
+#endif
+}
+#define RD_POISON_LDS(a) debug_poison_lds<sizeof(a)>(a)
+
 // Marks registers as read here.  Placed after a line's stores, it makes the compiler wait for
 // prefetched registers at that point, where the outstanding stores are younger than the
 // prefetch and need not complete; otherwise the wait lands at the loop head, whose merged

@@ -15,12 +15,19 @@
 #include <vector>
 
 #include "../../include/rdfocus.h"
+#include "rd_host.hpp"
 #include "rd_kernels.hpp"
 
 namespace {
 
-constexpr double kC = 299792458.0;
-constexpr double kTwoPi = 6.283185307179586476925286766559;
+using rdf::host::kC;
+using rdf::host::azimuth_five;
+using rdf::host::azimuth_pow2;
+using rdf::host::bluestein_m;
+using rdf::host::partial_overlap;
+using rdf::host::persistent_grid;
+using rdf::host::pow2_split;
+using rdf::host::roots_table;
 
 thread_local std::string g_last_error;
 
@@ -111,208 +118,10 @@ rd_status upload(T** dst, const std::vector<T>& src, const char* what) {
   return RD_OK;
 }
 
-// e^{-j 2 pi k / N}, k < N, evaluated in float64 and rounded once
-std::vector<float2> roots_table(int N) {
-  std::vector<float2> t(N);
-  for (int k = 0; k < N; ++k) {
-    const double a = kTwoPi * double(k) / double(N);
-    t[k] = make_float2(float(std::cos(a)), float(-std::sin(a)));
-  }
-  return t;
-}
-
-// Matched filter of nxmr.cn/news/101525 §2.1 (chirp spectrum precomputed on the host):
-// h[n] = w[n] exp(j pi Kr (n/Fs - Tp/2)^2) on [0, L), H[k] = conj(sum_n h[n] e^{-j2pi kn/Nr}),
-// by direct summation in float64 (exact twiddle index k n mod Nr), scaled by 1/Nr for the
-// inverse transform, rounded to float32 once.
-std::vector<float2> matched_filter(const rd_params& p, int L) {
-  const int Nr = p.Nr;
-  const double Kr = p.bandwidth_hz / p.pulse_s;
-  std::vector<double> hr(L), hi(L);
-  for (int n = 0; n < L; ++n) {
-    const double t = double(n) / p.fs_hz - p.pulse_s / 2.0;
-    double w = 1.0;
-    if (p.range_window == RD_WINDOW_HAMMING && L > 1) w = 0.54 - 0.46 * std::cos(kTwoPi * n / (L - 1));
-    const double ph = M_PI * Kr * t * t;
-    hr[n] = w * std::cos(ph);
-    hi[n] = w * std::sin(ph);
-  }
-  std::vector<double> c(Nr), s(Nr);
-  for (int m = 0; m < Nr; ++m) {
-    c[m] = std::cos(kTwoPi * m / Nr);
-    s[m] = std::sin(kTwoPi * m / Nr);
-  }
-  std::vector<float2> H(Nr);
-  for (int k = 0; k < Nr; ++k) {
-    double re = 0.0, im = 0.0;
-    int64_t idx = 0;  // (k * n) mod Nr
-    for (int n = 0; n < L; ++n) {
-      // h[n] e^{-j 2 pi idx / Nr}
-      re += hr[n] * c[idx] + hi[n] * s[idx];
-      im += hi[n] * c[idx] - hr[n] * s[idx];
-      idx += k;
-      if (idx >= Nr) idx -= Nr;
-    }
-    H[k] = make_float2(float(re / Nr), float(-im / Nr));  // conjugate, 1/Nr
-  }
-  return H;
-}
-
-// In-place radix-2 float64 FFT (forward, e^{-j...}) of a power-of-two length, for plan tables.
-void fft_pow2(std::vector<double>& re, std::vector<double>& im) {
-  const size_t n = re.size();
-  for (size_t i = 1, j = 0; i < n; ++i) {
-    size_t bit = n >> 1;
-    for (; j & bit; bit >>= 1) j ^= bit;
-    j ^= bit;
-    if (i < j) {
-      std::swap(re[i], re[j]);
-      std::swap(im[i], im[j]);
-    }
-  }
-  for (size_t len = 2; len <= n; len <<= 1) {
-    const size_t half = len / 2;
-    for (size_t k = 0; k < half; ++k) {
-      const double a = -kTwoPi * double(k) / double(len);
-      const double wr = std::cos(a), wi = std::sin(a);
-      for (size_t b = 0; b < n; b += len) {
-        const size_t u = b + k, v = u + half;
-        const double xr = re[v] * wr - im[v] * wi, xi = re[v] * wi + im[v] * wr;
-        re[v] = re[u] - xr;
-        im[v] = im[u] - xi;
-        re[u] += xr;
-        im[u] += xi;
-      }
-    }
-  }
-}
-
-// Range compression of a line of any length N as one zero-padded circular convolution of length
-// M >= N + L - 1 (L = replica length).  The length-N circular correlation
-//   rc[n] = sum_{i < L} x[(n + i) mod N] conj(h[i])
-// reads x[0 .. N + L - 2] of the periodically extended line; with g[k] = conj(h[L - 1 - k]) for
-// k < L (zero up to M), the linear convolution of that extended line with g holds rc[n] at
-// n + L - 1, and a length-M circular convolution aliases nothing onto [L - 1, N + L - 1) when
-// M >= N + L - 1.  Returns FFT_M(g) / M (the 1/M of the inverse transform folded in),
-// evaluated in float64 and rounded once.
-std::vector<float2> padded_filter(const rd_params& p, int L, int M) {
-  const double Kr = p.bandwidth_hz / p.pulse_s;
-  std::vector<double> re(size_t(M), 0.0), im(size_t(M), 0.0);
-  for (int n = 0; n < L; ++n) {
-    const double t = double(n) / p.fs_hz - p.pulse_s / 2.0;
-    double w = 1.0;
-    if (p.range_window == RD_WINDOW_HAMMING && L > 1) w = 0.54 - 0.46 * std::cos(kTwoPi * n / (L - 1));
-    const double ph = M_PI * Kr * t * t;
-    re[size_t(L - 1 - n)] = w * std::cos(ph);
-    im[size_t(L - 1 - n)] = -w * std::sin(ph);
-  }
-  fft_pow2(re, im);
-  std::vector<float2> out(static_cast<size_t>(M));
-  for (int k = 0; k < M; ++k) out[size_t(k)] = make_float2(float(re[size_t(k)] / M), float(im[size_t(k)] / M));
-  return out;
-}
-
-// Spectra of the Bluestein chirps for an azimuth DFT of length Na through columns of length M:
-// b[n] = exp(-sign j pi n^2 / Na) for |n| < Na, placed circularly (b[M - n] = b[n]), zero
-// elsewhere; B = FFT_M(b) / M (the 1/M of the inverse column transform folded in), evaluated in
-// float64 and rounded once, forward (sign -1) then inverse (sign +1), each in the column steps'
-// output row order (row r holds bin r / cb + ca (r % cb)).
-std::vector<float2> bluestein_spectra(int na, int m, int ca, int cb) {
-  std::vector<float2> out(static_cast<size_t>(2 * m));
-  for (int d = 0; d < 2; ++d) {
-    const double sign = d == 0 ? -1.0 : 1.0;
-    std::vector<double> re(size_t(m), 0.0), im(size_t(m), 0.0);
-    for (int n = 0; n < na; ++n) {
-      const int64_t q = (int64_t(n) * n) % (2 * int64_t(na));
-      const double ph = -sign * M_PI * double(q) / double(na);
-      re[size_t(n)] = std::cos(ph);
-      im[size_t(n)] = std::sin(ph);
-      if (n > 0) {
-        re[size_t(m - n)] = re[size_t(n)];
-        im[size_t(m - n)] = im[size_t(n)];
-      }
-    }
-    fft_pow2(re, im);
-    for (int r = 0; r < m; ++r) {
-      const int bin = r / cb + ca * (r % cb);
-      out[size_t(d * m + r)] = make_float2(float(re[size_t(bin)] / m), float(im[size_t(bin)] / m));
-    }
-  }
-  return out;
-}
-
-// RCMC tap weights (nxmr.cn/news/101525 §2.2 interpolates the migrated range; the 8-tap
-// Kaiser-windowed sinc is the interpolator).  For fraction f in [0, 1) the output reads samples
-// floor(x) - 3 .. floor(x) + 4 with weights w_j = sinc(f - j) K(f - j) / sum, K the Kaiser
-// window over the 8-tap span.  sinc(f - j) = (-1)^j sin(pi f) / (pi (f - j)); multiplying every
-// tap by the common factor pi prod_i (f - i) / sin(pi f) gives
-//   b_j(f) = (-1)^j K(f - j) prod_{i != j} (f - i),
-// smooth in f (no division, no f = 0 special case), with the same normalised weights.  Each b_j
-// is interpolated at 9 Chebyshev points of [0, 1] (degree 8; max error ~5e-9 of max|b|) and
-// expanded in monomials of x = f - 1/2.  By the symmetry b_{1-j}(x) = b_j(-x) only taps
-// j = 0, -1, -2, -3 are fitted; their even and odd parts serve the mirrored taps too.
-double bessel_i0(double z) {
-  const double y = 0.25 * z * z;
-  double term = 1.0, sum = 1.0;
-  for (int m = 1; m < 200 && term > 1e-18 * sum; ++m) {
-    term *= y / (double(m) * double(m));
-    sum += term;
-  }
-  return sum;
-}
-
-void rcmc_weight_polys(double beta, rdf::RcmcPoly* out) {
-  constexpr int D = rdf::kRcmcDeg, M = D + 1;
-  const double half = rdf::kRcmcTaps / 2.0;
-  const double i0b = bessel_i0(beta);
-  for (int q = 0; q < rdf::kRcmcTaps / 2; ++q) {
-    const int j = -q;
-    auto b = [&](double f) {
-      const double tt = f - j;
-      const double a = 1.0 - (tt / half) * (tt / half);
-      double v = bessel_i0(beta * std::sqrt(a > 0 ? a : 0.0)) / i0b;
-      for (int i = -(rdf::kRcmcTaps / 2 - 1); i <= rdf::kRcmcTaps / 2; ++i)
-        if (i != j) v *= (f - i);
-      return (j & 1) ? -v : v;
-    };
-    double cheb[M] = {};
-    for (int k = 0; k < M; ++k) {
-      double acc = 0.0;
-      for (int i = 0; i < M; ++i) {
-        const double th = M_PI * (i + 0.5) / M;
-        acc += b(0.5 + 0.5 * std::cos(th)) * std::cos(k * th);
-      }
-      cheb[k] = acc * 2.0 / M;
-    }
-    cheb[0] *= 0.5;
-    // sum_k cheb[k] T_k(u) -> monomials in u, then u = 2x
-    double mono[M] = {}, tkm1[M] = {}, tk[M] = {};
-    tkm1[0] = 1.0;                 // T_0
-    tk[1] = 1.0;                   // T_1
-    mono[0] += cheb[0];
-    for (int m = 0; m < M; ++m) mono[m] += cheb[1] * tk[m];
-    for (int k = 2; k < M; ++k) {
-      double tn[M] = {};
-      for (int m = 0; m < M; ++m) {
-        if (m > 0) tn[m] += 2.0 * tk[m - 1];
-        tn[m] -= tkm1[m];
-      }
-      for (int m = 0; m < M; ++m) {
-        mono[m] += cheb[k] * tn[m];
-        tkm1[m] = tk[m];
-        tk[m] = tn[m];
-      }
-    }
-    double p2 = 1.0;
-    for (int m = 0; m < M; ++m) {
-      const double cm = mono[m] * p2;  // coefficient of x^m
-      if (m % 2 == 0)
-        out->even[q][m / 2] = float(cm);
-      else
-        out->odd[q][m / 2] = float(cm);
-      p2 *= 2.0;
-    }
-  }
+// host complex tables (rd_c64) into the kernels' float2 arrays: the same 8-byte layout
+static_assert(sizeof(rd_c64) == sizeof(float2), "rd_c64 and float2 must share a layout");
+rd_status upload(float2** dst, const std::vector<rd_c64>& src, const char* what) {
+  return upload(reinterpret_cast<rd_c64**>(dst), src, what);
 }
 
 rd_status check_hip(hipError_t e, const char* what) {
@@ -329,47 +138,30 @@ rd_status check_call(rd_plan* plan) {
   return RD_OK;
 }
 
+// RD_DEBUG builds check each launch's geometry against the plan before launching and refuse the
+// launch (RD_ERR_LAUNCH, naming the failed condition) instead of running a kernel on a shape it
+// was not built for; other builds compile the checks away.
+#ifdef RD_DEBUG
+#define RD_EXPECT(cond)                                                                        \
+  do {                                                                                         \
+    if (!(cond)) return fail(RD_ERR_LAUNCH, "debug check failed (%s:%d): %s", __FILE__, __LINE__, #cond); \
+  } while (0)
+#else
+#define RD_EXPECT(cond) \
+  do {                  \
+  } while (0)
+#endif
+
 bool aligned8(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-
-// [a, a + n) and [b, b + n) overlap but are not the same buffer
-bool partial_overlap(const void* a, const void* b, size_t n) {
-  const char* x = static_cast<const char*>(a);
-  const char* y = static_cast<const char*>(b);
-  return x != y && x < y + n && y < x + n;
-}
-
-// Azimuth lengths of full-chain plans: the two steps of the transform must be built column
-// lengths (16, 32, 64, 128 and 25).
-bool azimuth_pow2(int na) { return na >= 256 && na <= 16384 && (na & (na - 1)) == 0; }
-// column transform length of the Bluestein form: a power of two >= 2 Na - 1 (at least 256)
-int bluestein_m(int na) {
-  int m = 256;
-  while (m < 2 * na - 1) m *= 2;
-  return m;
-}
-// Na = A B with A the largest power of two <= sqrt(Na) (Na a power of two >= 256)
-void pow2_split(int n, int* a, int* b) {
-  *a = 1;
-  while (*a * *a * 4 <= n) *a *= 2;
-  *b = n / *a;
-}
-bool azimuth_five(int na) {
-  if (na % 25 != 0) return false;
-  const int a = na / 25;
-  return a >= 16 && a <= 128 && (a & (a - 1)) == 0;
-}
-
-int persistent_grid(int occ, int cus, int64_t lines, int lpw) {
-  const int64_t need = (lines + lpw - 1) / lpw;
-  const int64_t resident = int64_t(occ > 0 ? occ : 1) * int64_t(cus > 0 ? cus : 1);
-  const int64_t g = need < resident ? need : resident;
-  return int(g > 0 ? g : 1);
-}
 
 // -------------------------------------------------------------------------- launch sequences
 // chained: the output feeds the azimuth chain (stored cacheable where the image fits the cache)
 rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, bool chained, hipStream_t s) {
+  RD_EXPECT(in && out && P->H && P->tw_r && P->rc_grid >= 1);
+  RD_EXPECT(P->rops->n == (P->pad_m ? P->pad_m : P->p.Nr));
+  RD_EXPECT(!P->pad_m || P->p.Nr + P->L - 1 <= P->pad_m);
+  RD_EXPECT(P->pad_m || P->rops->rc_tab_len() == 0 || P->rc_tab);
   if (P->rc_variant == 1)
     return check_hip(P->rops->range_compress_pf(in, out, P->H, P->tw_r, P->rc_tab, P->p.Na,
                                                 P->rc_grid, chained ? P->cached : 0, P->p.Nr,
@@ -380,6 +172,8 @@ rd_status run_range_compress(rd_plan* P, const float2* in, float2* out, bool cha
 }
 
 rd_status run_range_compress_f16(rd_plan* P, const void* in, void* out, bool chained, hipStream_t s) {
+  RD_EXPECT(in && out && P->f16_grid >= 1 && P->rops->range_compress_f16);
+  RD_EXPECT(!P->pad_m || P->p.Nr + P->L - 1 <= P->pad_m);
   return check_hip(P->rops->range_compress_f16(in, out, P->H, P->tw_r, P->rc_tab, P->p.Na, P->f16_grid,
                                                chained ? P->cached : 0, P->p.Nr, P->pad_m ? P->L - 1 : 0, s),
                    "binary16 range compression launch");
@@ -412,6 +206,8 @@ rdf::ColStep col_step(const rd_plan* P, bool forward, bool strided) {
 rd_status run_col(rd_plan* P, const void* src, void* dst, bool forward, bool strided, bool half,
                   hipStream_t s) {
   rdf::ColStep st = col_step(P, forward, strided);
+  RD_EXPECT(src && dst && P->ca * P->cb == P->col_n && P->col_n == (P->bs_m ? P->bs_m : P->p.Na));
+  RD_EXPECT((strided ? P->tw_A : P->tw_B) && st.L * st.sets == P->col_n);
   st.half = half ? 1 : 0;
   st.scale = 1.0f / float(st.L);
   return check_hip(rdf::launch_col_fft(src, dst, strided ? P->tw_A : P->tw_B, st, P->p.Nr, P->col_n,
@@ -427,6 +223,7 @@ rd_status run_bluestein(rd_plan* P, const void* src, void* dst, int sign, bool h
   const int Na = P->p.Na, M = P->bs_m;
   const int64_t Nr = P->p.Nr;
   const int h = half ? 1 : 0;
+  RD_EXPECT(src && dst && W && P->bs_fb && M >= 2 * Na - 1 && P->A == 1 && P->B == Na);
   rd_status st;
   if ((st = check_hip(rdf::launch_chirp_rows(src, W, Nr, Na, M, Na, sign, h, 0, 1.0f, s), "chirp launch")) != RD_OK)
     return st;
@@ -460,6 +257,8 @@ rd_status az_inverse(rd_plan* P, void* io, bool half, hipStream_t s, float2* ws 
 
 // The row stage with the constants c (rows in c's Doppler order); in place allowed
 rd_status run_rows_c(rd_plan* P, const void* src, void* dst, const rdf::AzRowConst& c, bool half, hipStream_t s) {
+  RD_EXPECT(src && dst && c.row && int64_t(c.A) * c.B == P->p.Na);
+  RD_EXPECT(c.halo >= 0 && c.halo <= P->rcmc_margin);
   if (P->pad_m)
     return check_hip(rdf::launch_rcmc_mf_any(src, dst, c, P->p.Na, P->p.Nr, P->cached, half, s), "RCMC launch");
   return check_hip(P->rops->rcmc_mf(src, dst, c, P->p.Na, 0, P->cached, half, s), "RCMC launch");
@@ -526,6 +325,7 @@ rd_status run_omega_k(rd_plan* plan, const void* echo, void* img, int32_t ref_bi
   c.halo = plan->wk_halo;
   c.inv_na = half ? 1.0f : float(1.0 / double(p.Na));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  RD_EXPECT(c.halo >= 5 && c.halo <= plan->rops->wk_cap && int64_t(c.A) * c.B == p.Na && plan->wk_grid >= 1);
   if ((st = az_forward(plan, echo, img, half, s)) != RD_OK) return st;
   if ((st = check_hip(plan->rops->omega_k_rows(img, img, plan->H, plan->tw_r, c, plan->az.w, p.Na, plan->wk_grid,
                                                plan->cached, half ? 1 : 0, s),
@@ -668,13 +468,14 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
   };
   {
     const int n_tf = pad_m ? pad_m : p.Nr;
-    const std::vector<float2> Hh = pad_m ? padded_filter(p, P->L, pad_m) : matched_filter(p, P->L);
-    const std::vector<float2> roots = roots_table(n_tf);
+    const std::vector<rd_c64> Hh =
+        pad_m ? rdf::host::padded_filter(p, P->L, pad_m) : rdf::host::matched_filter(p, P->L);
+    const std::vector<rd_c64> roots = roots_table(n_tf);
     if ((st = upload(&P->H, Hh, "matched filter")) != RD_OK) return bail(st);
     if ((st = upload(&P->tw_r, roots, "range twiddles")) != RD_OK) return bail(st);
     if (const int n = rops->rc_tab_len(); n > 0 && !pad_m) {
       std::vector<float2> tab(static_cast<size_t>(n));
-      rops->rc_tab_fill(Hh.data(), roots.data(), tab.data());
+      rops->rc_tab_fill(reinterpret_cast<const float2*>(Hh.data()), reinterpret_cast<const float2*>(roots.data()), tab.data());
       if ((st = upload(&P->rc_tab, tab, "range kernel table")) != RD_OK) return bail(st);
     }
   }
@@ -709,7 +510,6 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     return bail(st);
   if (all_az) {
     const int Na = p.Na;
-    const double lam = kC / p.carrier_hz;
     // Na = A B: A the largest power of two <= sqrt(Na) for powers of two; else A = Na / 25,
     // B = 25 (both steps are built column transform lengths)
     if (azimuth_five(Na)) {
@@ -727,35 +527,19 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     }
     P->A = P->bs_m ? 1 : P->ca;
     P->B = P->bs_m ? Na : P->cb;
-    std::vector<double> rowc(size_t(Na) * 4);
-    double max_shift = 0.0;
-    for (int k = 0; k < Na; ++k) {
-      const int kk = (k <= (Na - 1) / 2) ? k : k - Na;  // FFT bin order
-      const double f = double(kk) * p.prf_hz / double(Na);
-      const double u = std::pow(lam * f / (2.0 * p.velocity_mps), 2);
-      const double D = std::sqrt(1.0 - u);
-      const double Q = u / (D * (1.0 + D)) / P->dr;  // shift per metre of slant range, samples
-      rowc[4 * k + 0] = p.range_bin0_m * Q;          // Delta(n) = alpha + n beta
-      rowc[4 * k + 1] = P->dr * Q;
-      rowc[4 * k + 2] = 2.0 * D * p.range_bin0_m / lam;  // phase cycles = gamma + n delta
-      rowc[4 * k + 3] = 2.0 * D * P->dr / lam;
-      max_shift = std::max(max_shift, rowc[4 * k] + double(p.Nr - 1) * rowc[4 * k + 1]);
-    }
+    std::vector<double> rowc;
+    const double max_shift = rdf::host::doppler_row_coefficients(p, P->dr, &rowc);
     // taps reach floor(shift) + 4 samples past the output (one more for rounding differences
     // between this bound and the kernel's float64 shift)
     // (a plan whose migration exceeds the RCMC margin still serves omega-k and back-projection;
     // the range-Doppler entry points report it)
     P->rd_max_shift = max_shift;
     P->az.halo = std::min(int(std::floor(max_shift)) + 5, P->rcmc_margin);
-    // omega-k: the Stolt shift (sqrt(a^2 + b^2) - a) / df is largest at the lowest range
-    // frequency a = f0 - Fs/2 and the Doppler band edge b = c PRF / (4 V); the mapping needs
-    // a > b there (a real wavenumber at every sample)
+    // omega-k (where the geometry gives a real wavenumber at every sample)
     {
-      const double df = p.fs_hz / p.Nr;
-      const double amin = p.carrier_hz - double(p.Nr / 2) * df;
-      const double bmax = kC * p.prf_hz / (4.0 * p.velocity_mps);
-      if (rops->omega_k_rows && !pad_m && amin > bmax) {
-        P->wk_halo = int(std::floor((std::sqrt(amin * amin + bmax * bmax) - amin) / df)) + 5;
+      const int halo = rdf::host::stolt_halo(p);
+      if (rops->omega_k_rows && !pad_m && halo >= 0) {
+        P->wk_halo = halo;
         int occ = 0;
         if (rops->occupancy_wk(&occ) != hipSuccess) return bail(fail(RD_ERR_DEVICE, "occupancy query failed"));
         P->wk_grid = persistent_grid(occ, P->cus, Na, rops->lpw);
@@ -764,7 +548,7 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     if ((st = upload(&P->tw_A, roots_table(P->ca), "azimuth step twiddles")) != RD_OK) return bail(st);
     if ((st = upload(&P->tw_B, roots_table(P->cb), "azimuth step twiddles")) != RD_OK) return bail(st);
     if (P->bs_m) {
-      if ((st = upload(&P->bs_fb, bluestein_spectra(Na, P->bs_m, P->ca, P->cb), "Bluestein chirp spectra")) != RD_OK)
+      if ((st = upload(&P->bs_fb, rdf::host::bluestein_spectra(Na, P->bs_m, P->ca, P->cb), "Bluestein chirp spectra")) != RD_OK)
         return bail(st);
       if (hipMalloc(&P->bs_ws, size_t(P->bs_m) * size_t(p.Nr) * sizeof(float2)) != hipSuccess) {
         P->bs_ws = nullptr;
@@ -777,7 +561,7 @@ rd_status rd_plan_create(const rd_params* params, rd_plan** out) {
     P->az.B = P->B;
     P->az.inv_na = float(1.0 / double(Na));
     P->az.filter = 1;
-    rcmc_weight_polys(p.kaiser_beta, &P->az.w);
+    rdf::host::rcmc_weight_polys(p.kaiser_beta, &P->az.w);
     // The image passes run cacheable when the image fits well inside the 256 MB Infinity
     // Cache (RD_AZ_CACHE=0/1 overrides, for measurement).
     P->cached = int64_t(Na) * p.Nr * 8 <= (int64_t(160) << 20) ? 1 : 0;
@@ -1020,6 +804,7 @@ rd_status rd_backproject(rd_plan* plan, const rd_c64* rc, rd_c64* img, const rd_
   // library sincospi (a measurement variant).
   const char* v = std::getenv("RD_BP_SINCOS");
   const int native = (v && std::string(v) == "accurate") ? 0 : 1;
+  RD_EXPECT(c.nx > 0 && c.ny > 0 && c.Na > 0 && c.Nr > 0 && std::isfinite(c.step) && c.inv_dr > 0);
   return check_hip(rdf::launch_backproject(reinterpret_cast<const float2*>(rc), reinterpret_cast<float2*>(img),
                                            c, native, static_cast<hipStream_t>(stream)),
                    "back-projection launch");

@@ -45,6 +45,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   constexpr int R0 = ListInfo<typename C::Fwd>::first;
   constexpr int RL = ListInfo<typename C::Fwd>::last;
   __shared__ float2 lds[C::LPW * C::LDS];
+  RD_POISON_LDS(lds);
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * C::LDS;
@@ -184,6 +185,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
   constexpr int LBUF = C::LDS * (DB ? 2 : 1);
   constexpr bool SWAP = DB && (ListInfo<L>::count - 1) % 2 == 1;  // inverse starts on buffer b
   __shared__ float2 lds[C::LPW * LBUF + (TC::LDS > 0 ? TC::LDS : 1)];
+  RD_POISON_LDS(lds);
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * LBUF;
@@ -286,6 +288,7 @@ __global__ void __launch_bounds__(256, 4)
                           int64_t lines) {
   constexpr int N = 4096, T = 256, REG = 272;
   __shared__ float2 lds[16 * REG + 15 * 16];
+  RD_POISON_LDS(lds);
   float2* tw2 = lds + 16 * REG;  // W_256^{n0 k}: tw2[(k - 1) 16 + n0], k = 1..15
   const int t = threadIdx.x;
   const int g = t >> 4, l = t & 15;
@@ -419,6 +422,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   constexpr int RI = ListInfo<L>::first;
   constexpr int RO = ListInfo<L>::last;
   __shared__ float2 lds[C::LPW * C::LDS];
+  RD_POISON_LDS(lds);
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * C::LDS;
@@ -470,6 +474,8 @@ __global__ void __launch_bounds__(ColCfg<L>::WG)
                 "the column loads and stores below assume every lane's butterflies are live");
   __shared__ float2 lds[C::COLS * C::LDS + (TC::LDS > 0 ? TC::LDS : 1)];
   __shared__ float2 step_tw[L];  // inter-step twiddles W_Na^{DIR g t}, t < L
+  RD_POISON_LDS(lds);
+  RD_POISON_LDS(step_tw);
   const int col = threadIdx.x & 63;
   const int tid = threadIdx.x >> 6;
   float2* my = lds + col * C::LDS;
@@ -682,6 +688,7 @@ __global__ void __launch_bounds__(RowStage<N>::WG)
   static_assert(CH % T == 0 && R0 <= RS::P, "row layout");
   using G = Geom<CH, T, R0>;
   __shared__ float2 lds[RS::LPW * RS::LEN];
+  RD_POISON_LDS(lds);
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * RS::LEN;
@@ -841,6 +848,7 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
   using TC = TwCache<N, T, 1, L>;
   constexpr int REG = OkRow<N>::REG;
   __shared__ float2 lds[C::LPW * REG + (TC::LDS > 0 ? TC::LDS : 1)];
+  RD_POISON_LDS(lds);
   const int grp = threadIdx.x / T;
   const int tid = threadIdx.x - grp * T;
   float2* my = lds + grp * REG;
@@ -996,6 +1004,7 @@ __global__ void __launch_bounds__(256)
     k_corner_turn(const float2* __restrict__ in, float2* __restrict__ out, int64_t rows,
                   int64_t cols, int tiles_x, int tiles) {
   __shared__ float2 tile[kTurnTile * kTurnPitch];
+  RD_POISON_LDS(tile);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float2 cur[16];
   int t = blockIdx.x;

@@ -4,23 +4,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rd_host.hpp"
+
 namespace rdf {
 
 // RCMC + azimuth filter on one Doppler row k of the [Na][Nr] array (range along the row):
 //   Delta(n) = alpha_k + n beta_k   (= R(n) (1/D_k - 1) / dr, samples)
 //   T[n]     = sum_{j=-3..4} w_j(f) S[floor(n + Delta) + j],  f = frac(n + Delta)
 //   out[n]   = T[n] exp(+j 2 pi (gamma_k + n delta_k)) / Na   (= 4 pi R(n) D_k / lambda)
-// w_j(f) = b_j(f) / sum_i b_i(f), b_j(f) = (-1)^j K(f - j) prod_{i != j} (f - i): the Kaiser-
-// windowed sinc times a factor common to all taps (it cancels in the normalisation), which is
-// smooth in f.  The interpolator is symmetric, b_{1-j}(x) = b_j(-x) with x = f - 1/2, so taps
-// j = -q and 1 + q (q = 0..3) come from one degree-8 polynomial p_q(x) = E_q(x^2) + x O_q(x^2),
-// fitted on the host: b_{-q}(x) = E + x O and b_{1+q}(x) = E - x O.
-constexpr int kRcmcTaps = 8;
-constexpr int kRcmcDeg = 8;
-struct RcmcPoly {
-  float even[kRcmcTaps / 2][kRcmcDeg / 2 + 1];  // E_q, ascending powers of x^2
-  float odd[kRcmcTaps / 2][kRcmcDeg / 2];       // O_q, ascending powers of x^2
-};
+// w_j(f): the interpolator weights of RcmcPoly (rd_host.hpp), from polynomials fitted on the host.
 struct AzRowConst {
   const double* row;   // [Na][4]: alpha, beta, gamma, delta per Doppler bin (FFT order)
   int A, B;            // Na = A B; row r holds Doppler bin (r / B) + A (r % B)
