@@ -282,6 +282,10 @@ void rc4096_tab_fill(const float2* H, const float2* roots, float2* out) {
 // on one GPU): 55.1 us per launch against 56.8 us for the three-wave form that held filter and
 // prefetch for the whole line (166 VGPRs); reloading the filter at three waves alone is slower
 // (59-60 us).
+#ifndef RD_RC4096_MFMA
+#define RD_RC4096_MFMA 0
+#endif
+typedef float rdf_v4f __attribute__((ext_vector_type(4)));
 template <int SAUX, bool HALF = false>
 __global__ void __launch_bounds__(256, 4)
     k_range_compress_4096(const void* in, void* out, const float2* __restrict__ tab,
@@ -344,6 +348,68 @@ __global__ void __launch_bounds__(256, 4)
     Dft<16, -1>::run(v);
 #pragma unroll
     for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], tw2[(k - 1) * 16 + l]);
+#if RD_RC4096_MFMA
+    // Stage c, the filter and the mirror stage c as matrix products on the matrix cores: for each
+    // of this wave's four regions k0 (a batch of 16 vectors k1, 16 points n0 each),
+    // Y = F X (F the 16-point DFT matrix, X[n0][k1]), Y times the filter, Z = conj(F) Y.
+    {
+      exchange_sync<true>();
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lds[REG * g + 17 * k + l] = v[k];
+      exchange_sync<true>();
+      const int w4 = (t >> 6) * 4, lq = t & 15, lg = (t >> 4) & 3;
+      // k step s takes the points n0 = 4 lg + s of lane group lg: X in the B layout (column k1 =
+      // lane % 16), F in the A layout (row = lane % 16), and the product's rows 4 lg + i
+      // (i = 0..3) in the same lane group, ready as the next product's B operand.
+      float fr[4], fi[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float2 e = root_of<16>((lq * (4 * lg + st)) & 15);  // e^{-j 2 pi row k / 16}
+        fr[st] = e.x;
+        fi[st] = e.y;
+      }
+      const float2* hl = opaque(tab);
+      rdf_v4f yr[4], yi[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        rdf_v4f ar = {0.f, 0.f, 0.f, 0.f}, ai = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const float2 x = lds[REG * (w4 + b) + 17 * lq + 4 * lg + st];
+          ar = __builtin_amdgcn_mfma_f32_16x16x4f32(fr[st], x.x, ar, 0, 0, 0);
+          ar = __builtin_amdgcn_mfma_f32_16x16x4f32(fi[st], -x.y, ar, 0, 0, 0);
+          ai = __builtin_amdgcn_mfma_f32_16x16x4f32(fi[st], x.x, ai, 0, 0, 0);
+          ai = __builtin_amdgcn_mfma_f32_16x16x4f32(fr[st], x.y, ai, 0, 0, 0);
+        }
+        // the filter (carries 1/N) at X[k0 + 16 k1 + 256 k2], k2 = 4 lg + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float2 y = cmul(make_float2(ar[i], ai[i]), hl[(4 * lg + i) * 256 + 16 * (w4 + b) + lq]);
+          ar[i] = y.x;
+          ai[i] = y.y;
+        }
+        yr[b] = ar;
+        yi[b] = ai;
+      }
+      exchange_sync<true>();
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        rdf_v4f zr = {0.f, 0.f, 0.f, 0.f}, zi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          zr = __builtin_amdgcn_mfma_f32_16x16x4f32(fr[st], yr[b][st], zr, 0, 0, 0);
+          zr = __builtin_amdgcn_mfma_f32_16x16x4f32(fi[st], yi[b][st], zr, 0, 0, 0);
+          zi = __builtin_amdgcn_mfma_f32_16x16x4f32(fi[st], -yr[b][st], zi, 0, 0, 0);
+          zi = __builtin_amdgcn_mfma_f32_16x16x4f32(fr[st], yi[b][st], zi, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds[REG * (w4 + b) + 17 * lq + 4 * lg + i] = make_float2(zr[i], zi[i]);
+      }
+      // The next line's loads go out here, once the products' registers are free.
+      load(nxt, line + stride);
+      exchange_sync<true>();
+    }
+#else
     // The filter H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l), read from the
     // cache-resident table once per line, one pass before its use, instead of being held in
     // registers across lines (see the occupancy note above the kernel).
@@ -374,6 +440,7 @@ __global__ void __launch_bounds__(256, 4)
 #pragma unroll
     for (int n0 = 0; n0 < 16; ++n0) lds[REG * g + 17 * l + n0] = v[n0];
     exchange_sync<true>();
+#endif
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int k = dft_input_order<16>(i);
