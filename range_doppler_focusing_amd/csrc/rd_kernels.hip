@@ -478,6 +478,120 @@ __global__ void __launch_bounds__(256, 4)
 }
 
 // ------------------------------------------------------------------------------------------
+// Range compression of 16384-sample lines as four steps inside one workgroup of 16 waves, two
+// barriers per line.  With n = t + 1024 n_a (t < 1024, thread t) and k = k_a + 16 k_m:
+//   a: DFT16 over n_a -> k_a, times W_16384^{t k_a}                  (thread t, registers)
+//   exchange: sub-line k_a (element t) to wave k_a                    (workgroup barrier)
+//   m: 1024-point transform over t -> k_m in wave k_a: passes 16, 4, 16 with wave-local
+//      exchanges in the wave's own LDS row (lane l ends holding k_m = l + 64 r)
+// then the filter H[k_a + 16 k_m], the 1024-point inverse of each sub-line in its wave, the
+// sub-lines back to columns (the second barrier), the conjugate twiddles and the inverse DFT16,
+// leaving y[t + 1024 n_a] in thread t.  A wave reads and writes only its own LDS row between the
+// two barriers, and the next line's first exchange writes exactly the elements each thread read
+// in the last one, so no other barrier is needed.  The filter (in the order the threads hold it)
+// and the twiddles W_16384^{t k} come from the plan's table; the 1024-point pass twiddles live
+// in LDS.  The earlier form (Stockham passes 8, 16, 16, 8 over all 1024 threads) made three
+// workgroup exchanges per direction, twelve barriers per line.
+#ifndef RD_RC_16384
+#define RD_RC_16384 1
+#endif
+constexpr int kRc16kTab = 16 * 1024 + 15 * 1024;
+void rc16k_tab_fill(const float2* H, const float2* roots, float2* out) {
+  for (int r = 0; r < 16; ++r)
+    for (int t = 0; t < 1024; ++t) out[r * 1024 + t] = H[(t >> 6) + 16 * (t & 63) + 1024 * r];
+  for (int k = 1; k < 16; ++k)
+    for (int t = 0; t < 1024; ++t) out[16384 + (k - 1) * 1024 + t] = roots[(t * k) & 16383];
+}
+
+template <int SAUX, bool HALF = false>
+__global__ void __launch_bounds__(1024)
+    k_range_compress_16384(const void* in, void* out, const float2* __restrict__ tab, int64_t lines) {
+  constexpr int N = 16384, T = 1024, M = 1024, ROW = lds_len(M);
+  using SL = L_16_4_16;  // palindromic: the forward output layout is the inverse input layout
+  using TC = TwCache<M, 64, 1, SL>;
+  static_assert(TC::LDS > 0 && 16 * ROW + TC::LDS <= 163840 / 8, "LDS budget");
+  __shared__ float2 lds[16 * ROW + TC::LDS];
+  RD_POISON_LDS(lds);
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  float2* row = lds + wv * ROW;  // this wave's sub-line and exchange buffer
+  const int64_t stride = gridDim.x;
+  using Pre = typename std::conditional<HALF, unsigned int, float2>::type;
+  auto load = [&](Pre* dst, int64_t line) {
+    if constexpr (HALF)
+      load_line_h_packed<N, T, 16>(dst, LineIOh(in, N, line, 1, lines), 0, t);
+    else
+      load_line<N, T, 16>(dst, LineIO(static_cast<const float2*>(in), N, line, 1, lines), 0, t);
+  };
+  Pre nxt[16];
+  load(nxt, blockIdx.x);
+  TC twc;
+  twc.load_all(tab, lds + 16 * ROW, lane, t, T);
+  float2 w1[15];  // W_16384^{t k}, k = 1..15
+#pragma unroll
+  for (int k = 1; k < 16; ++k) w1[k - 1] = tab[16384 + (k - 1) * 1024 + t];
+  __syncthreads();
+  for (int64_t line = blockIdx.x; line < lines; line += stride) {
+    float2 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (HALF)
+        v[i] = h2_to_f2(nxt[i]);
+      else
+        v[i] = nxt[i];
+    }
+    // ---- forward: stage a
+    Dft<16, -1>::run(v);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lds[k * ROW + t] = v[k];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = dft_input_order<16>(i);
+      v[r] = row[lane + 64 * r];
+    }
+    PassesCached<M, 64, -1, 1, SL, true>::run(v, row, twc, lane);
+    // the filter for this thread's outputs (the other waves cover the cache latency)
+    float2 h[16];
+    {
+      const float2* hl = opaque(tab);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) h[r] = hl[r * 1024 + t];
+    }
+    // ---- filter (carries 1/N)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = cmul(v[r], h[r]);
+    // ---- inverse
+    PassesCached<M, 64, +1, 1, SL, true>::run(v, row, twc, lane);
+    // The next line's loads go out here, after the sub-line transforms, whose registers they
+    // would otherwise share.
+    load(nxt, line + stride);
+    exchange_sync<true>();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) row[lane + 64 * r] = v[r];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = dft_input_order<16>(i);
+      v[k] = lds[k * ROW + t];
+    }
+#pragma unroll
+    for (int k = 1; k < 16; ++k) {
+      float2 w = w1[k - 1];
+      w.y = -w.y;
+      v[k] = cmul(v[k], w);
+    }
+    Dft<16, +1>::run(v);
+    if constexpr (HALF)
+      store_line_h<N, T, 16, SAUX>(v, LineIOh(out, N, line, 1, lines), 0, t);
+    else
+      store_line<N, T, 16, SAUX>(v, LineIO(static_cast<float2*>(out), N, line, 1, lines), 0, t);
+    touch<16>(nxt);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // independent line transforms (azimuth FFT and the transform test hook); in == out allowed
 template <int N, int DIR>
 __global__ void __launch_bounds__(LineCfg<N>::WG)
@@ -1317,6 +1431,13 @@ hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const fl
       hipLaunchKernelGGL(k_range_compress_4096<kAuxStream>, dim3(grid), dim3(256), 0, s, in, out, tab, lines);
     return hipGetLastError();
   }
+  if constexpr (N == 16384 && RD_RC_16384) {
+    if (cached)
+      hipLaunchKernelGGL(k_range_compress_16384<kAuxCached>, dim3(grid), dim3(1024), 0, s, in, out, tab, lines);
+    else
+      hipLaunchKernelGGL(k_range_compress_16384<kAuxStream>, dim3(grid), dim3(1024), 0, s, in, out, tab, lines);
+    return hipGetLastError();
+  }
   if (cached)
     hipLaunchKernelGGL((k_range_compress_pf<N, PF, kAuxCached>), g, b, 0, s, in, out, H, tw, lines, N, 0);
   else
@@ -1369,6 +1490,8 @@ hipError_t occupancy_pf(int* rc, int pad) {
         rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream, true>, LineCfg<N>::WG, 0);
   if constexpr (N == 4096 && RD_RC_4096)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_4096<kAuxStream>, 256, 0);
+  if constexpr (N == 16384 && RD_RC_16384)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_16384<kAuxStream>, 1024, 0);
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream>,
                                                       LineCfg<N>::WG, 0);
 }
@@ -1441,11 +1564,13 @@ int rcmc_any_margin() { return RowStage<0>::MARGIN; }
 template <int N>
 int rc_tab_len() {
   if constexpr (N == 4096 && RD_RC_4096) return kRc4096Tab;
+  if constexpr (N == 16384 && RD_RC_16384) return kRc16kTab;
   return 0;
 }
 template <int N>
 void rc_tab_fill(const float2* H, const float2* roots, float2* out) {
   if constexpr (N == 4096 && RD_RC_4096) rc4096_tab_fill(H, roots, out);
+  if constexpr (N == 16384 && RD_RC_16384) rc16k_tab_fill(H, roots, out);
 }
 
 template <int N>
