@@ -485,6 +485,10 @@ template <> struct XPad<8192, 256> { static constexpr int P = 0, Q = 8192; };
 template <> struct XPad<6000, 1> { static constexpr int P = 1, Q = 200; };
 template <> struct XPad<6000, 10> { static constexpr int P = 2, Q = 300; };
 template <> struct XPad<6000, 60> { static constexpr int P = 4, Q = 600; };
+// 600 = 10 * 6 * 10 on one wave (the sub-line transform of the four-step 6000 kernel): model 30
+// and 36 conflict cycles for the two exchanges, against 168 and 46 with one pad per 16
+template <> struct XPad<600, 1> { static constexpr int P = 1, Q = 100; };
+template <> struct XPad<600, 10> { static constexpr int P = 1, Q = 60; };
 
 template <int N, int NS>
 __device__ __forceinline__ int xpad(int i) {
@@ -1170,6 +1174,11 @@ using L_8_4_8_4_8 = IntList<8, 4, 8, 4, 8>;
 using L_8_16_16_8 = IntList<8, 16, 16, 8>;
 using L_20_15_20 = IntList<20, 15, 20>;  // the earlier 6000-point list (RD_CFG6000 selects it)
 using L_10_6_10_10 = IntList<10, 6, 10, 10>;
+using L_10_6_10 = IntList<10, 6, 10>;  // the 600-point sub-line transform of the four-step 6000 kernel
+template <>
+struct TwLdsBudget<600> {
+  static constexpr int bytes = 8192;  // both inter-pass twiddle sets of 10 * 6 * 10 in LDS
+};
 
 RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, 1, false, false)

@@ -592,6 +592,156 @@ __global__ void __launch_bounds__(1024)
 }
 
 // ------------------------------------------------------------------------------------------
+// Range compression of 6000-sample lines as four steps inside one workgroup of 10 waves, two
+// barriers per line.  With n = t + 600 n_a (t = 60 w + l for wave w and lane l < 60; lanes 60..63
+// idle in the steps outside the sub-line transforms) and k = k_a + 10 k_m:
+//   a: DFT10 over n_a -> k_a, times W_6000^{t k_a}                  (thread t, registers)
+//   exchange: sub-line k_a (element t) to wave k_a                    (workgroup barrier)
+//   m: 600-point transform over t -> k_m in wave k_a: passes 10, 6, 10 (prime-factor DFT10 and
+//      DFT6) with wave-local exchanges in the wave's own LDS row (lane l < 60 ends holding
+//      k_m = l + 60 r)
+// then the filter H[k_a + 10 k_m], the inverse of each sub-line in its wave, the sub-lines back
+// to columns (the second barrier), the conjugate twiddles and the inverse DFT10, leaving
+// y[t + 600 n_a] in thread t.  The hazards are those of the 16384-point kernel.  About 56 KB of
+// LDS, so two workgroups share a CU.  The earlier form (passes 10, 6, 10, 10 over 600 threads)
+// made three workgroup exchanges per direction.
+#ifndef RD_RC_6000
+#define RD_RC_6000 1
+#endif
+#ifndef RD_RC6000_WPE
+#define RD_RC6000_WPE 5
+#endif
+constexpr int kRc6kTab = 10 * 640 + 9 * 640;
+void rc6k_tab_fill(const float2* H, const float2* roots, float2* out) {
+  for (int r = 0; r < 10; ++r)
+    for (int t = 0; t < 640; ++t) {
+      const int w = t >> 6, l = t & 63;
+      out[r * 640 + t] = l < 60 ? H[w + 10 * (l + 60 * r)] : make_float2(0.f, 0.f);
+    }
+  for (int k = 1; k < 10; ++k)
+    for (int t = 0; t < 640; ++t) {
+      const int w = t >> 6, l = t & 63;
+      out[6400 + (k - 1) * 640 + t] = l < 60 ? roots[((60 * w + l) * k) % 6000] : make_float2(1.f, 0.f);
+    }
+}
+
+template <int SAUX, bool HALF = false>
+__global__ void __launch_bounds__(640, RD_RC6000_WPE)
+    k_range_compress_6000(const void* in, void* out, const float2* __restrict__ tab, int64_t lines) {
+  constexpr int M = 600, ROW = lds_len(M), W = 10;
+  using SL = L_10_6_10;
+  using TC = TwCache<M, 64, 1, SL>;
+  static_assert(TC::LDS > 0, "pass twiddles in LDS");
+  __shared__ float2 lds[W * ROW + TC::LDS];
+  RD_POISON_LDS(lds);
+  const int thr = threadIdx.x, wv = thr >> 6, lane = thr & 63;
+  const bool act = lane < 60;
+  const int t = 60 * wv + lane;  // stage-a column (valid where act)
+  float2* row = lds + wv * ROW;
+  const int64_t stride = gridDim.x;
+  constexpr int ES = HALF ? 4 : 8;
+  // element t + 600 n_a of a line: lane offset t * ES (past the resource for idle lanes, so their
+  // loads read zero and their stores are dropped), pass offset n_a * 600 * ES (scalar)
+  const uint32_t off = act ? uint32_t(t) * ES : kBufOff;
+  auto rsrc = [&](const void* base, int64_t line) {
+    const int64_t n = line < lines ? 1 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base) + line * 6000 * ES), 0,
+                                             int(n * 6000 * ES), kBufDword3);
+  };
+  using Pre = typename std::conditional<HALF, unsigned int, float2>::type;
+  auto load = [&](Pre* dst, int64_t line) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(in, line < lines ? line : 0);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      const int r = dft_input_order<10>(i);
+      if constexpr (HALF)
+        dst[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, line < lines ? off : kBufOff, r * 600 * ES, kBufNonTemporal);
+      else
+        dst[r] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs, line < lines ? off : kBufOff,
+                                                                                 r * 600 * ES, kBufNonTemporal));
+    }
+  };
+  Pre nxt[10];
+  load(nxt, blockIdx.x);
+  TC twc;
+  twc.load_all(tab, lds + W * ROW, lane, thr, 640);
+  float2 w1[9];  // W_6000^{t k}, k = 1..9
+#pragma unroll
+  for (int k = 1; k < 10; ++k) w1[k - 1] = tab[6400 + (k - 1) * 640 + thr];
+  __syncthreads();
+  for (int64_t line = blockIdx.x; line < lines; line += stride) {
+    float2 v[MaxRegs<M, 64, SL>::value];  // 12: the radix-6 pass gives some lanes two butterflies
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      if constexpr (HALF)
+        v[i] = h2_to_f2(nxt[i]);
+      else
+        v[i] = nxt[i];
+    }
+    // ---- forward: stage a
+    Dft<10, -1>::run(v);
+#pragma unroll
+    for (int k = 1; k < 10; ++k) v[k] = cmul(v[k], w1[k - 1]);
+    if (act) {
+#pragma unroll
+      for (int k = 0; k < 10; ++k) lds[k * ROW + t] = v[k];
+    }
+    __syncthreads();
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        const int r = dft_input_order<10>(i);
+        v[r] = row[lane + 60 * r];
+      }
+    }
+    PassesCached<M, 64, -1, 1, SL, true>::run(v, row, twc, lane);
+    float2 h[10];
+    {
+      const float2* hl = opaque(tab);
+#pragma unroll
+      for (int r = 0; r < 10; ++r) h[r] = hl[r * 640 + thr];
+    }
+    // ---- filter (carries 1/N)
+#pragma unroll
+    for (int r = 0; r < 10; ++r) v[r] = cmul(v[r], h[r]);
+    // ---- inverse
+    PassesCached<M, 64, +1, 1, SL, true>::run(v, row, twc, lane);
+    load(nxt, line + stride);
+    exchange_sync<true>();
+    if (act) {
+#pragma unroll
+      for (int r = 0; r < 10; ++r) row[lane + 60 * r] = v[r];
+    }
+    __syncthreads();
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        const int k = dft_input_order<10>(i);
+        v[k] = lds[k * ROW + t];
+      }
+    }
+#pragma unroll
+    for (int k = 1; k < 10; ++k) {
+      float2 w = w1[k - 1];
+      w.y = -w.y;
+      v[k] = cmul(v[k], w);
+    }
+    Dft<10, +1>::run(v);
+    {
+      const __amdgpu_buffer_rsrc_t rs = rsrc(out, line);
+#pragma unroll
+      for (int r = 0; r < 10; ++r) {
+        if constexpr (HALF)
+          __builtin_amdgcn_raw_buffer_store_b32(f2_to_h2(v[r]), rs, off, r * 600 * ES, SAUX);
+        else
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(rdf_v2u, v[r]), rs, off, r * 600 * ES, SAUX);
+      }
+    }
+    touch<10>(nxt);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // independent line transforms (azimuth FFT and the transform test hook); in == out allowed
 template <int N, int DIR>
 __global__ void __launch_bounds__(LineCfg<N>::WG)
@@ -1431,6 +1581,13 @@ hipError_t launch_rc_pf(const float2* in, float2* out, const float2* H, const fl
       hipLaunchKernelGGL(k_range_compress_4096<kAuxStream>, dim3(grid), dim3(256), 0, s, in, out, tab, lines);
     return hipGetLastError();
   }
+  if constexpr (N == 6000 && RD_RC_6000) {
+    if (cached)
+      hipLaunchKernelGGL(k_range_compress_6000<kAuxCached>, dim3(grid), dim3(640), 0, s, in, out, tab, lines);
+    else
+      hipLaunchKernelGGL(k_range_compress_6000<kAuxStream>, dim3(grid), dim3(640), 0, s, in, out, tab, lines);
+    return hipGetLastError();
+  }
   if constexpr (N == 16384 && RD_RC_16384) {
     if (cached)
       hipLaunchKernelGGL(k_range_compress_16384<kAuxCached>, dim3(grid), dim3(1024), 0, s, in, out, tab, lines);
@@ -1456,6 +1613,8 @@ void launch_rc_f16_aux(const void* in, void* out, const float2* H, const float2*
                        out, H, tw, lines, n_line, skip);
   else if constexpr (N == 4096 && RD_RC_4096)
     hipLaunchKernelGGL((k_range_compress_4096<SAUX, true>), dim3(grid), dim3(256), 0, s, in, out, tab, lines);
+  else if constexpr (N == 6000 && RD_RC_6000)
+    hipLaunchKernelGGL((k_range_compress_6000<SAUX, true>), dim3(grid), dim3(640), 0, s, in, out, tab, lines);
   else
     hipLaunchKernelGGL((k_range_compress_pf<N, PF, SAUX, false, true>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in,
                        out, H, tw, lines, N, 0);
@@ -1479,6 +1638,8 @@ hipError_t occupancy_f16(int* rc, int pad) {
         rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream, true, true>, LineCfg<N>::WG, 0);
   if constexpr (N == 4096 && RD_RC_4096)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_4096<kAuxStream, true>, 256, 0);
+  if constexpr (N == 6000 && RD_RC_6000)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_6000<kAuxStream, true>, 640, 0);
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
       rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream, false, true>, LineCfg<N>::WG, 0);
 }
@@ -1492,6 +1653,8 @@ hipError_t occupancy_pf(int* rc, int pad) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_4096<kAuxStream>, 256, 0);
   if constexpr (N == 16384 && RD_RC_16384)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_16384<kAuxStream>, 1024, 0);
+  if constexpr (N == 6000 && RD_RC_6000)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_6000<kAuxStream>, 640, 0);
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream>,
                                                       LineCfg<N>::WG, 0);
 }
@@ -1565,12 +1728,14 @@ template <int N>
 int rc_tab_len() {
   if constexpr (N == 4096 && RD_RC_4096) return kRc4096Tab;
   if constexpr (N == 16384 && RD_RC_16384) return kRc16kTab;
+  if constexpr (N == 6000 && RD_RC_6000) return kRc6kTab;
   return 0;
 }
 template <int N>
 void rc_tab_fill(const float2* H, const float2* roots, float2* out) {
   if constexpr (N == 4096 && RD_RC_4096) rc4096_tab_fill(H, roots, out);
   if constexpr (N == 16384 && RD_RC_16384) rc16k_tab_fill(H, roots, out);
+  if constexpr (N == 6000 && RD_RC_6000) rc6k_tab_fill(H, roots, out);
 }
 
 template <int N>
