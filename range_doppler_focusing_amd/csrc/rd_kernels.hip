@@ -593,8 +593,9 @@ __global__ void __launch_bounds__(1024)
 
 // ------------------------------------------------------------------------------------------
 // Range compression of 6000-sample lines as four steps inside one workgroup of 10 waves, two
-// barriers per line.  With n = t + 600 n_a (t = 60 w + l for wave w and lane l < 60; lanes 60..63
-// idle in the steps outside the sub-line transforms) and k = k_a + 10 k_m:
+// barriers per line.  With n = t + 600 n_a (thread t < 600: every wave's line accesses are whole
+// 512-byte segments, 64-byte aligned; threads 600..639 idle outside the sub-line transforms) and
+// k = k_a + 10 k_m:
 //   a: DFT10 over n_a -> k_a, times W_6000^{t k_a}                  (thread t, registers)
 //   exchange: sub-line k_a (element t) to wave k_a                    (workgroup barrier)
 //   m: 600-point transform over t -> k_m in wave k_a: passes 10, 6, 10 (prime-factor DFT10 and
@@ -619,10 +620,7 @@ void rc6k_tab_fill(const float2* H, const float2* roots, float2* out) {
       out[r * 640 + t] = l < 60 ? H[w + 10 * (l + 60 * r)] : make_float2(0.f, 0.f);
     }
   for (int k = 1; k < 10; ++k)
-    for (int t = 0; t < 640; ++t) {
-      const int w = t >> 6, l = t & 63;
-      out[6400 + (k - 1) * 640 + t] = l < 60 ? roots[((60 * w + l) * k) % 6000] : make_float2(1.f, 0.f);
-    }
+    for (int t = 0; t < 640; ++t) out[6400 + (k - 1) * 640 + t] = t < 600 ? roots[(t * k) % 6000] : make_float2(1.f, 0.f);
 }
 
 template <int SAUX, bool HALF = false>
@@ -635,8 +633,9 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
   __shared__ float2 lds[W * ROW + TC::LDS];
   RD_POISON_LDS(lds);
   const int thr = threadIdx.x, wv = thr >> 6, lane = thr & 63;
-  const bool act = lane < 60;
-  const int t = 60 * wv + lane;  // stage-a column (valid where act)
+  const bool act = thr < 600;    // stage-a column t = thr
+  const bool lact = lane < 60;   // lanes of the 600-point sub-line transform
+  const int t = thr;
   float2* row = lds + wv * ROW;
   const int64_t stride = gridDim.x;
   constexpr int ES = HALF ? 4 : 8;
@@ -687,7 +686,7 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
       for (int k = 0; k < 10; ++k) lds[k * ROW + t] = v[k];
     }
     __syncthreads();
-    if (act) {
+    if (lact) {
 #pragma unroll
       for (int i = 0; i < 10; ++i) {
         const int r = dft_input_order<10>(i);
@@ -708,7 +707,7 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
     PassesCached<M, 64, +1, 1, SL, true>::run(v, row, twc, lane);
     load(nxt, line + stride);
     exchange_sync<true>();
-    if (act) {
+    if (lact) {
 #pragma unroll
       for (int r = 0; r < 10; ++r) row[lane + 60 * r] = v[r];
     }
