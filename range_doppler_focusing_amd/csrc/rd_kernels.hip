@@ -491,9 +491,13 @@ __global__ void __launch_bounds__(256, 4)
 // in the last one, so no other barrier is needed.  The filter (in the order the threads hold it)
 // and the twiddles W_16384^{t k} come from the plan's table; the 1024-point pass twiddles live
 // in LDS.  The earlier form (Stockham passes 8, 16, 16, 8 over all 1024 threads) made three
-// workgroup exchanges per direction, twelve barriers per line.
+// workgroup exchanges per direction, twelve barriers per line.  The binary16 form keeps its
+// prefetch packed and only the twiddles W^t, W^2t, W^4t, W^8t, forming the others as products.
 #ifndef RD_RC_16384
 #define RD_RC_16384 1
+#endif
+#ifndef RD_RC_16384_HALF
+#define RD_RC_16384_HALF 1  // binary16 storage through the same kernel (else the Stockham kernel)
 #endif
 constexpr int kRc16kTab = 16 * 1024 + 15 * 1024;
 void rc16k_tab_fill(const float2* H, const float2* roots, float2* out) {
@@ -501,6 +505,27 @@ void rc16k_tab_fill(const float2* H, const float2* roots, float2* out) {
     for (int t = 0; t < 1024; ++t) out[r * 1024 + t] = H[(t >> 6) + 16 * (t & 63) + 1024 * r];
   for (int k = 1; k < 16; ++k)
     for (int t = 0; t < 1024; ++t) out[16384 + (k - 1) * 1024 + t] = roots[(t * k) & 16383];
+}
+
+// x[k] *= w^k (CONJ: conj(w)^k), k = 1..15, with w^k formed from w^1, w^2, w^4, w^8 in w2[0..3]
+// (the base roots pass through an empty asm statement, so the products are formed at every
+// application instead of being hoisted out of a line loop into fifteen live registers)
+template <bool CONJ>
+__device__ __forceinline__ void twiddle16_derived(float2* x, const float2* w2) {
+  float2 p[16];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    const int hb = 1 << ilog2(k);
+    if (hb == k) {
+      p[k] = w2[ilog2(k)];
+      asm volatile("" : "+v"(p[k].x), "+v"(p[k].y));
+    } else {
+      p[k] = cmul(p[hb], p[k - hb]);
+    }
+    float2 w = p[k];
+    if (CONJ) w.y = -w.y;
+    x[k] = cmul(x[k], w);
+  }
 }
 
 template <int SAUX, bool HALF = false>
@@ -526,9 +551,17 @@ __global__ void __launch_bounds__(1024)
   load(nxt, blockIdx.x);
   TC twc;
   twc.load_all(tab, lds + 16 * ROW, lane, t, T);
-  float2 w1[15];  // W_16384^{t k}, k = 1..15
+  // W_16384^{t k}, k = 1..15; the binary16 form holds only k = 1, 2, 4, 8 and forms the others as
+  // products where they are applied (its registers would not fit the full set beside the rest)
+  constexpr int NW = HALF ? 4 : 15;
+  float2 w1[NW];
+  if constexpr (HALF) {
 #pragma unroll
-  for (int k = 1; k < 16; ++k) w1[k - 1] = tab[16384 + (k - 1) * 1024 + t];
+    for (int i = 0; i < NW; ++i) w1[i] = tab[16384 + ((1 << i) - 1) * 1024 + t];
+  } else {
+#pragma unroll
+    for (int k = 1; k < 16; ++k) w1[k - 1] = tab[16384 + (k - 1) * 1024 + t];
+  }
   __syncthreads();
   for (int64_t line = blockIdx.x; line < lines; line += stride) {
     float2 v[16];
@@ -541,8 +574,12 @@ __global__ void __launch_bounds__(1024)
     }
     // ---- forward: stage a
     Dft<16, -1>::run(v);
+    if constexpr (HALF) {
+      twiddle16_derived<false>(v, w1);
+    } else {
 #pragma unroll
-    for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
+      for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
+    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) lds[k * ROW + t] = v[k];
     __syncthreads();
@@ -576,11 +613,15 @@ __global__ void __launch_bounds__(1024)
       const int k = dft_input_order<16>(i);
       v[k] = lds[k * ROW + t];
     }
+    if constexpr (HALF) {
+      twiddle16_derived<true>(v, w1);
+    } else {
 #pragma unroll
-    for (int k = 1; k < 16; ++k) {
-      float2 w = w1[k - 1];
-      w.y = -w.y;
-      v[k] = cmul(v[k], w);
+      for (int k = 1; k < 16; ++k) {
+        float2 w = w1[k - 1];
+        w.y = -w.y;
+        v[k] = cmul(v[k], w);
+      }
     }
     Dft<16, +1>::run(v);
     if constexpr (HALF)
@@ -1614,6 +1655,8 @@ void launch_rc_f16_aux(const void* in, void* out, const float2* H, const float2*
     hipLaunchKernelGGL((k_range_compress_4096<SAUX, true>), dim3(grid), dim3(256), 0, s, in, out, tab, lines);
   else if constexpr (N == 6000 && RD_RC_6000)
     hipLaunchKernelGGL((k_range_compress_6000<SAUX, true>), dim3(grid), dim3(640), 0, s, in, out, tab, lines);
+  else if constexpr (N == 16384 && RD_RC_16384 && RD_RC_16384_HALF)
+    hipLaunchKernelGGL((k_range_compress_16384<SAUX, true>), dim3(grid), dim3(1024), 0, s, in, out, tab, lines);
   else
     hipLaunchKernelGGL((k_range_compress_pf<N, PF, SAUX, false, true>), dim3(grid), dim3(LineCfg<N>::WG), 0, s, in,
                        out, H, tw, lines, N, 0);
@@ -1639,6 +1682,8 @@ hipError_t occupancy_f16(int* rc, int pad) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_4096<kAuxStream, true>, 256, 0);
   if constexpr (N == 6000 && RD_RC_6000)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_6000<kAuxStream, true>, 640, 0);
+  if constexpr (N == 16384 && RD_RC_16384 && RD_RC_16384_HALF)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(rc, k_range_compress_16384<kAuxStream, true>, 1024, 0);
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(
       rc, k_range_compress_pf<N, RD_RC_PREFETCH && LineCfg<N>::PF, kAuxStream, false, true>, LineCfg<N>::WG, 0);
 }
