@@ -169,6 +169,34 @@ def test_range_compression_every_length(torch_dev, rdf, n, lines):
     check_stage(f"[range] n={n} lines={lines}", rc, O.range_compress(echo, params), STAGE_TOL)
 
 
+# Line counts above one round of the persistent grid and not a multiple of it (4096: 1024
+# workgroups; 6000: 512; 16384: 256 on 256 CUs): some workgroups take one line more than others,
+# and every line crosses the loop's prefetch, exchange and table paths at least twice.
+@pytest.mark.parametrize("n,lines", [(4096, 1531), (6000, 777), (16384, 301)], ids=lambda v: str(v))
+def test_range_compression_persistent_ragged(torch_dev, rdf, n, lines):
+    """The persistent range kernels over more lines than one grid round (float32 and binary16):
+    every line against the oracle, element by element per line; in place equals out of place."""
+    torch = torch_dev
+    rng = np.random.default_rng(5000 + n + lines)
+    fs = 120e6
+    params = dict(Na=lines, Nr=n, pulse_s=(n // 3) / fs, bandwidth_hz=90e6, fs_hz=fs, range_window=1)
+    echo = (rng.standard_normal((lines, n)) + 1j * rng.standard_normal((lines, n))).astype(np.complex64)
+    log(f"[range] persistent ragged: n={n} lines={lines}")
+    ref = O.range_compress(echo, params)
+    with rdf.Plan(**params) as plan:
+        x = dev(torch, echo)
+        rc = plan.range_compress(x).cpu().numpy()
+        plan.range_compress(x, out=x)
+        torch.cuda.synchronize()
+        assert np.array_equal(x.cpu().numpy(), rc)
+        check_stage(f"[range] persistent n={n} lines={lines}", rc, ref, STAGE_TOL)
+        eh = to_half(echo)
+        xh = torch.from_numpy(eh).to("cuda")
+        rch = plan.range_compress_f16(xh).cpu().numpy()
+    err = check_half(rch, O.range_compress(from_half(eh), params))
+    log(f"[range f16] persistent n={n} lines={lines} rel-L2 {err:.2e}")
+
+
 # (line length, replica length): padded transform lengths M = nextpow2(max(256, n + L - 1))
 # 256, 512, 1024, 2048, 4096, 8192, 16384, and replicas of one sample up to the whole line
 ANY_LENGTHS = [(1, 1), (7, 7), (127, 42), (129, 43), (300, 100), (700, 233), (1000, 333),
