@@ -142,9 +142,9 @@ double bessel_i0(double z) {
   return sum;
 }
 
-// Each b_j is interpolated at 9 Chebyshev points of [0, 1] (degree 8; max error ~5e-9 of
-// max|b|) and expanded in monomials of x = f - 1/2; only taps j = 0, -1, -2, -3 are fitted, their
-// even and odd parts serving the mirrored taps too.
+// Each b_j is interpolated at kRcmcDeg + 1 Chebyshev points of [0, 1] and expanded in monomials
+// of x = f - 1/2; only taps j = 0, -1, -2, -3 are fitted, their even and odd parts serving the
+// mirrored taps too.
 void rcmc_weight_polys(double beta, RcmcPoly* out) {
   constexpr int D = kRcmcDeg, M = D + 1;
   const double half = kRcmcTaps / 2.0;

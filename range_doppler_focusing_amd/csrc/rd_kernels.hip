@@ -1008,24 +1008,29 @@ __device__ __forceinline__ void rcmc_chunk(float2* v, const float2* my, const Az
         sincospif(2.0f * float(c1 - rint(c1)), &sn, &cs);
         rot = make_float2(cs, sn);
       }
+      // the shift x = alpha + n beta (n = n0 + j + r NB; x >= 0) in 32.32 fixed point: rounded
+      // once from float64 at r = 0, then advanced by the rounded step NB beta (accumulated error
+      // below 1e-8 samples over a thread's outputs); the high word is floor(x), the low word the
+      // fraction
+      int64_t X = static_cast<int64_t>(rint((alpha + double(n0 + j) * beta) * 4294967296.0));
+      const int64_t S = static_cast<int64_t>(rint(double(G::NB) * beta * 4294967296.0));
 #pragma unroll
-      for (int r = 0; r < R0; ++r) {
+      for (int r = 0; r < R0; ++r, X += S) {
         const int m = j + r * G::NB;  // position in the chunk
-        const double x = alpha + double(n0 + m) * beta;
-        const double fl = floor(x);
-        const float xf = float(x - fl) - 0.5f;
+        const int fl = static_cast<int>(X >> 32);
+        const float xf = fmaf(float(static_cast<uint32_t>(X)), 0x1p-32f, -0.5f);
         const float y = xf * xf;
-        const float2* tap = my + (m + int(fl));  // tap t reads sample n0 + m + fl + t - 3
+        const float2* tap = my + (m + fl);  // tap t reads sample n0 + m + fl + t - 3
         float2 acc = make_float2(0.f, 0.f);
         float es = 0.f;  // sum of the even parts: the weights sum to 2 es
 #pragma unroll
         for (int q = 0; q < kRcmcTaps / 2; ++q) {
-          float e = c.w.even[q][kRcmcDeg / 2];
+          float e = c.w.even[q][kRcmcEven - 1];
 #pragma unroll
-          for (int mm = kRcmcDeg / 2 - 1; mm >= 0; --mm) e = fmaf(e, y, c.w.even[q][mm]);
-          float o = c.w.odd[q][kRcmcDeg / 2 - 1];
+          for (int mm = kRcmcEven - 2; mm >= 0; --mm) e = fmaf(e, y, c.w.even[q][mm]);
+          float o = c.w.odd[q][kRcmcOdd - 1];
 #pragma unroll
-          for (int mm = kRcmcDeg / 2 - 2; mm >= 0; --mm) o = fmaf(o, y, c.w.odd[q][mm]);
+          for (int mm = kRcmcOdd - 2; mm >= 0; --mm) o = fmaf(o, y, c.w.odd[q][mm]);
           const float wa = fmaf(xf, o, e);    // tap j = -q   (t = 3 - q)
           const float wb = fmaf(-xf, o, e);   // tap j = 1 + q (t = 4 + q)
           const float2 sa = tap[3 - q], sb = tap[4 + q];
@@ -1310,12 +1315,12 @@ __global__ void __launch_bounds__(LineCfg<N>::WG)
           float es = 0.f;
 #pragma unroll
           for (int q = 0; q < kRcmcTaps / 2; ++q) {
-            float e = w.even[q][kRcmcDeg / 2];
+            float e = w.even[q][kRcmcEven - 1];
 #pragma unroll
-            for (int mm = kRcmcDeg / 2 - 1; mm >= 0; --mm) e = fmaf(e, y, w.even[q][mm]);
-            float o = w.odd[q][kRcmcDeg / 2 - 1];
+            for (int mm = kRcmcEven - 2; mm >= 0; --mm) e = fmaf(e, y, w.even[q][mm]);
+            float o = w.odd[q][kRcmcOdd - 1];
 #pragma unroll
-            for (int mm = kRcmcDeg / 2 - 2; mm >= 0; --mm) o = fmaf(o, y, w.odd[q][mm]);
+            for (int mm = kRcmcOdd - 2; mm >= 0; --mm) o = fmaf(o, y, w.odd[q][mm]);
             const float wa = fmaf(xf, o, e);
             const float wb = fmaf(-xf, o, e);
             const float2 sa = tap[3 - q], sb = tap[4 + q];

@@ -167,9 +167,9 @@ static void check_interpolator() {
     rcmc_weight_polys(beta, &P);
     auto poly = [&](int q, double x, bool mirror) {
       double e = 0, o = 0, x2 = x * x, pw = 1;
-      for (int i = 0; i <= rdf::kRcmcDeg / 2; ++i, pw *= x2) e += P.even[q][i] * pw;
+      for (int i = 0; i < rdf::kRcmcEven; ++i, pw *= x2) e += P.even[q][i] * pw;
       pw = 1;
-      for (int i = 0; i < rdf::kRcmcDeg / 2; ++i, pw *= x2) o += P.odd[q][i] * pw;
+      for (int i = 0; i < rdf::kRcmcOdd; ++i, pw *= x2) o += P.odd[q][i] * pw;
       return mirror ? e - x * o : e + x * o;
     };
     for (int s = 0; s <= 64; ++s) {
