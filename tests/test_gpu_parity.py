@@ -405,12 +405,12 @@ def test_range_compression_large_sampled_lines(torch_dev, rdf):
 
 
 # ------------------------------------------------------------------------------ full chain
-def check_targets(img, ref_img, targets):
+def check_targets(img, ref_img, targets, axes=("range", "azimuth")):
     for (m, n) in targets:
         pk = M.peak_near(img, m, n)
         assert pk == M.peak_near(ref_img, m, n), (m, n)
-        got, want = M.point_target(img, *pk), M.point_target(ref_img, *pk)
-        for axis in ("range", "azimuth"):
+        got, want = M.point_target(img, *pk, axes=axes), M.point_target(ref_img, *pk, axes=axes)
+        for axis in axes:
             for key in ("pslr_db", "islr_db"):
                 a, b = got[axis][key], want[axis][key]
                 if np.isinf(a) and a == b:        # no sidelobe in the window on either side
@@ -724,13 +724,15 @@ WK_BIG = SceneConfig(name="wk_large_migration_4096x1024", Na=4096, Nr=1024, puls
                      sep_range=9, sep_az=100)
 WK_C3AZ = C3.with_(name="wk_4096x512", Nr=512, pulse_s=1e-6, n_targets=3, noise_power=0.01)
 WK_6000 = C3.with_(name="wk_512x6000", Na=512, Nr=6000, n_targets=4)
+# 16384-sample rows on the 16384 x 16384 scene's platform, few enough pulses for the oracle
+WK_16K = C5.with_(name="wk_256x16384", Na=256, n_targets=3)
 
 
 def wk_ref_bin(cfg) -> int:
     return int(round((cfg.r_ref_m - cfg.range_bin0_m) / cfg.dr))
 
 
-@pytest.mark.parametrize("cfg", [C1, WK_BIG, WK_C3AZ, WK_6000, WK_800, WK_997], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, WK_BIG, WK_C3AZ, WK_6000, WK_800, WK_997, WK_16K], ids=lambda c: c.name)
 def test_omega_k_matches_oracle(torch_dev, rdf, cfg):
     """rd_omega_k against the oracle at the scene's reference bin and at bin 0; in place gives
     the same bits; targets at the oracle's pixels with the same PSLR / ISLR."""
@@ -749,7 +751,9 @@ def test_omega_k_matches_oracle(torch_dev, rdf, cfg):
             want = O.omega_k(sc.echo, p, ref)
             check_stage(f"[omega-k] {cfg.name} ref_bin={ref}", got, want, IMAGE_TOL)
             if ref == wk_ref_bin(cfg):
-                check_targets(got, want, sc.targets)
+                # 256 pulses of a platform whose aperture spans 8192: the azimuth response is wider
+                # than the metric window, so only the peak and the range cut are compared there
+                check_targets(got, want, sc.targets, axes=("range",) if cfg is WK_16K else ("range", "azimuth"))
 
 
 def test_omega_k_full_airborne_scene(torch_dev, rdf):
@@ -830,7 +834,7 @@ def test_omega_k_error_paths(torch_dev, rdf):
         assert ei.value.status == -2
 
 
-@pytest.mark.parametrize("cfg", [C1, C3, WK_C3AZ, WK_6000, WK_800, WK_997], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, C3, WK_C3AZ, WK_6000, WK_800, WK_997, WK_16K], ids=lambda c: c.name)
 def test_omega_k_f16(torch_dev, rdf, cfg):
     """rd_omega_k_f16: the image divided by Na against the oracle on the same binary16 echo
     (five stored stages: two forward azimuth steps, the row stage, two inverse steps; within the
