@@ -1458,29 +1458,31 @@ hipError_t launch_corner_turn(const float2* in, float2* out, int64_t rows, int64
 // (a = x - V m/PRF formed in float64); the pixel's constant phase 2 r / lambda (turns) and its
 // bin offset (r - range_bin0)/dr are split in float64 once per pixel, so the per-pulse float32
 // quantities (delta / dr, 2 delta / lambda) stay small; partial sums of 32 pulses go to float64.
-// One pulse's contribution to a pixel, added to (sr, si).
+// One pulse's contribution to a pixel, added to (sr, si).  xa is the pixel's along-track offset
+// from the platform at this pulse, x - V m / PRF, carried in float64 from pulse to pulse (one add
+// instead of forming it from m).  ib8 is 8 times the pixel's integer bin offset (clamped to
+// [-4 Nr, 4 Nr]); the bin t is clamped to 5 Nr + 2, so every index past the line stays past it
+// (ib + t >= Nr + 2) without overflowing 32 bits.
 template <bool NATIVE_SINCOS>
-__device__ __forceinline__ void bp_pulse(const float2* __restrict__ rc, const BpConst& c, int m,
-                                         double x, float rf, float fb, int ib, float k_bin,
-                                         float k_turn, uint32_t line_bytes, float& sr, float& si) {
-  const float a = float(fma(-double(m), c.step, x));
+__device__ __forceinline__ void bp_pulse(const float2* __restrict__ rc, const BpConst& c, int m, double& xa,
+                                         float rf, float fb, int ib8, float k_bin, float k_turn, float t_max,
+                                         uint32_t line_bytes, float& sr, float& si) {
+  const float a = float(xa);
+  xa -= c.step;
   const float a2 = a * a;
   const float d = __builtin_amdgcn_sqrtf(fmaf(rf, rf, a2));   // only in the denominator below
   const float delta = a2 * __builtin_amdgcn_rcpf(rf + d);     // d - r without cancellation
-  const float t = fmaf(delta, k_bin, fb);
+  const float t = fminf(fmaf(delta, k_bin, fb), t_max);       // >= 0: delta >= 0, fb in [0, 1)
   const float fl = floorf(t);
   const float w = t - fl;
-  // both samples outside the line read zero: clamp to -2 (both offsets wrap far past the line)
-  // or Nr (both at or past its end); idx = -1 reads zero and bin 0
-  int idx = ib + int(fl);
-  idx = idx < -2 ? -2 : (idx > c.Nr ? c.Nr : idx);
   const __amdgpu_buffer_rsrc_t line = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float2*>(rc + int64_t(m) * c.Nr), 0, int(line_bytes), kBufDword3);
-  // Two 8-byte loads, each range-checked on its own (a negative index wraps far past the line
-  // and reads zero; bin Nr reads zero).  The second offset is hidden from the compiler, which would
-  // otherwise fuse the pair into one 16-byte load whose range check is all-or-nothing and would
-  // drop the last in-line sample.
-  const uint32_t off = uint32_t(idx) * 8u;
+  // Two 8-byte loads at bins idx and idx + 1 (idx = ib + fl), each range-checked on its own: a
+  // negative idx wraps to an offset far past the line (>= 2^32 - 32 Nr) and reads zero, so idx = -1
+  // reads zero and bin 0; idx >= Nr reads zero twice.  The second offset is hidden from the
+  // compiler, which would otherwise fuse the pair into one 16-byte load whose range check is
+  // all-or-nothing and would drop the last in-line sample.
+  const uint32_t off = uint32_t(ib8) + (uint32_t(int(fl)) << 3);
   uint32_t off1 = off + 8u;
   asm volatile("" : "+v"(off1));
   const float2 s0 = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(line, off, 0, 0));
@@ -1505,16 +1507,17 @@ __global__ void __launch_bounds__(256)
   const int j = int(blockIdx.x) * 64 + int(threadIdx.x & 63);
   const int i = int(blockIdx.y) * 4 + int(threadIdx.x >> 6);
   const double r = c.r0 + double(j) * c.drp;
-  const double x = c.x0 + double(i) * c.dx;
+  double xa = c.x0 + double(i) * c.dx;
   // bin offset of the pixel's closest approach: integer part ib (clamped far outside the line,
   // where every sample reads zero anyway) and fraction fb
   double b0 = (r - c.rb0) * c.inv_dr;
   b0 = b0 < -4.0 * c.Nr ? -4.0 * c.Nr : (b0 > 4.0 * c.Nr ? 4.0 * c.Nr : b0);
   const double ibd = floor(b0);
-  const int ib = int(ibd);
+  const int ib8 = int(ibd) * 8;
   const float fb = float(b0 - ibd);
   const float rf = float(r);
   const float k_bin = float(c.inv_dr), k_turn = float(c.two_over_lam);
+  const float t_max = float(5 * c.Nr + 2);
   const uint32_t line_bytes = uint32_t(c.Nr) * 8u;
   double acc_r = 0.0, acc_i = 0.0;
   constexpr int BLK = 32;  // pulses summed in float32 before each float64 accumulation
@@ -1523,14 +1526,14 @@ __global__ void __launch_bounds__(256)
     float sr = 0.f, si = 0.f;
 #pragma unroll
     for (int k = 0; k < BLK; ++k)
-      bp_pulse<NATIVE_SINCOS>(rc, c, m0 + k, x, rf, fb, ib, k_bin, k_turn, line_bytes, sr, si);
+      bp_pulse<NATIVE_SINCOS>(rc, c, m0 + k, xa, rf, fb, ib8, k_bin, k_turn, t_max, line_bytes, sr, si);
     acc_r += double(sr);
     acc_i += double(si);
   }
   {
     float sr = 0.f, si = 0.f;
     for (int m = m0; m < c.Na; ++m)
-      bp_pulse<NATIVE_SINCOS>(rc, c, m, x, rf, fb, ib, k_bin, k_turn, line_bytes, sr, si);
+      bp_pulse<NATIVE_SINCOS>(rc, c, m, xa, rf, fb, ib8, k_bin, k_turn, t_max, line_bytes, sr, si);
     acc_r += double(sr);
     acc_i += double(si);
   }
