@@ -1508,8 +1508,10 @@ __global__ void __launch_bounds__(256)
   const int i = int(blockIdx.y) * 4 + int(threadIdx.x >> 6);
   const double r = c.r0 + double(j) * c.drp;
   double xa = c.x0 + double(i) * c.dx;
-  // bin offset of the pixel's closest approach: integer part ib (clamped far outside the line,
-  // where every sample reads zero anyway) and fraction fb
+  // bin offset of the pixel's closest approach: integer part ib and fraction fb.  ib is clamped to
+  // [-4 Nr, 4 Nr] so that the index arithmetic stays in 32 bits; a pixel beyond the clamp reads zero,
+  // which is the definition's value unless its range curve still reaches the line, a range excess
+  // of more than 3 Nr bins, far outside the float32 domain of the excess and its phase.
   double b0 = (r - c.rb0) * c.inv_dr;
   b0 = b0 < -4.0 * c.Nr ? -4.0 * c.Nr : (b0 > 4.0 * c.Nr ? 4.0 * c.Nr : b0);
   const double ibd = floor(b0);
