@@ -491,8 +491,8 @@ __global__ void __launch_bounds__(256, 4)
 // in the last one, so no other barrier is needed.  The filter (in the order the threads hold it)
 // and the twiddles W_16384^{t k} come from the plan's table; the 1024-point pass twiddles live
 // in LDS.  The earlier form (Stockham passes 8, 16, 16, 8 over all 1024 threads) made three
-// workgroup exchanges per direction, twelve barriers per line.  The binary16 form keeps its
-// prefetch packed and only the twiddles W^t, W^2t, W^4t, W^8t, forming the others as products.
+// workgroup exchanges per direction, twelve barriers per line.  Only the twiddles W^t, W^2t, W^4t,
+// W^8t are held, the others formed as products; the binary16 form keeps its prefetch packed.
 #ifndef RD_RC_16384
 #define RD_RC_16384 1
 #endif
@@ -551,17 +551,15 @@ __global__ void __launch_bounds__(1024)
   load(nxt, blockIdx.x);
   TC twc;
   twc.load_all(tab, lds + 16 * ROW, lane, t, T);
-  // W_16384^{t k}, k = 1..15; the binary16 form holds only k = 1, 2, 4, 8 and forms the others as
-  // products where they are applied (its registers would not fit the full set beside the rest)
-  constexpr int NW = HALF ? 4 : 15;
+  // W_16384^{t k}: only k = 1, 2, 4, 8 are held and the other eleven are formed as products where
+  // they are applied.  The registers this frees let the next line's loads go out earlier: after
+  // the filter multiply (float32: 115 VGPRs; holding all fifteen took 125 and put the loads after
+  // the inverse sub-line transform, 1.8% slower) or, with the binary16 prefetch packed, right
+  // after the first exchange (117 VGPRs; 4% faster than after the inverse sub-line transform).
+  constexpr int NW = 4;
   float2 w1[NW];
-  if constexpr (HALF) {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) w1[i] = tab[16384 + ((1 << i) - 1) * 1024 + t];
-  } else {
-#pragma unroll
-    for (int k = 1; k < 16; ++k) w1[k - 1] = tab[16384 + (k - 1) * 1024 + t];
-  }
+  for (int i = 0; i < NW; ++i) w1[i] = tab[16384 + ((1 << i) - 1) * 1024 + t];
   __syncthreads();
   for (int64_t line = blockIdx.x; line < lines; line += stride) {
     float2 v[16];
@@ -574,12 +572,7 @@ __global__ void __launch_bounds__(1024)
     }
     // ---- forward: stage a
     Dft<16, -1>::run(v);
-    if constexpr (HALF) {
-      twiddle16_derived<false>(v, w1);
-    } else {
-#pragma unroll
-      for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
-    }
+    twiddle16_derived<false>(v, w1);
 #pragma unroll
     for (int k = 0; k < 16; ++k) lds[k * ROW + t] = v[k];
     __syncthreads();
@@ -588,6 +581,7 @@ __global__ void __launch_bounds__(1024)
       const int r = dft_input_order<16>(i);
       v[r] = row[lane + 64 * r];
     }
+    if constexpr (HALF) load(nxt, line + stride);
     PassesCached<M, 64, -1, 1, SL, true>::run(v, row, twc, lane);
     // the filter for this thread's outputs (the other waves cover the cache latency)
     float2 h[16];
@@ -599,11 +593,9 @@ __global__ void __launch_bounds__(1024)
     // ---- filter (carries 1/N)
 #pragma unroll
     for (int r = 0; r < 16; ++r) v[r] = cmul(v[r], h[r]);
+    if constexpr (!HALF) load(nxt, line + stride);
     // ---- inverse
     PassesCached<M, 64, +1, 1, SL, true>::run(v, row, twc, lane);
-    // The next line's loads go out here, after the sub-line transforms, whose registers they
-    // would otherwise share.
-    load(nxt, line + stride);
     exchange_sync<true>();
 #pragma unroll
     for (int r = 0; r < 16; ++r) row[lane + 64 * r] = v[r];
@@ -613,16 +605,7 @@ __global__ void __launch_bounds__(1024)
       const int k = dft_input_order<16>(i);
       v[k] = lds[k * ROW + t];
     }
-    if constexpr (HALF) {
-      twiddle16_derived<true>(v, w1);
-    } else {
-#pragma unroll
-      for (int k = 1; k < 16; ++k) {
-        float2 w = w1[k - 1];
-        w.y = -w.y;
-        v[k] = cmul(v[k], w);
-      }
-    }
+    twiddle16_derived<true>(v, w1);
     Dft<16, +1>::run(v);
     if constexpr (HALF)
       store_line_h<N, T, 16, SAUX>(v, LineIOh(out, N, line, 1, lines), 0, t);
