@@ -275,17 +275,41 @@ void rc4096_tab_fill(const float2* H, const float2* roots, float2* out) {
 
 // Occupancy: four workgroups per CU (four waves per SIMD, 1024 workgroups, exactly four lines
 // each at 4096 lines) need at most 128 VGPRs.  Only the line (32 registers) and the twiddles W_4096
-// (30) are live across a whole line; the filter (32) is reloaded from the table every line before
-// stage c, and the next line's prefetch (32) is issued after the filter multiply, so the two never
-// coexist (114 VGPRs; the binary16 form keeps its prefetch packed, 16 registers, and fits in 128
-// without spilling).  Measured on MI355X (kernel trace, 3 x ~5300 launches, alternating
+// (30, or 8 where four are held) are live across a whole line; the filter (32) is reloaded from the
+// table every line before stage c, and the next line's prefetch (32) is issued after the filter
+// multiply, so the two never coexist (114 VGPRs with fifteen twiddles held, 96 with four; the
+// binary16 form keeps its prefetch packed, 16 registers, and fits in 128 without spilling).
+// Issuing the prefetch earlier (after the first exchange, or before stage a) measured 1.5-4 us
+// slower per launch.  Measured on MI355X (kernel trace, 3 x ~5300 launches, alternating
 // on one GPU): 55.1 us per launch against 56.8 us for the three-wave form that held filter and
 // prefetch for the whole line (166 VGPRs); reloading the filter at three waves alone is slower
 // (59-60 us).
 #ifndef RD_RC4096_MFMA
 #define RD_RC4096_MFMA 0
 #endif
+
 typedef float rdf_v4f __attribute__((ext_vector_type(4)));
+// x[k] *= w^k (CONJ: conj(w)^k), k = 1..15, with w^k formed from w^1, w^2, w^4, w^8 in w2[0..3]
+// (the base roots pass through an empty asm statement, so the products are formed at every
+// application instead of being hoisted out of a line loop into fifteen live registers)
+template <bool CONJ>
+__device__ __forceinline__ void twiddle16_derived(float2* x, const float2* w2) {
+  float2 p[16];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    const int hb = 1 << ilog2(k);
+    if (hb == k) {
+      p[k] = w2[ilog2(k)];
+      asm volatile("" : "+v"(p[k].x), "+v"(p[k].y));
+    } else {
+      p[k] = cmul(p[hb], p[k - hb]);
+    }
+    float2 w = p[k];
+    if (CONJ) w.y = -w.y;
+    x[k] = cmul(x[k], w);
+  }
+}
+
 template <int SAUX, bool HALF = false>
 __global__ void __launch_bounds__(256, 4)
     k_range_compress_4096(const void* in, void* out, const float2* __restrict__ tab,
@@ -310,8 +334,17 @@ __global__ void __launch_bounds__(256, 4)
   };
   Pre nxt[16];
   load(nxt, blockIdx.x);
-  float2 w1[15];  // W_4096^{t k}, k = 1..15
-  if constexpr (RD_RC4096_TWTAB) {
+  // W_4096^{t k}, k = 1..15.  The float32 form holds only k = 1, 2, 4, 8 and forms the others as
+  // products where they are applied (96 instead of 114 VGPRs; 55.8-56.2 against 56.5-56.7 us per
+  // launch, interleaved runs); the binary16 form holds all fifteen (its products measured 0.3 us
+  // slower).
+  constexpr bool DER = !HALF;
+  float2 w1[15];
+  if constexpr (DER) {
+    if (t < 240) tw2[t] = tab[4096 + 15 * 256 + t];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w1[i] = tab[4096 + ((1 << i) - 1) * 256 + t];
+  } else if constexpr (RD_RC4096_TWTAB) {
     if (t < 240) tw2[t] = tab[4096 + 15 * 256 + t];
 #pragma unroll
     for (int k = 1; k < 16; ++k) w1[k - 1] = tab[4096 + (k - 1) * 256 + t];
@@ -332,8 +365,12 @@ __global__ void __launch_bounds__(256, 4)
     }
     // ---- forward
     Dft<16, -1>::run(v);
+    if constexpr (DER) {
+      twiddle16_derived<false>(v, w1);
+    } else {
 #pragma unroll
-    for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
+      for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
+    }
     // No barrier before these writes: thread t writes element t of every region, exactly the
     // elements it alone read in the previous line's last exchange (its LDS accesses execute in
     // order), and every other access to them lies on the far side of the barriers below.
@@ -462,11 +499,15 @@ __global__ void __launch_bounds__(256, 4)
       const int k = dft_input_order<16>(i);
       v[k] = lds[REG * k + t];
     }
+    if constexpr (DER) {
+      twiddle16_derived<true>(v, w1);
+    } else {
 #pragma unroll
-    for (int k = 1; k < 16; ++k) {
-      float2 w = w1[k - 1];
-      w.y = -w.y;
-      v[k] = cmul(v[k], w);
+      for (int k = 1; k < 16; ++k) {
+        float2 w = w1[k - 1];
+        w.y = -w.y;
+        v[k] = cmul(v[k], w);
+      }
     }
     Dft<16, +1>::run(v);
     if constexpr (HALF)
@@ -505,27 +546,6 @@ void rc16k_tab_fill(const float2* H, const float2* roots, float2* out) {
     for (int t = 0; t < 1024; ++t) out[r * 1024 + t] = H[(t >> 6) + 16 * (t & 63) + 1024 * r];
   for (int k = 1; k < 16; ++k)
     for (int t = 0; t < 1024; ++t) out[16384 + (k - 1) * 1024 + t] = roots[(t * k) & 16383];
-}
-
-// x[k] *= w^k (CONJ: conj(w)^k), k = 1..15, with w^k formed from w^1, w^2, w^4, w^8 in w2[0..3]
-// (the base roots pass through an empty asm statement, so the products are formed at every
-// application instead of being hoisted out of a line loop into fifteen live registers)
-template <bool CONJ>
-__device__ __forceinline__ void twiddle16_derived(float2* x, const float2* w2) {
-  float2 p[16];
-#pragma unroll
-  for (int k = 1; k < 16; ++k) {
-    const int hb = 1 << ilog2(k);
-    if (hb == k) {
-      p[k] = w2[ilog2(k)];
-      asm volatile("" : "+v"(p[k].x), "+v"(p[k].y));
-    } else {
-      p[k] = cmul(p[hb], p[k - hb]);
-    }
-    float2 w = p[k];
-    if (CONJ) w.y = -w.y;
-    x[k] = cmul(x[k], w);
-  }
 }
 
 template <int SAUX, bool HALF = false>
