@@ -274,29 +274,29 @@ void rc4096_tab_fill(const float2* H, const float2* roots, float2* out) {
 }
 
 // Occupancy: four workgroups per CU (four waves per SIMD, 1024 workgroups, exactly four lines
-// each at 4096 lines) need at most 128 VGPRs.  Only the line (32 registers) and the twiddles W_4096
-// (30, or 8 where four are held) are live across a whole line; the filter (32) is reloaded from the
-// table every line before stage c, and the next line's prefetch (32) is issued after the filter
-// multiply, so the two never coexist (114 VGPRs with fifteen twiddles held, 96 with four; the
-// binary16 form keeps its prefetch packed, 16 registers, and fits in 128 without spilling).
-// Issuing the prefetch earlier (after the first exchange, or before stage a) measured 1.5-4 us
-// slower per launch.  Measured on MI355X (kernel trace, 3 x ~5300 launches, alternating
-// on one GPU): 55.1 us per launch against 56.8 us for the three-wave form that held filter and
-// prefetch for the whole line (166 VGPRs); reloading the filter at three waves alone is slower
-// (59-60 us).
+// each at 4096 lines) need at most 128 VGPRs.  Live across every line: the line (32 registers),
+// the filter (32, loaded once), four of the fifteen twiddles W_4096^{t k} (8; the other eleven are
+// formed as products where they are applied) and, from the filter multiply on, the next line's
+// prefetch (32): 126 VGPRs (binary16: 111, its prefetch packed at one register a sample).
+// Measured on MI355X (interleaved runs, 200 launches each): 52.7-53.3 us per launch against
+// 55.6-56.1 us when the fifteen twiddles are held and the filter is reloaded from the table before
+// stage c of every line (114 VGPRs), whose reads cost 128 MB of L2 traffic per launch; 56.8 us for
+// the three-wave form that held the filter and fifteen twiddles (166 VGPRs).  Issuing the prefetch
+// earlier (after the first exchange, or before stage a) measured 1.5-4 us slower.
 #ifndef RD_RC4096_MFMA
 #define RD_RC4096_MFMA 0
 #endif
 
 typedef float rdf_v4f __attribute__((ext_vector_type(4)));
-// x[k] *= w^k (CONJ: conj(w)^k), k = 1..15, with w^k formed from w^1, w^2, w^4, w^8 in w2[0..3]
+// x[k] *= w^k (CONJ: conj(w)^k), k = 1..K-1 (K <= 16), with w^k formed from w^1, w^2, w^4, w^8 in
+// w2[0..3]
 // (the base roots pass through an empty asm statement, so the products are formed at every
 // application instead of being hoisted out of a line loop into fifteen live registers)
-template <bool CONJ>
+template <bool CONJ, int K = 16>
 __device__ __forceinline__ void twiddle16_derived(float2* x, const float2* w2) {
-  float2 p[16];
+  float2 p[K];
 #pragma unroll
-  for (int k = 1; k < 16; ++k) {
+  for (int k = 1; k < K; ++k) {
     const int hb = 1 << ilog2(k);
     if (hb == k) {
       p[k] = w2[ilog2(k)];
@@ -334,11 +334,9 @@ __global__ void __launch_bounds__(256, 4)
   };
   Pre nxt[16];
   load(nxt, blockIdx.x);
-  // W_4096^{t k}, k = 1..15.  The float32 form holds only k = 1, 2, 4, 8 and forms the others as
-  // products where they are applied (96 instead of 114 VGPRs; 55.8-56.2 against 56.5-56.7 us per
-  // launch, interleaved runs); the binary16 form holds all fifteen (its products measured 0.3 us
-  // slower).
-  constexpr bool DER = !HALF;
+  // W_4096^{t k}, k = 1..15: only k = 1, 2, 4, 8 are held and the others are formed as products
+  // where they are applied, which leaves the registers to hold the filter across lines
+  constexpr bool DER = !RD_RC4096_MFMA;
   float2 w1[15];
   if constexpr (DER) {
     if (t < 240) tw2[t] = tab[4096 + 15 * 256 + t];
@@ -353,6 +351,12 @@ __global__ void __launch_bounds__(256, 4)
 #pragma unroll
     for (int k = 1; k < 16; ++k) w1[k - 1] = root_of<4096>((t * k) & 4095);
   }
+#if !RD_RC4096_MFMA
+  // the filter H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l), held for every line
+  float2 h[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) h[r] = tab[r * 256 + t];
+#endif
   __syncthreads();
   for (int64_t line = blockIdx.x; line < lines; line += stride) {
     float2 v[16];
@@ -447,15 +451,6 @@ __global__ void __launch_bounds__(256, 4)
       exchange_sync<true>();
     }
 #else
-    // The filter H[k0 + 16 k1 + 256 r] for this thread's (k0, k1) = (g, l), read from the
-    // cache-resident table once per line, one pass before its use, instead of being held in
-    // registers across lines (see the occupancy note above the kernel).
-    float2 h[16];
-    {
-      const float2* hl = opaque(tab);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) h[r] = hl[r * 256 + t];
-    }
     exchange_sync<true>();
 #pragma unroll
     for (int k = 0; k < 16; ++k) lds[REG * g + 17 * k + l] = v[k];
@@ -708,9 +703,15 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
   load(nxt, blockIdx.x);
   TC twc;
   twc.load_all(tab, lds + W * ROW, lane, thr, 640);
-  float2 w1[9];  // W_6000^{t k}, k = 1..9
+  // W_6000^{t k}, k = 1..9: only k = 1, 2, 4, 8 are held and the others are formed as products
+  // where they are applied, which leaves the registers to hold the filter H[k_a + 10 k_m] (this
+  // thread's outputs) across lines: 96 VGPRs, still two workgroups per CU
+  float2 w1[4];
 #pragma unroll
-  for (int k = 1; k < 10; ++k) w1[k - 1] = tab[6400 + (k - 1) * 640 + thr];
+  for (int i = 0; i < 4; ++i) w1[i] = tab[6400 + ((1 << i) - 1) * 640 + thr];
+  float2 h[10];
+#pragma unroll
+  for (int r = 0; r < 10; ++r) h[r] = tab[r * 640 + thr];
   __syncthreads();
   for (int64_t line = blockIdx.x; line < lines; line += stride) {
     float2 v[MaxRegs<M, 64, SL>::value];  // 12: the radix-6 pass gives some lanes two butterflies
@@ -723,8 +724,7 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
     }
     // ---- forward: stage a
     Dft<10, -1>::run(v);
-#pragma unroll
-    for (int k = 1; k < 10; ++k) v[k] = cmul(v[k], w1[k - 1]);
+    twiddle16_derived<false, 10>(v, w1);
     if (act) {
 #pragma unroll
       for (int k = 0; k < 10; ++k) lds[k * ROW + t] = v[k];
@@ -738,12 +738,6 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
       }
     }
     PassesCached<M, 64, -1, 1, SL, true>::run(v, row, twc, lane);
-    float2 h[10];
-    {
-      const float2* hl = opaque(tab);
-#pragma unroll
-      for (int r = 0; r < 10; ++r) h[r] = hl[r * 640 + thr];
-    }
     // ---- filter (carries 1/N)
 #pragma unroll
     for (int r = 0; r < 10; ++r) v[r] = cmul(v[r], h[r]);
@@ -763,12 +757,7 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
         v[k] = lds[k * ROW + t];
       }
     }
-#pragma unroll
-    for (int k = 1; k < 10; ++k) {
-      float2 w = w1[k - 1];
-      w.y = -w.y;
-      v[k] = cmul(v[k], w);
-    }
+    twiddle16_derived<true, 10>(v, w1);
     Dft<10, +1>::run(v);
     {
       const __amdgpu_buffer_rsrc_t rs = rsrc(out, line);
