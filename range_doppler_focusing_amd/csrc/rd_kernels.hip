@@ -597,10 +597,18 @@ __global__ void __launch_bounds__(1024)
       v[r] = row[lane + 64 * r];
     }
     if constexpr (HALF) load(nxt, line + stride);
-    PassesCached<M, 64, -1, 1, SL, true>::run(v, row, twc, lane);
-    // the filter for this thread's outputs (the other waves cover the cache latency)
+    // the filter for this thread's outputs: float32 issues its loads before the forward sub-line
+    // transform, which then covers their cache latency (915 -> 910 us per 16384^2 launch); the
+    // binary16 form, whose prefetch is in flight there, loads it after (earlier, it spills)
+    constexpr bool HEARLY = !HALF;
     float2 h[16];
-    {
+    if constexpr (HEARLY) {
+      const float2* hl = opaque(tab);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) h[r] = hl[r * 1024 + t];
+    }
+    PassesCached<M, 64, -1, 1, SL, true>::run(v, row, twc, lane);
+    if constexpr (!HEARLY) {
       const float2* hl = opaque(tab);
 #pragma unroll
       for (int r = 0; r < 16; ++r) h[r] = hl[r * 1024 + t];
