@@ -535,12 +535,14 @@ __global__ void __launch_bounds__(256, 4)
 #ifndef RD_RC_16384_HALF
 #define RD_RC_16384_HALF 1  // binary16 storage through the same kernel (else the Stockham kernel)
 #endif
-constexpr int kRc16kTab = 16 * 1024 + 15 * 1024;
+// the filter in the order the threads hold it, then W_16384^{t k} for k = 1, 2, 4, 8 (the kernel
+// forms the other eleven stage-a twiddles as products)
+constexpr int kRc16kTab = 16 * 1024 + 4 * 1024;
 void rc16k_tab_fill(const float2* H, const float2* roots, float2* out) {
   for (int r = 0; r < 16; ++r)
     for (int t = 0; t < 1024; ++t) out[r * 1024 + t] = H[(t >> 6) + 16 * (t & 63) + 1024 * r];
-  for (int k = 1; k < 16; ++k)
-    for (int t = 0; t < 1024; ++t) out[16384 + (k - 1) * 1024 + t] = roots[(t * k) & 16383];
+  for (int i = 0; i < 4; ++i)
+    for (int t = 0; t < 1024; ++t) out[16384 + i * 1024 + t] = roots[(t << i) & 16383];
 }
 
 template <int SAUX, bool HALF = false>
@@ -574,7 +576,7 @@ __global__ void __launch_bounds__(1024)
   constexpr int NW = 4;
   float2 w1[NW];
 #pragma unroll
-  for (int i = 0; i < NW; ++i) w1[i] = tab[16384 + ((1 << i) - 1) * 1024 + t];
+  for (int i = 0; i < NW; ++i) w1[i] = tab[16384 + i * 1024 + t];
   __syncthreads();
   for (int64_t line = blockIdx.x; line < lines; line += stride) {
     float2 v[16];
@@ -659,15 +661,17 @@ __global__ void __launch_bounds__(1024)
 #ifndef RD_RC6000_WPE
 #define RD_RC6000_WPE 5
 #endif
-constexpr int kRc6kTab = 10 * 640 + 9 * 640;
+// the filter in the order the threads hold it, then W_6000^{t k} for k = 1, 2, 4, 8 (the kernel
+// forms the other five stage-a twiddles as products)
+constexpr int kRc6kTab = 10 * 640 + 4 * 640;
 void rc6k_tab_fill(const float2* H, const float2* roots, float2* out) {
   for (int r = 0; r < 10; ++r)
     for (int t = 0; t < 640; ++t) {
       const int w = t >> 6, l = t & 63;
       out[r * 640 + t] = l < 60 ? H[w + 10 * (l + 60 * r)] : make_float2(0.f, 0.f);
     }
-  for (int k = 1; k < 10; ++k)
-    for (int t = 0; t < 640; ++t) out[6400 + (k - 1) * 640 + t] = t < 600 ? roots[(t * k) % 6000] : make_float2(1.f, 0.f);
+  for (int i = 0; i < 4; ++i)
+    for (int t = 0; t < 640; ++t) out[6400 + i * 640 + t] = t < 600 ? roots[(t << i) % 6000] : make_float2(1.f, 0.f);
 }
 
 template <int SAUX, bool HALF = false>
@@ -716,7 +720,7 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
   // thread's outputs) across lines: 96 VGPRs, still two workgroups per CU
   float2 w1[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w1[i] = tab[6400 + ((1 << i) - 1) * 640 + thr];
+  for (int i = 0; i < 4; ++i) w1[i] = tab[6400 + i * 640 + thr];
   float2 h[10];
 #pragma unroll
   for (int r = 0; r < 10; ++r) h[r] = tab[r * 640 + thr];
