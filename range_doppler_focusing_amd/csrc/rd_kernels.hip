@@ -293,7 +293,7 @@ typedef float rdf_v4f __attribute__((ext_vector_type(4)));
 // (the base roots pass through an empty asm statement, so the products are formed at every
 // application instead of being hoisted out of a line loop into fifteen live registers)
 template <bool CONJ, int K = 16>
-__device__ __forceinline__ void twiddle16_derived(float2* x, const float2* w2) {
+__device__ __forceinline__ void twiddles_from_powers(float2* x, const float2* w2) {
   float2 p[K];
 #pragma unroll
   for (int k = 1; k < K; ++k) {
@@ -370,7 +370,7 @@ __global__ void __launch_bounds__(256, 4)
     // ---- forward
     Dft<16, -1>::run(v);
     if constexpr (DER) {
-      twiddle16_derived<false>(v, w1);
+      twiddles_from_powers<false>(v, w1);
     } else {
 #pragma unroll
       for (int k = 1; k < 16; ++k) v[k] = cmul(v[k], w1[k - 1]);
@@ -495,7 +495,7 @@ __global__ void __launch_bounds__(256, 4)
       v[k] = lds[REG * k + t];
     }
     if constexpr (DER) {
-      twiddle16_derived<true>(v, w1);
+      twiddles_from_powers<true>(v, w1);
     } else {
 #pragma unroll
       for (int k = 1; k < 16; ++k) {
@@ -589,7 +589,7 @@ __global__ void __launch_bounds__(1024)
     }
     // ---- forward: stage a
     Dft<16, -1>::run(v);
-    twiddle16_derived<false>(v, w1);
+    twiddles_from_powers<false>(v, w1);
 #pragma unroll
     for (int k = 0; k < 16; ++k) lds[k * ROW + t] = v[k];
     __syncthreads();
@@ -630,7 +630,7 @@ __global__ void __launch_bounds__(1024)
       const int k = dft_input_order<16>(i);
       v[k] = lds[k * ROW + t];
     }
-    twiddle16_derived<true>(v, w1);
+    twiddles_from_powers<true>(v, w1);
     Dft<16, +1>::run(v);
     if constexpr (HALF)
       store_line_h<N, T, 16, SAUX>(v, LineIOh(out, N, line, 1, lines), 0, t);
@@ -736,7 +736,7 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
     }
     // ---- forward: stage a
     Dft<10, -1>::run(v);
-    twiddle16_derived<false, 10>(v, w1);
+    twiddles_from_powers<false, 10>(v, w1);
     if (act) {
 #pragma unroll
       for (int k = 0; k < 10; ++k) lds[k * ROW + t] = v[k];
@@ -769,7 +769,7 @@ __global__ void __launch_bounds__(640, RD_RC6000_WPE)
         v[k] = lds[k * ROW + t];
       }
     }
-    twiddle16_derived<true, 10>(v, w1);
+    twiddles_from_powers<true, 10>(v, w1);
     Dft<10, +1>::run(v);
     {
       const __amdgpu_buffer_rsrc_t rs = rsrc(out, line);
