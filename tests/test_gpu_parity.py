@@ -1076,6 +1076,36 @@ def test_entry_points_replay_from_a_captured_graph(torch_dev, rdf):
         del g
 
 
+@pytest.mark.parametrize("n", [4096, 6000, 16384], ids=lambda v: str(v))
+def test_range_compression_plans_alternating_on_one_stream(torch_dev, rdf, n):
+    """The persistent range kernels load their plan's filter and twiddles once per launch and hold
+    them across lines: launches of two plans with different replicas (Hamming and rectangular
+    windows, different pulse lengths), alternating back to back on one stream, each give exactly
+    the result of their own plan computed alone."""
+    torch = torch_dev
+    lines = 300 if n < 16384 else 96
+    base = C2.with_(Na=lines, Nr=n, fs_hz=C2.fs_hz * n / 4096)
+    pa_params = base.plan_params()
+    pb_params = dict(base.with_(pulse_s=base.pulse_s / 2).plan_params(), range_window=0)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn((lines, n), dtype=torch.complex64, device="cuda", generator=g)
+    with rdf.Plan(**pa_params) as pa, rdf.Plan(**pb_params) as pb:
+        ya, yb = pa.range_compress(x), pb.range_compress(x)
+        torch.cuda.synchronize()
+        assert not torch.equal(ya, yb)
+        s = torch.cuda.current_stream()
+        outs = []
+        for _ in range(4):
+            oa, ob = torch.empty_like(x), torch.empty_like(x)
+            rdf.rd_range_compress(pa.handle, x, oa, s)
+            rdf.rd_range_compress(pb.handle, x, ob, s)
+            outs.append((oa, ob))
+        torch.cuda.synchronize()
+        for oa, ob in outs:
+            assert torch.equal(oa, ya) and torch.equal(ob, yb)
+    log(f"[alternating] {n}: alternating plans give each plan's own result")
+
+
 def test_two_plans_on_two_streams_concurrently(torch_dev, rdf):
     """Two plans driven from two streams at once (range compression of one scene while another is
     focused, then omega-k): plans share no mutable device state, so each result equals the one
