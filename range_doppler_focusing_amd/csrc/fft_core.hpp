@@ -1184,7 +1184,7 @@ RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 8192, 1, false, false)
 RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, 1, false, false)
-RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 3, false, false)
+RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 3, true, false)
 RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, true, false, 8192, 4, true, true)
 RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, true, false, 16384, 1, true, true)
 #ifndef RD_CFG6000
