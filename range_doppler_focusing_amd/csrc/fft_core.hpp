@@ -1120,8 +1120,10 @@ struct LdsDouble<6000> {
 // powers of each root (PfLate/TwDerive above).  LATE: the prefetch is issued after the filter
 // multiply.  The long lines (8192, 16384: 512 / 1024 threads, at most 128 registers) need TWD
 // to fit a prefetch; measured on MI355X, prefetch + TWD + LATE is 5-7% faster there than no
-// prefetch.  At 4096, TWD would allow 4 waves per SIMD but its extra multiplies cancel the gain
-// (measured equal), so the full register sets stay.  6000 = 10 * 6 * 10 * 10 on 600 threads (at
+// prefetch.  At 2048 and 4096 TWD takes the padded range kernels (lines of any length) from two to
+// three workgroups per CU, or out of spilling (2048: 202 -> 163 registers, 16384 lines of 1200
+// samples 93 -> 90 us), and lets the omega-k row stage at 4096 fit three workgroups per CU.
+// (The 4096-point range kernel of the headline is a kernel of its own.)  6000 = 10 * 6 * 10 * 10 on 600 threads (at
 // most 12 points a thread) with the prefetch after the filter multiply and the filter read per
 // line: 142 registers and no spills, against 255 for 20 * 15 * 20 on 400 threads with the filter
 // in registers (measured on MI355X, 8192 lines: 301 against 335 us; the radix-20 butterflies
@@ -1183,7 +1185,7 @@ struct TwLdsBudget<600> {
 RDF_LINE_CFG(256, 16, L_16_16, L_16_16, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(512, 64, L_8_8_8, L_8_8_8, true, true, 4096, 1, false, false)
 RDF_LINE_CFG(1024, 64, L_16_4_16, L_16_4_16, true, true, 8192, 1, false, false)
-RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, 1, false, false)
+RDF_LINE_CFG(2048, 128, L_16_8_16, L_16_8_16, true, true, 4096, 1, true, false)
 RDF_LINE_CFG(4096, 256, L_16_16_16, L_16_16_16, true, true, 4096, 3, true, false)
 RDF_LINE_CFG(8192, 512, L_8_4_8_4_8, L_8_4_8_4_8, true, false, 8192, 4, true, true)
 RDF_LINE_CFG(16384, 1024, L_8_16_16_8, L_8_16_16_8, true, false, 16384, 1, true, true)
