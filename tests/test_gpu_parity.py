@@ -726,13 +726,20 @@ WK_C3AZ = C3.with_(name="wk_4096x512", Nr=512, pulse_s=1e-6, n_targets=3, noise_
 WK_6000 = C3.with_(name="wk_512x6000", Na=512, Nr=6000, n_targets=4)
 # 16384-sample rows on the 16384 x 16384 scene's platform, few enough pulses for the oracle
 WK_16K = C5.with_(name="wk_256x16384", Na=256, n_targets=3)
+# 2048- and 8192-sample rows on the 4096 x 4096 scene's platform
+WK_2K = C3.with_(name="wk_256x2048", Na=256, Nr=2048, n_targets=3)
+WK_8K = C3.with_(name="wk_256x8192", Na=256, Nr=8192, n_targets=3)
+# 256 pulses of platforms whose apertures span thousands: the azimuth response is wider than the
+# metric window, so only the peak and the range cut are compared there
+SHORT_APERTURE = (WK_16K, WK_2K, WK_8K)
 
 
 def wk_ref_bin(cfg) -> int:
     return int(round((cfg.r_ref_m - cfg.range_bin0_m) / cfg.dr))
 
 
-@pytest.mark.parametrize("cfg", [C1, WK_BIG, WK_C3AZ, WK_6000, WK_800, WK_997, WK_16K], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, WK_BIG, WK_C3AZ, WK_6000, WK_800, WK_997, WK_2K, WK_8K, WK_16K],
+                         ids=lambda c: c.name)
 def test_omega_k_matches_oracle(torch_dev, rdf, cfg):
     """rd_omega_k against the oracle at the scene's reference bin and at bin 0; in place gives
     the same bits; targets at the oracle's pixels with the same PSLR / ISLR."""
@@ -751,9 +758,8 @@ def test_omega_k_matches_oracle(torch_dev, rdf, cfg):
             want = O.omega_k(sc.echo, p, ref)
             check_stage(f"[omega-k] {cfg.name} ref_bin={ref}", got, want, IMAGE_TOL)
             if ref == wk_ref_bin(cfg):
-                # 256 pulses of a platform whose aperture spans 8192: the azimuth response is wider
-                # than the metric window, so only the peak and the range cut are compared there
-                check_targets(got, want, sc.targets, axes=("range",) if cfg is WK_16K else ("range", "azimuth"))
+                check_targets(got, want, sc.targets,
+                              axes=("range",) if cfg in SHORT_APERTURE else ("range", "azimuth"))
 
 
 def test_omega_k_full_airborne_scene(torch_dev, rdf):
@@ -834,7 +840,8 @@ def test_omega_k_error_paths(torch_dev, rdf):
         assert ei.value.status == -2
 
 
-@pytest.mark.parametrize("cfg", [C1, C3, WK_C3AZ, WK_6000, WK_800, WK_997, WK_16K], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, C3, WK_C3AZ, WK_6000, WK_800, WK_997, WK_2K, WK_8K, WK_16K],
+                         ids=lambda c: c.name)
 def test_omega_k_f16(torch_dev, rdf, cfg):
     """rd_omega_k_f16: the image divided by Na against the oracle on the same binary16 echo
     (five stored stages: two forward azimuth steps, the row stage, two inverse steps; within the
