@@ -1213,12 +1213,12 @@ __device__ __forceinline__ double sqrt_pos(double x) {
   return fma(fma(-s, s, x), h, s);
 }
 
-// At 4096 three workgroups share a CU (LDS 51 KB each) when the kernel fits 168 VGPRs: with the
-// per-sample loops fenced (TIGHT below) and the last pass's twiddles formed from powers it does,
-// spilling 28 B, 277.5-277.9 against 282.5-283.1 us at two workgroups (228 VGPRs) for the whole
-// 4096^2 omega-k.
+// At 2048 and 4096 three workgroups share a CU (LDS 50-51 KB each) when the kernel fits 168 VGPRs:
+// with the per-sample loops fenced (TIGHT below) and the last pass's twiddles formed from powers
+// it does, spilling 28-40 B.  Whole omega-k, against two workgroups per CU (207-228 VGPRs):
+// 4096^2 277.5-277.9 against 282.5-283.1 us, 4096 x 2048 143.6-143.8 against 146.9-147.0 us.
 template <int N, int AUX, bool HALF = false>
-__global__ void __launch_bounds__(LineCfg<N>::WG, (N == 4096 ? 3 : 1))
+__global__ void __launch_bounds__(LineCfg<N>::WG, (N == 2048 || N == 4096 ? 3 : 1))
     k_omega_k_row(const void* in, void* out, const float2* __restrict__ H,
                   const float2* __restrict__ tw, OkConst c, RcmcPoly w, int64_t rows) {
   using RIO = RowIO<HALF>;
@@ -1250,9 +1250,9 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, (N == 4096 ? 3 : 1))
     float2 v[C::P];
     // Where registers are tight, the rotation is hidden from the compiler once per row, so the
     // rotated offsets are formed where they are used instead of being hoisted out of the loop
-    // (32 registers for the whole kernel otherwise): that buys a wave per SIMD at 256, 512 and
-    // 4096 and cuts the spills at 6000 and 16384; elsewhere it only costs ~4% more instructions.
-    constexpr bool TIGHT = N <= 512 || N == 4096 || N == 6000 || N >= 16384;
+    // (32 registers for the whole kernel otherwise): that buys a wave per SIMD at 256, 512, 2048
+    // and 4096 and cuts the spills at 6000 and 16384; elsewhere it only costs ~4% more instructions.
+    constexpr bool TIGHT = N <= 512 || N == 2048 || N == 4096 || N == 6000 || N >= 16384;
     int rot = c.ref;
     if constexpr (TIGHT) asm volatile("" : "+s"(rot));
     // At 16384 (1024 threads: at most 128 registers) the per-sample loops below use a copy of
