@@ -242,12 +242,14 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
 //   b: DFT16 over n1 -> k1, times W_256^{n0 k1}             (thread 16 k0 + n0)
 //   c: DFT16 over n0 -> k2                                   (thread 16 k0 + k1)
 // and leaves X[k0 + 16 k1 + 256 k2] in thread 16 k0 + k1, which multiplies it by the filter
-// (held in that permuted order) and runs the inverse as the mirror image in
+// (held in registers in that permuted order for all the workgroup's lines) and runs the inverse
+// as the mirror image in
 // decimation-in-time order (c, b, a with conjugate roots, the twiddles before the DFTs), ending
 // with y[t + 256 n2] in thread t.  Steps b -> c and their mirror exchange data only inside a
 // group of 16 lanes (one wave), so they need no workgroup barrier; a -> b and its mirror are
-// workgroup exchanges, one barrier each (two per line).  Both directions use the same twiddles: W_4096^{t k0} in registers and
-// W_256^{n0 k1} in an LDS table.  LDS layout: region g = 0..15 of 272 elements (rows of 256 or
+// workgroup exchanges, one barrier each (two per line).  Both directions use the same twiddles:
+// W_4096^{t k0} in registers (float32 storage: the powers k0 = 1, 2, 4, 8, the others formed as
+// products; binary16: all fifteen) and W_256^{n0 k1} in an LDS table.  LDS layout: region g = 0..15 of 272 elements (rows of 256 or
 // 16 x 17, padded so that two 16-lane groups of a half-wave fall on complementary banks):
 // every exchange is free of bank conflicts under the gfx950 geometry (8-byte reads: 32 lanes
 // over 64 banks; 8-byte writes: 16 lanes over 32 banks).
