@@ -248,8 +248,9 @@ __global__ void __launch_bounds__(LineCfg<N>::WG, LineCfg<N>::WPE)
 // with y[t + 256 n2] in thread t.  Steps b -> c and their mirror exchange data only inside a
 // group of 16 lanes (one wave), so they need no workgroup barrier; a -> b and its mirror are
 // workgroup exchanges, one barrier each (two per line).  Both directions use the same twiddles:
-// W_4096^{t k0} in registers (float32 storage: the powers k0 = 1, 2, 4, 8, the others formed as
-// products; binary16: all fifteen) and W_256^{n0 k1} in an LDS table.  LDS layout: region g = 0..15 of 272 elements (rows of 256 or
+// W_4096^{t k0} in registers (the powers k0 = 1, 2, 4, 8, the others formed as products; the
+// matrix-core variant, which reads the plan's full table, holds all fifteen) and W_256^{n0 k1} in
+// an LDS table.  LDS layout: region g = 0..15 of 272 elements (rows of 256 or
 // 16 x 17, padded so that two 16-lane groups of a half-wave fall on complementary banks):
 // every exchange is free of bank conflicts under the gfx950 geometry (8-byte reads: 32 lanes
 // over 64 banks; 8-byte writes: 16 lanes over 32 banks).
